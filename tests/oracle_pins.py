@@ -1,0 +1,281 @@
+"""Pins of the reference oracle against facts that do not come from the oracle.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` and raises AssertionError if
+the oracle disagrees with a closed form, an invariant of the definition, a
+value the pages print, or a library routine that computes the same special
+case.  ``test_oracle.py`` runs them on the real oracle; ``test_oracle_mutants.py``
+runs them on deliberately broken builds of it and expects each break caught.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+from oracle import BF16, FP16
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """16-bit patterns of a bf16/fp16 tensor as a uint16 numpy array."""
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def _tdt(dtype):
+    return torch.bfloat16 if dtype == BF16 else torch.float16
+
+
+def rand_case(B, q_len, Hq, Hkv, D, S, seq_pos, dtype=BF16, seed=0, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    tdt = _tdt(dtype)
+    q = (torch.randn(B, q_len, Hq, D, generator=g) * scale).to(tdt)
+    kc = (torch.randn(B, Hkv, S, D, generator=g) * scale).to(tdt)
+    vc = (torch.randn(B, Hkv, S, D, generator=g) * scale).to(tdt)
+    kn = (torch.randn(B, q_len, Hkv, D, generator=g) * scale).to(tdt)
+    vn = (torch.randn(B, q_len, Hkv, D, generator=g) * scale).to(tdt)
+    sp = np.asarray(seq_pos, dtype=np.int32)
+    return q, kc, vc, kn, vn, sp
+
+
+# ---------------------------------------------------------------- decoding
+
+def pin_decode_bf16_all_patterns(orc):
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(pats.view(np.int16)).view(torch.bfloat16).double().numpy()
+    got = orc.decode(pats, BF16)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def pin_decode_fp16_all_patterns(orc):
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = pats.view(np.float16).astype(np.float64)
+    got = orc.decode(pats, FP16)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+# ---------------------------------------------------------------- append
+
+def pin_append_insert_slice_box(orc):
+    """The page's insert_slice box: [0, 0, offset, 0] + [1, 16, seq_len, 128]."""
+    gold = _golden("insert_slice_box.json")
+    B, H, S, D = gold["cache_shape"]
+    g = torch.Generator().manual_seed(7)
+    for case in gold["cases"]:
+        off, n = case["offset"], case["seq_len"]
+        kc = bits(torch.randn(B, H, S, D, generator=g).to(torch.bfloat16))
+        vc = bits(torch.randn(B, H, S, D, generator=g).to(torch.bfloat16))
+        # the page's block is [1, 16, seq_len, 128]; the oracle takes [B, q_len, Hkv, D]
+        blk_k = bits(torch.randn(1, H, n, D, generator=g).to(torch.bfloat16))
+        blk_v = bits(torch.randn(1, H, n, D, generator=g).to(torch.bfloat16))
+        kn = np.ascontiguousarray(blk_k.transpose(0, 2, 1, 3))
+        vn = np.ascontiguousarray(blk_v.transpose(0, 2, 1, 3))
+        k2, v2 = orc.kv_append(kc, vc, kn, vn, [off])
+        box = np.zeros((B, H, S, D), dtype=bool)
+        box[0:1, 0:H, off:off + n, 0:D] = True
+        for before, after, blk in ((kc, k2, blk_k), (vc, v2, blk_v)):
+            assert np.array_equal(after[~box], before[~box]), "element outside the box changed"
+            assert np.array_equal(after[box].reshape(1, H, n, D), blk), "box not written"
+
+
+def pin_append_ragged_batch(orc):
+    """Per-sequence offsets: sequence b gets its rows at seq_pos[b], nowhere else."""
+    B, q_len, Hkv, D, S = 3, 3, 2, 16, 20
+    q, kc, vc, kn, vn, sp = rand_case(B, q_len, 2, Hkv, D, S, [0, 9, 17])
+    kc, vc, kn, vn = bits(kc), bits(vc), bits(kn), bits(vn)
+    k2, v2 = orc.kv_append(kc, vc, kn, vn, sp)
+    for b in range(B):
+        for h in range(Hkv):
+            for s in range(S):
+                i = s - sp[b]
+                if 0 <= i < q_len:
+                    assert np.array_equal(k2[b, h, s], kn[b, i, h])
+                    assert np.array_equal(v2[b, h, s], vn[b, i, h])
+                else:
+                    assert np.array_equal(k2[b, h, s], kc[b, h, s])
+                    assert np.array_equal(v2[b, h, s], vc[b, h, s])
+
+
+# ---------------------------------------------------------------- attention
+
+def pin_one_key_context(orc):
+    """Only one visible key (seq_pos 0, one new token): every output row is that value row."""
+    for dtype in (BF16, FP16):
+        q, kc, vc, kn, vn, sp = rand_case(2, 1, 8, 2, 128, 16, [0, 0], dtype, seed=1)
+        k2, v2 = orc.kv_append(bits(kc), bits(vc), bits(kn), bits(vn), sp)
+        out = orc.gqa_decode(bits(q), k2, v2, sp, dtype)
+        vref = orc.decode(bits(vn), dtype)  # [B, 1, Hkv, D]
+        for hq in range(8):
+            assert np.array_equal(out[:, 0, hq, :], vref[:, 0, hq // 4, :])
+
+
+def pin_identical_keys_mean(orc):
+    """All visible keys equal: uniform weights, the output is the mean of the value rows."""
+    B, Hq, Hkv, D, S = 1, 4, 2, 128, 64
+    q, kc, vc, kn, vn, _ = rand_case(B, 1, Hq, Hkv, D, S, [0], seed=2)
+    kc[:] = kc[:, :, :1, :]
+    kn[:] = kc[:, :, :1, :].permute(0, 2, 1, 3)
+    ctx = 50
+    k2, v2 = orc.kv_append(bits(kc), bits(vc), bits(kn), bits(vn), [ctx - 1])
+    out = orc.gqa_decode(bits(q), k2, v2, [ctx - 1], BF16)
+    vdec = orc.decode(v2, BF16)
+    for hq in range(Hq):
+        mean = vdec[0, hq // 2, :ctx, :].sum(axis=0) / ctx
+        np.testing.assert_allclose(out[0, 0, hq], mean, rtol=1e-13, atol=1e-15)
+
+
+def pin_weights_sum_to_one(orc):
+    q, kc, vc, kn, vn, sp = rand_case(2, 3, 6, 3, 32, 40, [10, 36], seed=3)
+    k2, v2 = orc.kv_append(bits(kc), bits(vc), bits(kn), bits(vn), sp)
+    out, w = orc.gqa_decode(bits(q), k2, v2, sp, BF16, with_weights=True)
+    assert np.all(np.abs(w.sum(axis=-1) - 1.0) <= 1e-13)
+    assert np.all(w >= 0.0)
+    for b in range(2):
+        for i in range(3):
+            assert np.all(w[b, i, :, sp[b] + i + 1:] == 0.0)
+            assert np.all(w[b, i, :, :sp[b] + i + 1] > 0.0)
+
+
+def pin_causal_mask_table(orc):
+    """Visibility pattern equals the page's LessOrEqual/Less mask, worked out by hand."""
+    gold = _golden("causal_mask_table.json")
+    p, n, S = gold["seq_pos"], gold["q_len"], gold["cache_len"]
+    q, kc, vc, kn, vn, _ = rand_case(1, n, 2, 1, 8, S, [p], seed=4, scale=0.25)
+    k2, v2 = orc.kv_append(bits(kc), bits(vc), bits(kn), bits(vn), [p])
+    _, w = orc.gqa_decode(bits(q), k2, v2, [p], BF16, with_weights=True)
+    vis = np.asarray(gold["visible"], dtype=bool)
+    for hq in range(2):
+        assert np.array_equal(w[0, :, hq, :] > 0.0, vis)
+
+
+def pin_closed_form_three_keys(orc):
+    gold = _golden("closed_form_three_keys.json")
+    D = gold["head_dim"]
+    e = math.e
+    vals = np.asarray(gold["values"], dtype=np.float64)
+    expect = (vals[0] + e * vals[1] + e * e * vals[2]) / (1.0 + e + e * e)
+    for dtype in (BF16, FP16):
+        tdt = _tdt(dtype)
+        q = torch.tensor(gold["q"]).reshape(1, 1, 1, D).to(tdt)
+        kc = torch.zeros(1, 1, 4, D)
+        vc = torch.zeros(1, 1, 4, D)
+        kc[0, 0, :2] = torch.tensor(gold["keys"][:2])
+        vc[0, 0, :2] = torch.tensor(gold["values"][:2])
+        kn = torch.tensor(gold["keys"][2]).reshape(1, 1, 1, D)
+        vn = torch.tensor(gold["values"][2]).reshape(1, 1, 1, D)
+        kc[0, 0, 3] = float("nan")  # beyond the context: must not matter
+        vc[0, 0, 3] = float("nan")
+        k2, v2 = orc.kv_append(bits(kc.to(tdt)), bits(vc.to(tdt)), bits(kn.to(tdt)),
+                               bits(vn.to(tdt)), [2])
+        out = orc.gqa_decode(bits(q), k2, v2, [2], dtype)
+        np.testing.assert_allclose(out[0, 0, 0], expect, rtol=2e-15, atol=1e-15)
+
+
+def pin_gqa_equals_mha_repeated(orc):
+    """Query head hq uses KV head hq // (Hq/Hkv): same as MHA over repeat-interleaved KV heads."""
+    B, q_len, Hq, Hkv, D, S = 2, 2, 8, 2, 32, 24
+    q, kc, vc, kn, vn, sp = rand_case(B, q_len, Hq, Hkv, D, S, [5, 21], seed=5)
+    G = Hq // Hkv
+    k2, v2 = orc.kv_append(bits(kc), bits(vc), bits(kn), bits(vn), sp)
+    out = orc.gqa_decode(bits(q), k2, v2, sp, BF16)
+    k_rep = np.ascontiguousarray(np.repeat(k2, G, axis=1))
+    v_rep = np.ascontiguousarray(np.repeat(v2, G, axis=1))
+    out_mha = orc.gqa_decode(bits(q), k_rep, v_rep, sp, BF16)
+    assert np.array_equal(out, out_mha)
+
+
+def pin_torch_sdpa_float64(orc):
+    """Special case computed by a library: torch's CPU SDPA in float64 with enable_gqa."""
+    B, q_len, Hq, Hkv, D, S = 2, 3, 8, 2, 64, 48
+    q, kc, vc, kn, vn, sp = rand_case(B, q_len, Hq, Hkv, D, S, [7, 44], seed=6)
+    k2, v2 = orc.kv_append(bits(kc), bits(vc), bits(kn), bits(vn), sp)
+    out = orc.gqa_decode(bits(q), k2, v2, sp, BF16)
+    qd = q.double().permute(0, 2, 1, 3)                        # [B, Hq, q_len, D]
+    kd = torch.from_numpy(k2.view(np.int16)).view(torch.bfloat16).double()  # [B, Hkv, S, D]
+    vd = torch.from_numpy(v2.view(np.int16)).view(torch.bfloat16).double()
+    j = torch.arange(S)
+    for b in range(B):
+        tpos = sp[b] + torch.arange(q_len)
+        mask = (j[None, :] <= tpos[:, None]) & (j[None, :] < sp[b] + q_len)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qd[b:b + 1], kd[b:b + 1], vd[b:b + 1], attn_mask=mask[None, None], enable_gqa=True)
+        ref = ref.permute(0, 2, 1, 3).numpy()[0]
+        np.testing.assert_allclose(out[b], ref, rtol=1e-12, atol=1e-12)
+
+
+def pin_causal_prefix(orc):
+    """Query token 0 of a 4-token verify sees exactly what a 1-token step at the same slot sees."""
+    B, Hq, Hkv, D, S, p = 1, 4, 1, 64, 32, 20
+    q, kc, vc, kn, vn, _ = rand_case(B, 4, Hq, Hkv, D, S, [p], seed=8)
+    k4, v4 = orc.kv_append(bits(kc), bits(vc), bits(kn), bits(vn), [p])
+    out4 = orc.gqa_decode(bits(q), k4, v4, [p], BF16)
+    k1, v1 = orc.kv_append(bits(kc), bits(vc), bits(kn[:, :1]), bits(vn[:, :1]), [p])
+    out1 = orc.gqa_decode(bits(q[:, :1]), k1, v1, [p], BF16)
+    assert np.array_equal(out4[:, 0], out1[:, 0])
+    # and the later draft tokens see more keys, so their rows differ
+    assert not np.array_equal(out4[:, 3], out1[:, 0])
+
+
+def pin_value_homogeneity(orc):
+    """Doubling every value row doubles the output exactly (powers of two are exact)."""
+    q, kc, vc, kn, vn, sp = rand_case(1, 2, 4, 2, 32, 16, [9], seed=9)
+    k2, v2 = orc.kv_append(bits(kc), bits(vc), bits(kn), bits(vn), sp)
+    out = orc.gqa_decode(bits(q), k2, v2, sp, BF16)
+    _, v2x = orc.kv_append(bits(kc), bits(vc * 2), bits(kn), bits(vn * 2), sp)
+    out2 = orc.gqa_decode(bits(q), k2, v2x, sp, BF16)
+    assert np.array_equal(out2, 2.0 * out)
+
+
+def pin_key_permutation_invariance(orc):
+    """Reordering the (key, value) rows of the context leaves a one-token step unchanged."""
+    S, ctx = 64, 57
+    q, kc, vc, kn, vn, _ = rand_case(1, 1, 4, 2, 64, S, [ctx - 1], seed=10)
+    k2, v2 = orc.kv_append(bits(kc), bits(vc), bits(kn), bits(vn), [ctx - 1])
+    out = orc.gqa_decode(bits(q), k2, v2, [ctx - 1], BF16)
+    perm = np.random.default_rng(0).permutation(ctx)
+    k3, v3 = k2.copy(), v2.copy()
+    k3[:, :, :ctx] = k2[:, :, perm]
+    v3[:, :, :ctx] = v2[:, :, perm]
+    out3 = orc.gqa_decode(bits(q), k3, v3, [ctx - 1], BF16)
+    np.testing.assert_allclose(out3, out, rtol=1e-13, atol=1e-14)
+
+
+def pin_beyond_context_and_future_rows(orc):
+    """Rows past the context never matter; a later draft token's row is hidden from earlier ones."""
+    S, p = 32, 12
+    q, kc, vc, kn, vn, _ = rand_case(1, 2, 2, 1, 16, S, [p], seed=11)
+    k2, v2 = orc.kv_append(bits(kc), bits(vc), bits(kn), bits(vn), [p])
+    out = orc.gqa_decode(bits(q), k2, v2, [p], BF16)
+    nan, inf = np.uint16(0x7fc0), np.uint16(0x7f80)
+    k3, v3 = k2.copy(), v2.copy()
+    k3[:, :, p + 2:] = nan
+    v3[:, :, p + 2:] = inf
+    assert np.array_equal(orc.gqa_decode(bits(q), k3, v3, [p], BF16), out)
+    v4 = v2.copy()
+    v4[:, :, p + 1] = nan  # the second draft token's value row
+    out4 = orc.gqa_decode(bits(q), k2, v4, [p], BF16)
+    assert np.array_equal(out4[:, 0], out[:, 0])
+    assert np.all(np.isnan(out4[:, 1]))
+
+
+def pin_rows_api_matches_full(orc):
+    q, kc, vc, kn, vn, sp = rand_case(2, 2, 4, 2, 32, 20, [3, 17], seed=12)
+    k2, v2 = orc.kv_append(bits(kc), bits(vc), bits(kn), bits(vn), sp)
+    out = orc.gqa_decode(bits(q), k2, v2, sp, BF16)
+    rows = np.array([[0, 0, 0], [1, 1, 3], [1, 0, 2], [0, 1, 1]])
+    got = orc.gqa_decode_rows(bits(q), k2, v2, sp, rows, BF16)
+    for n, (b, i, hq) in enumerate(rows):
+        assert np.array_equal(got[n], out[b, i, hq])
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
