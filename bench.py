@@ -1,0 +1,207 @@
+#!/usr/bin/env python3
+"""Throughput of one decode step of GQA attention with KV append on one MI355X.
+
+A step is the whole path over one batch: for every layer, da_kv_append,
+da_gqa_decode_attn and da_gqa_decode_attn_combine, enqueued on one stream.
+The default workload is batched GQA decode with Hq 16 / Hkv 8 / head_dim 128,
+batch 32, context 8192, 28 layers (bf16, synthetic N(0,1)*0.5 inputs resident
+in HBM before timing starts).
+
+Prints ONE JSON line: KV GB/s (algorithmic bytes per step / step time), ms per
+step, the attention kernel's roofline fraction against the 8 TB/s HBM peak
+(its average duration measured with HIP events on the launch stream during
+the timed steps), and the fp64 CPU oracle's rate on a bounded sample of the
+same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--chunk", type=int, default=0, help="chunk_tokens override (0 = automatic)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time budget of the oracle sample")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(w, seq_pos):
+    """Bytes the step must move at least, per layer: K+V of the visible context read once,
+    q read, out written, new K/V read and written into the cache."""
+    E, D = 2, w.head_dim
+    ctx = [int(s) + w.q_len for s in seq_pos]
+    kv = 2 * w.n_kv_heads * sum(ctx) * D * E
+    q_out = 2 * w.batch * w.q_len * w.n_q_heads * D * E
+    append = 2 * 2 * w.batch * w.q_len * w.n_kv_heads * D * E
+    return kv, kv + q_out + append
+
+
+def counters_for(kernel_tag, workload):
+    """HBM traffic per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; else None."""
+    import hashlib
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                        f"counters_{kernel_tag}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "decode_attention_append_amd",
+                       "csrc", rec.get("source", ""))
+    if not os.path.exists(src):
+        return None
+    h = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if h != rec.get("source_sha256"):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, layers_host_fn, n_layers, budget_s):
+    """The oracle (append + attention, fp64, OpenMP) on whole layers of the workload until
+    about budget_s of CPU time is spent; returns the record for the JSON line."""
+    import numpy as np
+    import oracle
+    done_bytes, spent, n = 0, 0.0, 0
+    for layer in range(n_layers):
+        q, kc, vc, kn, vn, sp = layers_host_fn(layer)
+        t = time.perf_counter()
+        k2, v2 = oracle.kv_append(kc, vc, kn, vn, sp)
+        oracle.gqa_decode(q, k2, v2, sp, oracle.FP16 if w.dtype == "fp16" else oracle.BF16)
+        spent += time.perf_counter() - t
+        done_bytes += algorithmic_bytes(w, sp)[1]
+        n += 1
+        del k2, v2, kc, vc
+        if spent >= budget_s:
+            break
+    return {"value": done_bytes / spent / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{n} of {w.layers} layers of {w.name}, every sequence and head, "
+                      f"append + attention in fp64 ({spent:.1f} s)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the step shards by sequence or KV head with no exchange; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import decode_attention_append_amd as da
+    from decode_attention_append_amd.workloads import BENCH_WORKLOAD, WORKLOADS, make_layer
+
+    w = WORKLOADS[args.workload or BENCH_WORKLOAD]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] workload {w.name}: building {w.layers} layers on {torch.cuda.get_device_name(0)}",
+          file=sys.stderr, flush=True)
+
+    layers = [make_layer(w, l, dev) for l in range(w.layers)]
+    seq_pos = layers[0]["seq_pos"].cpu().numpy()
+    p = da.problem(w.batch, w.q_len, w.n_q_heads, w.n_kv_heads, w.head_dim, w.max_seq, w.dtype,
+                   chunk_tokens=args.chunk)
+    plan = da.plan_attention(p)
+    ws = da.new_workspace(p)
+    outs = [torch.empty_like(L["q"]) for L in layers]
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        for l, L in enumerate(layers):
+            da.kv_append(p, L["k_cache"], L["v_cache"], L["k_new"], L["v_new"], L["seq_pos"], stream)
+            if events is not None:
+                events[l][0].record(stream)
+            da.gqa_decode_attn(p, L["q"], L["k_cache"], L["v_cache"], L["seq_pos"], ws, stream)
+            if events is not None:
+                events[l][1].record(stream)
+            da.gqa_decode_attn_combine(p, ws, L["seq_pos"], outs[l], stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, HIP events around every attention launch on the launch stream
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+           for _ in range(w.layers)] for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for k in range(args.steps):
+        step(ev[k])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    attn_ms = [e0.elapsed_time(e1) for evk in ev for (e0, e1) in evk]
+
+    ms_per_step = ms_total / args.steps
+    kv_bytes, alg_bytes = algorithmic_bytes(w, seq_pos)
+    step_bytes = alg_bytes * w.layers
+    gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # dominant kernel: the split-context attention; its algorithmic bytes per launch are the
+    # K+V of the visible context (512 bytes per visible key per KV head) plus q
+    attn_avg_ms = float(np.mean(attn_ms))
+    attn_bytes = kv_bytes + w.batch * w.q_len * w.n_q_heads * w.head_dim * 2
+    attn_gbs = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
+    kernel_tag = "attn_split_" + plan["variant"]
+    traffic = counters_for(kernel_tag, w.name)
+
+    rec = {
+        "metric": "decode-attention KV GB/s (% of HBM peak) + us/step, Hq16/Hkv8/d128 ctx 8k",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "q_len": w.q_len, "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "context": int(seq_pos.max()) + w.q_len,
+                   "max_seq": w.max_seq, "layers": w.layers, "chunk_tokens": plan["chunk_tokens"],
+                   "variant": plan["variant"], "bytes_per_step": step_bytes},
+        "roofline": {"bound": "hbm", "kernel": kernel_tag, "achieved": round(attn_gbs, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+                     "avg_launch_us": round(attn_avg_ms * 1e3, 3), "bytes_per_launch": attn_bytes,
+                     "traffic": traffic},
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on a sample", file=sys.stderr, flush=True)
+
+        def host_layer_fn(l):
+            L = layers[l]
+
+            def u16(t):
+                return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+            return (u16(L["q"]), u16(L["k_cache"]), u16(L["v_cache"]), u16(L["k_new"]),
+                    u16(L["v_new"]), L["seq_pos"].cpu().numpy())
+        rec["cpu_baseline"] = cpu_baseline(w, host_layer_fn, w.layers, args.cpu_seconds)
+
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

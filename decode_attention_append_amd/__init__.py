@@ -1,0 +1,209 @@
+"""MI355X-native decode attention with KV-cache append.
+
+Thin ctypes binding over the C ABI in ``include/decode_attn.h`` (library
+``libdecode_attn.so``, built by ``build_lib.py``).  The functions here only
+marshal arguments: check that tensors are on the GPU, contiguous and of the
+declared shape and type, then pass raw device pointers and the current HIP
+stream.  Every step of the computation runs in the library's HIP kernels;
+there is no fallback of any kind, and importing the binding fails loudly if
+the library has not been built.
+
+Names follow the C entry points without their ``da_`` prefix:
+``kv_append``, ``gqa_decode_attn``, ``gqa_decode_attn_combine``,
+``workspace_bytes``, ``plan_attention``.
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+from . import workloads  # noqa: F401  (seeded input generator, no method arithmetic)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdecode_attn.so")
+
+DA_OK, DA_ERR_INVALID_ARG, DA_ERR_UNSUPPORTED, DA_ERR_WORKSPACE, DA_ERR_HIP = 0, -1, -2, -3, -4
+DA_BF16, DA_FP16 = 0, 1
+VARIANTS = {0: "valu", 1: "mfma"}
+_DTYPE_CODE = {torch.bfloat16: DA_BF16, torch.float16: DA_FP16}
+
+
+class DecodeAttnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_str(status)} (status {status})")
+        self.status = status
+
+
+class Problem(ctypes.Structure):
+    """Mirror of ``da_problem``."""
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("q_len", ctypes.c_int32),
+        ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("max_seq", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("chunk_tokens", ctypes.c_int32),
+    ]
+
+    def __repr__(self):
+        f = ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_)
+        return f"Problem({f})"
+
+
+class Plan(ctypes.Structure):
+    """Mirror of ``da_plan``."""
+    _fields_ = [
+        ("chunk_tokens", ctypes.c_int32),
+        ("n_chunks", ctypes.c_int32),
+        ("rows", ctypes.c_int32),
+        ("variant", ctypes.c_int32),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+EXPORTS = ("da_plan_attention", "da_workspace_bytes", "da_kv_append", "da_gqa_decode_attn",
+           "da_gqa_decode_attn_combine", "da_status_str")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with 'python -m decode_attention_append_amd.build_lib' "
+            "(the HIP library is required; there is no fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz, i32p = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p
+    pp = ctypes.POINTER(Problem)
+    lib.da_plan_attention.argtypes = [pp, ctypes.POINTER(Plan)]
+    lib.da_plan_attention.restype = ctypes.c_int
+    lib.da_workspace_bytes.argtypes = [pp]
+    lib.da_workspace_bytes.restype = sz
+    lib.da_kv_append.argtypes = [pp, vp, vp, vp, vp, i32p, vp]
+    lib.da_kv_append.restype = ctypes.c_int
+    lib.da_gqa_decode_attn.argtypes = [pp, vp, vp, vp, i32p, vp, sz, vp]
+    lib.da_gqa_decode_attn.restype = ctypes.c_int
+    lib.da_gqa_decode_attn_combine.argtypes = [pp, vp, sz, i32p, vp, vp]
+    lib.da_gqa_decode_attn_combine.restype = ctypes.c_int
+    lib.da_status_str.argtypes = [ctypes.c_int]
+    lib.da_status_str.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+def status_str(status: int) -> str:
+    return lib.da_status_str(status).decode()
+
+
+def problem(batch, q_len, n_q_heads, n_kv_heads, head_dim, max_seq, dtype, scale=0.0,
+            chunk_tokens=0) -> Problem:
+    if isinstance(dtype, torch.dtype):
+        dtype = _DTYPE_CODE[dtype]
+    elif isinstance(dtype, str):
+        dtype = {"bf16": DA_BF16, "fp16": DA_FP16}[dtype]
+    return Problem(batch, q_len, n_q_heads, n_kv_heads, head_dim, max_seq, dtype, float(scale),
+                   chunk_tokens)
+
+
+def problem_for(q: torch.Tensor, k_cache: torch.Tensor, scale=0.0, chunk_tokens=0) -> Problem:
+    """The problem described by q [B, q_len, Hq, D] and a cache [B, Hkv, S, D]."""
+    B, q_len, Hq, D = q.shape
+    _, Hkv, S, _ = k_cache.shape
+    return problem(B, q_len, Hq, Hkv, D, S, q.dtype, scale, chunk_tokens)
+
+
+def plan_attention(p: Problem) -> dict:
+    pl = Plan()
+    st = lib.da_plan_attention(ctypes.byref(p), ctypes.byref(pl))
+    if st != DA_OK:
+        raise DecodeAttnError(st, "da_plan_attention")
+    return {"chunk_tokens": pl.chunk_tokens, "n_chunks": pl.n_chunks, "rows": pl.rows,
+            "variant": VARIANTS[pl.variant], "workspace_bytes": pl.workspace_bytes}
+
+
+def workspace_bytes(p: Problem) -> int:
+    return lib.da_workspace_bytes(ctypes.byref(p))
+
+
+def new_workspace(p: Problem, device="cuda") -> torch.Tensor:
+    """A uint8 device buffer of workspace_bytes(p) (allocated by torch, owned by the caller)."""
+    n = workspace_bytes(p)
+    if n == 0:
+        raise DecodeAttnError(DA_ERR_INVALID_ARG, "workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _dev(t: torch.Tensor, name: str, shape=None, dtype=None) -> ctypes.c_void_p:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _elem(p: Problem):
+    return torch.float16 if p.dtype == DA_FP16 else torch.bfloat16
+
+
+def kv_append(p: Problem, k_cache, v_cache, k_new, v_new, seq_pos, stream=None):
+    """da_kv_append: k_cache[b, h, seq_pos[b] + i] = k_new[b, i, h] (and V), in place."""
+    e = _elem(p)
+    cs = (p.batch, p.n_kv_heads, p.max_seq, p.head_dim)
+    ns = (p.batch, p.q_len, p.n_kv_heads, p.head_dim)
+    st = lib.da_kv_append(ctypes.byref(p), _dev(k_cache, "k_cache", cs, e), _dev(v_cache, "v_cache", cs, e),
+                          _dev(k_new, "k_new", ns, e), _dev(v_new, "v_new", ns, e),
+                          _dev(seq_pos, "seq_pos", (p.batch,), torch.int32), _stream(stream))
+    if st != DA_OK:
+        raise DecodeAttnError(st, "da_kv_append")
+
+
+def gqa_decode_attn(p: Problem, q, k_cache, v_cache, seq_pos, workspace, stream=None):
+    """da_gqa_decode_attn: fp32 split-context partials into ``workspace``."""
+    e = _elem(p)
+    cs = (p.batch, p.n_kv_heads, p.max_seq, p.head_dim)
+    st = lib.da_gqa_decode_attn(ctypes.byref(p),
+                                _dev(q, "q", (p.batch, p.q_len, p.n_q_heads, p.head_dim), e),
+                                _dev(k_cache, "k_cache", cs, e), _dev(v_cache, "v_cache", cs, e),
+                                _dev(seq_pos, "seq_pos", (p.batch,), torch.int32),
+                                _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                                _stream(stream))
+    if st != DA_OK:
+        raise DecodeAttnError(st, "da_gqa_decode_attn")
+
+
+def gqa_decode_attn_combine(p: Problem, workspace, seq_pos, out, stream=None):
+    """da_gqa_decode_attn_combine: merge the partials into ``out`` [B, q_len, Hq, D]."""
+    e = _elem(p)
+    st = lib.da_gqa_decode_attn_combine(
+        ctypes.byref(p), _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _dev(seq_pos, "seq_pos", (p.batch,), torch.int32),
+        _dev(out, "out", (p.batch, p.q_len, p.n_q_heads, p.head_dim), e), _stream(stream))
+    if st != DA_OK:
+        raise DecodeAttnError(st, "da_gqa_decode_attn_combine")
+
+
+def decode_step(p: Problem, q, k_cache, v_cache, k_new, v_new, seq_pos, workspace, out, stream=None):
+    """The three calls of one decode step, in order, on one stream."""
+    kv_append(p, k_cache, v_cache, k_new, v_new, seq_pos, stream)
+    gqa_decode_attn(p, q, k_cache, v_cache, seq_pos, workspace, stream)
+    gqa_decode_attn_combine(p, workspace, seq_pos, out, stream)
+
+
+def default_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)

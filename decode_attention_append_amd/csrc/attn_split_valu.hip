@@ -1,0 +1,234 @@
+// Split-context attention partials on the vector ALU, for problems whose
+// query rows per KV head (Hq/Hkv * q_len) are fewer than 16.
+//
+// What is computed ("Qwen MoE BringUp", Per-Layer IR Patterns, "Attention
+// Computation", split as in the split-KV phase of the 3-phase flash decode in
+// "Architecture Diagram - Qwen3-30B-A3B (Extern Dispatch, 75 tok/s)"): for one
+// (sequence b, KV head h, chunk c of `chunk` keys) and each query row r of
+// that KV head,
+//     s_j  = (q_r . k_j) * scale * log2(e)          visible keys j of the chunk
+//     m    = max_j s_j,  p_j = 2^(s_j - m),  l = sum_j p_j
+//     acc  = sum_j p_j v_j                          (fp32 throughout)
+// and (m, l, acc) is written to the workspace.  The combine kernel merges the
+// chunks.  A key j is visible to query token i iff j <= seq_pos + i.
+//
+// Mapping on gfx950: one 256-lane workgroup per (b, h, chunk), serving every
+// query row of KV head h, so each K/V byte is read once.  Sixteen lanes hold
+// one 256-byte row (16 bytes each): a wave's 128-bit load covers four
+// consecutive keys, 1 KiB contiguous.  Q.K partial dots use the packed
+// dot2 (bf16/fp16 pair -> fp32) instruction, then a 16-lane DPP butterfly.
+// The chunk's scores go to LDS; the chunk is two-pass (all scores, then the
+// maximum, then P.V), so no running rescale is needed inside a chunk.
+#include "da_internal.h"
+
+#include <math.h>
+
+namespace da {
+
+template <bool F16, int RP>
+__global__ __launch_bounds__(256) void attn_split_valu_kernel(AttnParams p) {
+    extern __shared__ float lds[];  // scores [chunk][RP], later the wave sums [4][RP][128]
+    __shared__ float row_m[RP], row_l[RP];
+
+    const int n_chunks = p.n_chunks;
+    const int c = blockIdx.x % n_chunks;
+    const int bh = blockIdx.x / n_chunks;
+    const int b = bh / p.n_kv_heads;
+    const int h = bh - b * p.n_kv_heads;
+    const int sp = p.seq_pos[b];
+    if (sp < 0 || sp > p.max_seq - p.q_len) return;
+    const int ctx = sp + p.q_len;
+    const int t0 = c * p.chunk;
+    if (t0 >= ctx) return;  // chunk past the context: never read by the combine
+    const int n_tok = min(p.chunk, ctx - t0);
+    const int n_slab = (n_tok + 15) >> 4;  // 16-key slabs; a wave does one per step
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int gq = lane >> 4;  // which of the 4 keys of a 1 KiB load
+    const int cq = lane & 15;  // 16-byte column: dims 8*cq .. 8*cq+7
+
+    // Query rows: r = i * group + g is query token i of query head h*group + g.
+    uint32_t qr[RP][4];
+    int vis[RP];  // exclusive limit of the visible local key indices of row r
+#pragma unroll
+    for (int r = 0; r < RP; ++r) {
+        if (r < p.rows) {
+            const int i = r / p.group, g = r - i * p.group;
+            const uint8_t *qp = p.q +
+                                (((size_t)b * p.q_len + i) * p.n_q_heads + (size_t)h * p.group + g) *
+                                    kRowBytes +
+                                cq * 16;
+            const u32x4_t v = ld16(qp);
+            qr[r][0] = v[0];
+            qr[r][1] = v[1];
+            qr[r][2] = v[2];
+            qr[r][3] = v[3];
+            vis[r] = min(sp + i + 1 - t0, n_tok);
+        } else {
+            qr[r][0] = qr[r][1] = qr[r][2] = qr[r][3] = 0u;
+            vis[r] = 0;
+        }
+    }
+
+    const size_t head_off = ((size_t)bh * p.max_seq + t0) * kRowBytes + cq * 16;
+    const uint8_t *kb = p.k_cache + head_off;
+    const uint8_t *vb = p.v_cache + head_off;
+    const int last = n_tok - 1;  // loads past the context re-read the last row (masked)
+
+    // ---- pass 1: scores of the chunk into LDS ----------------------------------
+    {
+        u32x4_t cur[4], nxt[4];
+        int s = wave;
+        const int s0 = min(s, n_slab - 1);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) cur[u] = ld16(kb + (size_t)min(s0 * 16 + u * 4 + gq, last) * kRowBytes);
+        for (; s < n_slab; s += 4) {
+            const int sn = min(s + 4, n_slab - 1);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                nxt[u] = ld16(kb + (size_t)min(sn * 16 + u * 4 + gq, last) * kRowBytes);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int tl = s * 16 + u * 4 + gq;
+                float sc[RP];
+#pragma unroll
+                for (int r = 0; r < RP; ++r) {
+                    float a = dot2<F16>(qr[r][0], cur[u][0], 0.f);
+                    a = dot2<F16>(qr[r][1], cur[u][1], a);
+                    a = dot2<F16>(qr[r][2], cur[u][2], a);
+                    a = dot2<F16>(qr[r][3], cur[u][3], a);
+                    sc[r] = row16_sum(a);
+                }
+                if (cq == 0) {
+#pragma unroll
+                    for (int r = 0; r < RP; ++r)
+                        lds[tl * RP + r] = tl < vis[r] ? sc[r] * p.scale_log2 : -INFINITY;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) cur[u] = nxt[u];
+        }
+    }
+    __syncthreads();
+
+    // ---- chunk maximum and weights p = 2^(s - m), sum l ------------------------
+    const int n_pad = n_slab * 16;
+    for (int r = wave; r < RP; r += 4) {
+        float m = -INFINITY;
+        for (int t = lane; t < n_pad; t += 64) m = fmaxf(m, lds[t * RP + r]);
+        m = wave_max(m);
+        float l = 0.f;
+        for (int t = lane; t < n_pad; t += 64) {
+            const float e = (m == -INFINITY) ? 0.f : exp2_fast(lds[t * RP + r] - m);
+            lds[t * RP + r] = e;
+            l += e;
+        }
+        l = wave_sum(l);
+        if (lane == 0) {
+            row_m[r] = m;
+            row_l[r] = l;
+        }
+    }
+    __syncthreads();
+
+    // ---- pass 2: acc = sum_j p_j v_j ----------------------------------------------
+    float acc[RP][8];
+#pragma unroll
+    for (int r = 0; r < RP; ++r)
+#pragma unroll
+        for (int d = 0; d < 8; ++d) acc[r][d] = 0.f;
+    const int first_draft = sp - t0;  // local keys above this may be hidden from some rows
+    {
+        u32x4_t cur[4], nxt[4];
+        int s = wave;
+        const int s0 = min(s, n_slab - 1);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) cur[u] = ld16(vb + (size_t)min(s0 * 16 + u * 4 + gq, last) * kRowBytes);
+        for (; s < n_slab; s += 4) {
+            const int sn = min(s + 4, n_slab - 1);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                nxt[u] = ld16(vb + (size_t)min(sn * 16 + u * 4 + gq, last) * kRowBytes);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int tl = s * 16 + u * 4 + gq;
+                float pr[RP];
+#pragma unroll
+                for (int r = 0; r < RP; ++r) pr[r] = lds[tl * RP + r];
+                float vf[8];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) unpack2<F16>(cur[u][k], vf[2 * k], vf[2 * k + 1]);
+                if (tl > first_draft) {
+                    // a later draft token (or padding past the context): rows that
+                    // cannot see it must not touch its value row, even NaN * 0
+#pragma unroll
+                    for (int r = 0; r < RP; ++r)
+                        if (pr[r] != 0.f) {
+#pragma unroll
+                            for (int d = 0; d < 8; ++d) acc[r][d] = fmaf(pr[r], vf[d], acc[r][d]);
+                        }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < RP; ++r)
+#pragma unroll
+                        for (int d = 0; d < 8; ++d) acc[r][d] = fmaf(pr[r], vf[d], acc[r][d]);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) cur[u] = nxt[u];
+        }
+    }
+
+    // ---- reduce the four key slots of a wave, then the four waves ---------------
+#pragma unroll
+    for (int r = 0; r < RP; ++r)
+#pragma unroll
+        for (int d = 0; d < 8; ++d) {
+            acc[r][d] += __shfl_xor(acc[r][d], 16);
+            acc[r][d] += __shfl_xor(acc[r][d], 32);
+        }
+    __syncthreads();  // every wave is done with the scores
+    float *red = lds;  // [4][RP][128]
+    if (gq == 0) {
+#pragma unroll
+        for (int r = 0; r < RP; ++r)
+#pragma unroll
+            for (int d = 0; d < 8; ++d) red[(wave * RP + r) * kHeadDim + cq * 8 + d] = acc[r][d];
+    }
+    __syncthreads();
+
+    const size_t part = (size_t)bh * n_chunks + c;
+    float *wa = p.ws_acc + part * p.rows * kHeadDim;
+    for (int idx = tid; idx < p.rows * kHeadDim; idx += 256) {
+        const int r = idx >> 7, d = idx & (kHeadDim - 1);
+        wa[idx] = (red[(0 * RP + r) * kHeadDim + d] + red[(1 * RP + r) * kHeadDim + d]) +
+                  (red[(2 * RP + r) * kHeadDim + d] + red[(3 * RP + r) * kHeadDim + d]);
+    }
+    if (tid < p.rows) {
+        p.ws_ml[(part * p.rows + tid) * 2 + 0] = row_m[tid];
+        p.ws_ml[(part * p.rows + tid) * 2 + 1] = row_l[tid];
+    }
+}
+
+template <bool F16, int RP>
+static hipError_t launch_rp(const AttnParams &p, hipStream_t s) {
+    const int grid = p.batch * p.n_kv_heads * p.n_chunks;
+    const size_t lds_bytes = (size_t)RP * (p.chunk > 512 ? p.chunk : 512) * sizeof(float);
+    hipLaunchKernelGGL((attn_split_valu_kernel<F16, RP>), dim3(grid), dim3(256), lds_bytes, s, p);
+    return hipGetLastError();
+}
+
+template <bool F16>
+static hipError_t launch_dtype(const AttnParams &p, hipStream_t s) {
+    if (p.rows <= 1) return launch_rp<F16, 1>(p, s);
+    if (p.rows <= 2) return launch_rp<F16, 2>(p, s);
+    if (p.rows <= 4) return launch_rp<F16, 4>(p, s);
+    if (p.rows <= 8) return launch_rp<F16, 8>(p, s);
+    return launch_rp<F16, 16>(p, s);
+}
+
+hipError_t launch_attn_valu(const AttnParams &p, bool fp16, hipStream_t s) {
+    return fp16 ? launch_dtype<true>(p, s) : launch_dtype<false>(p, s);
+}
+
+}  // namespace da

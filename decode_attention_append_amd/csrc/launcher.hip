@@ -1,0 +1,180 @@
+// C-ABI entry points of libdecode_attn: argument checks, chunk planning and
+// launches on the caller's stream.  Nothing here allocates, synchronises or
+// reads device memory on the host.
+#include "decode_attn.h"
+#include "da_internal.h"
+
+#include <math.h>
+
+namespace {
+
+using namespace da;
+
+constexpr int kWorkgroupsWanted = 2048;  // 8 per compute unit on a 256-CU MI355X
+constexpr int kMaxSeq = 1 << 24;
+
+bool aligned16(const void *x) { return ((uintptr_t)x & 15u) == 0; }
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+da_status check_problem(const da_problem *p) {
+    if (!p) return DA_ERR_INVALID_ARG;
+    if (p->batch <= 0 || p->q_len <= 0 || p->n_q_heads <= 0 || p->n_kv_heads <= 0 ||
+        p->head_dim <= 0 || p->max_seq <= 0)
+        return DA_ERR_INVALID_ARG;
+    if (p->n_q_heads % p->n_kv_heads != 0) return DA_ERR_INVALID_ARG;
+    if (p->q_len > p->max_seq) return DA_ERR_INVALID_ARG;
+    if (isnan(p->scale) || isinf(p->scale)) return DA_ERR_INVALID_ARG;
+    if (p->chunk_tokens != 0 &&
+        (p->chunk_tokens < kTokenTile || p->chunk_tokens > kMaxChunk || p->chunk_tokens % kTokenTile))
+        return DA_ERR_INVALID_ARG;
+    if (p->dtype != DA_BF16 && p->dtype != DA_FP16) return DA_ERR_UNSUPPORTED;
+    if (p->head_dim != kHeadDim) return DA_ERR_UNSUPPORTED;
+    if (p->q_len > kMaxQLen) return DA_ERR_UNSUPPORTED;
+    if ((int64_t)(p->n_q_heads / p->n_kv_heads) * p->q_len > kMaxRows) return DA_ERR_UNSUPPORTED;
+    if (p->max_seq > kMaxSeq) return DA_ERR_UNSUPPORTED;
+    // grid sizes stay within int
+    if ((int64_t)p->batch * p->n_kv_heads * ((p->max_seq + kTokenTile - 1) / kTokenTile) > INT32_MAX / 2)
+        return DA_ERR_UNSUPPORTED;
+    if ((int64_t)p->batch * p->q_len * p->n_q_heads * 16 > INT32_MAX / 2) return DA_ERR_UNSUPPORTED;
+    return DA_OK;
+}
+
+// Keys per chunk: the largest power of two (<= 1024) that still gives the
+// launch about kWorkgroupsWanted workgroups, so the 256 compute units each get
+// several; the MFMA kernel's partials are 32 rows wide, so it keeps chunks of
+// at least 256 keys to bound the partials traffic.
+int auto_chunk(const da_problem *p, int rows) {
+    const int64_t units = (int64_t)p->batch * p->n_kv_heads;
+    const int min_chunk = rows >= 16 ? 256 : kTokenTile;
+    int chunk = 1024;
+    while (chunk > min_chunk && units * ((p->max_seq + chunk - 1) / chunk) < kWorkgroupsWanted) chunk >>= 1;
+    return chunk;
+}
+
+void plan_of(const da_problem *p, da_plan *pl) {
+    const int rows = (p->n_q_heads / p->n_kv_heads) * p->q_len;
+    const int chunk = p->chunk_tokens ? p->chunk_tokens : auto_chunk(p, rows);
+    const int n_chunks = (p->max_seq + chunk - 1) / chunk;
+    const int32_t bh = p->batch * p->n_kv_heads;
+    pl->chunk_tokens = chunk;
+    pl->n_chunks = n_chunks;
+    pl->rows = rows;
+    pl->variant = rows >= 16 ? DA_VARIANT_MFMA : DA_VARIANT_VALU;
+    pl->workspace_bytes = align256(ws_acc_floats(bh, n_chunks, rows) * sizeof(float)) +
+                          ws_ml_floats(bh, n_chunks, rows) * sizeof(float);
+}
+
+AttnParams attn_params(const da_problem *p, const da_plan &pl, const void *q, const void *k_cache,
+                       const void *v_cache, const int32_t *seq_pos, const void *workspace) {
+    AttnParams a;
+    a.q = (const uint8_t *)q;
+    a.k_cache = (const uint8_t *)k_cache;
+    a.v_cache = (const uint8_t *)v_cache;
+    a.seq_pos = seq_pos;
+    const int32_t bh = p->batch * p->n_kv_heads;
+    a.ws_acc = (float *)workspace;
+    a.ws_ml = (float *)((uint8_t *)workspace + align256(ws_acc_floats(bh, pl.n_chunks, pl.rows) * sizeof(float)));
+    a.batch = p->batch;
+    a.q_len = p->q_len;
+    a.n_q_heads = p->n_q_heads;
+    a.n_kv_heads = p->n_kv_heads;
+    a.max_seq = p->max_seq;
+    a.group = p->n_q_heads / p->n_kv_heads;
+    a.rows = pl.rows;
+    a.n_chunks = pl.n_chunks;
+    a.chunk = pl.chunk_tokens;
+    const double scale = p->scale > 0.f ? (double)p->scale : 1.0 / sqrt((double)p->head_dim);
+    a.scale_log2 = (float)(scale * 1.4426950408889634);  // log2(e)
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+da_status da_plan_attention(const da_problem *p, da_plan *plan) {
+    if (!plan) return DA_ERR_INVALID_ARG;
+    const da_status st = check_problem(p);
+    if (st != DA_OK) return st;
+    plan_of(p, plan);
+    return DA_OK;
+}
+
+size_t da_workspace_bytes(const da_problem *p) {
+    da_plan pl;
+    if (da_plan_attention(p, &pl) != DA_OK) return 0;
+    return pl.workspace_bytes;
+}
+
+da_status da_kv_append(const da_problem *p, void *k_cache, void *v_cache, const void *k_new,
+                       const void *v_new, const int32_t *seq_pos, void *stream) {
+    const da_status st = check_problem(p);
+    if (st != DA_OK) return st;
+    if (!k_cache || !v_cache || !k_new || !v_new || !seq_pos) return DA_ERR_INVALID_ARG;
+    if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new) ||
+        ((uintptr_t)seq_pos & 3u))
+        return DA_ERR_INVALID_ARG;
+    AppendParams a;
+    a.k_cache = (uint8_t *)k_cache;
+    a.v_cache = (uint8_t *)v_cache;
+    a.k_new = (const uint8_t *)k_new;
+    a.v_new = (const uint8_t *)v_new;
+    a.seq_pos = seq_pos;
+    a.batch = p->batch;
+    a.q_len = p->q_len;
+    a.n_kv_heads = p->n_kv_heads;
+    a.max_seq = p->max_seq;
+    const int threads = p->batch * p->q_len * p->n_kv_heads * 16;
+    (void)hipGetLastError();  // launch errors below are ours alone
+    return launch_kv_append(a, threads, (hipStream_t)stream) == hipSuccess ? DA_OK : DA_ERR_HIP;
+}
+
+da_status da_gqa_decode_attn(const da_problem *p, const void *q, const void *k_cache,
+                             const void *v_cache, const int32_t *seq_pos, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+    const da_status st = check_problem(p);
+    if (st != DA_OK) return st;
+    if (!q || !k_cache || !v_cache || !seq_pos || !workspace) return DA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace) ||
+        ((uintptr_t)seq_pos & 3u))
+        return DA_ERR_INVALID_ARG;
+    da_plan pl;
+    plan_of(p, &pl);
+    if (workspace_bytes < pl.workspace_bytes) return DA_ERR_WORKSPACE;
+    const AttnParams a = attn_params(p, pl, q, k_cache, v_cache, seq_pos, workspace);
+    (void)hipGetLastError();
+    const hipError_t e = pl.variant == DA_VARIANT_MFMA
+                             ? launch_attn_mfma(a, p->dtype == DA_FP16, (hipStream_t)stream)
+                             : launch_attn_valu(a, p->dtype == DA_FP16, (hipStream_t)stream);
+    return e == hipSuccess ? DA_OK : DA_ERR_HIP;
+}
+
+da_status da_gqa_decode_attn_combine(const da_problem *p, const void *workspace,
+                                     size_t workspace_bytes, const int32_t *seq_pos, void *out,
+                                     void *stream) {
+    const da_status st = check_problem(p);
+    if (st != DA_OK) return st;
+    if (!workspace || !seq_pos || !out) return DA_ERR_INVALID_ARG;
+    if (!aligned16(workspace) || !aligned16(out) || ((uintptr_t)seq_pos & 3u)) return DA_ERR_INVALID_ARG;
+    da_plan pl;
+    plan_of(p, &pl);
+    if (workspace_bytes < pl.workspace_bytes) return DA_ERR_WORKSPACE;
+    const AttnParams a = attn_params(p, pl, nullptr, nullptr, nullptr, seq_pos, workspace);
+    (void)hipGetLastError();
+    return launch_attn_combine(a, p->dtype == DA_FP16, out, (hipStream_t)stream) == hipSuccess ? DA_OK
+                                                                                                 : DA_ERR_HIP;
+}
+
+const char *da_status_str(da_status s) {
+    switch (s) {
+        case DA_OK: return "ok";
+        case DA_ERR_INVALID_ARG: return "invalid argument";
+        case DA_ERR_UNSUPPORTED: return "unsupported problem";
+        case DA_ERR_WORKSPACE: return "workspace too small";
+        case DA_ERR_HIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

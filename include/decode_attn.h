@@ -1,0 +1,149 @@
+/*
+ * decode_attn.h - one decode step of grouped-query attention over a KV cache,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The step, as the "Qwen MoE BringUp" page (iree-org/onnxruntime-ep-iree
+ * issue 34) describes it:
+ *
+ *   1. da_kv_append: the new K/V rows of the step are written into the
+ *      pre-allocated cache as one contiguous slice starting at the sequence's
+ *      seq_position (section "Per-Layer IR Patterns", 2. Self-Attention,
+ *      "KV Cache Update (EP rewrite: tensor.insert_slice)"; fix A5 explains why
+ *      the scatter with sequential indices is such a slice write; opportunity
+ *      10 keeps the cache a fixed-size buffer updated in place).
+ *   2. da_gqa_decode_attn: split-context attention.  Scores Q K^T times the
+ *      softmax scale, a causal mask (key j is visible to query token i iff
+ *      j <= seq_pos + i, which also keeps j below seq_pos + q_len), softmax, times V
+ *      (same page, "Attention Computation").  The context is cut into chunks;
+ *      each chunk's fp32 online-softmax partial (max, sum, weighted V sum) goes
+ *      to a caller-provided workspace.  One workgroup serves every query head
+ *      of one KV head, so each K/V byte is read from memory once ("Architecture
+ *      Diagram - Qwen3-30B-A3B (Extern Dispatch, 75 tok/s)": Paged Attention
+ *      3-phase decode, split-KV phase, GQA handled in the kernel).
+ *   3. da_gqa_decode_attn_combine: log-sum-exp merge of the chunk partials and
+ *      the final normalisation, rounded to nearest-even into bf16/fp16 (same
+ *      diagram, the reduce phase).
+ *
+ * All accumulation is fp32 (fix A7 of the same page; BP-3 of "Design:
+ * Execution Provider aware model building").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer argument except `p` is a DEVICE pointer, 16-byte aligned.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *    work is enqueued asynchronously on it, in call order; nothing here
+ *    synchronises, allocates, frees, or reads device memory on the host.
+ *  - The caller owns every buffer.  The library keeps no state between calls.
+ *  - Layouts (row-major, contiguous, element = 2-byte bf16 or fp16):
+ *        q, out          [B][q_len][Hq][D]
+ *        k_new, v_new    [B][q_len][Hkv][D]
+ *        k_cache,v_cache [B][Hkv][max_seq][D]
+ *        seq_pos         int32 [B]: cache slot of the sequence's first new token
+ *    Query head hq reads KV head hq / (Hq / Hkv) (consecutive query heads
+ *    share a KV head).  Multi-head attention is Hq == Hkv.
+ *  - Host-checkable errors are reported BEFORE anything is enqueued; on any
+ *    error return nothing has been launched.  Device-side preconditions
+ *    (0 <= seq_pos[b] and seq_pos[b] + q_len <= max_seq) cannot be checked on
+ *    the host without a synchronisation: they are the caller's contract.  A
+ *    sequence that breaks it is skipped by da_kv_append (its slice is not
+ *    written) and its attention output is unspecified, but no kernel reads or
+ *    writes outside the buffers described here.
+ *  - No exceptions cross this interface.
+ */
+#ifndef DECODE_ATTN_H
+#define DECODE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DA_OK = 0,
+    DA_ERR_INVALID_ARG = -1, /* null or misaligned pointer, non-positive size, Hq % Hkv != 0 */
+    DA_ERR_UNSUPPORTED = -2, /* valid but not implemented: head_dim != 128, q_len > 8, ... */
+    DA_ERR_WORKSPACE = -3,   /* workspace smaller than da_workspace_bytes() */
+    DA_ERR_HIP = -4          /* the HIP runtime refused a launch */
+} da_status;
+
+typedef enum { DA_BF16 = 0, DA_FP16 = 1 } da_dtype;
+
+/* Shape of one decode step.  Plain data, read only during the call. */
+typedef struct {
+    int32_t batch;        /* B >= 1                                               */
+    int32_t q_len;        /* new tokens per sequence this step, 1..8 (verify batches) */
+    int32_t n_q_heads;    /* Hq >= 1                                              */
+    int32_t n_kv_heads;   /* Hkv >= 1, Hq % Hkv == 0, (Hq / Hkv) * q_len <= 32    */
+    int32_t head_dim;     /* D; only 128 is implemented                           */
+    int32_t max_seq;      /* allocated cache length (slots per KV head)           */
+    int32_t dtype;        /* da_dtype of q, caches, new rows and out              */
+    float scale;          /* softmax scale; <= 0 selects 1 / sqrt(head_dim)       */
+    int32_t chunk_tokens; /* keys per split-context chunk: 0 = automatic, else a
+                             multiple of 64 (a tuning and testing override)       */
+} da_problem;
+
+/* What the library will launch for a problem (a pure function of *p). */
+typedef struct {
+    int32_t chunk_tokens;    /* keys per chunk                                 */
+    int32_t n_chunks;        /* chunks per (sequence, KV head) = ceil(max_seq / chunk_tokens) */
+    int32_t rows;            /* query rows per KV head = (Hq / Hkv) * q_len    */
+    int32_t variant;         /* DA_VARIANT_*                                   */
+    size_t workspace_bytes;  /* bytes of fp32 partials the attention needs     */
+} da_plan;
+
+enum { DA_VARIANT_VALU = 0, DA_VARIANT_MFMA = 1 };
+
+/*
+ * Plans the attention of *p: chunking, kernel variant, workspace size.  The
+ * variant is the MFMA kernel when rows >= 16 (Q K^T and P V are then real
+ * small matrix products), the vector-ALU kernel otherwise.
+ * Returns DA_OK, DA_ERR_INVALID_ARG or DA_ERR_UNSUPPORTED.  Host only.
+ */
+da_status da_plan_attention(const da_problem *p, da_plan *plan);
+
+/* Workspace bytes da_gqa_decode_attn needs for *p (0 if *p is invalid). */
+size_t da_workspace_bytes(const da_problem *p);
+
+/*
+ * KV append ("KV Cache Update (EP rewrite: tensor.insert_slice)"):
+ *   k_cache[b][h][seq_pos[b] + i][:] = k_new[b][i][h][:]   for i < q_len,
+ * and the same for v_cache / v_new.  A bit copy: every other cache byte is
+ * unchanged.  In place on the caller's cache.  k_new/v_new must not overlap
+ * the caches.
+ */
+da_status da_kv_append(const da_problem *p, void *k_cache, void *v_cache, const void *k_new,
+                       const void *v_new, const int32_t *seq_pos, void *stream);
+
+/*
+ * Split-context attention partials ("Attention Computation"; the split-KV
+ * phase of the 3-phase decode).  Reads q and the caches (which must already
+ * hold this step's rows: call da_kv_append first on the same stream), reads
+ * only the visible cache slots [0, seq_pos[b] + q_len), and writes fp32
+ * partials into `workspace` (at least da_workspace_bytes(p) bytes, not
+ * aliasing any other argument).  Chunks beyond a sequence's context are not
+ * written and not read later.
+ */
+da_status da_gqa_decode_attn(const da_problem *p, const void *q, const void *k_cache,
+                             const void *v_cache, const int32_t *seq_pos, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/*
+ * Combine (the log-sum-exp reduce phase): merges the partials of every live
+ * chunk and writes out[b][i][hq][:] rounded to nearest-even in p->dtype.
+ * `workspace` must hold the partials of a da_gqa_decode_attn call with the
+ * same *p and seq_pos, enqueued earlier on the same stream.
+ */
+da_status da_gqa_decode_attn_combine(const da_problem *p, const void *workspace,
+                                     size_t workspace_bytes, const int32_t *seq_pos, void *out,
+                                     void *stream);
+
+/* Static description of a status code. */
+const char *da_status_str(da_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DECODE_ATTN_H */

@@ -1,0 +1,113 @@
+"""The C-ABI library on the host: it loads, exports what the header declares, and
+rejects bad arguments with the documented status before touching the GPU."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import decode_attention_append_amd as da
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(da_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("da_kv_append", "da_gqa_decode_attn", "da_gqa_decode_attn_combine",
+              "da_workspace_bytes", "da_plan_attention", "da_status_str"):
+        assert n in names
+
+
+@pytest.mark.parametrize("name", declared_functions())
+def test_library_exports(name):
+    assert hasattr(da.lib, name), f"{name} declared in include/ but not exported"
+
+
+def test_exports_match_binding_list():
+    assert set(da.EXPORTS) <= set(declared_functions())
+
+
+def P(**kw):
+    base = dict(batch=2, q_len=1, n_q_heads=16, n_kv_heads=8, head_dim=128, max_seq=1024,
+                dtype="bf16")
+    base.update(kw)
+    return da.problem(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), da.DA_ERR_INVALID_ARG),
+    (dict(q_len=0), da.DA_ERR_INVALID_ARG),
+    (dict(n_q_heads=12, n_kv_heads=8), da.DA_ERR_INVALID_ARG),
+    (dict(max_seq=0), da.DA_ERR_INVALID_ARG),
+    (dict(q_len=9), da.DA_ERR_UNSUPPORTED),
+    (dict(head_dim=64), da.DA_ERR_UNSUPPORTED),
+    (dict(dtype=7), da.DA_ERR_UNSUPPORTED),
+    (dict(n_q_heads=64, n_kv_heads=1, q_len=1), da.DA_ERR_UNSUPPORTED),  # 64 rows per KV head
+    (dict(chunk_tokens=100), da.DA_ERR_INVALID_ARG),
+    (dict(chunk_tokens=4096), da.DA_ERR_INVALID_ARG),
+    (dict(q_len=8, max_seq=4), da.DA_ERR_INVALID_ARG),
+])
+def test_plan_rejects(kw, status):
+    p = P(**kw) if "dtype" not in kw or isinstance(kw["dtype"], str) else None
+    if p is None:
+        p = P()
+        p.dtype = kw["dtype"]
+    pl = da.Plan()
+    assert da.lib.da_plan_attention(ctypes.byref(p), ctypes.byref(pl)) == status
+    assert da.workspace_bytes(p) == 0
+
+
+def test_plan_is_pure_and_sized():
+    p = P(batch=32, max_seq=8192)
+    a, b = da.plan_attention(p), da.plan_attention(p)
+    assert a == b
+    rows = 2
+    n = a["n_chunks"]
+    assert n * a["chunk_tokens"] >= 8192 and (n - 1) * a["chunk_tokens"] < 8192
+    assert a["workspace_bytes"] >= 32 * 8 * n * rows * (128 + 2) * 4
+    assert a["variant"] == "valu"
+    assert da.plan_attention(P(q_len=4, n_q_heads=32, n_kv_heads=4))["variant"] == "mfma"
+    assert da.plan_attention(P(chunk_tokens=128))["chunk_tokens"] == 128
+
+
+def test_null_and_misaligned_pointers_rejected_before_launch():
+    p = P()
+    buf = (ctypes.c_uint8 * 64)()
+    good = ctypes.addressof(buf) + (-ctypes.addressof(buf)) % 16
+    assert da.lib.da_kv_append(ctypes.byref(p), None, good, good, good, good, None) == da.DA_ERR_INVALID_ARG
+    assert da.lib.da_kv_append(ctypes.byref(p), good + 2, good, good, good, good, None) == da.DA_ERR_INVALID_ARG
+    assert da.lib.da_gqa_decode_attn(ctypes.byref(p), good, good, good, good, None, 0, None) == \
+        da.DA_ERR_INVALID_ARG
+    assert da.lib.da_gqa_decode_attn(ctypes.byref(p), good, good, good, good, good, 16, None) == \
+        da.DA_ERR_WORKSPACE
+    assert da.lib.da_gqa_decode_attn_combine(ctypes.byref(p), good, 16, good, good, None) == \
+        da.DA_ERR_WORKSPACE
+    assert da.lib.da_gqa_decode_attn_combine(ctypes.byref(p), good, 1 << 30, good, good + 8, None) == \
+        da.DA_ERR_INVALID_ARG
+    bad = P(head_dim=64)
+    assert da.lib.da_kv_append(ctypes.byref(bad), good, good, good, good, good, None) == da.DA_ERR_UNSUPPORTED
+    assert da.lib.da_kv_append(None, good, good, good, good, good, None) == da.DA_ERR_INVALID_ARG
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4):
+        assert da.status_str(s) and da.status_str(s) != "unknown status"
+    assert da.status_str(5) == "unknown status"
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    p = P()
+    t = torch.zeros(2, 8, 1024, 128, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        da.kv_append(p, t, t, t, t, torch.zeros(2, dtype=torch.int32))

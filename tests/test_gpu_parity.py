@@ -1,0 +1,246 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+KV caches must match the oracle's append bit for bit over the whole
+allocation; outputs must satisfy |gpu - oracle| <= 1e-2 + 1e-2 |oracle|
+elementwise.
+"""
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_append_amd as da
+from decode_attention_append_amd.workloads import WORKLOADS, make_layer
+from tests import gpu_util as gu
+from tests.oracle_pins import bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+# ------------------------------------------------------------------ the five workloads
+
+@pytest.mark.parametrize("name", [
+    "qwen3_0p6b_b1_ctx512",
+    "gqa64x8_b4_ctx12k_16k",
+    "verify4_gqa32x4_b8_pos2048_8188",
+])
+def test_workload_full(name):
+    w = WORKLOADS[name]
+    _say(name, "layer 0, every output row")
+    inp = make_layer(w, 0, "cuda")
+    p = da.problem_for(inp["q"], inp["k_cache"])
+    stats = gu.check_layer(p, inp)
+    _say(name, da.plan_attention(p), stats)
+
+
+def test_workload_mha_fp16_layers():
+    w = WORKLOADS["qwen15moe_mha16_b1_ctx4096_24l"]
+    for layer in (0, 1, 23):
+        _say(w.name, "layer", layer)
+        inp = make_layer(w, layer, "cuda")
+        p = da.problem_for(inp["q"], inp["k_cache"])
+        stats = gu.check_layer(p, inp)
+        _say(w.name, layer, stats)
+
+
+def test_workload_batched_gqa_ctx8192():
+    """Full size (1 GiB caches per layer): whole cache bit-exact; all rows of layer 0,
+    sampled rows of layer 27."""
+    w = WORKLOADS["gqa16x8_b32_ctx8192_28l"]
+    _say(w.name, "layer 0 all rows")
+    inp = make_layer(w, 0, "cuda")
+    p = da.problem_for(inp["q"], inp["k_cache"])
+    gu.check_layer(p, inp)
+    del inp
+    _say(w.name, "layer 27 sampled rows")
+    inp = make_layer(w, 27, "cuda")
+    rng = np.random.default_rng(27)
+    rows = np.stack([rng.integers(0, w.batch, 64), np.zeros(64, int),
+                     rng.integers(0, w.n_q_heads, 64)], axis=1)
+    gu.check_layer(p, inp, rows=rows)
+
+
+# ------------------------------------------------------------------ shapes and edges
+
+@pytest.mark.parametrize("B,q_len,Hq,Hkv,S,seq_pos,dtype", [
+    (3, 1, 16, 8, 700, [0, 333, 699], torch.bfloat16),          # ragged, tail not a tile multiple
+    (2, 1, 16, 16, 1000, [999, 64], torch.float16),              # MHA fp16
+    (2, 1, 64, 8, 3000, [2999, 1537], torch.bfloat16),           # GQA 8 (rows 8)
+    (2, 1, 32, 8, 1200, [1199, 100], torch.bfloat16),            # rows 4
+    (2, 2, 24, 2, 600, [598, 255], torch.bfloat16),              # rows 24 -> MFMA
+    (2, 3, 12, 3, 900, [10, 896], torch.float16),                # rows 12 -> VALU 16-wide
+    (3, 4, 32, 4, 2100, [2096, 0, 1023], torch.bfloat16),        # verify 4 -> MFMA
+    (2, 4, 32, 4, 2100, [2096, 777], torch.float16),             # MFMA fp16
+    (2, 8, 4, 2, 500, [492, 3], torch.bfloat16),                 # q_len 8 rows 16 -> MFMA
+    (2, 8, 2, 2, 500, [492, 61], torch.bfloat16),                # q_len 8 MHA rows 8
+    (1, 1, 1, 1, 64, [63], torch.bfloat16),                      # smallest
+])
+def test_shapes(B, q_len, Hq, Hkv, S, seq_pos, dtype):
+    _say("shape", B, q_len, Hq, Hkv, S, seq_pos, dtype)
+    inp = gu.make_case(B, q_len, Hq, Hkv, S, seq_pos, dtype, seed=B * 1000 + S)
+    p = da.problem_for(inp["q"], inp["k_cache"])
+    gu.check_layer(p, inp)
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 256, 512, 1024, 2048])
+@pytest.mark.parametrize("q_len,Hq,Hkv", [(1, 16, 8), (1, 64, 8), (4, 32, 4)])
+def test_chunk_sweep(chunk, q_len, Hq, Hkv):
+    """Every chunk size agrees with the oracle: pins the split and the combine."""
+    _say("chunk", chunk, q_len, Hq, Hkv)
+    inp = gu.make_case(2, q_len, Hq, Hkv, 2500, [2500 - q_len, 1300], seed=chunk)
+    p = da.problem_for(inp["q"], inp["k_cache"], chunk_tokens=chunk)
+    gu.check_layer(p, inp)
+
+
+@pytest.mark.parametrize("q_len,Hq,Hkv", [(1, 16, 8), (1, 64, 8), (4, 32, 4), (1, 16, 16)])
+def test_one_key_returns_value_exactly(q_len, Hq, Hkv):
+    """seq_pos 0: query token 0 sees only its own key, so its output is v_new exactly."""
+    _say("one key", q_len, Hq, Hkv)
+    inp = gu.make_case(2, q_len, Hq, Hkv, 128, [0, 0], seed=5)
+    p = da.problem_for(inp["q"], inp["k_cache"])
+    out = gu.run_step(p, inp)
+    G = Hq // Hkv
+    expect = inp["v_new"][:, 0].repeat_interleave(G, dim=1)  # [B, Hq, D]
+    assert torch.equal(out[:, 0], expect)
+
+
+@pytest.mark.parametrize("q_len,Hq,Hkv", [(1, 16, 8), (1, 64, 8), (4, 32, 4)])
+def test_constant_values_return_value_exactly(q_len, Hq, Hkv):
+    S = 3000
+    _say("constant V", q_len, Hq, Hkv)
+    inp = gu.make_case(2, q_len, Hq, Hkv, S, [S - q_len, 1777], seed=6)
+    row = inp["v_cache"][0, 0, 0].clone()
+    inp["v_cache"][:] = row
+    inp["v_new"][:] = row
+    p = da.problem_for(inp["q"], inp["k_cache"])
+    out = gu.run_step(p, inp)
+    assert torch.equal(out, row.expand_as(out))
+
+
+@pytest.mark.parametrize("q_len,Hq,Hkv", [(1, 16, 8), (1, 64, 8), (4, 32, 4), (1, 16, 16)])
+def test_beyond_context_poison(q_len, Hq, Hkv):
+    """Cache slots at or past seq_pos + q_len hold NaN/inf: the output must not change."""
+    S = 1500
+    sp = [700, 1500 - q_len, 63]
+    _say("poison", q_len, Hq, Hkv)
+    inp = gu.make_case(3, q_len, Hq, Hkv, S, sp, seed=7)
+    clean = {k: v.clone() for k, v in inp.items()}
+    p = da.problem_for(inp["q"], inp["k_cache"])
+    out_clean = gu.run_step(p, clean)
+    for b, s in enumerate(sp):
+        inp["k_cache"][b, :, s + q_len:] = float("nan")
+        inp["v_cache"][b, :, s + q_len:] = float("inf")
+    out = gu.run_step(p, inp)
+    assert torch.equal(out, out_clean)
+    assert torch.isfinite(out.float()).all()
+
+
+def test_later_draft_token_hidden_from_earlier_rows_valu():
+    """A NaN value row of the second draft token leaves query token 0's rows finite
+    (vector-ALU variant: the mask excludes the row exactly)."""
+    q_len, Hq, Hkv = 2, 8, 2
+    inp = gu.make_case(1, q_len, Hq, Hkv, 256, [100], seed=8)
+    p = da.problem_for(inp["q"], inp["k_cache"])
+    assert da.plan_attention(p)["variant"] == "valu"
+    inp["v_new"][0, 1] = float("nan")
+    out = gu.run_step(p, inp)
+    assert torch.isfinite(out[:, 0].float()).all()
+    assert torch.isnan(out[:, 1].float()).all()
+
+
+def test_last_slot_and_exact_chunk_boundaries():
+    """Contexts that end exactly on, one before and one after chunk boundaries."""
+    S = 1024
+    for chunk in (64, 256):
+        sp = [chunk - 1, chunk, chunk - 2, S - 1]
+        _say("boundaries", chunk, sp)
+        inp = gu.make_case(4, 1, 16, 8, S, sp, seed=9)
+        p = da.problem_for(inp["q"], inp["k_cache"], chunk_tokens=chunk)
+        gu.check_layer(p, inp)
+
+
+def test_long_context_max_cache():
+    """A 128k-slot cache with one long sequence and one short one."""
+    S = 131072
+    _say("long", S)
+    inp = gu.make_case(2, 1, 16, 8, S, [S - 1, 5000], seed=10)
+    p = da.problem_for(inp["q"], inp["k_cache"])
+    rows = np.array([[0, 0, h] for h in range(16)] + [[1, 0, h] for h in range(0, 16, 5)])
+    gu.check_layer(p, inp, rows=rows)
+
+
+def test_custom_scale():
+    _say("scale")
+    inp = gu.make_case(2, 1, 16, 8, 600, [599, 300], seed=11)
+    p = da.problem_for(inp["q"], inp["k_cache"], scale=0.3)
+    gu.check_layer(p, inp)
+
+
+# ------------------------------------------------------------------ the ABI on the GPU
+
+def test_variant_choice():
+    assert da.plan_attention(da.problem(8, 4, 32, 4, 128, 8192, "bf16"))["variant"] == "mfma"
+    assert da.plan_attention(da.problem(4, 1, 64, 8, 128, 16384, "bf16"))["variant"] == "valu"
+    assert da.plan_attention(da.problem(1, 2, 8, 1, 128, 64, "bf16"))["variant"] == "mfma"
+    assert da.plan_attention(da.problem(1, 1, 15, 1, 128, 64, "bf16"))["variant"] == "valu"
+
+
+def test_errors_launch_nothing():
+    """Host-checkable errors return a status and enqueue nothing: the cache is untouched."""
+    import ctypes
+    inp = gu.make_case(2, 1, 16, 8, 256, [10, 20], seed=12)
+    before_k, before_v = inp["k_cache"].clone(), inp["v_cache"].clone()
+    good = da.problem_for(inp["q"], inp["k_cache"])
+    bad_dim = da.problem_for(inp["q"], inp["k_cache"])
+    bad_dim.head_dim = 64
+    ptr = {k: v.data_ptr() for k, v in inp.items()}
+
+    def append(prob, k_off=0):
+        return da.lib.da_kv_append(ctypes.byref(prob), ptr["k_cache"] + k_off, ptr["v_cache"],
+                                   ptr["k_new"], ptr["v_new"], ptr["seq_pos"], None)
+
+    assert append(bad_dim) == da.DA_ERR_UNSUPPORTED
+    assert append(good, k_off=2) == da.DA_ERR_INVALID_ARG  # misaligned cache pointer
+    ws = da.new_workspace(good)
+    st = da.lib.da_gqa_decode_attn(ctypes.byref(good), ptr["q"], ptr["k_cache"], ptr["v_cache"],
+                                   ptr["seq_pos"], ws.data_ptr(), ws.numel() - 1, None)
+    assert st == da.DA_ERR_WORKSPACE
+    torch.cuda.synchronize()
+    assert torch.equal(inp["k_cache"], before_k) and torch.equal(inp["v_cache"], before_v)
+
+
+def test_non_default_stream_ordering():
+    """Append, attention and combine enqueued on a side stream behind a long copy."""
+    inp = gu.make_case(4, 1, 16, 8, 4096, [4095, 100, 2000, 3000], seed=13)
+    p = da.problem_for(inp["q"], inp["k_cache"])
+    s = torch.cuda.Stream()
+    big = torch.empty(1 << 28, dtype=torch.uint8, device="cuda")
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        big.fill_(1)  # keeps the stream busy before the step starts
+        stats = gu.check_layer(p, inp, stream=s)
+    torch.cuda.synchronize()
+    _say("side stream", stats)
+
+
+def test_kernel_reads_caller_data():
+    """Two steps on different caches through the same workspace give each its own answer."""
+    a = gu.make_case(1, 1, 16, 8, 512, [511], seed=14)
+    b = gu.make_case(1, 1, 16, 8, 512, [511], seed=15)
+    p = da.problem_for(a["q"], a["k_cache"])
+    ws = da.new_workspace(p)
+    outs = []
+    for inp in (a, b):
+        out = torch.empty_like(inp["q"])
+        da.decode_step(p, inp["q"], inp["k_cache"], inp["v_cache"], inp["k_new"], inp["v_new"],
+                       inp["seq_pos"], ws, out)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert not torch.equal(outs[0], outs[1])
+    for inp, out in zip((a, b), outs):
+        ref = gu.oracle.gqa_decode(bits(inp["q"]), bits(inp["k_cache"]), bits(inp["v_cache"]),
+                                   inp["seq_pos"].cpu().numpy(), gu.oracle.BF16)
+        gu.compare_out(out, ref)
