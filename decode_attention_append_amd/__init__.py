@@ -47,6 +47,8 @@ class Problem(ctypes.Structure):
         ("dtype", ctypes.c_int32),
         ("scale", ctypes.c_float),
         ("chunk_tokens", ctypes.c_int32),
+        ("variant", ctypes.c_int32),
+        ("workgroups", ctypes.c_int32),
     ]
 
     def __repr__(self):
@@ -61,12 +63,15 @@ class Plan(ctypes.Structure):
         ("n_chunks", ctypes.c_int32),
         ("rows", ctypes.c_int32),
         ("variant", ctypes.c_int32),
+        ("balanced", ctypes.c_int32),
+        ("target_workgroups", ctypes.c_int32),
+        ("grid", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),
     ]
 
 
 EXPORTS = ("da_plan_attention", "da_workspace_bytes", "da_kv_append", "da_gqa_decode_attn",
-           "da_gqa_decode_attn_combine", "da_status_str")
+           "da_gqa_decode_attn_combine", "da_chunk_layout", "da_status_str")
 
 
 def _load():
@@ -87,46 +92,82 @@ def _load():
     lib.da_gqa_decode_attn.restype = ctypes.c_int
     lib.da_gqa_decode_attn_combine.argtypes = [pp, vp, sz, i32p, vp, vp]
     lib.da_gqa_decode_attn_combine.restype = ctypes.c_int
+    lib.da_chunk_layout.argtypes = [pp, vp, vp, vp]
+    lib.da_chunk_layout.restype = ctypes.c_int
     lib.da_status_str.argtypes = [ctypes.c_int]
     lib.da_status_str.restype = ctypes.c_char_p
     return lib
 
 
-lib = _load()
+_lib = None
+
+
+def _get_lib():
+    global _lib
+    if _lib is None:
+        _lib = _load()
+    return _lib
+
+
+def __getattr__(name):
+    # ``lib`` (the ctypes handle) loads on first use, so that building the library
+    # does not need an already-built one; a missing library still fails loudly there.
+    if name == "lib":
+        return _get_lib()
+    raise AttributeError(name)
 
 
 def status_str(status: int) -> str:
-    return lib.da_status_str(status).decode()
+    return _get_lib().da_status_str(status).decode()
 
 
 def problem(batch, q_len, n_q_heads, n_kv_heads, head_dim, max_seq, dtype, scale=0.0,
-            chunk_tokens=0) -> Problem:
+            chunk_tokens=0, variant=None, workgroups=0) -> Problem:
+    """variant: None (automatic), "valu" or "mfma"; chunk_tokens 0 = balanced chunks."""
     if isinstance(dtype, torch.dtype):
         dtype = _DTYPE_CODE[dtype]
     elif isinstance(dtype, str):
         dtype = {"bf16": DA_BF16, "fp16": DA_FP16}[dtype]
+    v = 0 if variant is None else {"valu": 1, "mfma": 2}[variant]
     return Problem(batch, q_len, n_q_heads, n_kv_heads, head_dim, max_seq, dtype, float(scale),
-                   chunk_tokens)
+                   chunk_tokens, v, workgroups)
 
 
-def problem_for(q: torch.Tensor, k_cache: torch.Tensor, scale=0.0, chunk_tokens=0) -> Problem:
+def problem_for(q: torch.Tensor, k_cache: torch.Tensor, scale=0.0, chunk_tokens=0,
+                variant=None, workgroups=0) -> Problem:
     """The problem described by q [B, q_len, Hq, D] and a cache [B, Hkv, S, D]."""
     B, q_len, Hq, D = q.shape
     _, Hkv, S, _ = k_cache.shape
-    return problem(B, q_len, Hq, Hkv, D, S, q.dtype, scale, chunk_tokens)
+    return problem(B, q_len, Hq, Hkv, D, S, q.dtype, scale, chunk_tokens, variant, workgroups)
 
 
 def plan_attention(p: Problem) -> dict:
     pl = Plan()
-    st = lib.da_plan_attention(ctypes.byref(p), ctypes.byref(pl))
+    st = _get_lib().da_plan_attention(ctypes.byref(p), ctypes.byref(pl))
     if st != DA_OK:
         raise DecodeAttnError(st, "da_plan_attention")
     return {"chunk_tokens": pl.chunk_tokens, "n_chunks": pl.n_chunks, "rows": pl.rows,
-            "variant": VARIANTS[pl.variant], "workspace_bytes": pl.workspace_bytes}
+            "variant": VARIANTS[pl.variant], "balanced": bool(pl.balanced),
+            "target_workgroups": pl.target_workgroups, "grid": pl.grid,
+            "workspace_bytes": pl.workspace_bytes}
+
+
+def chunk_layout(p: Problem, seq_pos) -> list:
+    """[(n_chunks, chunk_len)] per sequence for these seq_pos values (host computation)."""
+    import numpy as np
+    sp = np.ascontiguousarray(np.asarray(seq_pos, dtype=np.int32))
+    if sp.shape != (p.batch,):
+        raise ValueError("seq_pos must have one value per sequence")
+    n = np.zeros(p.batch, dtype=np.int32)
+    ln = np.zeros(p.batch, dtype=np.int32)
+    st = _get_lib().da_chunk_layout(ctypes.byref(p), sp.ctypes.data, n.ctypes.data, ln.ctypes.data)
+    if st != DA_OK:
+        raise DecodeAttnError(st, "da_chunk_layout")
+    return list(zip(n.tolist(), ln.tolist()))
 
 
 def workspace_bytes(p: Problem) -> int:
-    return lib.da_workspace_bytes(ctypes.byref(p))
+    return _get_lib().da_workspace_bytes(ctypes.byref(p))
 
 
 def new_workspace(p: Problem, device="cuda") -> torch.Tensor:
@@ -166,7 +207,7 @@ def kv_append(p: Problem, k_cache, v_cache, k_new, v_new, seq_pos, stream=None):
     e = _elem(p)
     cs = (p.batch, p.n_kv_heads, p.max_seq, p.head_dim)
     ns = (p.batch, p.q_len, p.n_kv_heads, p.head_dim)
-    st = lib.da_kv_append(ctypes.byref(p), _dev(k_cache, "k_cache", cs, e), _dev(v_cache, "v_cache", cs, e),
+    st = _get_lib().da_kv_append(ctypes.byref(p), _dev(k_cache, "k_cache", cs, e), _dev(v_cache, "v_cache", cs, e),
                           _dev(k_new, "k_new", ns, e), _dev(v_new, "v_new", ns, e),
                           _dev(seq_pos, "seq_pos", (p.batch,), torch.int32), _stream(stream))
     if st != DA_OK:
@@ -177,7 +218,7 @@ def gqa_decode_attn(p: Problem, q, k_cache, v_cache, seq_pos, workspace, stream=
     """da_gqa_decode_attn: fp32 split-context partials into ``workspace``."""
     e = _elem(p)
     cs = (p.batch, p.n_kv_heads, p.max_seq, p.head_dim)
-    st = lib.da_gqa_decode_attn(ctypes.byref(p),
+    st = _get_lib().da_gqa_decode_attn(ctypes.byref(p),
                                 _dev(q, "q", (p.batch, p.q_len, p.n_q_heads, p.head_dim), e),
                                 _dev(k_cache, "k_cache", cs, e), _dev(v_cache, "v_cache", cs, e),
                                 _dev(seq_pos, "seq_pos", (p.batch,), torch.int32),
@@ -190,7 +231,7 @@ def gqa_decode_attn(p: Problem, q, k_cache, v_cache, seq_pos, workspace, stream=
 def gqa_decode_attn_combine(p: Problem, workspace, seq_pos, out, stream=None):
     """da_gqa_decode_attn_combine: merge the partials into ``out`` [B, q_len, Hq, D]."""
     e = _elem(p)
-    st = lib.da_gqa_decode_attn_combine(
+    st = _get_lib().da_gqa_decode_attn_combine(
         ctypes.byref(p), _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _dev(seq_pos, "seq_pos", (p.batch,), torch.int32),
         _dev(out, "out", (p.batch, p.q_len, p.n_q_heads, p.head_dim), e), _stream(stream))

@@ -4,7 +4,7 @@
 // What is computed ("Qwen MoE BringUp", Per-Layer IR Patterns, "Attention
 // Computation", split as in the split-KV phase of the 3-phase flash decode in
 // "Architecture Diagram - Qwen3-30B-A3B (Extern Dispatch, 75 tok/s)"): for one
-// (sequence b, KV head h, chunk c of `chunk` keys) and each query row r of
+// (sequence b, KV head h, chunk c of the context) and each query row r of
 // that KV head,
 //     s_j  = (q_r . k_j) * scale * log2(e)          visible keys j of the chunk
 //     m    = max_j s_j,  p_j = 2^(s_j - m),  l = sum_j p_j
@@ -31,16 +31,14 @@ __global__ __launch_bounds__(256) void attn_split_valu_kernel(AttnParams p) {
     __shared__ float row_m[RP], row_l[RP];
 
     const int n_chunks = p.n_chunks;
-    const int c = blockIdx.x % n_chunks;
-    const int bh = blockIdx.x / n_chunks;
-    const int b = bh / p.n_kv_heads;
-    const int h = bh - b * p.n_kv_heads;
+    int b, h, c;
+    SeqChunks sc;
+    if (!locate(p, blockIdx.x, b, h, c, sc)) return;  // past the last chunk of the launch
+    const int bh = b * p.n_kv_heads + h;
     const int sp = p.seq_pos[b];
-    if (sp < 0 || sp > p.max_seq - p.q_len) return;
-    const int ctx = sp + p.q_len;
-    const int t0 = c * p.chunk;
-    if (t0 >= ctx) return;  // chunk past the context: never read by the combine
-    const int n_tok = min(p.chunk, ctx - t0);
+    const int ctx = sc.ctx;
+    const int t0 = c * sc.len;
+    const int n_tok = min(sc.len, ctx - t0);
     const int n_slab = (n_tok + 15) >> 4;  // 16-key slabs; a wave does one per step
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -90,19 +88,19 @@ __global__ __launch_bounds__(256) void attn_split_valu_kernel(AttnParams p) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int tl = s * 16 + u * 4 + gq;
-                float sc[RP];
+                float score[RP];
 #pragma unroll
                 for (int r = 0; r < RP; ++r) {
                     float a = dot2<F16>(qr[r][0], cur[u][0], 0.f);
                     a = dot2<F16>(qr[r][1], cur[u][1], a);
                     a = dot2<F16>(qr[r][2], cur[u][2], a);
                     a = dot2<F16>(qr[r][3], cur[u][3], a);
-                    sc[r] = row16_sum(a);
+                    score[r] = row16_sum(a);
                 }
                 if (cq == 0) {
 #pragma unroll
                     for (int r = 0; r < RP; ++r)
-                        lds[tl * RP + r] = tl < vis[r] ? sc[r] * p.scale_log2 : -INFINITY;
+                        lds[tl * RP + r] = tl < vis[r] ? score[r] * p.scale_log2 : -INFINITY;
                 }
             }
 #pragma unroll
@@ -211,24 +209,23 @@ __global__ __launch_bounds__(256) void attn_split_valu_kernel(AttnParams p) {
 }
 
 template <bool F16, int RP>
-static hipError_t launch_rp(const AttnParams &p, hipStream_t s) {
-    const int grid = p.batch * p.n_kv_heads * p.n_chunks;
-    const size_t lds_bytes = (size_t)RP * (p.chunk > 512 ? p.chunk : 512) * sizeof(float);
+static hipError_t launch_rp(const AttnParams &p, int grid, hipStream_t s) {
+    const size_t lds_bytes = (size_t)RP * (p.max_chunk > 512 ? p.max_chunk : 512) * sizeof(float);
     hipLaunchKernelGGL((attn_split_valu_kernel<F16, RP>), dim3(grid), dim3(256), lds_bytes, s, p);
     return hipGetLastError();
 }
 
 template <bool F16>
-static hipError_t launch_dtype(const AttnParams &p, hipStream_t s) {
-    if (p.rows <= 1) return launch_rp<F16, 1>(p, s);
-    if (p.rows <= 2) return launch_rp<F16, 2>(p, s);
-    if (p.rows <= 4) return launch_rp<F16, 4>(p, s);
-    if (p.rows <= 8) return launch_rp<F16, 8>(p, s);
-    return launch_rp<F16, 16>(p, s);
+static hipError_t launch_dtype(const AttnParams &p, int grid, hipStream_t s) {
+    if (p.rows <= 1) return launch_rp<F16, 1>(p, grid, s);
+    if (p.rows <= 2) return launch_rp<F16, 2>(p, grid, s);
+    if (p.rows <= 4) return launch_rp<F16, 4>(p, grid, s);
+    if (p.rows <= 8) return launch_rp<F16, 8>(p, grid, s);
+    return launch_rp<F16, 16>(p, grid, s);
 }
 
-hipError_t launch_attn_valu(const AttnParams &p, bool fp16, hipStream_t s) {
-    return fp16 ? launch_dtype<true>(p, s) : launch_dtype<false>(p, s);
+hipError_t launch_attn_valu(const AttnParams &p, int grid, bool fp16, hipStream_t s) {
+    return fp16 ? launch_dtype<true>(p, grid, s) : launch_dtype<false>(p, grid, s);
 }
 
 }  // namespace da

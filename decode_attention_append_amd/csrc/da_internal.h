@@ -36,9 +36,85 @@ struct AttnParams {
     int32_t batch, q_len, n_q_heads, n_kv_heads, max_seq;
     int32_t group;  // Hq / Hkv
     int32_t rows;   // group * q_len
-    int32_t n_chunks, chunk;
-    float scale_log2;  // softmax scale * log2(e): scores are kept in log2 units
+    int32_t n_chunks;      // chunk slots per (sequence, KV head) in the workspace
+    int32_t fixed_chunk;   // > 0: every chunk has this many keys; 0: balanced chunks
+    int32_t target_wg;     // balanced: workgroups to aim for over the whole launch
+    int32_t min_chunk;     // balanced: smallest chunk (multiple of 32)
+    int32_t max_chunk;     // largest chunk the kernel accepts (multiple of 32)
+    float scale_log2;      // softmax scale * log2(e): scores are kept in log2 units
 };
+
+// ---- split-context chunk plan, computed identically by every kernel ---------
+//
+// Balanced mode: the chunk length aims at an equal share of all visible keys
+// per workgroup, T = ceil32(Hkv * sum_b ctx_b / target_wg) clamped to
+// [min_chunk, max_chunk]; sequence b gets n_b = max(round(ctx_b / T),
+// ceil(ctx_b / max_chunk)) chunks of ceil32(ctx_b / n_b) keys, so chunks of
+// one sequence are equal and all chunks are close to T.  Fixed mode: chunks of
+// fixed_chunk keys.  A sequence whose seq_pos breaks the contract has no
+// chunks.  Workgroups are laid out sequence-major: for b, for h, for c.
+
+struct SeqChunks {
+    int n;      // chunks of this sequence (0 if its seq_pos is out of range)
+    int len;    // keys per chunk (the last may be shorter)
+    int ctx;    // visible keys
+};
+
+__host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+__host__ __device__ inline int round_up32(int a) { return (a + 31) & ~31; }
+
+__host__ __device__ inline bool seq_pos_ok(const AttnParams &p, int sp) {
+    return sp >= 0 && sp <= p.max_seq - p.q_len;
+}
+
+__host__ __device__ inline int balanced_chunk(const AttnParams &p) {
+    int64_t total = 0;
+    for (int b = 0; b < p.batch; ++b) {
+        const int sp = p.seq_pos[b];
+        if (seq_pos_ok(p, sp)) total += sp + p.q_len;
+    }
+    const int64_t want = (total * p.n_kv_heads + p.target_wg - 1) / p.target_wg;
+    int t = (int)(want < p.max_chunk ? want : p.max_chunk);
+    t = round_up32(t);
+    return t < p.min_chunk ? p.min_chunk : (t > p.max_chunk ? p.max_chunk : t);
+}
+
+__host__ __device__ inline SeqChunks seq_chunks(const AttnParams &p, int b, int T) {
+    SeqChunks s{0, 0, 0};
+    const int sp = p.seq_pos[b];
+    if (!seq_pos_ok(p, sp)) return s;
+    s.ctx = sp + p.q_len;
+    if (p.fixed_chunk > 0) {
+        s.len = p.fixed_chunk;
+        s.n = ceil_div(s.ctx, s.len);
+        return s;
+    }
+    int n = (2 * s.ctx + T) / (2 * T);  // round(ctx / T)
+    const int n_cap = ceil_div(s.ctx, p.max_chunk);
+    if (n < n_cap) n = n_cap;
+    if (n < 1) n = 1;
+    if (n > p.n_chunks) n = p.n_chunks;
+    s.n = n;
+    s.len = round_up32(ceil_div(s.ctx, n));
+    s.n = ceil_div(s.ctx, s.len);  // rounding the length up may leave the last chunk empty
+    return s;
+}
+
+// Which (b, h, c) workgroup `w` owns; false if w is past the last chunk.
+__host__ __device__ inline bool locate(const AttnParams &p, int w, int &b, int &h, int &c, SeqChunks &sc) {
+    const int T = p.fixed_chunk > 0 ? p.fixed_chunk : balanced_chunk(p);
+    for (b = 0; b < p.batch; ++b) {
+        sc = seq_chunks(p, b, T);
+        const int here = sc.n * p.n_kv_heads;
+        if (w < here) {
+            h = w / sc.n;
+            c = w - h * sc.n;
+            return true;
+        }
+        w -= here;
+    }
+    return false;
+}
 
 // Workspace carving, shared by the attention and the combine.
 inline size_t ws_acc_floats(int32_t bh, int32_t n_chunks, int32_t rows) {
@@ -51,8 +127,8 @@ inline size_t ws_ml_floats(int32_t bh, int32_t n_chunks, int32_t rows) {
 // ---- host-side launch entry points (one per translation unit) ---------------
 
 hipError_t launch_kv_append(const AppendParams &p, int threads_total, hipStream_t s);
-hipError_t launch_attn_valu(const AttnParams &p, bool fp16, hipStream_t s);
-hipError_t launch_attn_mfma(const AttnParams &p, bool fp16, hipStream_t s);
+hipError_t launch_attn_valu(const AttnParams &p, int grid, bool fp16, hipStream_t s);
+hipError_t launch_attn_mfma(const AttnParams &p, int grid, bool fp16, hipStream_t s);
 hipError_t launch_attn_combine(const AttnParams &p, bool fp16, void *out, hipStream_t s);
 
 // ---- device helpers --------------------------------------------------------
@@ -61,6 +137,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));

@@ -10,8 +10,9 @@ namespace {
 
 using namespace da;
 
-constexpr int kWorkgroupsWanted = 2048;  // 8 per compute unit on a 256-CU MI355X
-constexpr int kMaxSeq = 1 << 24;
+constexpr int kMaxSeq = 1 << 21;       // 2M slots: at most 2048 chunks of the shortest max chunk (1024)
+constexpr int kMaxChunks = 2048;       // the combine keeps one weight per chunk in LDS
+constexpr int kMaxValuRows = 16;       // the vector-ALU kernel's widest row set
 
 bool aligned16(const void *x) { return ((uintptr_t)x & 15u) == 0; }
 
@@ -28,11 +29,17 @@ da_status check_problem(const da_problem *p) {
     if (p->chunk_tokens != 0 &&
         (p->chunk_tokens < kTokenTile || p->chunk_tokens > kMaxChunk || p->chunk_tokens % kTokenTile))
         return DA_ERR_INVALID_ARG;
+    if (p->variant < 0 || p->variant > DA_VARIANT_MFMA + 1) return DA_ERR_INVALID_ARG;
+    if (p->workgroups < 0 || p->workgroups > (1 << 20)) return DA_ERR_INVALID_ARG;
     if (p->dtype != DA_BF16 && p->dtype != DA_FP16) return DA_ERR_UNSUPPORTED;
     if (p->head_dim != kHeadDim) return DA_ERR_UNSUPPORTED;
     if (p->q_len > kMaxQLen) return DA_ERR_UNSUPPORTED;
     if ((int64_t)(p->n_q_heads / p->n_kv_heads) * p->q_len > kMaxRows) return DA_ERR_UNSUPPORTED;
     if (p->max_seq > kMaxSeq) return DA_ERR_UNSUPPORTED;
+    if (p->variant == DA_VARIANT_VALU + 1 && (p->n_q_heads / p->n_kv_heads) * p->q_len > kMaxValuRows)
+        return DA_ERR_UNSUPPORTED;
+    if (p->chunk_tokens != 0 && (p->max_seq + p->chunk_tokens - 1) / p->chunk_tokens > kMaxChunks)
+        return DA_ERR_UNSUPPORTED;
     // grid sizes stay within int
     if ((int64_t)p->batch * p->n_kv_heads * ((p->max_seq + kTokenTile - 1) / kTokenTile) > INT32_MAX / 2)
         return DA_ERR_UNSUPPORTED;
@@ -40,29 +47,54 @@ da_status check_problem(const da_problem *p) {
     return DA_OK;
 }
 
-// Keys per chunk: the largest power of two (<= 1024) that still gives the
-// launch about kWorkgroupsWanted workgroups, so the 256 compute units each get
-// several; the MFMA kernel's partials are 32 rows wide, so it keeps chunks of
-// at least 256 keys to bound the partials traffic.
-int auto_chunk(const da_problem *p, int rows) {
-    const int64_t units = (int64_t)p->batch * p->n_kv_heads;
-    const int min_chunk = rows >= 16 ? 256 : kTokenTile;
-    int chunk = 1024;
-    while (chunk > min_chunk && units * ((p->max_seq + chunk - 1) / chunk) < kWorkgroupsWanted) chunk >>= 1;
-    return chunk;
+// Workgroups to aim for in balanced mode, per kernel: enough for every one of
+// the 256 compute units to hold a few resident workgroups at the kernel's
+// occupancy, so that the dispatcher balances what the chunking does not.
+int default_target(int variant, int rows) {
+    if (variant == DA_VARIANT_MFMA) return rows > 16 ? 256 : 512;
+    return 1024;
 }
+
+// Longest chunk a kernel accepts: the vector-ALU kernel keeps the chunk's
+// scores in LDS (rows x chunk floats, at most 64 KiB).
+int max_chunk_of(int variant, int rows) {
+    if (variant == DA_VARIANT_MFMA) return 4096;
+    const int rp = rows <= 1 ? 1 : rows <= 2 ? 2 : rows <= 4 ? 4 : rows <= 8 ? 8 : 16;
+    return rp <= 8 ? 2048 : 1024;
+}
+
+constexpr int kMinChunk = 64;
 
 void plan_of(const da_problem *p, da_plan *pl) {
     const int rows = (p->n_q_heads / p->n_kv_heads) * p->q_len;
-    const int chunk = p->chunk_tokens ? p->chunk_tokens : auto_chunk(p, rows);
-    const int n_chunks = (p->max_seq + chunk - 1) / chunk;
-    const int32_t bh = p->batch * p->n_kv_heads;
-    pl->chunk_tokens = chunk;
-    pl->n_chunks = n_chunks;
+    const int variant = p->variant ? p->variant - 1 : (rows >= 16 ? DA_VARIANT_MFMA : DA_VARIANT_VALU);
+    const int units = p->batch * p->n_kv_heads;
     pl->rows = rows;
-    pl->variant = rows >= 16 ? DA_VARIANT_MFMA : DA_VARIANT_VALU;
-    pl->workspace_bytes = align256(ws_acc_floats(bh, n_chunks, rows) * sizeof(float)) +
-                          ws_ml_floats(bh, n_chunks, rows) * sizeof(float);
+    pl->variant = variant;
+    if (p->chunk_tokens) {  // fixed chunks
+        pl->balanced = 0;
+        pl->chunk_tokens = p->chunk_tokens;
+        pl->n_chunks = (p->max_seq + p->chunk_tokens - 1) / p->chunk_tokens;
+        pl->target_workgroups = units * pl->n_chunks;
+        pl->grid = units * pl->n_chunks;
+    } else {
+        const int max_chunk = max_chunk_of(variant, rows);
+        pl->balanced = 1;
+        pl->chunk_tokens = max_chunk;
+        // slots for the most chunks a sequence can get; max_seq <= 2048 * max_chunk
+        // keeps ceil(ctx / max_chunk) within them, so no chunk exceeds max_chunk
+        const int slots = (p->max_seq + kMinChunk - 1) / kMinChunk;
+        pl->n_chunks = slots < kMaxChunks ? slots : kMaxChunks;
+        pl->target_workgroups = p->workgroups > 0 ? p->workgroups : default_target(variant, rows);
+        // at most target + one rounding chunk per (sequence, head), or every
+        // sequence in chunks of max_chunk keys when the target is too few
+        const int64_t a = (int64_t)pl->target_workgroups + units;
+        const int64_t b = (int64_t)units * ((p->max_seq + max_chunk - 1) / max_chunk);
+        pl->grid = (int32_t)(a > b ? a : b);
+    }
+    const int32_t bh = units;
+    pl->workspace_bytes = align256(ws_acc_floats(bh, pl->n_chunks, rows) * sizeof(float)) +
+                          ws_ml_floats(bh, pl->n_chunks, rows) * sizeof(float);
 }
 
 AttnParams attn_params(const da_problem *p, const da_plan &pl, const void *q, const void *k_cache,
@@ -83,7 +115,10 @@ AttnParams attn_params(const da_problem *p, const da_plan &pl, const void *q, co
     a.group = p->n_q_heads / p->n_kv_heads;
     a.rows = pl.rows;
     a.n_chunks = pl.n_chunks;
-    a.chunk = pl.chunk_tokens;
+    a.fixed_chunk = pl.balanced ? 0 : pl.chunk_tokens;
+    a.target_wg = pl.target_workgroups;
+    a.min_chunk = kMinChunk;
+    a.max_chunk = pl.chunk_tokens;
     const double scale = p->scale > 0.f ? (double)p->scale : 1.0 / sqrt((double)p->head_dim);
     a.scale_log2 = (float)(scale * 1.4426950408889634);  // log2(e)
     return a;
@@ -145,8 +180,8 @@ da_status da_gqa_decode_attn(const da_problem *p, const void *q, const void *k_c
     const AttnParams a = attn_params(p, pl, q, k_cache, v_cache, seq_pos, workspace);
     (void)hipGetLastError();
     const hipError_t e = pl.variant == DA_VARIANT_MFMA
-                             ? launch_attn_mfma(a, p->dtype == DA_FP16, (hipStream_t)stream)
-                             : launch_attn_valu(a, p->dtype == DA_FP16, (hipStream_t)stream);
+                             ? launch_attn_mfma(a, pl.grid, p->dtype == DA_FP16, (hipStream_t)stream)
+                             : launch_attn_valu(a, pl.grid, p->dtype == DA_FP16, (hipStream_t)stream);
     return e == hipSuccess ? DA_OK : DA_ERR_HIP;
 }
 
@@ -164,6 +199,23 @@ da_status da_gqa_decode_attn_combine(const da_problem *p, const void *workspace,
     (void)hipGetLastError();
     return launch_attn_combine(a, p->dtype == DA_FP16, out, (hipStream_t)stream) == hipSuccess ? DA_OK
                                                                                                  : DA_ERR_HIP;
+}
+
+da_status da_chunk_layout(const da_problem *p, const int32_t *seq_pos_host, int32_t *n_chunks,
+                          int32_t *chunk_len) {
+    const da_status st = check_problem(p);
+    if (st != DA_OK) return st;
+    if (!seq_pos_host || !n_chunks || !chunk_len) return DA_ERR_INVALID_ARG;
+    da_plan pl;
+    plan_of(p, &pl);
+    const AttnParams a = attn_params(p, pl, nullptr, nullptr, nullptr, seq_pos_host, nullptr);
+    const int T = a.fixed_chunk > 0 ? a.fixed_chunk : balanced_chunk(a);
+    for (int b = 0; b < p->batch; ++b) {
+        const SeqChunks sc = seq_chunks(a, b, T);
+        n_chunks[b] = sc.n;
+        chunk_len[b] = sc.n ? sc.len : 0;
+    }
+    return DA_OK;
 }
 
 const char *da_status_str(da_status s) {

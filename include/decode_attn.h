@@ -82,23 +82,41 @@ typedef struct {
     float scale;          /* softmax scale; <= 0 selects 1 / sqrt(head_dim)       */
     int32_t chunk_tokens; /* keys per split-context chunk: 0 = automatic, else a
                              multiple of 64 (a tuning and testing override)       */
+    int32_t variant;      /* attention kernel: 0 = automatic, else DA_VARIANT_* + 1
+                             (a tuning and testing override; the vector-ALU kernel
+                             takes at most 16 rows per KV head)                   */
+    int32_t workgroups;   /* balanced chunking: attention workgroups to aim for,
+                             0 = automatic (a tuning override)                    */
 } da_problem;
 
-/* What the library will launch for a problem (a pure function of *p). */
+/*
+ * What the library will launch for a problem (a pure function of *p).
+ *
+ * Chunking.  With chunk_tokens == 0 the chunks are balanced on the device:
+ * from the actual seq_pos values, every sequence's context is cut into equal
+ * chunks whose length is close to an equal share of all visible keys per
+ * workgroup (about `target_workgroups` of them), never longer than
+ * `chunk_tokens` (the plan's maximum) and never shorter than 64 keys.  With an
+ * explicit chunk_tokens every chunk has that length.  Either way the
+ * attention and the combine derive the same chunks from the same seq_pos.
+ */
 typedef struct {
-    int32_t chunk_tokens;    /* keys per chunk                                 */
-    int32_t n_chunks;        /* chunks per (sequence, KV head) = ceil(max_seq / chunk_tokens) */
-    int32_t rows;            /* query rows per KV head = (Hq / Hkv) * q_len    */
-    int32_t variant;         /* DA_VARIANT_*                                   */
-    size_t workspace_bytes;  /* bytes of fp32 partials the attention needs     */
+    int32_t chunk_tokens;    /* longest chunk (fixed mode: every chunk)          */
+    int32_t n_chunks;        /* chunk slots per (sequence, KV head) in the workspace */
+    int32_t rows;            /* query rows per KV head = (Hq / Hkv) * q_len      */
+    int32_t variant;         /* DA_VARIANT_*                                     */
+    int32_t balanced;        /* 1: balanced chunks, 0: fixed chunks              */
+    int32_t target_workgroups; /* balanced: workgroups aimed at                  */
+    int32_t grid;            /* workgroups launched (an upper bound; extras exit) */
+    size_t workspace_bytes;  /* bytes of fp32 partials the attention needs       */
 } da_plan;
 
 enum { DA_VARIANT_VALU = 0, DA_VARIANT_MFMA = 1 };
 
 /*
  * Plans the attention of *p: chunking, kernel variant, workspace size.  The
- * variant is the MFMA kernel when rows >= 16 (Q K^T and P V are then real
- * small matrix products), the vector-ALU kernel otherwise.
+ * automatic variant is the MFMA kernel when rows >= 16 (Q K^T and P V are then
+ * real small matrix products), the vector-ALU kernel otherwise.
  * Returns DA_OK, DA_ERR_INVALID_ARG or DA_ERR_UNSUPPORTED.  Host only.
  */
 da_status da_plan_attention(const da_problem *p, da_plan *plan);
@@ -138,6 +156,16 @@ da_status da_gqa_decode_attn(const da_problem *p, const void *q, const void *k_c
 da_status da_gqa_decode_attn_combine(const da_problem *p, const void *workspace,
                                      size_t workspace_bytes, const int32_t *seq_pos, void *out,
                                      void *stream);
+
+/*
+ * The chunking da_gqa_decode_attn and the combine will use for these seq_pos
+ * values, computed on the host (seq_pos_host is a HOST array of p->batch
+ * values; the kernels derive the same layout from the device copy).  Writes
+ * per sequence the number of chunks and their length in keys (0, 0 for a
+ * sequence whose seq_pos breaks the contract).  Host only, no GPU needed.
+ */
+da_status da_chunk_layout(const da_problem *p, const int32_t *seq_pos_host, int32_t *n_chunks,
+                          int32_t *chunk_len);
 
 /* Static description of a status code. */
 const char *da_status_str(da_status s);

@@ -72,12 +72,26 @@ def test_plan_is_pure_and_sized():
     a, b = da.plan_attention(p), da.plan_attention(p)
     assert a == b
     rows = 2
-    n = a["n_chunks"]
-    assert n * a["chunk_tokens"] >= 8192 and (n - 1) * a["chunk_tokens"] < 8192
-    assert a["workspace_bytes"] >= 32 * 8 * n * rows * (128 + 2) * 4
-    assert a["variant"] == "valu"
+    assert a["balanced"] and a["variant"] == "valu"
+    assert a["n_chunks"] == 8192 // 64  # one slot per 64 keys, the shortest chunk
+    assert a["workspace_bytes"] >= 32 * 8 * a["n_chunks"] * rows * (128 + 2) * 4
+    assert a["grid"] >= a["target_workgroups"] + 32 * 8
     assert da.plan_attention(P(q_len=4, n_q_heads=32, n_kv_heads=4))["variant"] == "mfma"
-    assert da.plan_attention(P(chunk_tokens=128))["chunk_tokens"] == 128
+    fixed = da.plan_attention(P(chunk_tokens=128))
+    assert not fixed["balanced"] and fixed["chunk_tokens"] == 128 and fixed["n_chunks"] == 8
+    assert fixed["grid"] == 2 * 8 * 8
+    assert da.plan_attention(P(workgroups=77))["target_workgroups"] == 77
+    assert da.plan_attention(P(variant="mfma"))["variant"] == "mfma"
+
+
+def test_plan_bounds():
+    # the combine keeps one weight per chunk slot: never more than 2048 slots
+    big = da.plan_attention(P(batch=1, n_q_heads=16, n_kv_heads=1, max_seq=1 << 21))
+    assert big["n_chunks"] <= 2048 and big["chunk_tokens"] * 2048 >= (1 << 21)
+    assert da.workspace_bytes(P(max_seq=(1 << 21) + 64)) == 0
+    assert da.workspace_bytes(P(chunk_tokens=64, max_seq=64 * 2049)) == 0
+    # forcing the vector-ALU kernel past its 16 rows is refused
+    assert da.workspace_bytes(P(n_q_heads=32, n_kv_heads=1, variant="valu")) == 0
 
 
 def test_null_and_misaligned_pointers_rejected_before_launch():

@@ -1,0 +1,87 @@
+"""Host logic of the split-context chunking (the same code the kernels run on the device).
+
+For any seq_pos values: the chunks of a sequence tile its visible context with no
+empty chunk, stay within the kernel's longest chunk and the workspace's chunk
+slots, and the launch grid covers every chunk.
+"""
+import numpy as np
+import pytest
+
+import decode_attention_append_amd as da
+
+
+def check_layout(p, seq_pos):
+    plan = da.plan_attention(p)
+    lay = da.chunk_layout(p, seq_pos)
+    total = 0
+    for sp, (n, ln) in zip(seq_pos, lay):
+        if sp < 0 or sp + p.q_len > p.max_seq:
+            assert (n, ln) == (0, 0)
+            continue
+        ctx = sp + p.q_len
+        assert n >= 1 and ln >= 1
+        assert ln % 32 == 0
+        assert ln <= plan["chunk_tokens"], "chunk longer than the kernel accepts"
+        assert n <= plan["n_chunks"], "more chunks than workspace slots"
+        assert (n - 1) * ln < ctx <= n * ln, "chunks must tile the context, last one non-empty"
+        if not plan["balanced"]:
+            assert ln == plan["chunk_tokens"]
+        total += n
+    total *= p.n_kv_heads
+    assert total <= plan["grid"], "launch grid misses chunks"
+    return plan, lay, total
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_layouts(seed):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 40))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    q_len = int(rng.integers(1, 9))
+    while G * q_len > 32:
+        q_len -= 1
+    S = int(rng.choice([64, 100, 512, 777, 4096, 8192, 16384, 65536]))
+    S = max(S, q_len)
+    chunk = int(rng.choice([0, 0, 0, 64, 128, 256, 1024, 2048]))
+    if chunk and -(-S // chunk) > 2048:
+        chunk = 0
+    variant = [None, "valu", "mfma"][int(rng.integers(0, 3))]
+    if variant == "valu" and G * q_len > 16:
+        variant = None
+    wg = int(rng.choice([0, 0, 1, 37, 256, 5000]))
+    p = da.problem(B, q_len, G * Hkv, Hkv, 128, S, "bf16", chunk_tokens=chunk, variant=variant,
+                   workgroups=wg)
+    kind = rng.integers(0, 3)
+    if kind == 0:
+        sp = rng.integers(0, S - q_len + 1, B)
+    elif kind == 1:  # one long, many short
+        sp = np.zeros(B, dtype=np.int64)
+        sp[0] = S - q_len
+    else:  # all full
+        sp = np.full(B, S - q_len)
+    check_layout(p, sp.astype(np.int32))
+
+
+def test_contract_breaking_positions_get_no_chunks():
+    p = da.problem(4, 2, 16, 8, 128, 1000, "bf16")
+    _, lay, _ = check_layout(p, np.array([-1, 999, 998, 500], np.int32))
+    assert lay[0] == (0, 0) and lay[1] == (0, 0) and lay[2][0] >= 1
+
+
+def test_balanced_chunks_are_equal_share():
+    """Ragged long contexts (GQA 64:8, batch 4, 12k..16k): every chunk close to one
+    workgroup's share of all keys."""
+    p = da.problem(4, 1, 64, 8, 128, 16384, "bf16", workgroups=512)
+    sp = np.array([15488, 13371, 15557, 14115], np.int32)
+    plan, lay, total = check_layout(p, sp)
+    share = 8 * int((sp + 1).sum()) / 512
+    for n, ln in lay:
+        assert 0.9 * share <= ln <= 1.15 * share
+    assert 0.9 * 512 <= total <= 512 + 32  # lengths round up to 32 keys
+
+
+def test_fixed_chunks_match_override():
+    p = da.problem(2, 1, 16, 8, 128, 2500, "bf16", chunk_tokens=256)
+    _, lay, _ = check_layout(p, np.array([2499, 1300], np.int32))
+    assert lay == [(10, 256), (6, 256)]

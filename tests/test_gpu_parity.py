@@ -85,6 +85,23 @@ def test_shapes(B, q_len, Hq, Hkv, S, seq_pos, dtype):
     gu.check_layer(p, inp)
 
 
+@pytest.mark.parametrize("variant", ["valu", "mfma"])
+@pytest.mark.parametrize("B,q_len,Hq,Hkv,S,seq_pos,dtype", [
+    (2, 1, 64, 8, 3000, [2999, 1537], torch.bfloat16),           # rows 8
+    (2, 1, 16, 8, 700, [0, 699], torch.bfloat16),                # rows 2
+    (2, 1, 16, 16, 1000, [999, 64], torch.float16),              # rows 1, fp16
+    (2, 2, 32, 4, 900, [898, 250], torch.bfloat16),              # rows 16, causal
+    (2, 3, 12, 3, 900, [10, 896], torch.float16),                # rows 12, causal
+])
+def test_forced_variant(variant, B, q_len, Hq, Hkv, S, seq_pos, dtype):
+    """Both attention kernels agree with the oracle on every shape they both accept."""
+    _say("variant", variant, B, q_len, Hq, Hkv, S, seq_pos, dtype)
+    inp = gu.make_case(B, q_len, Hq, Hkv, S, seq_pos, dtype, seed=S + q_len)
+    p = da.problem_for(inp["q"], inp["k_cache"], variant=variant)
+    assert da.plan_attention(p)["variant"] == variant
+    gu.check_layer(p, inp)
+
+
 @pytest.mark.parametrize("chunk", [64, 128, 256, 512, 1024, 2048])
 @pytest.mark.parametrize("q_len,Hq,Hkv", [(1, 16, 8), (1, 64, 8), (4, 32, 4)])
 def test_chunk_sweep(chunk, q_len, Hq, Hkv):
