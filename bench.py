@@ -34,6 +34,13 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle sample")
+    ap.add_argument("--flush", choices=["auto", "on", "off"], default="auto",
+                    help="read a 2 GiB buffer before every timed step (outside the timing) so the "
+                         "step starts with cold caches; auto = on when one step touches less than "
+                         "1 GiB, which the 256 MB Infinity Cache could otherwise serve")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain 1 GiB device copy three times, so that hardware "
+                         "byte counters can be scaled by a kernel of known traffic")
     return ap.parse_args()
 
 
@@ -49,21 +56,20 @@ def algorithmic_bytes(w, seq_pos):
 
 
 def counters_for(kernel_tag, workload):
-    """HBM traffic per launch from the committed rocprofv3 counter summary, if it was
-    taken on the current kernel source; else None."""
-    import hashlib
+    """HBM bytes per launch of the kernel from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known size), if it was taken
+    on the current kernel sources; else None."""
+    from decode_attention_append_amd import profiling
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                         f"counters_{kernel_tag}_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "decode_attention_append_amd",
-                       "csrc", rec.get("source", ""))
-    if not os.path.exists(src):
-        return None
-    h = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if h != rec.get("source_sha256"):
+    try:
+        if profiling.source_hash(rec["source"]) != rec.get("source_sha256"):
+            return None
+    except (KeyError, OSError):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -108,6 +114,13 @@ def main():
     w = WORKLOADS[args.workload or BENCH_WORKLOAD]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     print(f"[bench] workload {w.name}: building {w.layers} layers on {torch.cuda.get_device_name(0)}",
           file=sys.stderr, flush=True)
 
@@ -136,22 +149,33 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    kv_bytes, alg_bytes = algorithmic_bytes(w, seq_pos)
+    step_bytes = alg_bytes * w.layers
+    flush = args.flush == "on" or (args.flush == "auto" and step_bytes < (1 << 30))
+    flush_buf = torch.ones(1 << 30, dtype=torch.bfloat16, device=dev) if flush else None
+
     # timed region: K steps, HIP events around every attention launch on the launch stream
     ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
            for _ in range(w.layers)] for _ in range(args.steps)]
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    marks = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+             for _ in range(args.steps if flush else 1)]
     torch.cuda.synchronize()
-    t_start.record(stream)
-    for k in range(args.steps):
-        step(ev[k])
-    t_end.record(stream)
+    if flush:
+        for k in range(args.steps):
+            flush_buf.sum(dtype=torch.float32)  # outside the timed span of the step
+            marks[k][0].record(stream)
+            step(ev[k])
+            marks[k][1].record(stream)
+    else:
+        marks[0][0].record(stream)
+        for k in range(args.steps):
+            step(ev[k])
+        marks[0][1].record(stream)
     torch.cuda.synchronize()
-    ms_total = t_start.elapsed_time(t_end)
+    ms_total = sum(a.elapsed_time(b) for a, b in marks)
     attn_ms = [e0.elapsed_time(e1) for evk in ev for (e0, e1) in evk]
 
     ms_per_step = ms_total / args.steps
-    kv_bytes, alg_bytes = algorithmic_bytes(w, seq_pos)
-    step_bytes = alg_bytes * w.layers
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
 
     # dominant kernel: the split-context attention; its algorithmic bytes per launch are the
@@ -180,7 +204,8 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "q_len": w.q_len, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "context": int(seq_pos.max()) + w.q_len,
                    "max_seq": w.max_seq, "layers": w.layers, "chunk_tokens": plan["chunk_tokens"],
-                   "variant": plan["variant"], "bytes_per_step": step_bytes},
+                   "variant": plan["variant"], "bytes_per_step": step_bytes,
+                   "cold_cache_flush": flush},
         "roofline": {"bound": "hbm", "kernel": kernel_tag, "achieved": round(attn_gbs, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
                      "avg_launch_us": round(attn_avg_ms * 1e3, 3), "bytes_per_launch": attn_bytes,

@@ -1,7 +1,7 @@
 // Split-context attention partials on the matrix cores.  With many query
-// rows sharing each key (e.g. a 4-token speculative verify with 8 query heads
-// per KV head: 32 rows), Q K^T and P V are real small matrix products, so they
-// run as bf16/fp16 MFMA with fp32 accumulation ("Architecture Diagram -
+// rows sharing each key (8 query heads per KV head, or a 4-token speculative
+// verify with 8 query heads per KV head: 32 rows), Q K^T and P V are real small
+// matrix products, so they run as bf16/fp16 MFMA with fp32 accumulation ("Architecture Diagram -
 // Qwen3-30B-A3B", paged attention: fp16 in, fp32 accumulate; "Attention
 // Computation" for what is computed).
 //
@@ -9,10 +9,14 @@
 // and query row r, (m, l, acc) with scores in log2 units, written to the
 // workspace for the combine kernel.
 //
-// Mapping on gfx950 (wave64, v_mfma_f32_16x16x32_{bf16,f16}; RB blocks of 16
-// query rows, RB = 1 or 2):
-//  - a workgroup of 4 waves owns one (b, h, chunk); wave w takes 32-key tiles
-//    w, w+4, ... and loads tile t+4 while it computes tile t;
+// Mapping on gfx950 (wave64, v_mfma_f32_16x16x32_{bf16,f16}):
+//  - a workgroup of 4 waves owns one (b, h, chunk); two fit on a compute unit.
+//    Query rows come in RG groups of 16 (RG = 1 for up to 16 rows, 2 for up
+//    to 32); the waves split into RG row groups, and within a row group wave w
+//    takes 32-key tiles w, w + W, ... (W = 4 / RG), alternating between two
+//    register buffers so that its next tile is in flight while it computes
+//    the current one.  With two row groups both read every tile; the second
+//    read of a tile is served by the compute unit's caches, not by HBM;
 //  - scores come out transposed, S^T[key][row] = K q^T, so lane l holds 8
 //    scores of ONE query row (row = l % 16) and that row's running max, sum
 //    and rescale factor stay in the lane; the scores then feed P V as its B
@@ -61,7 +65,25 @@ struct Tile {
     u32x4_t v[8];     // V: slot u, dims 8i .. 8i+7
 };
 
-__device__ __forceinline__ void load_tile(Tile &t, const uint8_t *kb, const uint8_t *vb, int tb, int last,
+// A whole 32-key tile inside the chunk: a few base addresses, immediate offsets.
+__device__ __forceinline__ void load_full(Tile &t, const uint8_t *kb, const uint8_t *vb, int tb, int l16, int q) {
+    const uint8_t *kr = kb + (size_t)(tb + l16) * kRowBytes + 16 * q;
+#pragma unroll
+    for (int kblk = 0; kblk < 2; ++kblk)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) t.k[kblk][s] = ld16(kr + 16 * kRowBytes * kblk + 64 * s);
+    const uint8_t *v0 = vb + (size_t)(tb + 4 * q) * kRowBytes + 16 * l16;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        t.v[u] = ld16(v0 + u * kRowBytes);
+        t.v[u + 4] = ld16(v0 + (16 + u) * kRowBytes);
+    }
+}
+
+// The chunk's last, partial tile: keys past `last` re-read row `last` (their
+// scores are masked), and their value rows are zeroed so a non-finite last row
+// cannot reach the other rows as 0 * inf.
+__device__ __forceinline__ void load_tail(Tile &t, const uint8_t *kb, const uint8_t *vb, int tb, int last,
                                           int l16, int q) {
 #pragma unroll
     for (int kblk = 0; kblk < 2; ++kblk) {
@@ -70,13 +92,24 @@ __device__ __forceinline__ void load_tile(Tile &t, const uint8_t *kb, const uint
         for (int s = 0; s < 4; ++s) t.k[kblk][s] = ld16(kr + 64 * s);
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) t.v[u] = ld16(vb + (size_t)min(tb + pv_key(q, u), last) * kRowBytes + 16 * l16);
+    for (int u = 0; u < 8; ++u) {
+        const int key = tb + pv_key(q, u);
+        t.v[u] = ld16(vb + (size_t)min(key, last) * kRowBytes + 16 * l16);
+        if (key > last) t.v[u] = u32x4_t{0u, 0u, 0u, 0u};
+    }
 }
 
-template <bool F16, int RB>
-__global__ __launch_bounds__(256) void attn_split_mfma_kernel(AttnParams p) {
-    __shared__ float obuf[2][16 * RB * kObufStride];
-    __shared__ float wave_m[4][16 * RB], wave_l[4][16 * RB];
+constexpr int kMfmaWaves = 4;
+
+template <bool F16, int RG>
+__global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_split_mfma_kernel(AttnParams p) {
+    constexpr int W = kMfmaWaves / RG;  // waves per row group
+    constexpr int NSLICE = W / 2;       // LDS slices of the fixed-order merge
+    static_assert(NSLICE == 1 || NSLICE == 2 || NSLICE == 4, "merge sums 1, 2 or 4 slices");
+    constexpr int RB = 1;               // row blocks per wave
+    __shared__ float obuf[RG][NSLICE][16 * kObufStride];
+    __shared__ float wave_m[kMfmaWaves][16], wave_l[kMfmaWaves][16];
 
     const int n_chunks = p.n_chunks;
     int b, h, c;
@@ -89,15 +122,18 @@ __global__ __launch_bounds__(256) void attn_split_mfma_kernel(AttnParams p) {
     const int n_tok = min(sc.len, ctx - t0);
     const int last = n_tok - 1;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
     const int l16 = lane & 15, q = lane >> 4;
+    const int rg = wave / W;  // this wave's row group: rows 16*rg .. 16*rg + 15
+    const int tw = wave - rg * W;
 
     // B operand of S^T = K q^T: lane holds q[row][dims 64s + 16q .. +16 bytes), s = 0..3
     u32x4_t qop[RB][4];
-    int vis[RB];  // exclusive local key limit of this lane's row in each row block
+    int vis[RB];  // exclusive local key limit of this lane's row
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-        const int row = rb * 16 + l16;
+        const int row = rg * 16 + l16;
         if (row < p.rows) {
             const int i = row / p.group, g = row - i * p.group;
             const uint8_t *qp =
@@ -127,30 +163,19 @@ __global__ __launch_bounds__(256) void attn_split_mfma_kernel(AttnParams p) {
     }
 
     const int n_tile = (n_tok + 31) >> 5;
-    Tile cur, nxt;
-    load_tile(cur, kb, vb, min(wave, n_tile - 1) * 32, last, l16, q);
-    for (int tt = wave; tt < n_tile; tt += 4) {
+
+    // One 32-key tile: S^T, online softmax, O^T += V^T P^T.
+    auto compute = [&](Tile &t, int tt) {
         const int tb = tt * 32;
-        // prefetch the wave's next tile (or re-read this one, already in cache)
-        load_tile(nxt, kb, vb, (tt + 4 < n_tile ? tt + 4 : tt) * 32, last, l16, q);
-
-        // zero value rows past the context (copies of the last row) so a
-        // non-finite last row cannot reach the other rows as 0 * inf
-        if (tb + 31 > last) {
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-                if (tb + pv_key(q, u) > last) cur.v[u] = u32x4_t{0u, 0u, 0u, 0u};
-        }
-
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-            // S^T for the two 16-key blocks: lane holds keys tb + 16*kblk + 4q + v of row l16
+            // S^T for the two 16-key blocks: lane holds keys tb + 16*kblk + 4q + v of its row
             f32x4_t st[2];
 #pragma unroll
             for (int kblk = 0; kblk < 2; ++kblk) {
                 st[kblk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s = 0; s < 4; ++s) st[kblk] = mfma16<F16>(cur.k[kblk][s], qop[rb][s], st[kblk]);
+                for (int s = 0; s < 4; ++s) st[kblk] = mfma16<F16>(t.k[kblk][s], qop[rb][s], st[kblk]);
             }
             float s2[8];
             float mt = -INFINITY;
@@ -192,70 +217,92 @@ __global__ __launch_bounds__(256) void attn_split_mfma_kernel(AttnParams p) {
                 u32x4_t vop;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    vop[j] = __builtin_amdgcn_perm(cur.v[2 * j + 1][word], cur.v[2 * j][word], sel);
+                    vop[j] = __builtin_amdgcn_perm(t.v[2 * j + 1][word], t.v[2 * j][word], sel);
                 oacc[rb][o] = mfma16<F16>(vop, pop, oacc[rb][o]);
             }
         }
-        cur = nxt;
+    };
+
+    // Full tiles: two register buffers used in turn, with no copy between them,
+    // so a wave waits only for the older tile while the newer one is in flight.
+    // This wave's full tiles are tw, tw + W, ...; when their count is even the
+    // last prefetch re-reads the final tile (from cache) and is not used.
+    const int n_full = n_tok >> 5;
+    const int nt = tw < n_full ? (n_full - 1 - tw) / W + 1 : 0;
+    if (nt > 0) {
+        Tile ta, tb_;
+        load_full(ta, kb, vb, tw * 32, l16, q);
+        int i = 0;
+        for (; i + 2 <= nt; i += 2) {
+            load_full(tb_, kb, vb, (tw + (i + 1) * W) * 32, l16, q);
+            compute(ta, tw + i * W);
+            load_full(ta, kb, vb, (tw + min(i + 2, nt - 1) * W) * 32, l16, q);
+            compute(tb_, tw + (i + 1) * W);
+        }
+        if (i < nt) compute(ta, tw + i * W);
+    }
+    // the partial tail tile, if any, belongs to the wave whose turn comes next
+    if ((n_tok & 31) && tw == n_full % W) {
+        Tile tt_;
+        load_tail(tt_, kb, vb, n_full * 32, last, l16, q);
+        compute(tt_, n_full);
     }
 
-    // ---- merge the four waves' (m, l, O) in a fixed order ------------------------
-    // Waves 0 and 1 store their rescaled O^T into two LDS slices, waves 2 and 3
-    // add theirs into slice 0 and 1, and the write-out sums the two slices:
-    // (w0 + w2) + (w1 + w3), the same order on every run.
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        l_run[rb] += __shfl_xor(l_run[rb], 16);
-        l_run[rb] += __shfl_xor(l_run[rb], 32);
-        if (q == 0) {
-            wave_m[wave][rb * 16 + l16] = m_run[rb];
-            wave_l[wave][rb * 16 + l16] = l_run[rb];
-        }
+    // ---- merge the waves of each row group in a fixed order -----------------------
+    // Waves 0 .. NSLICE-1 of a row group store their rescaled O^T into their own
+    // LDS slice, waves NSLICE .. W-1 add theirs into slice (w - NSLICE), and the
+    // write-out sums the slices pairwise: the same order on every run.
+    l_run[0] += __shfl_xor(l_run[0], 16);
+    l_run[0] += __shfl_xor(l_run[0], 32);
+    if (q == 0) {
+        wave_m[wave][l16] = m_run[0];
+        wave_l[wave][l16] = l_run[0];
     }
     __syncthreads();
-    float f[RB];
+    float m_fin = -INFINITY;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        const int row = rb * 16 + l16;
-        const float m_fin =
-            fmaxf(fmaxf(wave_m[0][row], wave_m[1][row]), fmaxf(wave_m[2][row], wave_m[3][row]));
-        f[rb] = (m_run[rb] == -INFINITY) ? 0.f : exp2_fast(m_run[rb] - m_fin);
-    }
-    float *slice = obuf[wave & 1];
-    if (wave < 2) {
+    for (int w = 0; w < W; ++w) m_fin = fmaxf(m_fin, wave_m[rg * W + w][l16]);
+    const float f = (m_run[0] == -INFINITY) ? 0.f : exp2_fast(m_run[0] - m_fin);
+    float *slice = obuf[rg][tw % NSLICE];
+    if (tw < NSLICE) {
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
+        for (int o = 0; o < 8; ++o)
 #pragma unroll
-            for (int o = 0; o < 8; ++o)
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    slice[(rb * 16 + l16) * kObufStride + 8 * (4 * q + v) + o] = oacc[rb][o][v] * f[rb];
+            for (int v = 0; v < 4; ++v) slice[l16 * kObufStride + 8 * (4 * q + v) + o] = oacc[0][o][v] * f;
     }
     __syncthreads();
-    if (wave >= 2) {
+    if (tw >= NSLICE) {
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
+        for (int o = 0; o < 8; ++o)
 #pragma unroll
-            for (int o = 0; o < 8; ++o)
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    slice[(rb * 16 + l16) * kObufStride + 8 * (4 * q + v) + o] += oacc[rb][o][v] * f[rb];
+            for (int v = 0; v < 4; ++v) slice[l16 * kObufStride + 8 * (4 * q + v) + o] += oacc[0][o][v] * f;
     }
     __syncthreads();
 
     const size_t part = (size_t)bh * n_chunks + c;
     float *wa = p.ws_acc + part * p.rows * kHeadDim;
-    for (int idx = tid; idx < p.rows * kHeadDim; idx += 256) {
+    for (int idx = tid; idx < p.rows * kHeadDim; idx += 64 * kMfmaWaves) {
         const int r = idx >> 7, d = idx & (kHeadDim - 1);
-        wa[idx] = obuf[0][r * kObufStride + d] + obuf[1][r * kObufStride + d];
+        const int g = r >> 4, rr = r & 15;
+        const int o = rr * kObufStride + d;
+        float sum;
+        if constexpr (NSLICE == 1)
+            sum = obuf[g][0][o];
+        else if constexpr (NSLICE == 2)
+            sum = obuf[g][0][o] + obuf[g][1][o];
+        else
+            sum = (obuf[g][0][o] + obuf[g][1][o]) + (obuf[g][2][o] + obuf[g][3][o]);
+        wa[idx] = sum;
     }
     if (tid < p.rows) {
-        const int r = tid;
-        const float mf = fmaxf(fmaxf(wave_m[0][r], wave_m[1][r]), fmaxf(wave_m[2][r], wave_m[3][r]));
+        const int r = tid, g = r >> 4, rr = r & 15;
+        float mf = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < W; ++w) mf = fmaxf(mf, wave_m[g * W + w][rr]);
         float lf = 0.f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w)
-            if (wave_m[w][r] != -INFINITY) lf += exp2_fast(wave_m[w][r] - mf) * wave_l[w][r];
+        for (int w = 0; w < W; ++w)
+            if (wave_m[g * W + w][rr] != -INFINITY) lf += exp2_fast(wave_m[g * W + w][rr] - mf) * wave_l[g * W + w][rr];
         p.ws_ml[(part * p.rows + r) * 2 + 0] = mf;
         p.ws_ml[(part * p.rows + r) * 2 + 1] = lf;
     }
@@ -264,9 +311,9 @@ __global__ __launch_bounds__(256) void attn_split_mfma_kernel(AttnParams p) {
 template <bool F16>
 static hipError_t launch_dtype(const AttnParams &p, int grid, hipStream_t s) {
     if (p.rows <= 16)
-        hipLaunchKernelGGL((attn_split_mfma_kernel<F16, 1>), dim3(grid), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((attn_split_mfma_kernel<F16, 1>), dim3(grid), dim3(64 * kMfmaWaves), 0, s, p);
     else
-        hipLaunchKernelGGL((attn_split_mfma_kernel<F16, 2>), dim3(grid), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((attn_split_mfma_kernel<F16, 2>), dim3(grid), dim3(64 * kMfmaWaves), 0, s, p);
     return hipGetLastError();
 }
 

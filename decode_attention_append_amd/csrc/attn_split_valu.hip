@@ -18,7 +18,9 @@
 // consecutive keys, 1 KiB contiguous.  Q.K partial dots use the packed
 // dot2 (bf16/fp16 pair -> fp32) instruction, then a 16-lane DPP butterfly.
 // The chunk's scores go to LDS; the chunk is two-pass (all scores, then the
-// maximum, then P.V), so no running rescale is needed inside a chunk.
+// maximum, then P.V), so no running rescale is needed inside a chunk.  Each
+// wave streams its 16-key slabs through two register buffers in turn, so the
+// next slab is in flight while the current one is computed.
 #include "da_internal.h"
 
 #include <math.h>
@@ -41,7 +43,8 @@ __global__ __launch_bounds__(256) void attn_split_valu_kernel(AttnParams p) {
     const int n_tok = min(sc.len, ctx - t0);
     const int n_slab = (n_tok + 15) >> 4;  // 16-key slabs; a wave does one per step
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
     const int gq = lane >> 4;  // which of the 4 keys of a 1 KiB load
     const int cq = lane & 15;  // 16-byte column: dims 8*cq .. 8*cq+7
 
@@ -73,40 +76,58 @@ __global__ __launch_bounds__(256) void attn_split_valu_kernel(AttnParams p) {
     const uint8_t *vb = p.v_cache + head_off;
     const int last = n_tok - 1;  // loads past the context re-read the last row (masked)
 
-    // ---- pass 1: scores of the chunk into LDS ----------------------------------
-    {
-        u32x4_t cur[4], nxt[4];
-        int s = wave;
-        const int s0 = min(s, n_slab - 1);
+    // Slab loads: four 128-bit loads per lane cover 16 keys (1 KiB each).  Full
+    // slabs use one base address and immediate offsets; the last, partial slab
+    // re-reads row `last` for keys past the chunk (those are masked).
+    const int n_full = n_tok >> 4;
+    auto load_slab = [&](u32x4_t (&buf)[4], const uint8_t *base, int s_) {
+        if (s_ < n_full) {
+            const uint8_t *r0 = base + (size_t)(s_ * 16 + gq) * kRowBytes;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) cur[u] = ld16(kb + (size_t)min(s0 * 16 + u * 4 + gq, last) * kRowBytes);
-        for (; s < n_slab; s += 4) {
-            const int sn = min(s + 4, n_slab - 1);
+            for (int u = 0; u < 4; ++u) buf[u] = ld16(r0 + u * 4 * kRowBytes);
+        } else {
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-                nxt[u] = ld16(kb + (size_t)min(sn * 16 + u * 4 + gq, last) * kRowBytes);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int tl = s * 16 + u * 4 + gq;
-                float score[RP];
-#pragma unroll
-                for (int r = 0; r < RP; ++r) {
-                    float a = dot2<F16>(qr[r][0], cur[u][0], 0.f);
-                    a = dot2<F16>(qr[r][1], cur[u][1], a);
-                    a = dot2<F16>(qr[r][2], cur[u][2], a);
-                    a = dot2<F16>(qr[r][3], cur[u][3], a);
-                    score[r] = row16_sum(a);
-                }
-                if (cq == 0) {
-#pragma unroll
-                    for (int r = 0; r < RP; ++r)
-                        lds[tl * RP + r] = tl < vis[r] ? score[r] * p.scale_log2 : -INFINITY;
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) cur[u] = nxt[u];
+            for (int u = 0; u < 4; ++u) buf[u] = ld16(base + (size_t)min(s_ * 16 + u * 4 + gq, last) * kRowBytes);
         }
-    }
+    };
+    // This wave's slabs are wave, wave + 4, ...: two buffers used in turn, no copy
+    // between iterations, so a wave waits only for the older slab.
+    const int ns = wave < n_slab ? (n_slab - 1 - wave) / 4 + 1 : 0;
+    auto two_buffer_pass = [&](const uint8_t *base, auto &&body) {
+        if (ns == 0) return;
+        u32x4_t b0[4], b1[4];
+        load_slab(b0, base, wave);
+        int i = 0;
+        for (; i + 2 <= ns; i += 2) {
+            load_slab(b1, base, wave + (i + 1) * 4);
+            body(b0, wave + i * 4);
+            load_slab(b0, base, wave + min(i + 2, ns - 1) * 4);
+            body(b1, wave + (i + 1) * 4);
+        }
+        if (i < ns) body(b0, wave + i * 4);
+    };
+
+    // ---- pass 1: scores of the chunk into LDS ----------------------------------
+    two_buffer_pass(kb, [&](u32x4_t (&cur)[4], int s_) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int tl = s_ * 16 + u * 4 + gq;
+            float score[RP];
+#pragma unroll
+            for (int r = 0; r < RP; ++r) {
+                float a = dot2<F16>(qr[r][0], cur[u][0], 0.f);
+                a = dot2<F16>(qr[r][1], cur[u][1], a);
+                a = dot2<F16>(qr[r][2], cur[u][2], a);
+                a = dot2<F16>(qr[r][3], cur[u][3], a);
+                score[r] = row16_sum(a);
+            }
+            if (cq == 0) {
+#pragma unroll
+                for (int r = 0; r < RP; ++r)
+                    lds[tl * RP + r] = tl < vis[r] ? score[r] * p.scale_log2 : -INFINITY;
+            }
+        }
+    });
     __syncthreads();
 
     // ---- chunk maximum and weights p = 2^(s - m), sum l ------------------------
@@ -136,46 +157,33 @@ __global__ __launch_bounds__(256) void attn_split_valu_kernel(AttnParams p) {
 #pragma unroll
         for (int d = 0; d < 8; ++d) acc[r][d] = 0.f;
     const int first_draft = sp - t0;  // local keys above this may be hidden from some rows
-    {
-        u32x4_t cur[4], nxt[4];
-        int s = wave;
-        const int s0 = min(s, n_slab - 1);
+    two_buffer_pass(vb, [&](u32x4_t (&cur)[4], int s_) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) cur[u] = ld16(vb + (size_t)min(s0 * 16 + u * 4 + gq, last) * kRowBytes);
-        for (; s < n_slab; s += 4) {
-            const int sn = min(s + 4, n_slab - 1);
+        for (int u = 0; u < 4; ++u) {
+            const int tl = s_ * 16 + u * 4 + gq;
+            float pr[RP];
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-                nxt[u] = ld16(vb + (size_t)min(sn * 16 + u * 4 + gq, last) * kRowBytes);
+            for (int r = 0; r < RP; ++r) pr[r] = lds[tl * RP + r];
+            float vf[8];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int tl = s * 16 + u * 4 + gq;
-                float pr[RP];
+            for (int k = 0; k < 4; ++k) unpack2<F16>(cur[u][k], vf[2 * k], vf[2 * k + 1]);
+            if (tl > first_draft) {
+                // a later draft token (or padding past the context): rows that
+                // cannot see it must not touch its value row, even NaN * 0
 #pragma unroll
-                for (int r = 0; r < RP; ++r) pr[r] = lds[tl * RP + r];
-                float vf[8];
-#pragma unroll
-                for (int k = 0; k < 4; ++k) unpack2<F16>(cur[u][k], vf[2 * k], vf[2 * k + 1]);
-                if (tl > first_draft) {
-                    // a later draft token (or padding past the context): rows that
-                    // cannot see it must not touch its value row, even NaN * 0
-#pragma unroll
-                    for (int r = 0; r < RP; ++r)
-                        if (pr[r] != 0.f) {
-#pragma unroll
-                            for (int d = 0; d < 8; ++d) acc[r][d] = fmaf(pr[r], vf[d], acc[r][d]);
-                        }
-                } else {
-#pragma unroll
-                    for (int r = 0; r < RP; ++r)
+                for (int r = 0; r < RP; ++r)
+                    if (pr[r] != 0.f) {
 #pragma unroll
                         for (int d = 0; d < 8; ++d) acc[r][d] = fmaf(pr[r], vf[d], acc[r][d]);
-                }
-            }
+                    }
+            } else {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) cur[u] = nxt[u];
+                for (int r = 0; r < RP; ++r)
+#pragma unroll
+                    for (int d = 0; d < 8; ++d) acc[r][d] = fmaf(pr[r], vf[d], acc[r][d]);
+            }
         }
-    }
+    });
 
     // ---- reduce the four key slots of a wave, then the four waves ---------------
 #pragma unroll

@@ -51,7 +51,7 @@ da_status check_problem(const da_problem *p) {
 // the 256 compute units to hold a few resident workgroups at the kernel's
 // occupancy, so that the dispatcher balances what the chunking does not.
 int default_target(int variant, int rows) {
-    if (variant == DA_VARIANT_MFMA) return rows > 16 ? 256 : 512;
+    if (variant == DA_VARIANT_MFMA) return 256;  // one 4-wave workgroup per compute unit (two fit)
     return 1024;
 }
 
@@ -65,9 +65,16 @@ int max_chunk_of(int variant, int rows) {
 
 constexpr int kMinChunk = 64;
 
+// Rows per KV head from which the matrix-core kernel is used.  Below 8 rows the
+// vector-ALU kernel is memory-bound (its dot products cost about 4 wave
+// instructions per key and row); at 8 rows it needs some 34 wave instructions
+// per key and becomes ALU-bound near 40% of HBM bandwidth, while the MFMA
+// kernel streams at over 60%.
+constexpr int kMfmaRows = 8;
+
 void plan_of(const da_problem *p, da_plan *pl) {
     const int rows = (p->n_q_heads / p->n_kv_heads) * p->q_len;
-    const int variant = p->variant ? p->variant - 1 : (rows >= 16 ? DA_VARIANT_MFMA : DA_VARIANT_VALU);
+    const int variant = p->variant ? p->variant - 1 : (rows >= kMfmaRows ? DA_VARIANT_MFMA : DA_VARIANT_VALU);
     const int units = p->batch * p->n_kv_heads;
     pl->rows = rows;
     pl->variant = variant;

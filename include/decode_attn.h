@@ -115,8 +115,9 @@ enum { DA_VARIANT_VALU = 0, DA_VARIANT_MFMA = 1 };
 
 /*
  * Plans the attention of *p: chunking, kernel variant, workspace size.  The
- * automatic variant is the MFMA kernel when rows >= 16 (Q K^T and P V are then
- * real small matrix products), the vector-ALU kernel otherwise.
+ * automatic variant is the MFMA kernel when rows >= 8 (Q K^T and P V are then
+ * small matrix products, and on the vector ALU they would cost more issue
+ * slots than streaming the keys from HBM), the vector-ALU kernel otherwise.
  * Returns DA_OK, DA_ERR_INVALID_ARG or DA_ERR_UNSUPPORTED.  Host only.
  */
 da_status da_plan_attention(const da_problem *p, da_plan *plan);

@@ -75,7 +75,8 @@ def test_workload_batched_gqa_ctx8192():
     (3, 4, 32, 4, 2100, [2096, 0, 1023], torch.bfloat16),        # verify 4 -> MFMA
     (2, 4, 32, 4, 2100, [2096, 777], torch.float16),             # MFMA fp16
     (2, 8, 4, 2, 500, [492, 3], torch.bfloat16),                 # q_len 8 rows 16 -> MFMA
-    (2, 8, 2, 2, 500, [492, 61], torch.bfloat16),                # q_len 8 MHA rows 8
+    (2, 8, 2, 2, 500, [492, 61], torch.bfloat16),                # q_len 8 MHA rows 8 -> MFMA
+    (2, 4, 8, 8, 700, [696, 300], torch.bfloat16),               # q_len 4 MHA rows 4 -> VALU
     (1, 1, 1, 1, 64, [63], torch.bfloat16),                      # smallest
 ])
 def test_shapes(B, q_len, Hq, Hkv, S, seq_pos, dtype):
@@ -160,7 +161,7 @@ def test_later_draft_token_hidden_from_earlier_rows_valu():
     (vector-ALU variant: the mask excludes the row exactly)."""
     q_len, Hq, Hkv = 2, 8, 2
     inp = gu.make_case(1, q_len, Hq, Hkv, 256, [100], seed=8)
-    p = da.problem_for(inp["q"], inp["k_cache"])
+    p = da.problem_for(inp["q"], inp["k_cache"], variant="valu")
     assert da.plan_attention(p)["variant"] == "valu"
     inp["v_new"][0, 1] = float("nan")
     out = gu.run_step(p, inp)
@@ -200,9 +201,11 @@ def test_custom_scale():
 
 def test_variant_choice():
     assert da.plan_attention(da.problem(8, 4, 32, 4, 128, 8192, "bf16"))["variant"] == "mfma"
-    assert da.plan_attention(da.problem(4, 1, 64, 8, 128, 16384, "bf16"))["variant"] == "valu"
+    assert da.plan_attention(da.problem(4, 1, 64, 8, 128, 16384, "bf16"))["variant"] == "mfma"
+    assert da.plan_attention(da.problem(4, 1, 32, 8, 128, 16384, "bf16"))["variant"] == "valu"
     assert da.plan_attention(da.problem(1, 2, 8, 1, 128, 64, "bf16"))["variant"] == "mfma"
-    assert da.plan_attention(da.problem(1, 1, 15, 1, 128, 64, "bf16"))["variant"] == "valu"
+    assert da.plan_attention(da.problem(1, 1, 15, 1, 128, 64, "bf16"))["variant"] == "mfma"
+    assert da.plan_attention(da.problem(1, 1, 7, 1, 128, 64, "bf16"))["variant"] == "valu"
 
 
 def test_errors_launch_nothing():
