@@ -48,7 +48,7 @@ class Problem(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("chunk_tokens", ctypes.c_int32),
         ("variant", ctypes.c_int32),
-        ("workgroups", ctypes.c_int32),
+        ("work_items", ctypes.c_int32),
     ]
 
     def __repr__(self):
@@ -64,8 +64,8 @@ class Plan(ctypes.Structure):
         ("rows", ctypes.c_int32),
         ("variant", ctypes.c_int32),
         ("balanced", ctypes.c_int32),
-        ("target_workgroups", ctypes.c_int32),
-        ("grid", ctypes.c_int32),
+        ("target_items", ctypes.c_int32),
+        ("items", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),
     ]
 
@@ -122,7 +122,7 @@ def status_str(status: int) -> str:
 
 
 def problem(batch, q_len, n_q_heads, n_kv_heads, head_dim, max_seq, dtype, scale=0.0,
-            chunk_tokens=0, variant=None, workgroups=0) -> Problem:
+            chunk_tokens=0, variant=None, work_items=0) -> Problem:
     """variant: None (automatic), "valu" or "mfma"; chunk_tokens 0 = balanced chunks."""
     if isinstance(dtype, torch.dtype):
         dtype = _DTYPE_CODE[dtype]
@@ -130,15 +130,15 @@ def problem(batch, q_len, n_q_heads, n_kv_heads, head_dim, max_seq, dtype, scale
         dtype = {"bf16": DA_BF16, "fp16": DA_FP16}[dtype]
     v = 0 if variant is None else {"valu": 1, "mfma": 2}[variant]
     return Problem(batch, q_len, n_q_heads, n_kv_heads, head_dim, max_seq, dtype, float(scale),
-                   chunk_tokens, v, workgroups)
+                   chunk_tokens, v, work_items)
 
 
 def problem_for(q: torch.Tensor, k_cache: torch.Tensor, scale=0.0, chunk_tokens=0,
-                variant=None, workgroups=0) -> Problem:
+                variant=None, work_items=0) -> Problem:
     """The problem described by q [B, q_len, Hq, D] and a cache [B, Hkv, S, D]."""
     B, q_len, Hq, D = q.shape
     _, Hkv, S, _ = k_cache.shape
-    return problem(B, q_len, Hq, Hkv, D, S, q.dtype, scale, chunk_tokens, variant, workgroups)
+    return problem(B, q_len, Hq, Hkv, D, S, q.dtype, scale, chunk_tokens, variant, work_items)
 
 
 def plan_attention(p: Problem) -> dict:
@@ -148,7 +148,7 @@ def plan_attention(p: Problem) -> dict:
         raise DecodeAttnError(st, "da_plan_attention")
     return {"chunk_tokens": pl.chunk_tokens, "n_chunks": pl.n_chunks, "rows": pl.rows,
             "variant": VARIANTS[pl.variant], "balanced": bool(pl.balanced),
-            "target_workgroups": pl.target_workgroups, "grid": pl.grid,
+            "target_items": pl.target_items, "items": pl.items,
             "workspace_bytes": pl.workspace_bytes}
 
 

@@ -10,13 +10,15 @@
 // workspace for the combine kernel.
 //
 // Mapping on gfx950 (wave64, v_mfma_f32_16x16x32_{bf16,f16}):
-//  - a workgroup of 4 waves owns one (b, h, chunk); two fit on a compute unit.
-//    Query rows come in RG groups of 16 (RG = 1 for up to 16 rows, 2 for up
-//    to 32); the waves split into RG row groups, and within a row group wave w
-//    takes 32-key tiles w, w + W, ... (W = 4 / RG), alternating between two
-//    register buffers so that its next tile is in flight while it computes
-//    the current one.  With two row groups both read every tile; the second
-//    read of a tile is served by the compute unit's caches, not by HBM;
+//  - every wave owns one (b, h, chunk) and writes that chunk's partial
+//    itself: no barrier, no LDS and no cross-wave merge, so a wave never
+//    waits for its neighbours and keeps its loads in flight until its chunk
+//    ends.  Query rows come in RG groups of 16 (RG = 1 for up to 16 rows, 2
+//    for up to 32); with two groups a pair of waves shares one chunk, each
+//    computing its 16 rows from the same tiles (the second read of a tile is
+//    served by the compute unit's caches, not by HBM).  A wave streams its
+//    32-key tiles through two register buffers in turn, so its next tile is
+//    in flight while it computes the current one;
 //  - scores come out transposed, S^T[key][row] = K q^T, so lane l holds 8
 //    scores of ONE query row (row = l % 16) and that row's running max, sum
 //    and rescale factor stay in the lane; the scores then feed P V as its B
@@ -99,34 +101,28 @@ __device__ __forceinline__ void load_tail(Tile &t, const uint8_t *kb, const uint
     }
 }
 
-constexpr int kMfmaWaves = 4;
+constexpr int kMfmaWaves = 4;  // waves per workgroup (independent chunks or pairs)
 
 template <bool F16, int RG>
 __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_split_mfma_kernel(AttnParams p) {
-    constexpr int W = kMfmaWaves / RG;  // waves per row group
-    constexpr int NSLICE = W / 2;       // LDS slices of the fixed-order merge
-    static_assert(NSLICE == 1 || NSLICE == 2 || NSLICE == 4, "merge sums 1, 2 or 4 slices");
-    constexpr int RB = 1;               // row blocks per wave
-    __shared__ float obuf[RG][NSLICE][16 * kObufStride];
-    __shared__ float wave_m[kMfmaWaves][16], wave_l[kMfmaWaves][16];
+    constexpr int RB = 1;  // row blocks per wave
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
+    const int rg = wave % RG;                                   // this wave's 16-row group
+    const int item = blockIdx.x * (kMfmaWaves / RG) + wave / RG;
 
     const int n_chunks = p.n_chunks;
     int b, h, c;
     SeqChunks sc;
-    if (!locate(p, blockIdx.x, b, h, c, sc)) return;  // past the last chunk of the launch
+    if (!locate(p, item, b, h, c, sc)) return;  // past the last chunk of the launch
     const int bh = b * p.n_kv_heads + h;
     const int sp = p.seq_pos[b];
     const int ctx = sc.ctx;
     const int t0 = c * sc.len;
     const int n_tok = min(sc.len, ctx - t0);
     const int last = n_tok - 1;
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
     const int l16 = lane & 15, q = lane >> 4;
-    const int rg = wave / W;  // this wave's row group: rows 16*rg .. 16*rg + 15
-    const int tw = wave - rg * W;
 
     // B operand of S^T = K q^T: lane holds q[row][dims 64s + 16q .. +16 bytes), s = 0..3
     u32x4_t qop[RB][4];
@@ -223,97 +219,66 @@ void attn_split_mfma_kernel(AttnParams p) {
         }
     };
 
-    // Full tiles: two register buffers used in turn, with no copy between them,
-    // so a wave waits only for the older tile while the newer one is in flight.
-    // This wave's full tiles are tw, tw + W, ...; when their count is even the
-    // last prefetch re-reads the final tile (from cache) and is not used.
-    const int n_full = n_tok >> 5;
-    const int nt = tw < n_full ? (n_full - 1 - tw) / W + 1 : 0;
+    // Full tiles through two register buffers used in turn, with no copy between
+    // them, so the wave waits only for the older tile while the newer one is in
+    // flight.  When the count is even the last prefetch re-reads the final tile
+    // (from cache) and is not used.  The partial tail tile is peeled off.
+    const int nt = n_tok >> 5;
     if (nt > 0) {
         Tile ta, tb_;
-        load_full(ta, kb, vb, tw * 32, l16, q);
+        load_full(ta, kb, vb, 0, l16, q);
         int i = 0;
         for (; i + 2 <= nt; i += 2) {
-            load_full(tb_, kb, vb, (tw + (i + 1) * W) * 32, l16, q);
-            compute(ta, tw + i * W);
-            load_full(ta, kb, vb, (tw + min(i + 2, nt - 1) * W) * 32, l16, q);
-            compute(tb_, tw + (i + 1) * W);
+            load_full(tb_, kb, vb, (i + 1) * 32, l16, q);
+            compute(ta, i);
+            load_full(ta, kb, vb, min(i + 2, nt - 1) * 32, l16, q);
+            compute(tb_, i + 1);
         }
-        if (i < nt) compute(ta, tw + i * W);
+        if (i < nt) compute(ta, i);
     }
-    // the partial tail tile, if any, belongs to the wave whose turn comes next
-    if ((n_tok & 31) && tw == n_full % W) {
+    if (n_tok & 31) {
         Tile tt_;
-        load_tail(tt_, kb, vb, n_full * 32, last, l16, q);
-        compute(tt_, n_full);
+        load_tail(tt_, kb, vb, nt * 32, last, l16, q);
+        compute(tt_, nt);
     }
 
-    // ---- merge the waves of each row group in a fixed order -----------------------
-    // Waves 0 .. NSLICE-1 of a row group store their rescaled O^T into their own
-    // LDS slice, waves NSLICE .. W-1 add theirs into slice (w - NSLICE), and the
-    // write-out sums the slices pairwise: the same order on every run.
+    // ---- this wave's partial: O^T (lane: row l16, dims 8*(4q+v)+o), m, l ---------
     l_run[0] += __shfl_xor(l_run[0], 16);
     l_run[0] += __shfl_xor(l_run[0], 32);
-    if (q == 0) {
-        wave_m[wave][l16] = m_run[0];
-        wave_l[wave][l16] = l_run[0];
-    }
-    __syncthreads();
-    float m_fin = -INFINITY;
+    const int row = rg * 16 + l16;
+    if (row < p.rows) {
+        const size_t part = ((size_t)bh * n_chunks + c) * p.rows + row;
+        float *wa = p.ws_acc + part * kHeadDim;
 #pragma unroll
-    for (int w = 0; w < W; ++w) m_fin = fmaxf(m_fin, wave_m[rg * W + w][l16]);
-    const float f = (m_run[0] == -INFINITY) ? 0.f : exp2_fast(m_run[0] - m_fin);
-    float *slice = obuf[rg][tw % NSLICE];
-    if (tw < NSLICE) {
+        for (int v = 0; v < 4; ++v)
 #pragma unroll
-        for (int o = 0; o < 8; ++o)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) slice[l16 * kObufStride + 8 * (4 * q + v) + o] = oacc[0][o][v] * f;
-    }
-    __syncthreads();
-    if (tw >= NSLICE) {
-#pragma unroll
-        for (int o = 0; o < 8; ++o)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) slice[l16 * kObufStride + 8 * (4 * q + v) + o] += oacc[0][o][v] * f;
-    }
-    __syncthreads();
-
-    const size_t part = (size_t)bh * n_chunks + c;
-    float *wa = p.ws_acc + part * p.rows * kHeadDim;
-    for (int idx = tid; idx < p.rows * kHeadDim; idx += 64 * kMfmaWaves) {
-        const int r = idx >> 7, d = idx & (kHeadDim - 1);
-        const int g = r >> 4, rr = r & 15;
-        const int o = rr * kObufStride + d;
-        float sum;
-        if constexpr (NSLICE == 1)
-            sum = obuf[g][0][o];
-        else if constexpr (NSLICE == 2)
-            sum = obuf[g][0][o] + obuf[g][1][o];
-        else
-            sum = (obuf[g][0][o] + obuf[g][1][o]) + (obuf[g][2][o] + obuf[g][3][o]);
-        wa[idx] = sum;
-    }
-    if (tid < p.rows) {
-        const int r = tid, g = r >> 4, rr = r & 15;
-        float mf = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < W; ++w) mf = fmaxf(mf, wave_m[g * W + w][rr]);
-        float lf = 0.f;
-#pragma unroll
-        for (int w = 0; w < W; ++w)
-            if (wave_m[g * W + w][rr] != -INFINITY) lf += exp2_fast(wave_m[g * W + w][rr] - mf) * wave_l[g * W + w][rr];
-        p.ws_ml[(part * p.rows + r) * 2 + 0] = mf;
-        p.ws_ml[(part * p.rows + r) * 2 + 1] = lf;
+            for (int o = 0; o < 8; o += 4) {
+                // dims 8*(4q+v) + o .. +3 are four consecutive floats of this lane
+                float4 x;
+                x.x = oacc[0][o][v];
+                x.y = oacc[0][o + 1][v];
+                x.z = oacc[0][o + 2][v];
+                x.w = oacc[0][o + 3][v];
+                *reinterpret_cast<float4 *>(wa + 8 * (4 * q + v) + o) = x;
+            }
+        if (q == 0) {
+            p.ws_ml[part * 2 + 0] = m_run[0];
+            p.ws_ml[part * 2 + 1] = l_run[0];
+        }
     }
 }
 
+// `items` = chunks in the launch (an upper bound); a workgroup takes 4 of them
+// (16-row problems) or 2 wave pairs (17..32 rows).
 template <bool F16>
-static hipError_t launch_dtype(const AttnParams &p, int grid, hipStream_t s) {
-    if (p.rows <= 16)
+static hipError_t launch_dtype(const AttnParams &p, int items, hipStream_t s) {
+    if (p.rows <= 16) {
+        const int grid = (items + kMfmaWaves - 1) / kMfmaWaves;
         hipLaunchKernelGGL((attn_split_mfma_kernel<F16, 1>), dim3(grid), dim3(64 * kMfmaWaves), 0, s, p);
-    else
+    } else {
+        const int grid = (items + kMfmaWaves / 2 - 1) / (kMfmaWaves / 2);
         hipLaunchKernelGGL((attn_split_mfma_kernel<F16, 2>), dim3(grid), dim3(64 * kMfmaWaves), 0, s, p);
+    }
     return hipGetLastError();
 }
 

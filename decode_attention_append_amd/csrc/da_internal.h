@@ -38,7 +38,7 @@ struct AttnParams {
     int32_t rows;   // group * q_len
     int32_t n_chunks;      // chunk slots per (sequence, KV head) in the workspace
     int32_t fixed_chunk;   // > 0: every chunk has this many keys; 0: balanced chunks
-    int32_t target_wg;     // balanced: workgroups to aim for over the whole launch
+    int32_t target_wg;     // balanced: chunks to aim for over the whole launch
     int32_t min_chunk;     // balanced: smallest chunk (multiple of 32)
     int32_t max_chunk;     // largest chunk the kernel accepts (multiple of 32)
     float scale_log2;      // softmax scale * log2(e): scores are kept in log2 units
@@ -47,12 +47,12 @@ struct AttnParams {
 // ---- split-context chunk plan, computed identically by every kernel ---------
 //
 // Balanced mode: the chunk length aims at an equal share of all visible keys
-// per workgroup, T = ceil32(Hkv * sum_b ctx_b / target_wg) clamped to
+// per chunk, T = ceil32(Hkv * sum_b ctx_b / target_wg) clamped to
 // [min_chunk, max_chunk]; sequence b gets n_b = max(round(ctx_b / T),
 // ceil(ctx_b / max_chunk)) chunks of ceil32(ctx_b / n_b) keys, so chunks of
 // one sequence are equal and all chunks are close to T.  Fixed mode: chunks of
 // fixed_chunk keys.  A sequence whose seq_pos breaks the contract has no
-// chunks.  Workgroups are laid out sequence-major: for b, for h, for c.
+// chunks.  Work items (chunks) are laid out sequence-major: for b, for h, for c.
 
 struct SeqChunks {
     int n;      // chunks of this sequence (0 if its seq_pos is out of range)
@@ -100,7 +100,7 @@ __host__ __device__ inline SeqChunks seq_chunks(const AttnParams &p, int b, int 
     return s;
 }
 
-// Which (b, h, c) workgroup `w` owns; false if w is past the last chunk.
+// Which (b, h, c) work item `w` is; false if w is past the last chunk.
 __host__ __device__ inline bool locate(const AttnParams &p, int w, int &b, int &h, int &c, SeqChunks &sc) {
     const int T = p.fixed_chunk > 0 ? p.fixed_chunk : balanced_chunk(p);
     for (b = 0; b < p.batch; ++b) {
@@ -127,8 +127,8 @@ inline size_t ws_ml_floats(int32_t bh, int32_t n_chunks, int32_t rows) {
 // ---- host-side launch entry points (one per translation unit) ---------------
 
 hipError_t launch_kv_append(const AppendParams &p, int threads_total, hipStream_t s);
-hipError_t launch_attn_valu(const AttnParams &p, int grid, bool fp16, hipStream_t s);
-hipError_t launch_attn_mfma(const AttnParams &p, int grid, bool fp16, hipStream_t s);
+hipError_t launch_attn_valu(const AttnParams &p, int items, bool fp16, hipStream_t s);
+hipError_t launch_attn_mfma(const AttnParams &p, int items, bool fp16, hipStream_t s);
 hipError_t launch_attn_combine(const AttnParams &p, bool fp16, void *out, hipStream_t s);
 
 // ---- device helpers --------------------------------------------------------

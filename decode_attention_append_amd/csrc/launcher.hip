@@ -30,7 +30,7 @@ da_status check_problem(const da_problem *p) {
         (p->chunk_tokens < kTokenTile || p->chunk_tokens > kMaxChunk || p->chunk_tokens % kTokenTile))
         return DA_ERR_INVALID_ARG;
     if (p->variant < 0 || p->variant > DA_VARIANT_MFMA + 1) return DA_ERR_INVALID_ARG;
-    if (p->workgroups < 0 || p->workgroups > (1 << 20)) return DA_ERR_INVALID_ARG;
+    if (p->work_items < 0 || p->work_items > (1 << 20)) return DA_ERR_INVALID_ARG;
     if (p->dtype != DA_BF16 && p->dtype != DA_FP16) return DA_ERR_UNSUPPORTED;
     if (p->head_dim != kHeadDim) return DA_ERR_UNSUPPORTED;
     if (p->q_len > kMaxQLen) return DA_ERR_UNSUPPORTED;
@@ -47,11 +47,12 @@ da_status check_problem(const da_problem *p) {
     return DA_OK;
 }
 
-// Workgroups to aim for in balanced mode, per kernel: enough for every one of
-// the 256 compute units to hold a few resident workgroups at the kernel's
-// occupancy, so that the dispatcher balances what the chunking does not.
+// Chunks to aim for in balanced mode, per kernel: a few per compute unit (256
+// on MI355X) at the kernel's occupancy.  A vector-ALU chunk is a 4-wave
+// workgroup (about 7 fit per compute unit); an MFMA chunk is one wave, or a
+// pair of waves above 16 rows (8 waves fit per compute unit).
 int default_target(int variant, int rows) {
-    if (variant == DA_VARIANT_MFMA) return 256;  // one 4-wave workgroup per compute unit (two fit)
+    if (variant == DA_VARIANT_MFMA) return rows > 16 ? 1024 : 2048;
     return 1024;
 }
 
@@ -82,8 +83,8 @@ void plan_of(const da_problem *p, da_plan *pl) {
         pl->balanced = 0;
         pl->chunk_tokens = p->chunk_tokens;
         pl->n_chunks = (p->max_seq + p->chunk_tokens - 1) / p->chunk_tokens;
-        pl->target_workgroups = units * pl->n_chunks;
-        pl->grid = units * pl->n_chunks;
+        pl->target_items = units * pl->n_chunks;
+        pl->items = units * pl->n_chunks;
     } else {
         const int max_chunk = max_chunk_of(variant, rows);
         pl->balanced = 1;
@@ -92,12 +93,12 @@ void plan_of(const da_problem *p, da_plan *pl) {
         // keeps ceil(ctx / max_chunk) within them, so no chunk exceeds max_chunk
         const int slots = (p->max_seq + kMinChunk - 1) / kMinChunk;
         pl->n_chunks = slots < kMaxChunks ? slots : kMaxChunks;
-        pl->target_workgroups = p->workgroups > 0 ? p->workgroups : default_target(variant, rows);
+        pl->target_items = p->work_items > 0 ? p->work_items : default_target(variant, rows);
         // at most target + one rounding chunk per (sequence, head), or every
         // sequence in chunks of max_chunk keys when the target is too few
-        const int64_t a = (int64_t)pl->target_workgroups + units;
+        const int64_t a = (int64_t)pl->target_items + units;
         const int64_t b = (int64_t)units * ((p->max_seq + max_chunk - 1) / max_chunk);
-        pl->grid = (int32_t)(a > b ? a : b);
+        pl->items = (int32_t)(a > b ? a : b);
     }
     const int32_t bh = units;
     pl->workspace_bytes = align256(ws_acc_floats(bh, pl->n_chunks, rows) * sizeof(float)) +
@@ -123,7 +124,7 @@ AttnParams attn_params(const da_problem *p, const da_plan &pl, const void *q, co
     a.rows = pl.rows;
     a.n_chunks = pl.n_chunks;
     a.fixed_chunk = pl.balanced ? 0 : pl.chunk_tokens;
-    a.target_wg = pl.target_workgroups;
+    a.target_wg = pl.target_items;
     a.min_chunk = kMinChunk;
     a.max_chunk = pl.chunk_tokens;
     const double scale = p->scale > 0.f ? (double)p->scale : 1.0 / sqrt((double)p->head_dim);
@@ -187,8 +188,8 @@ da_status da_gqa_decode_attn(const da_problem *p, const void *q, const void *k_c
     const AttnParams a = attn_params(p, pl, q, k_cache, v_cache, seq_pos, workspace);
     (void)hipGetLastError();
     const hipError_t e = pl.variant == DA_VARIANT_MFMA
-                             ? launch_attn_mfma(a, pl.grid, p->dtype == DA_FP16, (hipStream_t)stream)
-                             : launch_attn_valu(a, pl.grid, p->dtype == DA_FP16, (hipStream_t)stream);
+                             ? launch_attn_mfma(a, pl.items, p->dtype == DA_FP16, (hipStream_t)stream)
+                             : launch_attn_valu(a, pl.items, p->dtype == DA_FP16, (hipStream_t)stream);
     return e == hipSuccess ? DA_OK : DA_ERR_HIP;
 }
 

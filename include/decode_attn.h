@@ -85,8 +85,8 @@ typedef struct {
     int32_t variant;      /* attention kernel: 0 = automatic, else DA_VARIANT_* + 1
                              (a tuning and testing override; the vector-ALU kernel
                              takes at most 16 rows per KV head)                   */
-    int32_t workgroups;   /* balanced chunking: attention workgroups to aim for,
-                             0 = automatic (a tuning override)                    */
+    int32_t work_items;   /* balanced chunking: chunks to aim for over the whole
+                             launch, 0 = automatic (a tuning override)            */
 } da_problem;
 
 /*
@@ -94,11 +94,13 @@ typedef struct {
  *
  * Chunking.  With chunk_tokens == 0 the chunks are balanced on the device:
  * from the actual seq_pos values, every sequence's context is cut into equal
- * chunks whose length is close to an equal share of all visible keys per
- * workgroup (about `target_workgroups` of them), never longer than
- * `chunk_tokens` (the plan's maximum) and never shorter than 64 keys.  With an
- * explicit chunk_tokens every chunk has that length.  Either way the
- * attention and the combine derive the same chunks from the same seq_pos.
+ * chunks whose length is close to an equal share of all visible keys (about
+ * `target_items` chunks in all), never longer than `chunk_tokens` (the plan's
+ * maximum) and never shorter than 64 keys.  With an explicit chunk_tokens every
+ * chunk has that length.  Either way the attention and the combine derive the
+ * same chunks from the same seq_pos.  A chunk is the work of one workgroup on
+ * the vector-ALU kernel and of one wave (a pair of waves above 16 rows) on the
+ * MFMA kernel.
  */
 typedef struct {
     int32_t chunk_tokens;    /* longest chunk (fixed mode: every chunk)          */
@@ -106,8 +108,8 @@ typedef struct {
     int32_t rows;            /* query rows per KV head = (Hq / Hkv) * q_len      */
     int32_t variant;         /* DA_VARIANT_*                                     */
     int32_t balanced;        /* 1: balanced chunks, 0: fixed chunks              */
-    int32_t target_workgroups; /* balanced: workgroups aimed at                  */
-    int32_t grid;            /* workgroups launched (an upper bound; extras exit) */
+    int32_t target_items;    /* balanced: chunks aimed at                        */
+    int32_t items;           /* chunks launched for (an upper bound; extras exit) */
     size_t workspace_bytes;  /* bytes of fp32 partials the attention needs       */
 } da_plan;
 

@@ -75,12 +75,12 @@ def test_plan_is_pure_and_sized():
     assert a["balanced"] and a["variant"] == "valu"
     assert a["n_chunks"] == 8192 // 64  # one slot per 64 keys, the shortest chunk
     assert a["workspace_bytes"] >= 32 * 8 * a["n_chunks"] * rows * (128 + 2) * 4
-    assert a["grid"] >= a["target_workgroups"] + 32 * 8
+    assert a["items"] >= a["target_items"] + 32 * 8
     assert da.plan_attention(P(q_len=4, n_q_heads=32, n_kv_heads=4))["variant"] == "mfma"
     fixed = da.plan_attention(P(chunk_tokens=128))
     assert not fixed["balanced"] and fixed["chunk_tokens"] == 128 and fixed["n_chunks"] == 8
-    assert fixed["grid"] == 2 * 8 * 8
-    assert da.plan_attention(P(workgroups=77))["target_workgroups"] == 77
+    assert fixed["items"] == 2 * 8 * 8
+    assert da.plan_attention(P(work_items=77))["target_items"] == 77
     assert da.plan_attention(P(variant="mfma"))["variant"] == "mfma"
 
 

@@ -28,7 +28,7 @@ def check_layout(p, seq_pos):
             assert ln == plan["chunk_tokens"]
         total += n
     total *= p.n_kv_heads
-    assert total <= plan["grid"], "launch grid misses chunks"
+    assert total <= plan["items"], "launch grid misses chunks"
     return plan, lay, total
 
 
@@ -51,7 +51,7 @@ def test_random_layouts(seed):
         variant = None
     wg = int(rng.choice([0, 0, 1, 37, 256, 5000]))
     p = da.problem(B, q_len, G * Hkv, Hkv, 128, S, "bf16", chunk_tokens=chunk, variant=variant,
-                   workgroups=wg)
+                   work_items=wg)
     kind = rng.integers(0, 3)
     if kind == 0:
         sp = rng.integers(0, S - q_len + 1, B)
@@ -72,7 +72,7 @@ def test_contract_breaking_positions_get_no_chunks():
 def test_balanced_chunks_are_equal_share():
     """Ragged long contexts (GQA 64:8, batch 4, 12k..16k): every chunk close to one
     workgroup's share of all keys."""
-    p = da.problem(4, 1, 64, 8, 128, 16384, "bf16", workgroups=512)
+    p = da.problem(4, 1, 64, 8, 128, 16384, "bf16", work_items=512)
     sp = np.array([15488, 13371, 15557, 14115], np.int32)
     plan, lay, total = check_layout(p, sp)
     share = 8 * int((sp + 1).sum()) / 512
