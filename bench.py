@@ -1,8 +1,11 @@
 #!/usr/bin/env python3
 """Throughput of one decode step of GQA attention with KV append on one MI355X.
 
-A step is the whole path over one batch: for every layer, da_kv_append,
-da_gqa_decode_attn and da_gqa_decode_attn_combine, enqueued on one stream.
+A step is the whole path over one batch: for every layer, the KV append, the
+split-context attention and the combine, enqueued on one stream.  By default
+each layer is one da_decode_step call (append and merge fused into the
+attention launch where the plan allows); --path separate times the three
+separate calls da_kv_append, da_gqa_decode_attn, da_gqa_decode_attn_combine.
 The default workload is batched GQA decode with Hq 16 / Hkv 8 / head_dim 128,
 batch 32, context 8192, 28 layers (bf16, synthetic N(0,1)*0.5 inputs resident
 in HBM before timing starts).
@@ -13,7 +16,8 @@ step, the attention kernel's roofline fraction against the 8 TB/s HBM peak
 the timed steps), and the fp64 CPU oracle's rate on a bounded sample of the
 same workload.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--path step|separate]
+                    [--no-cpu-baseline]
 """
 import argparse
 import json
@@ -31,6 +35,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--chunk", type=int, default=0, help="chunk_tokens override (0 = automatic)")
+    ap.add_argument("--path", choices=["step", "separate"], default="step",
+                    help="step: one da_decode_step per layer; separate: the three calls per layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle sample")
@@ -135,7 +141,7 @@ def main():
 
     stream = torch.cuda.current_stream()
 
-    def step(events=None):
+    def step_separate(events=None):
         for l, L in enumerate(layers):
             da.kv_append(p, L["k_cache"], L["v_cache"], L["k_new"], L["v_new"], L["seq_pos"], stream)
             if events is not None:
@@ -144,6 +150,17 @@ def main():
             if events is not None:
                 events[l][1].record(stream)
             da.gqa_decode_attn_combine(p, ws, L["seq_pos"], outs[l], stream)
+
+    def step_fused(events=None):
+        for l, L in enumerate(layers):
+            if events is not None:
+                events[l][0].record(stream)
+            da.decode_step(p, L["q"], L["k_cache"], L["v_cache"], L["k_new"], L["v_new"], L["seq_pos"], ws,
+                           outs[l], stream)
+            if events is not None:
+                events[l][1].record(stream)
+
+    step = step_fused if args.path == "step" else step_separate
 
     for _ in range(args.warmup):
         step()
@@ -178,13 +195,19 @@ def main():
     ms_per_step = ms_total / args.steps
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
 
-    # dominant kernel: the split-context attention; its algorithmic bytes per launch are the
-    # K+V of the visible context (512 bytes per visible key per KV head) plus q
+    # dominant kernel: the split-context attention.  Its algorithmic bytes per launch are the
+    # K+V of the visible context (512 bytes per visible key per KV head) plus q; in the
+    # one-launch step also the new rows' cache writes and, with the merge fused, the output.
+    # (There the new rows are read once, from k_new, as part of the visible context.)
     attn_avg_ms = float(np.mean(attn_ms))
-    attn_bytes = kv_bytes + w.batch * w.q_len * w.n_q_heads * w.head_dim * 2
-    attn_gbs = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
+    q_bytes = w.batch * w.q_len * w.n_q_heads * w.head_dim * 2
+    attn_bytes = kv_bytes + q_bytes
     kernel_tag = "attn_split_" + plan["variant"]
-    traffic = counters_for(kernel_tag, w.name)
+    if args.path == "step":
+        attn_bytes += 2 * w.batch * w.q_len * w.n_kv_heads * w.head_dim * 2 + q_bytes
+        kernel_tag += "_step" if plan["fused_combine"] else "_step+attn_combine"
+    attn_gbs = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
+    traffic = counters_for(kernel_tag, w.name) if "+" not in kernel_tag else None
 
     rec = {
         "metric": "decode-attention KV GB/s (% of HBM peak) + us/step, Hq16/Hkv8/d128 ctx 8k",
@@ -204,7 +227,9 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "q_len": w.q_len, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "context": int(seq_pos.max()) + w.q_len,
                    "max_seq": w.max_seq, "layers": w.layers, "chunk_tokens": plan["chunk_tokens"],
-                   "variant": plan["variant"], "bytes_per_step": step_bytes,
+                   "variant": plan["variant"], "path": args.path,
+                   "fused_merge": bool(plan["fused_combine"]) and args.path == "step",
+                   "bytes_per_step": step_bytes,
                    "cold_cache_flush": flush},
         "roofline": {"bound": "hbm", "kernel": kernel_tag, "achieved": round(attn_gbs, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),

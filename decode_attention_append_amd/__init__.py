@@ -10,7 +10,9 @@ the library has not been built.
 
 Names follow the C entry points without their ``da_`` prefix:
 ``kv_append``, ``gqa_decode_attn``, ``gqa_decode_attn_combine``,
-``workspace_bytes``, ``plan_attention``.
+``decode_step`` (the one-launch step), ``workspace_init``,
+``workspace_bytes``, ``plan_attention``.  ``decode_step_separate`` runs the
+three separate calls in order.
 """
 import ctypes
 import math
@@ -66,12 +68,14 @@ class Plan(ctypes.Structure):
         ("balanced", ctypes.c_int32),
         ("target_items", ctypes.c_int32),
         ("items", ctypes.c_int32),
+        ("fused_combine", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),
     ]
 
 
 EXPORTS = ("da_plan_attention", "da_workspace_bytes", "da_kv_append", "da_gqa_decode_attn",
-           "da_gqa_decode_attn_combine", "da_chunk_layout", "da_status_str")
+           "da_gqa_decode_attn_combine", "da_workspace_init", "da_decode_step", "da_chunk_layout",
+           "da_status_str")
 
 
 def _load():
@@ -92,6 +96,10 @@ def _load():
     lib.da_gqa_decode_attn.restype = ctypes.c_int
     lib.da_gqa_decode_attn_combine.argtypes = [pp, vp, sz, i32p, vp, vp]
     lib.da_gqa_decode_attn_combine.restype = ctypes.c_int
+    lib.da_workspace_init.argtypes = [pp, vp, sz, vp]
+    lib.da_workspace_init.restype = ctypes.c_int
+    lib.da_decode_step.argtypes = [pp, vp, vp, vp, vp, vp, i32p, vp, sz, vp, vp]
+    lib.da_decode_step.restype = ctypes.c_int
     lib.da_chunk_layout.argtypes = [pp, vp, vp, vp]
     lib.da_chunk_layout.restype = ctypes.c_int
     lib.da_status_str.argtypes = [ctypes.c_int]
@@ -149,7 +157,7 @@ def plan_attention(p: Problem) -> dict:
     return {"chunk_tokens": pl.chunk_tokens, "n_chunks": pl.n_chunks, "rows": pl.rows,
             "variant": VARIANTS[pl.variant], "balanced": bool(pl.balanced),
             "target_items": pl.target_items, "items": pl.items,
-            "workspace_bytes": pl.workspace_bytes}
+            "fused_combine": bool(pl.fused_combine), "workspace_bytes": pl.workspace_bytes}
 
 
 def chunk_layout(p: Problem, seq_pos) -> list:
@@ -170,12 +178,15 @@ def workspace_bytes(p: Problem) -> int:
     return _get_lib().da_workspace_bytes(ctypes.byref(p))
 
 
-def new_workspace(p: Problem, device="cuda") -> torch.Tensor:
-    """A uint8 device buffer of workspace_bytes(p) (allocated by torch, owned by the caller)."""
+def new_workspace(p: Problem, device="cuda", stream=None) -> torch.Tensor:
+    """A uint8 device buffer of workspace_bytes(p) (allocated by torch, owned by the
+    caller), prepared by workspace_init on ``stream``."""
     n = workspace_bytes(p)
     if n == 0:
         raise DecodeAttnError(DA_ERR_INVALID_ARG, "workspace_bytes")
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    workspace_init(p, ws, stream)
+    return ws
 
 
 def _stream(stream):
@@ -239,8 +250,33 @@ def gqa_decode_attn_combine(p: Problem, workspace, seq_pos, out, stream=None):
         raise DecodeAttnError(st, "da_gqa_decode_attn_combine")
 
 
+def workspace_init(p: Problem, workspace, stream=None):
+    """da_workspace_init: zero the one-launch step's arrival counters in ``workspace``."""
+    st = _get_lib().da_workspace_init(ctypes.byref(p), _dev(workspace, "workspace"),
+                                      workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != DA_OK:
+        raise DecodeAttnError(st, "da_workspace_init")
+
+
 def decode_step(p: Problem, q, k_cache, v_cache, k_new, v_new, seq_pos, workspace, out, stream=None):
-    """The three calls of one decode step, in order, on one stream."""
+    """da_decode_step: append + attention + combine, in one launch where the plan allows."""
+    e = _elem(p)
+    cs = (p.batch, p.n_kv_heads, p.max_seq, p.head_dim)
+    ns = (p.batch, p.q_len, p.n_kv_heads, p.head_dim)
+    qs = (p.batch, p.q_len, p.n_q_heads, p.head_dim)
+    st = _get_lib().da_decode_step(
+        ctypes.byref(p), _dev(q, "q", qs, e), _dev(k_cache, "k_cache", cs, e), _dev(v_cache, "v_cache", cs, e),
+        _dev(k_new, "k_new", ns, e), _dev(v_new, "v_new", ns, e),
+        _dev(seq_pos, "seq_pos", (p.batch,), torch.int32),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _dev(out, "out", qs, e), _stream(stream))
+    if st != DA_OK:
+        raise DecodeAttnError(st, "da_decode_step")
+
+
+def decode_step_separate(p: Problem, q, k_cache, v_cache, k_new, v_new, seq_pos, workspace, out,
+                         stream=None):
+    """The three separate calls of one decode step, in order, on one stream."""
     kv_append(p, k_cache, v_cache, k_new, v_new, seq_pos, stream)
     gqa_decode_attn(p, q, k_cache, v_cache, seq_pos, workspace, stream)
     gqa_decode_attn_combine(p, workspace, seq_pos, out, stream)

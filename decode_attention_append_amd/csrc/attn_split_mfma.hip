@@ -82,22 +82,44 @@ __device__ __forceinline__ void load_full(Tile &t, const uint8_t *kb, const uint
     }
 }
 
-// The chunk's last, partial tile: keys past `last` re-read row `last` (their
-// scores are masked), and their value rows are zeroed so a non-finite last row
-// cannot reach the other rows as 0 * inf.
-__device__ __forceinline__ void load_tail(Tile &t, const uint8_t *kb, const uint8_t *vb, int tb, int last,
-                                          int l16, int q) {
+// Where a tile's rows come from when they are not all plain cache rows: the
+// chunk's partial last tile (keys past `last` re-read row `last`, their scores
+// are masked and their value rows zeroed so a non-finite last row cannot reach
+// other rows as 0 * inf), and in the one-launch step the tiles holding this
+// step's new rows (local keys from `new_first` on), which are read from
+// k_new / v_new and, by `store`, appended to the cache.
+struct RowSource {
+    const uint8_t *knew, *vnew;  // new rows of (b, h), row i at + i * stride
+    uint8_t *kw, *vw;            // writable cache of (b, h) at the chunk start
+    size_t stride;
+    int new_first;
+    bool store;
+};
+
+__device__ __forceinline__ void load_rows(Tile &t, const uint8_t *kb, const uint8_t *vb, int tb, int last,
+                                          int l16, int q, const RowSource &rs) {
 #pragma unroll
     for (int kblk = 0; kblk < 2; ++kblk) {
-        const uint8_t *kr = kb + (size_t)min(tb + 16 * kblk + l16, last) * kRowBytes + 16 * q;
+        const int key = min(tb + 16 * kblk + l16, last);
+        const uint8_t *kr = key >= rs.new_first ? rs.knew + (size_t)(key - rs.new_first) * rs.stride + 16 * q
+                                                : kb + (size_t)key * kRowBytes + 16 * q;
 #pragma unroll
         for (int s = 0; s < 4; ++s) t.k[kblk][s] = ld16(kr + 64 * s);
+        if (rs.store && key >= rs.new_first && tb + 16 * kblk + l16 <= last) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                *reinterpret_cast<u32x4_t *>(rs.kw + (size_t)key * kRowBytes + 16 * q + 64 * s) = t.k[kblk][s];
+        }
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-        const int key = tb + pv_key(q, u);
-        t.v[u] = ld16(vb + (size_t)min(key, last) * kRowBytes + 16 * l16);
-        if (key > last) t.v[u] = u32x4_t{0u, 0u, 0u, 0u};
+        const int k_raw = tb + pv_key(q, u);
+        const int key = min(k_raw, last);
+        t.v[u] = ld16(key >= rs.new_first ? rs.vnew + (size_t)(key - rs.new_first) * rs.stride + 16 * l16
+                                          : vb + (size_t)key * kRowBytes + 16 * l16);
+        if (k_raw > last) t.v[u] = u32x4_t{0u, 0u, 0u, 0u};
+        else if (rs.store && key >= rs.new_first)
+            *reinterpret_cast<u32x4_t *>(rs.vw + (size_t)key * kRowBytes + 16 * l16) = t.v[u];
     }
 }
 
@@ -115,7 +137,12 @@ void attn_split_mfma_kernel(AttnParams p) {
     const int n_chunks = p.n_chunks;
     int b, h, c;
     SeqChunks sc;
-    if (!locate(p, item, b, h, c, sc)) return;  // past the last chunk of the launch
+    int rest = item;
+    if (!locate(p, rest, b, h, c, sc)) {  // past the last chunk of the launch
+        if (p.out && rg == 0 && rest < p.batch && !seq_pos_ok(p, p.seq_pos[rest]))
+            flag_sequence_nan<F16>(p, rest, lane, 64);
+        return;
+    }
     const int bh = b * p.n_kv_heads + h;
     const int sp = p.seq_pos[b];
     const int ctx = sc.ctx;
@@ -219,11 +246,27 @@ void attn_split_mfma_kernel(AttnParams p) {
         }
     };
 
-    // Full tiles through two register buffers used in turn, with no copy between
-    // them, so the wave waits only for the older tile while the newer one is in
-    // flight.  When the count is even the last prefetch re-reads the final tile
-    // (from cache) and is not used.  The partial tail tile is peeled off.
-    const int nt = n_tok >> 5;
+    // Full tiles below this step's new rows go through two register buffers used
+    // in turn, with no copy between them, so the wave waits only for the older
+    // tile while the newer one is in flight.  When their count is even the last
+    // prefetch re-reads the final tile (from cache) and is not used.  The tiles
+    // that hold new rows or run past the chunk take the per-row path.
+    RowSource rs;
+    rs.new_first = p.k_new ? sp - t0 : n_tok;
+    rs.store = p.k_new != nullptr && rg == 0;
+    rs.stride = (size_t)p.n_kv_heads * kRowBytes;
+    if (p.k_new) {
+        const size_t noff = ((size_t)b * p.q_len * p.n_kv_heads + h) * kRowBytes;
+        rs.knew = p.k_new + noff;
+        rs.vnew = p.v_new + noff;
+        rs.kw = p.k_cache_w + head_off;
+        rs.vw = p.v_cache_w + head_off;
+    } else {
+        rs.knew = rs.vnew = nullptr;
+        rs.kw = rs.vw = nullptr;
+    }
+    const int n_all = (n_tok + 31) >> 5;
+    const int nt = min(n_tok >> 5, max(rs.new_first, 0) >> 5);
     if (nt > 0) {
         Tile ta, tb_;
         load_full(ta, kb, vb, 0, l16, q);
@@ -236,35 +279,52 @@ void attn_split_mfma_kernel(AttnParams p) {
         }
         if (i < nt) compute(ta, i);
     }
-    if (n_tok & 31) {
+    for (int i = nt; i < n_all; ++i) {
         Tile tt_;
-        load_tail(tt_, kb, vb, nt * 32, last, l16, q);
-        compute(tt_, nt);
+        load_rows(tt_, kb, vb, i * 32, last, l16, q, rs);
+        compute(tt_, i);
     }
 
     // ---- this wave's partial: O^T (lane: row l16, dims 8*(4q+v)+o), m, l ---------
+    // When the one-launch step merges in this launch, device-scope stores (the
+    // merge may read them from another XCD); else plain stores, which the L2
+    // gathers into whole lines (a lane's 16-byte pieces are scattered).
     l_run[0] += __shfl_xor(l_run[0], 16);
     l_run[0] += __shfl_xor(l_run[0], 32);
     const int row = rg * 16 + l16;
     if (row < p.rows) {
         const size_t part = ((size_t)bh * n_chunks + c) * p.rows + row;
         float *wa = p.ws_acc + part * kHeadDim;
+        const bool dev = p.counters != nullptr;
 #pragma unroll
         for (int v = 0; v < 4; ++v)
 #pragma unroll
             for (int o = 0; o < 8; o += 4) {
                 // dims 8*(4q+v) + o .. +3 are four consecutive floats of this lane
-                float4 x;
-                x.x = oacc[0][o][v];
-                x.y = oacc[0][o + 1][v];
-                x.z = oacc[0][o + 2][v];
-                x.w = oacc[0][o + 3][v];
-                *reinterpret_cast<float4 *>(wa + 8 * (4 * q + v) + o) = x;
+                float *dst = wa + 8 * (4 * q + v) + o;
+                if (dev) {
+                    st_dev4(dst, oacc[0][o][v], oacc[0][o + 1][v], oacc[0][o + 2][v], oacc[0][o + 3][v]);
+                } else {
+                    *reinterpret_cast<float4 *>(dst) =
+                        make_float4(oacc[0][o][v], oacc[0][o + 1][v], oacc[0][o + 2][v], oacc[0][o + 3][v]);
+                }
             }
         if (q == 0) {
-            p.ws_ml[part * 2 + 0] = m_run[0];
-            p.ws_ml[part * 2 + 1] = l_run[0];
+            if (dev) {
+                st_dev(p.ws_ml + part * 2 + 0, m_run[0]);
+                st_dev(p.ws_ml + part * 2 + 1, l_run[0]);
+            } else {
+                p.ws_ml[part * 2 + 0] = m_run[0];
+                p.ws_ml[part * 2 + 1] = l_run[0];
+            }
         }
+    }
+
+    // One-launch step: the wave whose partial arrives last for (b, h) merges all
+    // its rows and resets the arrival counter for the next call.
+    if (p.counters && last_arrival(&p.counters[bh], sc.n * RG, lane)) {
+        for (int r = 0; r < p.rows; ++r) merge_row_wave<F16>(p, p.out, bh, b, h, r, sc.n, lane);
+        if (lane == 0) p.counters[bh] = 0;
     }
 }
 

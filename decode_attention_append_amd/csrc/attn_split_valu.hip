@@ -27,15 +27,71 @@
 
 namespace da {
 
+// The one-launch step's merge of every query row of (b, h) over its n chunks,
+// by the whole workgroup.  With at most 16 chunks, or 4 rows or more, each wave
+// merges whole rows (r = wave, wave + 4, ...); otherwise the four waves split
+// each row's chunks into four consecutive ranges and their merge states are
+// combined in LDS in a fixed order.  `red` is LDS of at least 4 * 128 + 8
+// floats.  Uniform across the workgroup (it has barriers).
+template <bool F16>
+__device__ void merge_rows_block(const AttnParams &p, float *red, int bh, int b, int h, int n, int tid) {
+    const int lane = tid & 63, wave = tid >> 6;
+    if (n <= 16 || p.rows >= 4) {
+        for (int r = wave; r < p.rows; r += 4) merge_row_wave<F16>(p, p.out, bh, b, h, r, n, lane);
+        return;
+    }
+    float *wm = red + 4 * kHeadDim, *wl = wm + 4;
+    const int c_lo = wave * n / 4, c_hi = (wave + 1) * n / 4;
+    for (int r = 0; r < p.rows; ++r) {
+        const MergeState s = merge_range(p, (size_t)bh * p.n_chunks * p.rows + r, c_lo, c_hi, lane);
+        red[wave * kHeadDim + 2 * lane] = s.a0;
+        red[wave * kHeadDim + 2 * lane + 1] = s.a1;
+        if (lane == 0) {
+            wm[wave] = s.m;
+            wl[wave] = s.l;
+        }
+        __syncthreads();
+        if (wave == 0) {
+            const float M = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+            float f[4];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) f[w] = wm[w] == -INFINITY ? 0.f : exp2_fast(wm[w] - M);
+            const float L = (f[0] * wl[0] + f[1] * wl[1]) + (f[2] * wl[2] + f[3] * wl[3]);
+            float o[2];
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int d = 2 * lane + k;
+                o[k] = ((f[0] * red[d] + f[1] * red[kHeadDim + d]) +
+                        (f[2] * red[2 * kHeadDim + d] + f[3] * red[3 * kHeadDim + d])) /
+                       L;
+            }
+            out_row_words(p, p.out, b, h, r)[lane] =
+                (uint32_t)round16<F16>(o[0]) | ((uint32_t)round16<F16>(o[1]) << 16);
+        }
+        __syncthreads();
+    }
+}
+
+// The one-launch step's append and merge are compiled for up to 8 rows; the
+// 16-row kernel (only used when the vector-ALU kernel is forced) has no
+// registers to spare for them, and the launcher runs that step as three launches.
+constexpr int kValuOneLaunchRows = 8;
+
 template <bool F16, int RP>
 __global__ __launch_bounds__(256) void attn_split_valu_kernel(AttnParams p) {
+    constexpr bool kOneLaunch = RP <= kValuOneLaunchRows;
     extern __shared__ float lds[];  // scores [chunk][RP], later the wave sums [4][RP][128]
     __shared__ float row_m[RP], row_l[RP];
 
     const int n_chunks = p.n_chunks;
     int b, h, c;
     SeqChunks sc;
-    if (!locate(p, blockIdx.x, b, h, c, sc)) return;  // past the last chunk of the launch
+    int item = blockIdx.x;
+    if (!locate(p, item, b, h, c, sc)) {  // past the last chunk of the launch
+        if (kOneLaunch && p.out && item < p.batch && !seq_pos_ok(p, p.seq_pos[item]))
+            flag_sequence_nan<F16>(p, item, threadIdx.x, 256);
+        return;
+    }
     const int bh = b * p.n_kv_heads + h;
     const int sp = p.seq_pos[b];
     const int ctx = sc.ctx;
@@ -79,36 +135,59 @@ __global__ __launch_bounds__(256) void attn_split_valu_kernel(AttnParams p) {
     // Slab loads: four 128-bit loads per lane cover 16 keys (1 KiB each).  Full
     // slabs use one base address and immediate offsets; the last, partial slab
     // re-reads row `last` for keys past the chunk (those are masked).
+    // In the one-launch step, local keys from `new_first` on are this step's new
+    // rows: they are read from k_new / v_new and stored into the cache here
+    // (no other chunk touches them).
     const int n_full = n_tok >> 4;
-    auto load_slab = [&](u32x4_t (&buf)[4], const uint8_t *base, int s_) {
-        if (s_ < n_full) {
+    const bool fused_append = kOneLaunch && p.k_new != nullptr;
+    const int new_first = fused_append ? sp - t0 : n_tok;
+    const size_t new_stride = (size_t)p.n_kv_heads * kRowBytes;
+    const size_t new_off = ((size_t)b * p.q_len * p.n_kv_heads + h) * kRowBytes + cq * 16;
+    auto load_slab = [&](u32x4_t (&buf)[4], const uint8_t *base, const uint8_t *nbase, uint8_t *wbase, int s_) {
+        if (s_ < n_full && (s_ + 1) * 16 <= new_first) {
             const uint8_t *r0 = base + (size_t)(s_ * 16 + gq) * kRowBytes;
 #pragma unroll
             for (int u = 0; u < 4; ++u) buf[u] = ld16(r0 + u * 4 * kRowBytes);
         } else {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) buf[u] = ld16(base + (size_t)min(s_ * 16 + u * 4 + gq, last) * kRowBytes);
+            for (int u = 0; u < 4; ++u) {
+                const int t = min(s_ * 16 + u * 4 + gq, last);
+                buf[u] = ld16(t >= new_first ? nbase + (size_t)(t - new_first) * new_stride
+                                             : base + (size_t)t * kRowBytes);
+            }
+            if (fused_append) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int t = s_ * 16 + u * 4 + gq;
+                    if (t >= new_first && t <= last)
+                        *reinterpret_cast<u32x4_t *>(wbase + (size_t)t * kRowBytes) = buf[u];
+                }
+            }
         }
     };
     // This wave's slabs are wave, wave + 4, ...: two buffers used in turn, no copy
     // between iterations, so a wave waits only for the older slab.
     const int ns = wave < n_slab ? (n_slab - 1 - wave) / 4 + 1 : 0;
-    auto two_buffer_pass = [&](const uint8_t *base, auto &&body) {
+    auto two_buffer_pass = [&](const uint8_t *base, const uint8_t *nbase, uint8_t *wbase, auto &&body) {
         if (ns == 0) return;
         u32x4_t b0[4], b1[4];
-        load_slab(b0, base, wave);
+        load_slab(b0, base, nbase, wbase, wave);
         int i = 0;
         for (; i + 2 <= ns; i += 2) {
-            load_slab(b1, base, wave + (i + 1) * 4);
+            load_slab(b1, base, nbase, wbase, wave + (i + 1) * 4);
             body(b0, wave + i * 4);
-            load_slab(b0, base, wave + min(i + 2, ns - 1) * 4);
+            load_slab(b0, base, nbase, wbase, wave + min(i + 2, ns - 1) * 4);
             body(b1, wave + (i + 1) * 4);
         }
         if (i < ns) body(b0, wave + i * 4);
     };
 
     // ---- pass 1: scores of the chunk into LDS ----------------------------------
-    two_buffer_pass(kb, [&](u32x4_t (&cur)[4], int s_) {
+    const uint8_t *knb = fused_append ? p.k_new + new_off : nullptr;
+    const uint8_t *vnb = fused_append ? p.v_new + new_off : nullptr;
+    uint8_t *kwb = fused_append ? p.k_cache_w + head_off : nullptr;
+    uint8_t *vwb = fused_append ? p.v_cache_w + head_off : nullptr;
+    two_buffer_pass(kb, knb, kwb, [&](u32x4_t (&cur)[4], int s_) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int tl = s_ * 16 + u * 4 + gq;
@@ -157,7 +236,7 @@ __global__ __launch_bounds__(256) void attn_split_valu_kernel(AttnParams p) {
 #pragma unroll
         for (int d = 0; d < 8; ++d) acc[r][d] = 0.f;
     const int first_draft = sp - t0;  // local keys above this may be hidden from some rows
-    two_buffer_pass(vb, [&](u32x4_t (&cur)[4], int s_) {
+    two_buffer_pass(vb, vnb, vwb, [&](u32x4_t (&cur)[4], int s_) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int tl = s_ * 16 + u * 4 + gq;
@@ -205,20 +284,39 @@ __global__ __launch_bounds__(256) void attn_split_valu_kernel(AttnParams p) {
 
     const size_t part = (size_t)bh * n_chunks + c;
     float *wa = p.ws_acc + part * p.rows * kHeadDim;
+    // device-scope stores: the one-launch step's merge may read them from another XCD
     for (int idx = tid; idx < p.rows * kHeadDim; idx += 256) {
         const int r = idx >> 7, d = idx & (kHeadDim - 1);
-        wa[idx] = (red[(0 * RP + r) * kHeadDim + d] + red[(1 * RP + r) * kHeadDim + d]) +
-                  (red[(2 * RP + r) * kHeadDim + d] + red[(3 * RP + r) * kHeadDim + d]);
+        st_dev(wa + idx, (red[(0 * RP + r) * kHeadDim + d] + red[(1 * RP + r) * kHeadDim + d]) +
+                             (red[(2 * RP + r) * kHeadDim + d] + red[(3 * RP + r) * kHeadDim + d]));
     }
     if (tid < p.rows) {
-        p.ws_ml[(part * p.rows + tid) * 2 + 0] = row_m[tid];
-        p.ws_ml[(part * p.rows + tid) * 2 + 1] = row_l[tid];
+        st_dev(p.ws_ml + (part * p.rows + tid) * 2 + 0, row_m[tid]);
+        st_dev(p.ws_ml + (part * p.rows + tid) * 2 + 1, row_l[tid]);
+    }
+
+    // One-launch step: the workgroup that stores the last partial of (b, h)
+    // merges all its rows and resets the arrival counter for the next call.
+    if (kOneLaunch && p.counters) {
+        __shared__ int s_last;
+        wait_mem();       // this wave's partial stores are complete
+        __syncthreads();  // and so are the other waves'
+        if (tid == 0)
+            s_last = __hip_atomic_fetch_add(&p.counters[bh], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                     sc.n - 1;
+        __syncthreads();
+        if (s_last) {
+            merge_rows_block<F16>(p, lds, bh, b, h, sc.n, tid);
+            if (tid == 0) p.counters[bh] = 0;
+        }
     }
 }
 
 template <bool F16, int RP>
 static hipError_t launch_rp(const AttnParams &p, int grid, hipStream_t s) {
-    const size_t lds_bytes = (size_t)RP * (p.max_chunk > 512 ? p.max_chunk : 512) * sizeof(float);
+    // scores of the longest chunk; at least the wave sums [4][RP][128] and the
+    // fused merge's 4 * 128 + 8 floats
+    const size_t lds_bytes = (size_t)RP * (p.max_chunk > 520 ? p.max_chunk : 520) * sizeof(float);
     hipLaunchKernelGGL((attn_split_valu_kernel<F16, RP>), dim3(grid), dim3(256), lds_bytes, s, p);
     return hipGetLastError();
 }

@@ -4,6 +4,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 namespace da {
@@ -42,6 +43,16 @@ struct AttnParams {
     int32_t min_chunk;     // balanced: smallest chunk (multiple of 32)
     int32_t max_chunk;     // largest chunk the kernel accepts (multiple of 32)
     float scale_log2;      // softmax scale * log2(e): scores are kept in log2 units
+    int32_t seq_chunk_cap; // balanced: at most this many chunks per sequence unless its
+                           //   length needs more of max_chunk keys (0: no cap)
+
+    // One-launch step (all null for the separate entry points):
+    uint8_t *k_cache_w;        // k_cache as writable: the fused append stores new rows here
+    uint8_t *v_cache_w;
+    const uint8_t *k_new;      // [B][q_len][Hkv][D]: the chunk holding a sequence's new
+    const uint8_t *v_new;      //   positions reads them from here and appends them
+    int32_t *counters;         // [B*Hkv] chunk arrivals for the fused combine (0 between calls)
+    uint16_t *out;             // output written by the fused combine
 };
 
 // ---- split-context chunk plan, computed identically by every kernel ---------
@@ -50,7 +61,8 @@ struct AttnParams {
 // per chunk, T = ceil32(Hkv * sum_b ctx_b / target_wg) clamped to
 // [min_chunk, max_chunk]; sequence b gets n_b = max(round(ctx_b / T),
 // ceil(ctx_b / max_chunk)) chunks of ceil32(ctx_b / n_b) keys, so chunks of
-// one sequence are equal and all chunks are close to T.  Fixed mode: chunks of
+// one sequence are equal and all chunks are close to T.  With seq_chunk_cap,
+// round(ctx_b / T) is first capped at it (fewer, longer chunks).  Fixed mode: chunks of
 // fixed_chunk keys.  A sequence whose seq_pos breaks the contract has no
 // chunks.  Work items (chunks) are laid out sequence-major: for b, for h, for c.
 
@@ -90,6 +102,7 @@ __host__ __device__ inline SeqChunks seq_chunks(const AttnParams &p, int b, int 
         return s;
     }
     int n = (2 * s.ctx + T) / (2 * T);  // round(ctx / T)
+    if (p.seq_chunk_cap > 0 && n > p.seq_chunk_cap) n = p.seq_chunk_cap;
     const int n_cap = ceil_div(s.ctx, p.max_chunk);
     if (n < n_cap) n = n_cap;
     if (n < 1) n = 1;
@@ -100,8 +113,9 @@ __host__ __device__ inline SeqChunks seq_chunks(const AttnParams &p, int b, int 
     return s;
 }
 
-// Which (b, h, c) work item `w` is; false if w is past the last chunk.
-__host__ __device__ inline bool locate(const AttnParams &p, int w, int &b, int &h, int &c, SeqChunks &sc) {
+// Which (b, h, c) work item `w` is; false if w is past the last chunk, and then
+// `w` is left as the item's index counted from the first item past the chunks.
+__host__ __device__ inline bool locate(const AttnParams &p, int &w, int &b, int &h, int &c, SeqChunks &sc) {
     const int T = p.fixed_chunk > 0 ? p.fixed_chunk : balanced_chunk(p);
     for (b = 0; b < p.batch; ++b) {
         sc = seq_chunks(p, b, T);
@@ -127,6 +141,7 @@ inline size_t ws_ml_floats(int32_t bh, int32_t n_chunks, int32_t rows) {
 // ---- host-side launch entry points (one per translation unit) ---------------
 
 hipError_t launch_kv_append(const AppendParams &p, int threads_total, hipStream_t s);
+hipError_t launch_fill_zero(int32_t *x, int n, hipStream_t s);
 hipError_t launch_attn_valu(const AttnParams &p, int items, bool fp16, hipStream_t s);
 hipError_t launch_attn_mfma(const AttnParams &p, int items, bool fp16, hipStream_t s);
 hipError_t launch_attn_combine(const AttnParams &p, bool fp16, void *out, hipStream_t s);
@@ -212,5 +227,152 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- partials shared across workgroups (the one-launch step's merge) ---------
+//
+// The merge of the one-launch step reads partials that workgroups on other
+// XCDs wrote in the same launch, and each XCD has its own L2.  A release fence
+// would write back the whole L2 after every partial (measured: it more than
+// doubled the kernel's time), so instead:
+//  - every partial is stored with a device-scope store, which writes through
+//    the L2 to device-coherent memory;
+//  - the storing wave waits until those stores are complete (vmcnt 0) before
+//    it counts its arrival with a device-scope atomic add;
+//  - the last arriver, which only gets there after every other arrival and so
+//    after every other partial store completed, reads the partials with
+//    device-scope loads, which fetch from device-coherent memory rather than
+//    a possibly stale L2 line.
+
+__device__ __forceinline__ void st_dev(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev4(float *p, float a, float b, float c, float d) {
+    uint64_t *q = reinterpret_cast<uint64_t *>(p);
+    __hip_atomic_store(q, (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q + 1, (uint64_t)__float_as_uint(c) | ((uint64_t)__float_as_uint(d) << 32),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 ld_dev2(const float *p) {
+    const uint64_t x =
+        __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_float2(__uint_as_float((uint32_t)x), __uint_as_float((uint32_t)(x >> 32)));
+}
+// Wait until every memory access this wave issued is complete; also a compiler
+// barrier, so no access moves across it.
+__device__ __forceinline__ void wait_mem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Counts one arrival on `counter` once this wave's partial stores are complete.
+// True for the last of `arrivals` arrivals per (b, h): that wave then merges
+// every row and resets the counter for the next call.
+__device__ inline bool last_arrival(int32_t *counter, int arrivals, int lane) {
+    wait_mem();
+    int prev = 0;
+    if (lane == 0) prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    prev = __shfl(prev, 0);
+    return prev == arrivals - 1;
+}
+
+// Log-sum-exp merge state of one query row over some chunks: running maximum m
+// (log2 units), sum l = sum_c 2^(m_c - m) l_c and this lane's two dims of
+// sum_c 2^(m_c - m) acc_c.
+struct MergeState {
+    float m, l, a0, a1;
+};
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Merge of chunks [c_lo, c_hi) of partial row `part` (= (b * Hkv + h) *
+// n_chunks * rows + r) by one wave; lane j takes dims 2j and 2j + 1.
+//  - Per group of up to 64 chunks, lane k loads chunk k's (m, l): one
+//    wave-wide max and sum give the group's weights w_k = 2^(m_k - M) and
+//    sum of w_k l_k at once.
+//  - The value rows are read sixteen chunks at a time with buffer loads that
+//    share one lane offset and take the chunk offset from a scalar register
+//    (no address registers per load), the first sixteen already in flight
+//    while (m, l) are reduced.  Each is weighted by w_k, read from lane k.
+// A chunk the row saw no key of (m_k = -inf) has weight 0.  Every load is
+// device-scope (the partials may come from other XCDs in the same launch).
+__device__ inline MergeState merge_range(const AttnParams &p, size_t part, int c_lo, int c_hi, int lane) {
+    const float *ml = p.ws_ml + part * 2;
+    const uint32_t cs_ml = (uint32_t)p.rows * 2;             // floats between chunks
+    const uint32_t cs_acc = (uint32_t)p.rows * kHeadDim * 4;  // bytes between chunks
+    const __amdgpu_buffer_rsrc_t acc =
+        __builtin_amdgcn_make_buffer_rsrc(p.ws_acc + part * kHeadDim, 0, (int)(cs_acc * (uint32_t)p.n_chunks),
+                                          0x00020000);
+    constexpr int kDevScope = 16;  // cache policy of the buffer loads: device scope
+    const int voff = lane * 8;
+    MergeState s{-INFINITY, 0.f, 0.f, 0.f};
+    for (int g = c_lo; g < c_hi; g += 64) {
+        const int cnt = min(64, c_hi - g);
+        float m = -INFINITY, l = 0.f;
+        if (lane < cnt) {
+            m = ld_dev(ml + (size_t)(g + lane) * cs_ml);
+            l = ld_dev(ml + (size_t)(g + lane) * cs_ml + 1);
+        }
+        f32x2_t v[16];
+        auto load_batch = [&](int j) {
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                v[u] = j + u < cnt ? __builtin_amdgcn_raw_buffer_load_b64(acc, voff, (g + j + u) * cs_acc, kDevScope)
+                                   : f32x2_t{0.f, 0.f};
+        };
+        load_batch(0);
+        const float M = fmaxf(s.m, wave_max(m));
+        if (M == -INFINITY) continue;
+        const float f = s.m == -INFINITY ? 0.f : exp2_fast(s.m - M);
+        const float w = m == -INFINITY ? 0.f : exp2_fast(m - M);
+        s.l = fmaf(s.l, f, wave_sum(w * l));
+        s.a0 *= f;
+        s.a1 *= f;
+        s.m = M;
+        for (int j = 0;;) {
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                if (j + u < cnt) {
+                    const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j + u));
+                    s.a0 = fmaf(wu, v[u].x, s.a0);
+                    s.a1 = fmaf(wu, v[u].y, s.a1);
+                }
+            }
+            j += 16;
+            if (j >= cnt) break;
+            load_batch(j);
+        }
+    }
+    return s;
+}
+
+// Output row r of (b, h) as 32-bit words (two 16-bit elements each).
+__device__ __forceinline__ uint32_t *out_row_words(const AttnParams &p, uint16_t *out, int b, int h, int r) {
+    const int i = r / p.group, g = r - i * p.group;
+    return reinterpret_cast<uint32_t *>(out +
+                                        (((size_t)b * p.q_len + i) * p.n_q_heads + (size_t)h * p.group + g) * kHeadDim);
+}
+
+// Merge of query row r of (b, h) over its n chunks by one wave, written to out:
+//     out = (sum_c 2^(m_c - M) acc_c) / (sum_c 2^(m_c - M) l_c),  M = max_c m_c,
+// rounded to nearest even.
+template <bool F16>
+__device__ inline void merge_row_wave(const AttnParams &p, uint16_t *out, int bh, int b, int h, int r, int n,
+                                      int lane) {
+    const MergeState s = merge_range(p, (size_t)bh * p.n_chunks * p.rows + r, 0, n, lane);
+    out_row_words(p, out, b, h, r)[lane] =
+        (uint32_t)round16<F16>(s.a0 / s.l) | ((uint32_t)round16<F16>(s.a1 / s.l) << 16);
+}
+
+// One-launch step: the output rows of sequence b, whose seq_pos breaks the
+// contract (it has no chunks), are flagged with NaN, as the separate combine
+// does.  Written by `n_lanes` lanes starting at `lane`.
+template <bool F16>
+__device__ inline void flag_sequence_nan(const AttnParams &p, int b, int lane, int n_lanes) {
+    const uint32_t nan16 = F16 ? 0x7e00u : 0x7fc0u;
+    uint32_t *o = reinterpret_cast<uint32_t *>(p.out + (size_t)b * p.q_len * p.n_q_heads * kHeadDim);
+    const int words = p.q_len * p.n_q_heads * (kHeadDim / 2);
+    for (int x = lane; x < words; x += n_lanes) o[x] = nan16 | (nan16 << 16);
+}
 
 }  // namespace da

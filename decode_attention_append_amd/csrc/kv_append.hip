@@ -36,4 +36,18 @@ hipError_t launch_kv_append(const AppendParams &p, int threads_total, hipStream_
     return hipGetLastError();
 }
 
+// Zero fill of a small int32 array (the arrival counters of the one-launch
+// step).  A kernel rather than a memset so that the call can be captured into
+// a HIP graph.
+__global__ __launch_bounds__(256) void fill_zero_kernel(int32_t *x, int n) {
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t < n) x[t] = 0;
+}
+
+hipError_t launch_fill_zero(int32_t *x, int n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((n + 255) / 256), dim3(256), 0, s, x, n);
+    return hipGetLastError();
+}
+
 }  // namespace da

@@ -73,6 +73,24 @@ constexpr int kMinChunk = 64;
 // kernel streams at over 60%.
 constexpr int kMfmaRows = 8;
 
+// Most chunk-rows (chunks x query rows) one (sequence, KV head) may have for
+// the one-launch step to merge them inside the attention launch: one wave
+// merges them on the MFMA kernel (eight chunk loads in flight), a whole
+// workgroup on the vector-ALU kernel (32 in flight).  Beyond that the separate
+// combine launch, with a workgroup per row, finishes sooner.
+constexpr int kFusedMergeRowsWave = 64;
+constexpr int kFusedMergeRowsBlock = 512;
+
+// Chunks per sequence (balanced mode) when the one-launch step merges in the
+// launch: every chunk counts its arrival on one atomic per (sequence, KV
+// head), and those serialise; measured on a batch-1, 16-head, 4k-context MHA
+// step, 16 chunks of 256 keys beat 64 chunks of 64 keys by a fifth.
+constexpr int kOneLaunchSeqChunks = 16;
+
+// The vector-ALU kernel carries the one-launch step's append and merge up to 8
+// rows; beyond (only when it is forced) da_decode_step makes three launches.
+bool one_launch_capable(int variant, int rows) { return variant == DA_VARIANT_MFMA || rows <= 8; }
+
 void plan_of(const da_problem *p, da_plan *pl) {
     const int rows = (p->n_q_heads / p->n_kv_heads) * p->q_len;
     const int variant = p->variant ? p->variant - 1 : (rows >= kMfmaRows ? DA_VARIANT_MFMA : DA_VARIANT_VALU);
@@ -100,9 +118,30 @@ void plan_of(const da_problem *p, da_plan *pl) {
         const int64_t b = (int64_t)units * ((p->max_seq + max_chunk - 1) / max_chunk);
         pl->items = (int32_t)(a > b ? a : b);
     }
+    // the one-launch step merges inside the attention launch when the last chunk
+    // of a (sequence, KV head) can merge its rows quickly: at most
+    // kFusedMergeRows chunk-rows per (sequence, KV head), bounded over all
+    // seq_pos values.  There a balanced sequence gets at most
+    // kOneLaunchSeqChunks chunks, or ceil(max_seq / max_chunk) if more.
+    int64_t nb_max = pl->n_chunks;
+    if (pl->balanced) {
+        const int64_t need = (p->max_seq + pl->chunk_tokens - 1) / pl->chunk_tokens;
+        const int64_t bound = need > kOneLaunchSeqChunks ? need : kOneLaunchSeqChunks;
+        if (bound < nb_max) nb_max = bound;
+    }
+    pl->fused_combine = one_launch_capable(variant, rows) &&
+                        nb_max * rows <= (variant == DA_VARIANT_MFMA ? kFusedMergeRowsWave : kFusedMergeRowsBlock);
     const int32_t bh = units;
     pl->workspace_bytes = align256(ws_acc_floats(bh, pl->n_chunks, rows) * sizeof(float)) +
-                          ws_ml_floats(bh, pl->n_chunks, rows) * sizeof(float);
+                          align256(ws_ml_floats(bh, pl->n_chunks, rows) * sizeof(float)) +
+                          (size_t)bh * sizeof(int32_t);
+}
+
+// Arrival counters of the one-launch step: int32 [B * Hkv] after the partials.
+int32_t *counters_of(const da_problem *p, const da_plan &pl, void *workspace) {
+    const int32_t bh = p->batch * p->n_kv_heads;
+    return (int32_t *)((uint8_t *)workspace + align256(ws_acc_floats(bh, pl.n_chunks, pl.rows) * sizeof(float)) +
+                       align256(ws_ml_floats(bh, pl.n_chunks, pl.rows) * sizeof(float)));
 }
 
 AttnParams attn_params(const da_problem *p, const da_plan &pl, const void *q, const void *k_cache,
@@ -129,6 +168,11 @@ AttnParams attn_params(const da_problem *p, const da_plan &pl, const void *q, co
     a.max_chunk = pl.chunk_tokens;
     const double scale = p->scale > 0.f ? (double)p->scale : 1.0 / sqrt((double)p->head_dim);
     a.scale_log2 = (float)(scale * 1.4426950408889634);  // log2(e)
+    a.seq_chunk_cap = 0;
+    a.k_cache_w = a.v_cache_w = nullptr;
+    a.k_new = a.v_new = nullptr;
+    a.counters = nullptr;
+    a.out = nullptr;
     return a;
 }
 
@@ -207,6 +251,71 @@ da_status da_gqa_decode_attn_combine(const da_problem *p, const void *workspace,
     (void)hipGetLastError();
     return launch_attn_combine(a, p->dtype == DA_FP16, out, (hipStream_t)stream) == hipSuccess ? DA_OK
                                                                                                  : DA_ERR_HIP;
+}
+
+da_status da_workspace_init(const da_problem *p, void *workspace, size_t workspace_bytes, void *stream) {
+    const da_status st = check_problem(p);
+    if (st != DA_OK) return st;
+    if (!workspace || !aligned16(workspace)) return DA_ERR_INVALID_ARG;
+    da_plan pl;
+    plan_of(p, &pl);
+    if (workspace_bytes < pl.workspace_bytes) return DA_ERR_WORKSPACE;
+    (void)hipGetLastError();
+    return launch_fill_zero(counters_of(p, pl, workspace), p->batch * p->n_kv_heads, (hipStream_t)stream) ==
+                   hipSuccess
+               ? DA_OK
+               : DA_ERR_HIP;
+}
+
+da_status da_decode_step(const da_problem *p, const void *q, void *k_cache, void *v_cache, const void *k_new,
+                         const void *v_new, const int32_t *seq_pos, void *workspace, size_t workspace_bytes,
+                         void *out, void *stream) {
+    const da_status st = check_problem(p);
+    if (st != DA_OK) return st;
+    if (!q || !k_cache || !v_cache || !k_new || !v_new || !seq_pos || !workspace || !out)
+        return DA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new) ||
+        !aligned16(workspace) || !aligned16(out) || ((uintptr_t)seq_pos & 3u))
+        return DA_ERR_INVALID_ARG;
+    da_plan pl;
+    plan_of(p, &pl);
+    if (workspace_bytes < pl.workspace_bytes) return DA_ERR_WORKSPACE;
+    const bool fp16 = p->dtype == DA_FP16;
+    hipStream_t s = (hipStream_t)stream;
+    AttnParams a = attn_params(p, pl, q, k_cache, v_cache, seq_pos, workspace);
+    if (!one_launch_capable(pl.variant, pl.rows)) {  // append, attention, combine
+        AppendParams ap;
+        ap.k_cache = (uint8_t *)k_cache;
+        ap.v_cache = (uint8_t *)v_cache;
+        ap.k_new = (const uint8_t *)k_new;
+        ap.v_new = (const uint8_t *)v_new;
+        ap.seq_pos = seq_pos;
+        ap.batch = p->batch;
+        ap.q_len = p->q_len;
+        ap.n_kv_heads = p->n_kv_heads;
+        ap.max_seq = p->max_seq;
+        (void)hipGetLastError();
+        hipError_t e = launch_kv_append(ap, p->batch * p->q_len * p->n_kv_heads * 16, s);
+        if (e == hipSuccess) e = launch_attn_valu(a, pl.items, fp16, s);
+        if (e == hipSuccess) e = launch_attn_combine(a, fp16, out, s);
+        return e == hipSuccess ? DA_OK : DA_ERR_HIP;
+    }
+    a.k_cache_w = (uint8_t *)k_cache;
+    a.v_cache_w = (uint8_t *)v_cache;
+    a.k_new = (const uint8_t *)k_new;
+    a.v_new = (const uint8_t *)v_new;
+    int items = pl.items;
+    if (pl.fused_combine) {
+        a.seq_chunk_cap = pl.balanced ? kOneLaunchSeqChunks : 0;
+        a.counters = counters_of(p, pl, workspace);
+        a.out = (uint16_t *)out;
+        items += p->batch;  // the items past the chunks flag contract-breaking sequences
+    }
+    (void)hipGetLastError();
+    hipError_t e = pl.variant == DA_VARIANT_MFMA ? launch_attn_mfma(a, items, fp16, s)
+                                                 : launch_attn_valu(a, items, fp16, s);
+    if (e == hipSuccess && !pl.fused_combine) e = launch_attn_combine(a, fp16, out, s);
+    return e == hipSuccess ? DA_OK : DA_ERR_HIP;
 }
 
 da_status da_chunk_layout(const da_problem *p, const int32_t *seq_pos_host, int32_t *n_chunks,

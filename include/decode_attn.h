@@ -110,7 +110,9 @@ typedef struct {
     int32_t balanced;        /* 1: balanced chunks, 0: fixed chunks              */
     int32_t target_items;    /* balanced: chunks aimed at                        */
     int32_t items;           /* chunks launched for (an upper bound; extras exit) */
-    size_t workspace_bytes;  /* bytes of fp32 partials the attention needs       */
+    int32_t fused_combine;   /* da_decode_step merges inside its attention launch */
+    size_t workspace_bytes;  /* bytes of fp32 partials (and the arrival counters
+                                of da_decode_step) the attention needs           */
 } da_plan;
 
 enum { DA_VARIANT_VALU = 0, DA_VARIANT_MFMA = 1 };
@@ -159,6 +161,48 @@ da_status da_gqa_decode_attn(const da_problem *p, const void *q, const void *k_c
 da_status da_gqa_decode_attn_combine(const da_problem *p, const void *workspace,
                                      size_t workspace_bytes, const int32_t *seq_pos, void *out,
                                      void *stream);
+
+/*
+ * Prepares a workspace for da_decode_step: zeroes its arrival counters (one
+ * int32 per sequence and KV head, after the partials), on `stream`, with a
+ * kernel (no memset).  Call once after allocating the workspace, before its
+ * first da_decode_step; every da_decode_step leaves the counters at zero again.
+ * The three separate entry points neither need nor touch them.
+ */
+da_status da_workspace_init(const da_problem *p, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The whole decode step in one launch where it pays: KV append + attention +
+ * combine with the results of da_kv_append, da_gqa_decode_attn and
+ * da_gqa_decode_attn_combine called in that order (the same three steps of the
+ * "Qwen MoE BringUp" page, Per-Layer IR Patterns, 2. Self-Attention, run as
+ * the 3-phase decode of "Architecture Diagram - Qwen3-30B-A3B (Extern
+ * Dispatch, 75 tok/s)"; the same page's update "11.6ms / 86 tok/s decode on
+ * RX 7900 XTX", Key findings, measures per-dispatch overhead as over a quarter
+ * of decode time and names fewer dispatches the main remaining opportunity).
+ *
+ *  - Append: the chunk holding a sequence's new positions reads those rows
+ *    from k_new / v_new instead of the cache and stores them into the cache
+ *    (a bit copy, same bytes as da_kv_append).  No chunk reads them from the
+ *    cache, so there is no ordering hazard inside the launch.
+ *  - Combine: with plan.fused_combine, every chunk counts its arrival on its
+ *    (sequence, KV head) counter in the workspace, and the last one to arrive
+ *    merges that head's rows into `out` and resets the counter; balanced
+ *    chunking then gives a sequence at most 16 chunks (unless its length needs
+ *    more chunks of the plan's longest length), so da_chunk_layout describes
+ *    only the separate calls.  Otherwise the separate combine kernel follows on
+ *    the same stream (two launches), and when the vector-ALU kernel is forced
+ *    above 8 rows the step is the three separate launches.
+ *
+ * The workspace must have been prepared by da_workspace_init (once), and no
+ * two calls may use one workspace concurrently (they would race on the
+ * partials and the counters).  Contract-breaking seq_pos values: as for the
+ * separate calls, the sequence's cache is not written and its output rows are
+ * NaN.  k_new / v_new / q / out must not overlap the caches or the workspace.
+ */
+da_status da_decode_step(const da_problem *p, const void *q, void *k_cache, void *v_cache, const void *k_new,
+                         const void *v_new, const int32_t *seq_pos, void *workspace, size_t workspace_bytes,
+                         void *out, void *stream);
 
 /*
  * The chunking da_gqa_decode_attn and the combine will use for these seq_pos

@@ -14,14 +14,19 @@ def odt(dtype) -> int:
     return oracle.FP16 if dtype == torch.float16 else oracle.BF16
 
 
-def run_step(p, inp, stream=None):
-    """One decode step on the GPU.  ``inp`` holds device tensors; the caches are
-    updated in place.  Returns the output tensor (device)."""
-    ws = da.new_workspace(p)
+PATHS = ("separate", "step")  # the three separate calls; the one-launch da_decode_step
+
+
+def run_step(p, inp, stream=None, path="step", ws=None):
+    """One decode step on the GPU through ``path``.  ``inp`` holds device tensors; the
+    caches are updated in place.  Returns the output tensor (device)."""
+    if ws is None:
+        ws = da.new_workspace(p, stream=stream)
     out = torch.empty((p.batch, p.q_len, p.n_q_heads, p.head_dim), dtype=inp["q"].dtype,
                       device=inp["q"].device)
-    da.decode_step(p, inp["q"], inp["k_cache"], inp["v_cache"], inp["k_new"], inp["v_new"],
-                   inp["seq_pos"], ws, out, stream)
+    fn = da.decode_step if path == "step" else da.decode_step_separate
+    fn(p, inp["q"], inp["k_cache"], inp["v_cache"], inp["k_new"], inp["v_new"], inp["seq_pos"], ws, out,
+       stream)
     return out
 
 
@@ -43,32 +48,43 @@ def compare_out(got: torch.Tensor, ref: np.ndarray, what: str = ""):
     return stats
 
 
-def check_layer(p, inp, rows=None, stream=None):
-    """Runs a step; checks the whole cache bit for bit and the output against the oracle.
+def check_layer(p, inp, rows=None, stream=None, paths=PATHS):
+    """Runs a step through each of ``paths`` (each from the same starting caches; the
+    last one updates ``inp`` in place), checks the whole cache bit for bit and the
+    output against the oracle.
 
     rows: None for every output row, else an [n, 3] array of (b, i, hq) to check.
-    Returns output diagnostics.
+    Returns the output diagnostics of each path.
     """
     dt = odt(inp["q"].dtype)
     kc0, vc0 = bits(inp["k_cache"]), bits(inp["v_cache"])
     kn, vn = bits(inp["k_new"]), bits(inp["v_new"])
     sp = inp["seq_pos"].cpu().numpy()
-    out = run_step(p, inp, stream)
-    torch.cuda.synchronize()
     k_ref, v_ref = oracle.kv_append(kc0, vc0, kn, vn, sp)
     del kc0, vc0
-    assert np.array_equal(bits(inp["k_cache"]), k_ref), "k_cache differs from the oracle's append"
-    assert np.array_equal(bits(inp["v_cache"]), v_ref), "v_cache differs from the oracle's append"
     qb = bits(inp["q"])
+    scale = p.scale if p.scale > 0 else None
     if rows is None:
-        ref = oracle.gqa_decode(qb, k_ref, v_ref, sp, dt, scale=p.scale if p.scale > 0 else None)
-        return compare_out(out, ref, "all rows")
-    rows = np.asarray(rows, dtype=np.int32).reshape(-1, 3)
-    ref = oracle.gqa_decode_rows(qb, k_ref, v_ref, sp, rows, dt,
-                                 scale=p.scale if p.scale > 0 else None)
-    o = out.cpu()
-    got = torch.stack([o[b, i, hq] for b, i, hq in rows])
-    return compare_out(got, ref, "sampled rows")
+        ref = oracle.gqa_decode(qb, k_ref, v_ref, sp, dt, scale=scale)
+    else:
+        rows = np.asarray(rows, dtype=np.int32).reshape(-1, 3)
+        ref = oracle.gqa_decode_rows(qb, k_ref, v_ref, sp, rows, dt, scale=scale)
+    stats = {}
+    for n, path in enumerate(paths):
+        last = n == len(paths) - 1
+        run = inp if last else dict(inp, k_cache=inp["k_cache"].clone(), v_cache=inp["v_cache"].clone())
+        out = run_step(p, run, stream, path)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(run["k_cache"]), k_ref), f"{path}: k_cache differs from the oracle's append"
+        assert np.array_equal(bits(run["v_cache"]), v_ref), f"{path}: v_cache differs from the oracle's append"
+        if rows is None:
+            stats[path] = compare_out(out, ref, f"{path}: all rows")
+        else:
+            o = out.cpu()
+            got = torch.stack([o[b, i, hq] for b, i, hq in rows])
+            stats[path] = compare_out(got, ref, f"{path}: sampled rows")
+        del run, out
+    return stats
 
 
 def make_case(B, q_len, Hq, Hkv, S, seq_pos, dtype=torch.bfloat16, seed=0, scale=1.0,

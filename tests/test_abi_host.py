@@ -113,6 +113,41 @@ def test_null_and_misaligned_pointers_rejected_before_launch():
     assert da.lib.da_kv_append(None, good, good, good, good, good, None) == da.DA_ERR_INVALID_ARG
 
 
+def test_decode_step_rejects_before_launch():
+    p = P()
+    buf = (ctypes.c_uint8 * 64)()
+    good = ctypes.addressof(buf) + (-ctypes.addressof(buf)) % 16
+    args = [good] * 6
+    assert da.lib.da_decode_step(ctypes.byref(p), *args, good, 16, good, None) == da.DA_ERR_WORKSPACE
+    assert da.lib.da_decode_step(ctypes.byref(p), *args, good, 1 << 30, good + 4, None) == da.DA_ERR_INVALID_ARG
+    assert da.lib.da_decode_step(ctypes.byref(p), None, *args[1:], good, 1 << 30, good, None) == \
+        da.DA_ERR_INVALID_ARG
+    assert da.lib.da_decode_step(ctypes.byref(P(head_dim=64)), *args, good, 1 << 30, good, None) == \
+        da.DA_ERR_UNSUPPORTED
+    assert da.lib.da_workspace_init(ctypes.byref(p), good, 16, None) == da.DA_ERR_WORKSPACE
+    assert da.lib.da_workspace_init(ctypes.byref(p), None, 1 << 30, None) == da.DA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("shape,fused", [
+    (dict(batch=32, n_q_heads=16, n_kv_heads=8, max_seq=8192), True),    # vector ALU, 2 rows
+    (dict(batch=1, n_q_heads=16, n_kv_heads=16, max_seq=4096, dtype="fp16"), True),  # MHA
+    (dict(batch=1, max_seq=512), True),
+    (dict(batch=4, n_q_heads=64, n_kv_heads=8, max_seq=16384), False),   # MFMA, 8 rows, long
+    (dict(batch=8, q_len=4, n_q_heads=32, n_kv_heads=4, max_seq=8192), False),  # MFMA, 32 rows
+    (dict(batch=1, n_q_heads=64, n_kv_heads=8, max_seq=512), True),      # MFMA, 8 chunks at most
+    (dict(batch=1, n_q_heads=16, n_kv_heads=1, max_seq=65536, variant="valu"), False),
+])
+def test_plan_fused_merge(shape, fused):
+    """The one-launch step merges inside the attention launch only when every
+    (sequence, KV head) has few chunk-rows, whatever the seq_pos values."""
+    pl = da.plan_attention(P(**shape))
+    assert pl["fused_combine"] == fused
+    units = shape["batch"] * shape.get("n_kv_heads", 8)
+    # the counters sit after the partials
+    rows = pl["rows"]
+    assert pl["workspace_bytes"] >= units * pl["n_chunks"] * rows * (128 + 2) * 4 + units * 4
+
+
 def test_status_strings():
     for s in (0, -1, -2, -3, -4):
         assert da.status_str(s) and da.status_str(s) != "unknown status"

@@ -2,7 +2,8 @@
 
 KV caches must match the oracle's append bit for bit over the whole
 allocation; outputs must satisfy |gpu - oracle| <= 1e-2 + 1e-2 |oracle|
-elementwise.
+elementwise.  Unless a test says otherwise, every case runs both through the
+three separate calls and through the one-launch da_decode_step.
 """
 import numpy as np
 import pytest
@@ -113,50 +114,55 @@ def test_chunk_sweep(chunk, q_len, Hq, Hkv):
     gu.check_layer(p, inp)
 
 
+@pytest.mark.parametrize("path", gu.PATHS)
 @pytest.mark.parametrize("q_len,Hq,Hkv", [(1, 16, 8), (1, 64, 8), (4, 32, 4), (1, 16, 16)])
-def test_one_key_returns_value_exactly(q_len, Hq, Hkv):
+def test_one_key_returns_value_exactly(q_len, Hq, Hkv, path):
     """seq_pos 0: query token 0 sees only its own key, so its output is v_new exactly."""
-    _say("one key", q_len, Hq, Hkv)
+    _say("one key", q_len, Hq, Hkv, path)
     inp = gu.make_case(2, q_len, Hq, Hkv, 128, [0, 0], seed=5)
     p = da.problem_for(inp["q"], inp["k_cache"])
-    out = gu.run_step(p, inp)
+    out = gu.run_step(p, inp, path=path)
     G = Hq // Hkv
     expect = inp["v_new"][:, 0].repeat_interleave(G, dim=1)  # [B, Hq, D]
     assert torch.equal(out[:, 0], expect)
 
 
+@pytest.mark.parametrize("path", gu.PATHS)
 @pytest.mark.parametrize("q_len,Hq,Hkv", [(1, 16, 8), (1, 64, 8), (4, 32, 4)])
-def test_constant_values_return_value_exactly(q_len, Hq, Hkv):
+def test_constant_values_return_value_exactly(q_len, Hq, Hkv, path):
     S = 3000
-    _say("constant V", q_len, Hq, Hkv)
+    _say("constant V", q_len, Hq, Hkv, path)
     inp = gu.make_case(2, q_len, Hq, Hkv, S, [S - q_len, 1777], seed=6)
     row = inp["v_cache"][0, 0, 0].clone()
     inp["v_cache"][:] = row
     inp["v_new"][:] = row
     p = da.problem_for(inp["q"], inp["k_cache"])
-    out = gu.run_step(p, inp)
+    out = gu.run_step(p, inp, path=path)
     assert torch.equal(out, row.expand_as(out))
 
 
+@pytest.mark.parametrize("path", gu.PATHS)
 @pytest.mark.parametrize("q_len,Hq,Hkv", [(1, 16, 8), (1, 64, 8), (4, 32, 4), (1, 16, 16)])
-def test_beyond_context_poison(q_len, Hq, Hkv):
-    """Cache slots at or past seq_pos + q_len hold NaN/inf: the output must not change."""
+def test_beyond_context_poison(q_len, Hq, Hkv, path):
+    """Cache slots at or past seq_pos + q_len hold NaN/inf, and so do the slots the
+    step appends to before it writes them: the output must not change."""
     S = 1500
     sp = [700, 1500 - q_len, 63]
-    _say("poison", q_len, Hq, Hkv)
+    _say("poison", q_len, Hq, Hkv, path)
     inp = gu.make_case(3, q_len, Hq, Hkv, S, sp, seed=7)
     clean = {k: v.clone() for k, v in inp.items()}
     p = da.problem_for(inp["q"], inp["k_cache"])
-    out_clean = gu.run_step(p, clean)
+    out_clean = gu.run_step(p, clean, path=path)
     for b, s in enumerate(sp):
-        inp["k_cache"][b, :, s + q_len:] = float("nan")
-        inp["v_cache"][b, :, s + q_len:] = float("inf")
-    out = gu.run_step(p, inp)
+        inp["k_cache"][b, :, s:] = float("nan")
+        inp["v_cache"][b, :, s:] = float("inf")
+    out = gu.run_step(p, inp, path=path)
     assert torch.equal(out, out_clean)
     assert torch.isfinite(out.float()).all()
 
 
-def test_later_draft_token_hidden_from_earlier_rows_valu():
+@pytest.mark.parametrize("path", gu.PATHS)
+def test_later_draft_token_hidden_from_earlier_rows_valu(path):
     """A NaN value row of the second draft token leaves query token 0's rows finite
     (vector-ALU variant: the mask excludes the row exactly)."""
     q_len, Hq, Hkv = 2, 8, 2
@@ -164,7 +170,7 @@ def test_later_draft_token_hidden_from_earlier_rows_valu():
     p = da.problem_for(inp["q"], inp["k_cache"], variant="valu")
     assert da.plan_attention(p)["variant"] == "valu"
     inp["v_new"][0, 1] = float("nan")
-    out = gu.run_step(p, inp)
+    out = gu.run_step(p, inp, path=path)
     assert torch.isfinite(out[:, 0].float()).all()
     assert torch.isnan(out[:, 1].float()).all()
 
@@ -264,3 +270,87 @@ def test_kernel_reads_caller_data():
         ref = gu.oracle.gqa_decode(bits(inp["q"]), bits(inp["k_cache"]), bits(inp["v_cache"]),
                                    inp["seq_pos"].cpu().numpy(), gu.oracle.BF16)
         gu.compare_out(out, ref)
+
+
+# ------------------------------------------------------------------ the one-launch step
+
+@pytest.mark.parametrize("B,q_len,Hq,Hkv,S,sp0,fused", [
+    (3, 1, 16, 8, 3000, [2990, 100, 1500], True),      # vector ALU, merge in the launch
+    (1, 1, 64, 8, 512, [500], True),                   # MFMA, 8 rows, merge in the launch
+    (4, 1, 64, 8, 16384, [15000, 12288, 16380, 13000], False),  # MFMA, separate merge
+    (2, 4, 32, 4, 2100, [2000, 60], False),            # MFMA, 32 rows, separate merge
+    (2, 4, 8, 8, 700, [600, 61], True),                # vector ALU, 4 draft tokens
+])
+def test_decode_loop_reuses_workspace(B, q_len, Hq, Hkv, S, sp0, fused):
+    """Consecutive steps through one workspace (its arrival counters must return to
+    zero after every step), the cache growing by q_len per step and fresh q / new
+    rows each step, checked against the oracle step by step."""
+    p = da.problem(B, q_len, Hq, Hkv, 128, S, "bf16")
+    assert da.plan_attention(p)["fused_combine"] == fused
+    inp = gu.make_case(B, q_len, Hq, Hkv, S, sp0, seed=S + B)
+    ws = da.new_workspace(p)
+    k_ref, v_ref = bits(inp["k_cache"]), bits(inp["v_cache"])
+    sp = np.asarray(sp0, dtype=np.int32)
+    gen = torch.Generator(device="cpu").manual_seed(S)
+    for it in range(4):
+        _say("decode loop", B, q_len, Hq, Hkv, S, "step", it, sp.tolist())
+        if it:
+            for k in ("q", "k_new", "v_new"):
+                inp[k] = torch.randn(inp[k].shape, generator=gen).to(torch.bfloat16).cuda()
+            inp["seq_pos"] = torch.as_tensor(sp).cuda()
+        out = gu.run_step(p, inp, ws=ws)
+        torch.cuda.synchronize()
+        k_ref, v_ref = gu.oracle.kv_append(k_ref, v_ref, bits(inp["k_new"]), bits(inp["v_new"]), sp)
+        assert np.array_equal(bits(inp["k_cache"]), k_ref), f"step {it}: k_cache"
+        assert np.array_equal(bits(inp["v_cache"]), v_ref), f"step {it}: v_cache"
+        ref = gu.oracle.gqa_decode(bits(inp["q"]), k_ref, v_ref, sp, gu.oracle.BF16)
+        gu.compare_out(out, ref, f"step {it}")
+        sp = np.minimum(sp + q_len, S - q_len).astype(np.int32)
+
+
+@pytest.mark.parametrize("path", gu.PATHS)
+@pytest.mark.parametrize("q_len,Hq,Hkv,S", [(1, 16, 8, 1000), (1, 64, 8, 1000), (1, 64, 8, 512),
+                                            (4, 32, 4, 1000)])
+def test_contract_breaking_seq_pos(q_len, Hq, Hkv, S, path):
+    """seq_pos -1 and seq_pos past max_seq - q_len: that sequence's cache is untouched
+    and its output rows are NaN; the other sequences are unaffected (merged in the
+    attention launch or by the separate combine)."""
+    sp = [-1, S // 2, S - q_len + 1, S - q_len]
+    _say("contract", q_len, Hq, Hkv, path, sp)
+    inp = gu.make_case(4, q_len, Hq, Hkv, S, sp, seed=16)
+    kc0, vc0 = bits(inp["k_cache"]), bits(inp["v_cache"])
+    p = da.problem_for(inp["q"], inp["k_cache"])
+    out = gu.run_step(p, inp, path=path)
+    torch.cuda.synchronize()
+    kc, vc = bits(inp["k_cache"]), bits(inp["v_cache"])
+    for b in (0, 2):
+        assert np.array_equal(kc[b], kc0[b]) and np.array_equal(vc[b], vc0[b])
+        assert torch.isnan(out[b].float()).all()
+    good = [1, 3]
+    sub = lambda x: np.ascontiguousarray(x[good])  # noqa: E731
+    spg = np.asarray(sp, dtype=np.int32)[good]
+    k_ref, v_ref = gu.oracle.kv_append(sub(kc0), sub(vc0), sub(bits(inp["k_new"])), sub(bits(inp["v_new"])), spg)
+    assert np.array_equal(kc[good], k_ref) and np.array_equal(vc[good], v_ref)
+    ref = gu.oracle.gqa_decode(sub(bits(inp["q"])), k_ref, v_ref, spg, gu.oracle.BF16)
+    gu.compare_out(out[good], ref)
+
+
+def test_decode_step_errors_launch_nothing():
+    import ctypes
+    inp = gu.make_case(2, 1, 16, 8, 256, [10, 20], seed=17)
+    before_k = inp["k_cache"].clone()
+    p = da.problem_for(inp["q"], inp["k_cache"])
+    ws = da.new_workspace(p)
+    out = torch.zeros_like(inp["q"])
+    ptr = {k: v.data_ptr() for k, v in inp.items()}
+
+    def step(nbytes, out_ptr):
+        return da.lib.da_decode_step(ctypes.byref(p), ptr["q"], ptr["k_cache"], ptr["v_cache"], ptr["k_new"],
+                                     ptr["v_new"], ptr["seq_pos"], ws.data_ptr(), nbytes, out_ptr, None)
+
+    assert step(ws.numel() - 1, out.data_ptr()) == da.DA_ERR_WORKSPACE
+    assert step(ws.numel(), out.data_ptr() + 2) == da.DA_ERR_INVALID_ARG
+    assert step(ws.numel(), None) == da.DA_ERR_INVALID_ARG
+    assert da.lib.da_workspace_init(ctypes.byref(p), ws.data_ptr(), ws.numel() - 1, None) == da.DA_ERR_WORKSPACE
+    torch.cuda.synchronize()
+    assert torch.equal(inp["k_cache"], before_k) and not out.any()
