@@ -37,6 +37,9 @@ def parse():
     ap.add_argument("--chunk", type=int, default=0, help="chunk_tokens override (0 = automatic)")
     ap.add_argument("--path", choices=["step", "separate"], default="step",
                     help="step: one da_decode_step per layer; separate: the three calls per layer")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one whole step (every layer) into a HIP graph and time its replays; the "
+                         "kernel roofline then comes from an eager pass of the same steps afterwards")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle sample")
@@ -140,23 +143,24 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
+    launch_stream = [stream]  # None while a graph is being captured: the binding then uses torch's stream
 
     def step_separate(events=None):
         for l, L in enumerate(layers):
-            da.kv_append(p, L["k_cache"], L["v_cache"], L["k_new"], L["v_new"], L["seq_pos"], stream)
+            da.kv_append(p, L["k_cache"], L["v_cache"], L["k_new"], L["v_new"], L["seq_pos"], launch_stream[0])
             if events is not None:
                 events[l][0].record(stream)
-            da.gqa_decode_attn(p, L["q"], L["k_cache"], L["v_cache"], L["seq_pos"], ws, stream)
+            da.gqa_decode_attn(p, L["q"], L["k_cache"], L["v_cache"], L["seq_pos"], ws, launch_stream[0])
             if events is not None:
                 events[l][1].record(stream)
-            da.gqa_decode_attn_combine(p, ws, L["seq_pos"], outs[l], stream)
+            da.gqa_decode_attn_combine(p, ws, L["seq_pos"], outs[l], launch_stream[0])
 
     def step_fused(events=None):
         for l, L in enumerate(layers):
             if events is not None:
                 events[l][0].record(stream)
             da.decode_step(p, L["q"], L["k_cache"], L["v_cache"], L["k_new"], L["v_new"], L["seq_pos"], ws,
-                           outs[l], stream)
+                           outs[l], launch_stream[0])
             if events is not None:
                 events[l][1].record(stream)
 
@@ -177,19 +181,35 @@ def main():
     marks = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
              for _ in range(args.steps if flush else 1)]
     torch.cuda.synchronize()
-    if flush:
-        for k in range(args.steps):
-            flush_buf.sum(dtype=torch.float32)  # outside the timed span of the step
-            marks[k][0].record(stream)
-            step(ev[k])
-            marks[k][1].record(stream)
+
+    def timed(run):
+        if flush:
+            for k in range(args.steps):
+                flush_buf.sum(dtype=torch.float32)  # outside the timed span of the step
+                marks[k][0].record(stream)
+                run(k)
+                marks[k][1].record(stream)
+        else:
+            marks[0][0].record(stream)
+            for k in range(args.steps):
+                run(k)
+            marks[0][1].record(stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in marks)
+
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        launch_stream[0] = None
+        with torch.cuda.graph(graph):
+            step()
+        launch_stream[0] = stream
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ms_total = timed(lambda k: graph.replay())
+        timed(lambda k: step(ev[k]))  # eager pass for the kernel's own duration
     else:
-        marks[0][0].record(stream)
-        for k in range(args.steps):
-            step(ev[k])
-        marks[0][1].record(stream)
-    torch.cuda.synchronize()
-    ms_total = sum(a.elapsed_time(b) for a, b in marks)
+        ms_total = timed(lambda k: step(ev[k]))
     attn_ms = [e0.elapsed_time(e1) for evk in ev for (e0, e1) in evk]
 
     ms_per_step = ms_total / args.steps
@@ -227,7 +247,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "q_len": w.q_len, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "context": int(seq_pos.max()) + w.q_len,
                    "max_seq": w.max_seq, "layers": w.layers, "chunk_tokens": plan["chunk_tokens"],
-                   "variant": plan["variant"], "path": args.path,
+                   "variant": plan["variant"], "path": args.path, "graph": args.graph,
                    "fused_merge": bool(plan["fused_combine"]) and args.path == "step",
                    "bytes_per_step": step_bytes,
                    "cold_cache_flush": flush},
