@@ -59,6 +59,12 @@ class Oracle:
         lib.oracle_gqa_decode.restype = ctypes.c_int
         lib.oracle_gqa_decode_rows.argtypes = [i32] * 7 + [f64] + [p] * 4 + [i32] + [p] * 4
         lib.oracle_gqa_decode_rows.restype = ctypes.c_int
+        lib.oracle_encode_bf16.argtypes = [f64]
+        lib.oracle_encode_bf16.restype = ctypes.c_uint16
+        lib.oracle_encode_fp16.argtypes = [f64]
+        lib.oracle_encode_fp16.restype = ctypes.c_uint16
+        lib.oracle_rope_rows.argtypes = [i32, i32, i32, p, p, p, p]
+        lib.oracle_rope_rows.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
@@ -71,6 +77,44 @@ class Oracle:
         bits = _u16(bits)
         flat = bits.ravel()
         return np.array([f(int(x)) for x in flat], dtype=np.float64).reshape(bits.shape)
+
+    def encode(self, values, dtype: int) -> np.ndarray:
+        """float64 -> 16-bit patterns (round to nearest even), element by element in C."""
+        f = self.lib.oracle_encode_fp16 if dtype == FP16 else self.lib.oracle_encode_bf16
+        v = np.asarray(values, dtype=np.float64)
+        return np.array([f(float(x)) for x in v.ravel()], dtype=np.uint16).reshape(v.shape)
+
+    def rope_rows(self, rows, positions, freqs, dtype: int) -> np.ndarray:
+        """Rotary embedding of ``rows`` [..., D] (16-bit patterns) at ``positions`` (one per
+        row, shape rows.shape[:-1]) with the D/2 float32 ``freqs``; returns new patterns."""
+        x = _u16(rows)
+        D = x.shape[-1]
+        pos = _i32(positions).reshape(-1)
+        if pos.size * D != x.size:
+            raise ValueError("one position per row")
+        f = np.ascontiguousarray(np.asarray(freqs, dtype=np.float32))
+        if f.shape != (D // 2,):
+            raise ValueError("freqs must hold D/2 values")
+        out = np.empty_like(x)
+        if self.lib.oracle_rope_rows(dtype, pos.size, D, _ptr(pos), _ptr(f), _ptr(x), _ptr(out)) != 0:
+            raise ValueError("bad row length")
+        return out
+
+    def rope_q(self, q, seq_pos, freqs, dtype: int) -> np.ndarray:
+        """q [B, q_len, Hq, D] rotated at position seq_pos[b] + i (new patterns)."""
+        q = _u16(q)
+        B, q_len, Hq, _ = q.shape
+        pos = _i32(seq_pos)[:, None, None] + np.arange(q_len, dtype=np.int32)[None, :, None]
+        return self.rope_rows(q, np.broadcast_to(pos, (B, q_len, Hq)), freqs, dtype)
+
+    def kv_append_rope(self, k_cache, v_cache, k_new, v_new, seq_pos, freqs, dtype: int):
+        """The append with the new K rows rotated at their positions seq_pos[b] + i first
+        (V rows unchanged); returns (k_cache', v_cache')."""
+        kn = _u16(k_new)
+        B, q_len, Hkv, _ = kn.shape
+        pos = _i32(seq_pos)[:, None, None] + np.arange(q_len, dtype=np.int32)[None, :, None]
+        k_rot = self.rope_rows(kn, np.broadcast_to(pos, (B, q_len, Hkv)), freqs, dtype)
+        return self.kv_append(k_cache, v_cache, k_rot, v_new, seq_pos)
 
     def kv_append(self, k_cache, v_cache, k_new, v_new, seq_pos):
         """Returns (k_cache', v_cache') as new uint16 arrays; the inputs are not modified.
@@ -161,3 +205,19 @@ def gqa_decode(*args, **kw):
 
 def gqa_decode_rows(*args, **kw):
     return default().gqa_decode_rows(*args, **kw)
+
+
+def encode(values, dtype):
+    return default().encode(values, dtype)
+
+
+def rope_rows(*args, **kw):
+    return default().rope_rows(*args, **kw)
+
+
+def rope_q(*args, **kw):
+    return default().rope_q(*args, **kw)
+
+
+def kv_append_rope(*args, **kw):
+    return default().kv_append_rope(*args, **kw)

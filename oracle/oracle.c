@@ -259,3 +259,86 @@ int oracle_gqa_decode_rows(int32_t dtype, int32_t B, int32_t q_len, int32_t Hq, 
                    row_b[n], row_i[n], row_hq[n], out_rows + (size_t)n * D, NULL);
     return 0;
 }
+
+/* ---- element encoding (round to nearest, ties to even), from the formats ---
+ * A 16-bit format with `ebits` exponent bits (bias 2^(ebits-1) - 1) and
+ * `mbits` fraction bits.  The value is rounded once, directly from double.
+ * NaN becomes the quiet NaN with only the top fraction bit set; magnitudes
+ * that round past the largest finite value become infinity.
+ */
+static uint16_t encode16(double x, int ebits, int mbits)
+{
+    const int bias = (1 << (ebits - 1)) - 1;
+    const int emax_field = (1 << ebits) - 1;            /* all-ones exponent field */
+    const uint16_t sign = signbit(x) ? (uint16_t)0x8000 : 0;
+    const double ax = fabs(x);
+    if (isnan(x))
+        return (uint16_t)((emax_field << mbits) | (1 << (mbits - 1)));
+    if (isinf(x))
+        return (uint16_t)(sign | (emax_field << mbits));
+    if (ax == 0.0)
+        return sign;
+    int e2;
+    frexp(ax, &e2);                 /* ax = f * 2^e2, f in [0.5, 1) */
+    int e = e2 - 1;                 /* ax in [2^e, 2^(e+1)) */
+    const int emin = 1 - bias;      /* exponent of the smallest normal */
+    if (e < emin)
+        e = emin;                   /* subnormals share the smallest normal's quantum */
+    const double quantum = ldexp(1.0, e - mbits);
+    double n = nearbyint(ax / quantum);                 /* exact scaling, then RNE */
+    if (n >= ldexp(1.0, mbits + 1)) {                   /* rounded up into the next binade */
+        n /= 2.0;
+        e += 1;
+    }
+    if (n < ldexp(1.0, mbits))                          /* subnormal (only when e == emin) */
+        return (uint16_t)(sign | (uint16_t)n);
+    const int field = e + bias;
+    if (field >= emax_field)
+        return (uint16_t)(sign | (emax_field << mbits));
+    return (uint16_t)(sign | (field << mbits) | ((uint16_t)n - (1 << mbits)));
+}
+
+uint16_t oracle_encode_bf16(double x) { return encode16(x, 8, 7); }
+uint16_t oracle_encode_fp16(double x) { return encode16(x, 5, 10); }
+
+static uint16_t encode(int dtype, double x)
+{
+    return dtype == ORACLE_FP16 ? oracle_encode_fp16(x) : oracle_encode_bf16(x);
+}
+
+/* ---- rotary position embedding of rows ------------------------------------
+ * "Qwen MoE BringUp", Per-Layer IR Patterns, 2. Self-Attention, "Rotary
+ * Position Embeddings (RoPE)": a row at absolute position `pos` is rotated by
+ * angles a_j = pos * freqs[j] (j < D/2), the product formed in single precision
+ * as the page does (position cast to f32, then a f32 MatMul with the f32
+ * frequency table); the table is doubled so dims j and j + D/2 share a_j; and
+ *     out = x * cos(a) + rotate_half(x) * sin(a),  rotate_half(x) = [-x2, x1]
+ * where x1, x2 are the two halves.  Per pair:
+ *     out[j]       = x[j] cos a_j - x[j+D/2] sin a_j
+ *     out[j+D/2]   = x[j+D/2] cos a_j + x[j] sin a_j.
+ * cos, sin and the rotation are evaluated in double here and the result is
+ * rounded once to the row's 16-bit format.
+ *
+ * rows: n rows of D 16-bit elements; pos: n positions; freqs: D/2 floats.
+ */
+int oracle_rope_rows(int32_t dtype, int32_t n, int32_t D, const int32_t *pos, const float *freqs,
+                     const uint16_t *in, uint16_t *out)
+{
+    if (D <= 0 || D % 2)
+        return -1;
+    const int32_t half = D / 2;
+#pragma omp parallel for schedule(static)
+    for (int32_t r = 0; r < n; ++r) {
+        const uint16_t *x = in + (size_t)r * D;
+        uint16_t *y = out + (size_t)r * D;
+        for (int32_t j = 0; j < half; ++j) {
+            /* the exact product of two floats fits a double; one rounding to float */
+            const float a = (float)((double)(float)pos[r] * (double)freqs[j]);
+            const double c = cos((double)a), s = sin((double)a);
+            const double x1 = decode(dtype, x[j]), x2 = decode(dtype, x[j + half]);
+            y[j] = encode(dtype, x1 * c - x2 * s);
+            y[j + half] = encode(dtype, x2 * c + x1 * s);
+        }
+    }
+    return 0;
+}

@@ -278,4 +278,154 @@ def pin_rows_api_matches_full(orc):
         assert np.array_equal(got[n], out[b, i, hq])
 
 
+# ---------------------------------------------------------------- encoding
+
+def _all_patterns():
+    return np.arange(65536, dtype=np.uint32).astype(np.uint16)
+
+
+def pin_encode_round_trip_all_patterns(orc):
+    """Every finite pattern decodes and re-encodes to itself; NaNs stay NaN."""
+    for dtype in (BF16, FP16):
+        pats = _all_patterns()
+        vals = orc.decode(pats, dtype)
+        back = orc.encode(vals, dtype)
+        nan = np.isnan(vals)
+        assert np.array_equal(back[~nan], pats[~nan])
+        assert np.isnan(orc.decode(back[nan], dtype)).all()
+
+
+def _spread(rng, n):
+    """Doubles over the whole 16-bit ranges: subnormals, normals, near overflow, both signs."""
+    mag = np.exp2(rng.uniform(-30, 18, n)) * rng.uniform(1, 2, n)
+    return np.where(rng.random(n) < 0.5, -mag, mag)
+
+
+def pin_encode_fp16_matches_numpy(orc):
+    """numpy's float64 -> float16 conversion rounds to nearest even in one step."""
+    rng = np.random.default_rng(3)
+    x = _spread(rng, 20000)
+    with np.errstate(over="ignore"):  # magnitudes past 65504 round to infinity on both sides
+        ref = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(orc.encode(x, FP16), ref)
+
+
+def pin_encode_bf16_matches_torch_on_floats(orc):
+    """For values exactly representable in float32, torch's float32 -> bfloat16 rounding
+    (nearest even) is the one rounding step."""
+    rng = np.random.default_rng(4)
+    x32 = _spread(rng, 20000).astype(np.float32)
+    x32 = x32[np.abs(x32) < 3.0e38]
+    ref = torch.from_numpy(x32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(orc.encode(x32.astype(np.float64), BF16), ref)
+
+
+def pin_encode_bf16_direct_rounding(orc):
+    """Cases the bfloat16 definition fixes, including two a float32 detour would get wrong
+    (a tie broken by bits beyond float32)."""
+    cases = [
+        (1.0 + 2.0 ** -8, 0x3F80),                 # tie between 1 and 1+2^-7: even
+        (1.0 + 2.0 ** -8 + 2.0 ** -40, 0x3F81),    # just above the tie: up
+        (1.0 + 3 * 2.0 ** -8, 0x3F82),             # tie between 0x3F81 and 0x3F82: even
+        (1.0 + 3 * 2.0 ** -8 - 2.0 ** -45, 0x3F81),
+        (-2.0, 0xC000),
+        ((2.0 - 2.0 ** -7) * 2.0 ** 127, 0x7F7F),  # largest finite
+        ((2.0 - 2.0 ** -8) * 2.0 ** 127, 0x7F80),  # ties up to infinity
+        (2.0 ** -133, 0x0001),                     # smallest subnormal
+        (2.0 ** -134, 0x0000),                     # half of it: tie to even zero
+        (1.5 * 2.0 ** -134, 0x0001),
+    ]
+    for x, want in cases:
+        assert int(orc.encode([x], BF16)[0]) == want, (x, hex(want))
+
+
+# ---------------------------------------------------------------- rotary embedding
+
+def qwen_freqs(D, theta=1.0e6):
+    """Inverse frequencies theta^(-2j/D), j < D/2, as a float32 table (an input)."""
+    return (theta ** (-np.arange(0, D, 2, dtype=np.float64) / D)).astype(np.float32)
+
+
+def _complex_rotation(x, positions, freqs):
+    """Reference: dims j and j + D/2 as the real and imaginary parts of z_j, multiplied
+    by exp(i a_j) with a_j the float32 product of position and frequency."""
+    half = x.shape[-1] // 2
+    a = (np.float32(1) * positions.astype(np.float32)[:, None] * freqs[None, :]).astype(np.float64)
+    z = (x[:, :half] + 1j * x[:, half:]) * np.exp(1j * a)
+    return np.concatenate([z.real, z.imag], axis=1)
+
+
+def _ulp(ref, mbits, emin):
+    e = np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** emin)))
+    return np.exp2(e - mbits)
+
+
+def pin_rope_position_zero_is_identity(orc):
+    for dtype in (BF16, FP16):
+        q, _, _, kn, _, _ = rand_case(2, 3, 4, 2, 128, 8, [0, 0], dtype, seed=21)
+        x = bits(q).reshape(-1, 128)
+        out = orc.rope_rows(x, np.zeros(x.shape[0], np.int32), qwen_freqs(128), dtype)
+        assert np.array_equal(out, x)
+
+
+def pin_rope_is_complex_rotation(orc):
+    """Against complex multiplication in numpy: correctly rounded to the 16-bit format
+    (bit-identical to numpy's rounding for fp16; within half an ulp for bf16)."""
+    rng = np.random.default_rng(22)
+    for dtype, freqs in ((FP16, qwen_freqs(128)), (BF16, qwen_freqs(128, 1.0e4))):
+        q, _, _, _, _, _ = rand_case(1, 1, 64, 1, 128, 1, [0], dtype, seed=23)
+        x = bits(q).reshape(-1, 128)
+        pos = rng.integers(0, 1 << 20, x.shape[0]).astype(np.int32)
+        pos[:4] = [1, 2, 4095, 16383]
+        got = orc.rope_rows(x, pos, freqs, dtype)
+        ref = _complex_rotation(orc.decode(x, dtype), pos, freqs)
+        if dtype == FP16:
+            assert np.array_equal(got, ref.astype(np.float16).view(np.uint16))
+        else:
+            err = np.abs(orc.decode(got, BF16) - ref)
+            assert (err <= 0.5 * _ulp(ref, 7, -126) * (1 + 1e-9)).all()
+
+
+def pin_rope_relative_position(orc):
+    """With power-of-two frequencies every angle is exact, and the score between a query at
+    position m and a key at position n depends only on m - n."""
+    D = 128
+    freqs = np.exp2(-np.arange(D // 2, dtype=np.float64) / 4.0).astype(np.float32)
+    freqs = np.exp2(np.floor(np.log2(freqs))).astype(np.float32)
+    q, _, _, kn, _, _ = rand_case(1, 1, 8, 8, D, 1, [0], BF16, seed=24)
+    qx, kx = bits(q).reshape(-1, D), bits(kn).reshape(-1, D)
+    for m, n in ((7, 3), (100, 36), (1000, 1)):
+        a = orc.decode(orc.rope_rows(qx, np.full(8, m, np.int32), freqs, BF16), BF16)
+        b = orc.decode(orc.rope_rows(kx, np.full(8, n, np.int32), freqs, BF16), BF16)
+        c = orc.decode(orc.rope_rows(qx, np.full(8, m - n, np.int32), freqs, BF16), BF16)
+        k0 = orc.decode(kx, BF16)
+        lhs, rhs = (a * b).sum(1), (c * k0).sum(1)
+        assert np.abs(lhs - rhs).max() < 0.25, (m, n, np.abs(lhs - rhs).max())
+
+
+def pin_rope_append_and_query_positions(orc):
+    """The rotated append writes k_new[b, i] rotated at seq_pos[b] + i (V unchanged), and
+    the rotated query row (b, i) uses the same position; checked row by row against the
+    complex rotation."""
+    freqs = qwen_freqs(128)
+    q, kc, vc, kn, vn, sp = rand_case(2, 3, 4, 2, 128, 40, [5, 30], FP16, seed=25)
+    k2, v2 = orc.kv_append_rope(bits(kc), bits(vc), bits(kn), bits(vn), sp, freqs, FP16)
+    k_plain, v_plain = orc.kv_append(bits(kc), bits(vc), bits(kn), bits(vn), sp)
+    assert np.array_equal(v2, v_plain)
+    qr = orc.rope_q(bits(q), sp, freqs, FP16)
+    for b in range(2):
+        for i in range(3):
+            pos = np.array([sp[b] + i] * 2, np.int32)
+            want_k = _complex_rotation(orc.decode(bits(kn)[b, i], FP16), pos, freqs)
+            assert np.array_equal(k2[b, :, sp[b] + i], want_k.astype(np.float16).view(np.uint16))
+            pos_q = np.array([sp[b] + i] * 4, np.int32)
+            want_q = _complex_rotation(orc.decode(bits(q)[b, i], FP16), pos_q, freqs)
+            assert np.array_equal(qr[b, i], want_q.astype(np.float16).view(np.uint16))
+    untouched = np.ones(k2.shape[2], bool)
+    for b in range(2):
+        untouched[:] = True
+        untouched[sp[b]:sp[b] + 3] = False
+        assert np.array_equal(k2[b][:, untouched], k_plain[b][:, untouched])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

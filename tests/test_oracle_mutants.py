@@ -38,6 +38,18 @@ MUTANTS = [
      "ldexp(1.0 + frac / 512.0, expo - 15)"),
     ("query token position ignored", "seq_pos[b] + i, seq_pos[b] + q_len, scale",
      "seq_pos[b], seq_pos[b] + q_len, scale"),
+    ("rope rotation sign", "y[j] = encode(dtype, x1 * c - x2 * s);",
+     "y[j] = encode(dtype, x1 * c + x2 * s);"),
+    ("rope pairs adjacent dims", "x2 = decode(dtype, x[j + half]);", "x2 = decode(dtype, x[j ^ 1]);"),
+    ("rope angle in double precision",
+     "const float a = (float)((double)(float)pos[r] * (double)freqs[j]);",
+     "const double a = (double)pos[r] * (double)freqs[j];"),
+    ("rope position off by one", "(double)(float)pos[r] * (double)freqs[j]",
+     "(double)(float)(pos[r] + 1) * (double)freqs[j]"),
+    ("encode truncates", "double n = nearbyint(ax / quantum);", "double n = floor(ax / quantum);"),
+    ("encode ties away from zero", "double n = nearbyint(ax / quantum);", "double n = round(ax / quantum);"),
+    ("encode subnormal quantum", "e = emin;                   /* subnormals",
+     "e = emin - 1;               /* subnormals"),
 ]
 
 
