@@ -37,6 +37,9 @@ def parse():
     ap.add_argument("--chunk", type=int, default=0, help="chunk_tokens override (0 = automatic)")
     ap.add_argument("--path", choices=["step", "separate"], default="step",
                     help="step: one da_decode_step per layer; separate: the three calls per layer")
+    ap.add_argument("--rope", type=float, default=0.0, metavar="THETA",
+                    help="fuse the rotary embedding with this base (e.g. 1e6): the append rotates new K "
+                         "rows and the attention rotates q")
     ap.add_argument("--graph", action="store_true",
                     help="capture one whole step (every layer) into a HIP graph and time its replays; the "
                          "kernel roofline then comes from an eager pass of the same steps afterwards")
@@ -83,17 +86,23 @@ def counters_for(kernel_tag, workload):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, layers_host_fn, n_layers, budget_s):
-    """The oracle (append + attention, fp64, OpenMP) on whole layers of the workload until
-    about budget_s of CPU time is spent; returns the record for the JSON line."""
+def cpu_baseline(w, layers_host_fn, n_layers, budget_s, freqs=None):
+    """The oracle (append + attention, fp64, OpenMP; with the rotary embedding when a
+    table is given) on whole layers of the workload until about budget_s of CPU time is
+    spent; returns the record for the JSON line."""
     import numpy as np
     import oracle
+    dt = oracle.FP16 if w.dtype == "fp16" else oracle.BF16
     done_bytes, spent, n = 0, 0.0, 0
     for layer in range(n_layers):
         q, kc, vc, kn, vn, sp = layers_host_fn(layer)
         t = time.perf_counter()
-        k2, v2 = oracle.kv_append(kc, vc, kn, vn, sp)
-        oracle.gqa_decode(q, k2, v2, sp, oracle.FP16 if w.dtype == "fp16" else oracle.BF16)
+        if freqs is None:
+            k2, v2 = oracle.kv_append(kc, vc, kn, vn, sp)
+        else:
+            k2, v2 = oracle.kv_append_rope(kc, vc, kn, vn, sp, freqs, dt)
+            q = oracle.rope_q(q, sp, freqs, dt)
+        oracle.gqa_decode(q, k2, v2, sp, dt)
         spent += time.perf_counter() - t
         done_bytes += algorithmic_bytes(w, sp)[1]
         n += 1
@@ -118,7 +127,7 @@ def main():
     import torch
 
     import decode_attention_append_amd as da
-    from decode_attention_append_amd.workloads import BENCH_WORKLOAD, WORKLOADS, make_layer
+    from decode_attention_append_amd.workloads import BENCH_WORKLOAD, WORKLOADS, make_layer, rope_freqs
 
     w = WORKLOADS[args.workload or BENCH_WORKLOAD]
     dev = torch.device("cuda:0")
@@ -135,8 +144,9 @@ def main():
 
     layers = [make_layer(w, l, dev) for l in range(w.layers)]
     seq_pos = layers[0]["seq_pos"].cpu().numpy()
+    freqs = rope_freqs(w.head_dim, args.rope, dev) if args.rope > 0 else None
     p = da.problem(w.batch, w.q_len, w.n_q_heads, w.n_kv_heads, w.head_dim, w.max_seq, w.dtype,
-                   chunk_tokens=args.chunk)
+                   chunk_tokens=args.chunk, rope_freqs=freqs)
     plan = da.plan_attention(p)
     ws = da.new_workspace(p)
     outs = [torch.empty_like(L["q"]) for L in layers]
@@ -226,6 +236,8 @@ def main():
     if args.path == "step":
         attn_bytes += 2 * w.batch * w.q_len * w.n_kv_heads * w.head_dim * 2 + q_bytes
         kernel_tag += "_step" if plan["fused_combine"] else "_step+attn_combine"
+    if args.rope > 0:
+        kernel_tag = kernel_tag.replace("attn_split_" + plan["variant"], "attn_split_" + plan["variant"] + "_rope")
     attn_gbs = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
     traffic = counters_for(kernel_tag, w.name) if "+" not in kernel_tag else None
 
@@ -248,6 +260,7 @@ def main():
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "context": int(seq_pos.max()) + w.q_len,
                    "max_seq": w.max_seq, "layers": w.layers, "chunk_tokens": plan["chunk_tokens"],
                    "variant": plan["variant"], "path": args.path, "graph": args.graph,
+                   "rope_theta": args.rope if args.rope > 0 else None,
                    "fused_merge": bool(plan["fused_combine"]) and args.path == "step",
                    "bytes_per_step": step_bytes,
                    "cold_cache_flush": flush},
@@ -268,7 +281,8 @@ def main():
                 return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
             return (u16(L["q"]), u16(L["k_cache"]), u16(L["v_cache"]), u16(L["k_new"]),
                     u16(L["v_new"]), L["seq_pos"].cpu().numpy())
-        rec["cpu_baseline"] = cpu_baseline(w, host_layer_fn, w.layers, args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline(w, host_layer_fn, w.layers, args.cpu_seconds,
+                                           None if freqs is None else freqs.cpu().numpy())
 
     print(json.dumps(rec), flush=True)
 

@@ -51,6 +51,7 @@ class Problem(ctypes.Structure):
         ("chunk_tokens", ctypes.c_int32),
         ("variant", ctypes.c_int32),
         ("work_items", ctypes.c_int32),
+        ("rope_freqs", ctypes.c_void_p),
     ]
 
     def __repr__(self):
@@ -130,23 +131,30 @@ def status_str(status: int) -> str:
 
 
 def problem(batch, q_len, n_q_heads, n_kv_heads, head_dim, max_seq, dtype, scale=0.0,
-            chunk_tokens=0, variant=None, work_items=0) -> Problem:
-    """variant: None (automatic), "valu" or "mfma"; chunk_tokens 0 = balanced chunks."""
+            chunk_tokens=0, variant=None, work_items=0, rope_freqs=None) -> Problem:
+    """variant: None (automatic), "valu" or "mfma"; chunk_tokens 0 = balanced chunks.
+    rope_freqs: None, or a float32 GPU tensor of head_dim/2 rotary frequencies (the
+    problem keeps a reference to it)."""
     if isinstance(dtype, torch.dtype):
         dtype = _DTYPE_CODE[dtype]
     elif isinstance(dtype, str):
         dtype = {"bf16": DA_BF16, "fp16": DA_FP16}[dtype]
     v = 0 if variant is None else {"valu": 1, "mfma": 2}[variant]
-    return Problem(batch, q_len, n_q_heads, n_kv_heads, head_dim, max_seq, dtype, float(scale),
-                   chunk_tokens, v, work_items)
+    rp = None
+    if rope_freqs is not None:
+        rp = _dev(rope_freqs, "rope_freqs", (head_dim // 2,), torch.float32)
+    pr = Problem(batch, q_len, n_q_heads, n_kv_heads, head_dim, max_seq, dtype, float(scale),
+                 chunk_tokens, v, work_items, rp)
+    pr._rope_ref = rope_freqs  # keeps the table alive as long as the problem
+    return pr
 
 
 def problem_for(q: torch.Tensor, k_cache: torch.Tensor, scale=0.0, chunk_tokens=0,
-                variant=None, work_items=0) -> Problem:
+                variant=None, work_items=0, rope_freqs=None) -> Problem:
     """The problem described by q [B, q_len, Hq, D] and a cache [B, Hkv, S, D]."""
     B, q_len, Hq, D = q.shape
     _, Hkv, S, _ = k_cache.shape
-    return problem(B, q_len, Hq, Hkv, D, S, q.dtype, scale, chunk_tokens, variant, work_items)
+    return problem(B, q_len, Hq, Hkv, D, S, q.dtype, scale, chunk_tokens, variant, work_items, rope_freqs)
 
 
 def plan_attention(p: Problem) -> dict:

@@ -93,9 +93,12 @@ struct RowSource {
     uint8_t *kw, *vw;            // writable cache of (b, h) at the chunk start
     size_t stride;
     int new_first;
+    int t0;             // absolute position of local key 0
+    const float *rope;  // rotary table: new K rows are rotated at t0 + key first
     bool store;
 };
 
+template <bool F16>
 __device__ __forceinline__ void load_rows(Tile &t, const uint8_t *kb, const uint8_t *vb, int tb, int last,
                                           int l16, int q, const RowSource &rs) {
 #pragma unroll
@@ -105,6 +108,10 @@ __device__ __forceinline__ void load_rows(Tile &t, const uint8_t *kb, const uint
                                                 : kb + (size_t)key * kRowBytes + 16 * q;
 #pragma unroll
         for (int s = 0; s < 4; ++s) t.k[kblk][s] = ld16(kr + 64 * s);
+        if (rs.rope && key >= rs.new_first) {
+            rope8<F16>(t.k[kblk][0], t.k[kblk][2], rs.t0 + key, rs.rope, 8 * q);
+            rope8<F16>(t.k[kblk][1], t.k[kblk][3], rs.t0 + key, rs.rope, 32 + 8 * q);
+        }
         if (rs.store && key >= rs.new_first && tb + 16 * kblk + l16 <= last) {
 #pragma unroll
             for (int s = 0; s < 4; ++s)
@@ -163,6 +170,12 @@ void attn_split_mfma_kernel(AttnParams p) {
                 p.q + (((size_t)b * p.q_len + i) * p.n_q_heads + (size_t)h * p.group + g) * kRowBytes + 16 * q;
 #pragma unroll
             for (int s = 0; s < 4; ++s) qop[rb][s] = ld16(qp + 64 * s);
+            if (p.rope_freqs) {
+                // rotary embedding at seq_pos + i: this lane holds dims 8q + 32s .. +7,
+                // so pieces s and s + 2 are the two halves of the same pairs
+                rope8<F16>(qop[rb][0], qop[rb][2], sp + i, p.rope_freqs, 8 * q);
+                rope8<F16>(qop[rb][1], qop[rb][3], sp + i, p.rope_freqs, 32 + 8 * q);
+            }
             vis[rb] = min(sp + i + 1 - t0, n_tok);
         } else {
 #pragma unroll
@@ -253,6 +266,8 @@ void attn_split_mfma_kernel(AttnParams p) {
     // that hold new rows or run past the chunk take the per-row path.
     RowSource rs;
     rs.new_first = p.k_new ? sp - t0 : n_tok;
+    rs.t0 = t0;
+    rs.rope = p.k_new ? p.rope_freqs : nullptr;
     rs.store = p.k_new != nullptr && rg == 0;
     rs.stride = (size_t)p.n_kv_heads * kRowBytes;
     if (p.k_new) {
@@ -281,7 +296,7 @@ void attn_split_mfma_kernel(AttnParams p) {
     }
     for (int i = nt; i < n_all; ++i) {
         Tile tt_;
-        load_rows(tt_, kb, vb, i * 32, last, l16, q, rs);
+        load_rows<F16>(tt_, kb, vb, i * 32, last, l16, q, rs);
         compute(tt_, i);
     }
 

@@ -72,14 +72,18 @@ __device__ void merge_rows_block(const AttnParams &p, float *red, int bh, int b,
     }
 }
 
-// The one-launch step's append and merge are compiled for up to 8 rows; the
-// 16-row kernel (only used when the vector-ALU kernel is forced) has no
-// registers to spare for them, and the launcher runs that step as three launches.
+// The one-launch step's append and merge, and the rotary embedding of q, are
+// compiled for up to 8 rows; the 16-row kernel (only used when the vector-ALU
+// kernel is forced) has no registers to spare for them: the launcher runs that
+// step as three launches and refuses it a rotary table.
 constexpr int kValuOneLaunchRows = 8;
 
-template <bool F16, int RP>
+// ROPE: the problem has a rotary table (a separate instantiation, so that the
+// rotation's registers never weigh on the kernel without one).
+template <bool F16, int RP, bool ROPE>
 __global__ __launch_bounds__(256) void attn_split_valu_kernel(AttnParams p) {
     constexpr bool kOneLaunch = RP <= kValuOneLaunchRows;
+    static_assert(!ROPE || kOneLaunch, "the rotary embedding is compiled up to 8 rows");
     extern __shared__ float lds[];  // scores [chunk][RP], later the wave sums [4][RP][128]
     __shared__ float row_m[RP], row_l[RP];
 
@@ -126,60 +130,86 @@ __global__ __launch_bounds__(256) void attn_split_valu_kernel(AttnParams p) {
             vis[r] = 0;
         }
     }
+    if (ROPE) {  // rotary embedding of the query rows at seq_pos + i
+#pragma unroll
+        for (int r = 0; r < RP; ++r) {
+            u32x4_t v = {qr[r][0], qr[r][1], qr[r][2], qr[r][3]};
+            rope_row16<F16>(v, cq, sp + r / p.group, p.rope_freqs, r < p.rows);
+            qr[r][0] = v[0];
+            qr[r][1] = v[1];
+            qr[r][2] = v[2];
+            qr[r][3] = v[3];
+        }
+    }
 
     const size_t head_off = ((size_t)bh * p.max_seq + t0) * kRowBytes + cq * 16;
     const uint8_t *kb = p.k_cache + head_off;
     const uint8_t *vb = p.v_cache + head_off;
     const int last = n_tok - 1;  // loads past the context re-read the last row (masked)
 
-    // Slab loads: four 128-bit loads per lane cover 16 keys (1 KiB each).  Full
-    // slabs use one base address and immediate offsets; the last, partial slab
-    // re-reads row `last` for keys past the chunk (those are masked).
-    // In the one-launch step, local keys from `new_first` on are this step's new
-    // rows: they are read from k_new / v_new and stored into the cache here
-    // (no other chunk touches them).
-    const int n_full = n_tok >> 4;
+    // Slab loads: four 128-bit loads per lane cover 16 keys (1 KiB each).
+    //  - Fast slabs (full, and below this step's new rows) use one base address
+    //    and immediate offsets; a wave streams them through two register buffers
+    //    used in turn, with no copy between iterations, so it waits only for the
+    //    older slab.
+    //  - The rest, at most the chunk's last couple of slabs, go row by row: keys
+    //    past the chunk re-read row `last` (masked later), and in the one-launch
+    //    step the new rows (local keys from new_first on) are read from k_new /
+    //    v_new, rotated in the K pass when there is a rotary table, and stored
+    //    into the cache (no other chunk touches them).
     const bool fused_append = kOneLaunch && p.k_new != nullptr;
     const int new_first = fused_append ? sp - t0 : n_tok;
+    const int n_fast = min(n_tok >> 4, max(new_first, 0) >> 4);
     const size_t new_stride = (size_t)p.n_kv_heads * kRowBytes;
     const size_t new_off = ((size_t)b * p.q_len * p.n_kv_heads + h) * kRowBytes + cq * 16;
-    auto load_slab = [&](u32x4_t (&buf)[4], const uint8_t *base, const uint8_t *nbase, uint8_t *wbase, int s_) {
-        if (s_ < n_full && (s_ + 1) * 16 <= new_first) {
-            const uint8_t *r0 = base + (size_t)(s_ * 16 + gq) * kRowBytes;
+    auto load_fast = [&](u32x4_t (&buf)[4], const uint8_t *base, int s_) {
+        const uint8_t *r0 = base + (size_t)(s_ * 16 + gq) * kRowBytes;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) buf[u] = ld16(r0 + u * 4 * kRowBytes);
-        } else {
+        for (int u = 0; u < 4; ++u) buf[u] = ld16(r0 + u * 4 * kRowBytes);
+    };
+    auto load_rows = [&](u32x4_t (&buf)[4], const uint8_t *base, const uint8_t *nbase, uint8_t *wbase, bool rot,
+                         int s_) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int t = min(s_ * 16 + u * 4 + gq, last);
+            buf[u] = ld16(t >= new_first ? nbase + (size_t)(t - new_first) * new_stride : base + (size_t)t * kRowBytes);
+        }
+        if (ROPE && rot) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int t = min(s_ * 16 + u * 4 + gq, last);
-                buf[u] = ld16(t >= new_first ? nbase + (size_t)(t - new_first) * new_stride
-                                             : base + (size_t)t * kRowBytes);
+                rope_row16<F16>(buf[u], cq, t0 + t, p.rope_freqs, t >= new_first);
             }
-            if (fused_append) {
+        }
+        if (fused_append) {
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int t = s_ * 16 + u * 4 + gq;
-                    if (t >= new_first && t <= last)
-                        *reinterpret_cast<u32x4_t *>(wbase + (size_t)t * kRowBytes) = buf[u];
-                }
+            for (int u = 0; u < 4; ++u) {
+                const int t = s_ * 16 + u * 4 + gq;
+                if (t >= new_first && t <= last) *reinterpret_cast<u32x4_t *>(wbase + (size_t)t * kRowBytes) = buf[u];
             }
         }
     };
-    // This wave's slabs are wave, wave + 4, ...: two buffers used in turn, no copy
-    // between iterations, so a wave waits only for the older slab.
-    const int ns = wave < n_slab ? (n_slab - 1 - wave) / 4 + 1 : 0;
-    auto two_buffer_pass = [&](const uint8_t *base, const uint8_t *nbase, uint8_t *wbase, auto &&body) {
-        if (ns == 0) return;
-        u32x4_t b0[4], b1[4];
-        load_slab(b0, base, nbase, wbase, wave);
-        int i = 0;
-        for (; i + 2 <= ns; i += 2) {
-            load_slab(b1, base, nbase, wbase, wave + (i + 1) * 4);
-            body(b0, wave + i * 4);
-            load_slab(b0, base, nbase, wbase, wave + min(i + 2, ns - 1) * 4);
-            body(b1, wave + (i + 1) * 4);
+    // This wave's slabs are wave, wave + 4, ...
+    const int nf = wave < n_fast ? (n_fast - 1 - wave) / 4 + 1 : 0;
+    const int first_slow = n_fast + (((wave - n_fast) % 4) + 4) % 4;
+    auto pass = [&](const uint8_t *base, const uint8_t *nbase, uint8_t *wbase, bool rot, auto &&body) {
+        if (nf > 0) {
+            u32x4_t b0[4], b1[4];
+            load_fast(b0, base, wave);
+            int i = 0;
+            for (; i + 2 <= nf; i += 2) {
+                load_fast(b1, base, wave + (i + 1) * 4);
+                body(b0, wave + i * 4);
+                load_fast(b0, base, wave + min(i + 2, nf - 1) * 4);
+                body(b1, wave + (i + 1) * 4);
+            }
+            if (i < nf) body(b0, wave + i * 4);
         }
-        if (i < ns) body(b0, wave + i * 4);
+        for (int s_ = first_slow; s_ < n_slab; s_ += 4) {
+            u32x4_t b0[4];
+            load_rows(b0, base, nbase, wbase, rot, s_);
+            body(b0, s_);
+        }
     };
 
     // ---- pass 1: scores of the chunk into LDS ----------------------------------
@@ -187,7 +217,7 @@ __global__ __launch_bounds__(256) void attn_split_valu_kernel(AttnParams p) {
     const uint8_t *vnb = fused_append ? p.v_new + new_off : nullptr;
     uint8_t *kwb = fused_append ? p.k_cache_w + head_off : nullptr;
     uint8_t *vwb = fused_append ? p.v_cache_w + head_off : nullptr;
-    two_buffer_pass(kb, knb, kwb, [&](u32x4_t (&cur)[4], int s_) {
+    pass(kb, knb, kwb, fused_append, [&](u32x4_t (&cur)[4], int s_) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int tl = s_ * 16 + u * 4 + gq;
@@ -236,7 +266,7 @@ __global__ __launch_bounds__(256) void attn_split_valu_kernel(AttnParams p) {
 #pragma unroll
         for (int d = 0; d < 8; ++d) acc[r][d] = 0.f;
     const int first_draft = sp - t0;  // local keys above this may be hidden from some rows
-    two_buffer_pass(vb, vnb, vwb, [&](u32x4_t (&cur)[4], int s_) {
+    pass(vb, vnb, vwb, false, [&](u32x4_t (&cur)[4], int s_) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int tl = s_ * 16 + u * 4 + gq;
@@ -314,10 +344,17 @@ __global__ __launch_bounds__(256) void attn_split_valu_kernel(AttnParams p) {
 
 template <bool F16, int RP>
 static hipError_t launch_rp(const AttnParams &p, int grid, hipStream_t s) {
+    if constexpr (RP <= kValuOneLaunchRows) {
+        if (p.rope_freqs) {
+            const size_t lds = (size_t)RP * (p.max_chunk > 520 ? p.max_chunk : 520) * sizeof(float);
+            hipLaunchKernelGGL((attn_split_valu_kernel<F16, RP, true>), dim3(grid), dim3(256), lds, s, p);
+            return hipGetLastError();
+        }
+    }
     // scores of the longest chunk; at least the wave sums [4][RP][128] and the
     // fused merge's 4 * 128 + 8 floats
     const size_t lds_bytes = (size_t)RP * (p.max_chunk > 520 ? p.max_chunk : 520) * sizeof(float);
-    hipLaunchKernelGGL((attn_split_valu_kernel<F16, RP>), dim3(grid), dim3(256), lds_bytes, s, p);
+    hipLaunchKernelGGL((attn_split_valu_kernel<F16, RP, false>), dim3(grid), dim3(256), lds_bytes, s, p);
     return hipGetLastError();
 }
 

@@ -24,6 +24,7 @@ struct AppendParams {
     const uint8_t *k_new;
     const uint8_t *v_new;
     const int32_t *seq_pos;
+    const float *rope_freqs;   // D/2 rotary frequencies, or null: k_new is copied as is
     int32_t batch, q_len, n_kv_heads, max_seq;
 };
 
@@ -43,6 +44,8 @@ struct AttnParams {
     int32_t min_chunk;     // balanced: smallest chunk (multiple of 32)
     int32_t max_chunk;     // largest chunk the kernel accepts (multiple of 32)
     float scale_log2;      // softmax scale * log2(e): scores are kept in log2 units
+    const float *rope_freqs;  // D/2 rotary frequencies, or null: q (and fused-appended
+                              //   k_new rows) are used as given
     int32_t seq_chunk_cap; // balanced: at most this many chunks per sequence unless its
                            //   length needs more of max_chunk keys (0: no cap)
 
@@ -140,7 +143,7 @@ inline size_t ws_ml_floats(int32_t bh, int32_t n_chunks, int32_t rows) {
 
 // ---- host-side launch entry points (one per translation unit) ---------------
 
-hipError_t launch_kv_append(const AppendParams &p, int threads_total, hipStream_t s);
+hipError_t launch_kv_append(const AppendParams &p, int threads_total, bool fp16, hipStream_t s);
 hipError_t launch_fill_zero(int32_t *x, int n, hipStream_t s);
 hipError_t launch_attn_valu(const AttnParams &p, int items, bool fp16, hipStream_t s);
 hipError_t launch_attn_mfma(const AttnParams &p, int items, bool fp16, hipStream_t s);
@@ -205,6 +208,62 @@ __device__ __forceinline__ float round_trip16(float x) {
         return (float)(_Float16)x;
     else
         return __uint_as_float((uint32_t)round16<false>(x) << 16);
+}
+
+// ---- rotary embedding ("Qwen MoE BringUp", Per-Layer IR Patterns, RoPE) -----
+// A row at position pos rotates each pair (x at dim j, y at dim j + D/2) by the
+// angle a_j = pos * freqs[j], formed as a float32 product like the page's f32
+// MatMul:  x' = x cos a - y sin a,  y' = y cos a + x sin a, in fp32 with one
+// rounding back to 16 bits.  The angle is reduced in double precision to a
+// fraction of a turn, a / 2pi - rint(a / 2pi) (exact to about 1e-10 turns for
+// the largest positions), and the hardware sine and cosine take that fraction
+// (v_sin_f32 / v_cos_f32 work in turns).
+__device__ __forceinline__ void rope_pair(float &x, float &y, int pos, float freq) {
+    const float a = __fmul_rn((float)pos, freq);
+    const double turns = (double)a * 0.15915494309189533577;  // 1 / (2 pi)
+    const float fr = (float)(turns - rint(turns));
+    const float sn = __builtin_amdgcn_sinf(fr);
+    const float cs = __builtin_amdgcn_cosf(fr);
+    const float nx = fmaf(x, cs, -(y * sn));
+    const float ny = fmaf(y, cs, x * sn);
+    x = nx;
+    y = ny;
+}
+
+// Rotates eight pairs held as 16-bit elements: `lo` holds dims j0 .. j0+7, `hi`
+// dims j0+64 .. j0+71 (head_dim 128).
+template <bool F16>
+__device__ __forceinline__ void rope8(u32x4_t &lo, u32x4_t &hi, int pos, const float *freqs, int j0) {
+    const f32x4_t f0 = *reinterpret_cast<const f32x4_t *>(freqs + j0);
+    const f32x4_t f1 = *reinterpret_cast<const f32x4_t *>(freqs + j0 + 4);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        float x0, x1, y0, y1;
+        unpack2<F16>(lo[w], x0, x1);
+        unpack2<F16>(hi[w], y0, y1);
+        const float fa = w < 2 ? f0[2 * w] : f1[2 * w - 4];
+        const float fb = w < 2 ? f0[2 * w + 1] : f1[2 * w - 3];
+        rope_pair(x0, y0, pos, fa);
+        rope_pair(x1, y1, pos, fb);
+        lo[w] = (uint32_t)round16<F16>(x0) | ((uint32_t)round16<F16>(x1) << 16);
+        hi[w] = (uint32_t)round16<F16>(y0) | ((uint32_t)round16<F16>(y1) << 16);
+    }
+}
+
+// The same when sixteen lanes hold one row, 16 bytes (dims 8c .. 8c+7) each:
+// lane c pairs with lane c ^ 8 of its group.  Every lane of the wave must call
+// it (it shuffles); `apply` says whether this lane's piece is rotated.
+template <bool F16>
+__device__ __forceinline__ void rope_row16(u32x4_t &piece, int c, int pos, const float *freqs, bool apply) {
+    u32x4_t other;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) other[w] = (uint32_t)__shfl_xor((int)piece[w], 8);
+    if (!apply) return;
+    if (c < 8) {
+        rope8<F16>(piece, other, pos, freqs, 8 * c);
+    } else {
+        rope8<F16>(other, piece, pos, freqs, 8 * (c - 8));
+    }
 }
 
 // Sum over the 16 lanes of a DPP row (each lane gets the total).

@@ -5,34 +5,44 @@
 //
 // One lane moves 16 bytes of K and 16 bytes of V: sixteen lanes cover one
 // 128-dim row, a wave covers four rows with fully coalesced 128-bit loads and
-// stores.  A pure bit copy: no arithmetic touches the data.
+// stores.  Without a rotary table it is a pure bit copy: no arithmetic touches
+// the data.  With one, each K row is rotated at its position seq_pos + i first
+// (the RoPE block of the same page; lanes c and c ^ 8 of a row hold the two
+// halves of each rotated pair and swap them with one shuffle).
 #include "da_internal.h"
 
 namespace da {
 
+template <bool F16>
 __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p, int threads_total) {
     const int t = blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= threads_total) return;
     const int piece = t & 15;         // 16-byte piece of the 256-byte row
     const int row = t >> 4;           // (b, i, h) in k_new's [B][q_len][Hkv] order
     const int h = row % p.n_kv_heads;
     const int i = (row / p.n_kv_heads) % p.q_len;
-    const int b = row / (p.n_kv_heads * p.q_len);
+    const int b = min(row / (p.n_kv_heads * p.q_len), p.batch - 1);
     const int sp = p.seq_pos[b];
-    if (sp < 0 || sp > p.max_seq - p.q_len) return;  // broken contract: write nothing
-    const size_t src = (size_t)row * kRowBytes + piece * 16;
+    // a sequence that breaks the contract is skipped (both lanes of every pair
+    // belong to the same row, so they agree)
+    const bool ok = t < threads_total && sp >= 0 && sp <= p.max_seq - p.q_len;
+    const size_t src = (size_t)min(row, threads_total / 16 - 1) * kRowBytes + piece * 16;
+    u32x4_t k = ld16(p.k_new + src);
+    if (p.rope_freqs) rope_row16<F16>(k, piece, sp + i, p.rope_freqs, ok);
+    if (!ok) return;
     const size_t dst = (((size_t)b * p.n_kv_heads + h) * p.max_seq + (size_t)(sp + i)) * kRowBytes +
                        piece * 16;
-    const u32x4_t k = ld16(p.k_new + src);
     const u32x4_t v = ld16(p.v_new + src);
     *reinterpret_cast<u32x4_t *>(p.k_cache + dst) = k;
     *reinterpret_cast<u32x4_t *>(p.v_cache + dst) = v;
 }
 
-hipError_t launch_kv_append(const AppendParams &p, int threads_total, hipStream_t s) {
+hipError_t launch_kv_append(const AppendParams &p, int threads_total, bool fp16, hipStream_t s) {
     const int block = 256;
     const int grid = (threads_total + block - 1) / block;
-    hipLaunchKernelGGL(kv_append_kernel, dim3(grid), dim3(block), 0, s, p, threads_total);
+    if (fp16)
+        hipLaunchKernelGGL(kv_append_kernel<true>, dim3(grid), dim3(block), 0, s, p, threads_total);
+    else
+        hipLaunchKernelGGL(kv_append_kernel<false>, dim3(grid), dim3(block), 0, s, p, threads_total);
     return hipGetLastError();
 }
 

@@ -31,12 +31,17 @@ da_status check_problem(const da_problem *p) {
         return DA_ERR_INVALID_ARG;
     if (p->variant < 0 || p->variant > DA_VARIANT_MFMA + 1) return DA_ERR_INVALID_ARG;
     if (p->work_items < 0 || p->work_items > (1 << 20)) return DA_ERR_INVALID_ARG;
+    if (p->rope_freqs && !aligned16(p->rope_freqs)) return DA_ERR_INVALID_ARG;
     if (p->dtype != DA_BF16 && p->dtype != DA_FP16) return DA_ERR_UNSUPPORTED;
     if (p->head_dim != kHeadDim) return DA_ERR_UNSUPPORTED;
     if (p->q_len > kMaxQLen) return DA_ERR_UNSUPPORTED;
     if ((int64_t)(p->n_q_heads / p->n_kv_heads) * p->q_len > kMaxRows) return DA_ERR_UNSUPPORTED;
     if (p->max_seq > kMaxSeq) return DA_ERR_UNSUPPORTED;
     if (p->variant == DA_VARIANT_VALU + 1 && (p->n_q_heads / p->n_kv_heads) * p->q_len > kMaxValuRows)
+        return DA_ERR_UNSUPPORTED;
+    // the vector-ALU kernel rotates q only up to 8 rows (it is chosen automatically
+    // only below 8)
+    if (p->rope_freqs && p->variant == DA_VARIANT_VALU + 1 && (p->n_q_heads / p->n_kv_heads) * p->q_len > 8)
         return DA_ERR_UNSUPPORTED;
     if (p->chunk_tokens != 0 && (p->max_seq + p->chunk_tokens - 1) / p->chunk_tokens > kMaxChunks)
         return DA_ERR_UNSUPPORTED;
@@ -169,6 +174,7 @@ AttnParams attn_params(const da_problem *p, const da_plan &pl, const void *q, co
     const double scale = p->scale > 0.f ? (double)p->scale : 1.0 / sqrt((double)p->head_dim);
     a.scale_log2 = (float)(scale * 1.4426950408889634);  // log2(e)
     a.seq_chunk_cap = 0;
+    a.rope_freqs = p->rope_freqs;
     a.k_cache_w = a.v_cache_w = nullptr;
     a.k_new = a.v_new = nullptr;
     a.counters = nullptr;
@@ -208,13 +214,15 @@ da_status da_kv_append(const da_problem *p, void *k_cache, void *v_cache, const 
     a.k_new = (const uint8_t *)k_new;
     a.v_new = (const uint8_t *)v_new;
     a.seq_pos = seq_pos;
+    a.rope_freqs = p->rope_freqs;
     a.batch = p->batch;
     a.q_len = p->q_len;
     a.n_kv_heads = p->n_kv_heads;
     a.max_seq = p->max_seq;
     const int threads = p->batch * p->q_len * p->n_kv_heads * 16;
     (void)hipGetLastError();  // launch errors below are ours alone
-    return launch_kv_append(a, threads, (hipStream_t)stream) == hipSuccess ? DA_OK : DA_ERR_HIP;
+    return launch_kv_append(a, threads, p->dtype == DA_FP16, (hipStream_t)stream) == hipSuccess ? DA_OK
+                                                                                                  : DA_ERR_HIP;
 }
 
 da_status da_gqa_decode_attn(const da_problem *p, const void *q, const void *k_cache,
@@ -290,12 +298,13 @@ da_status da_decode_step(const da_problem *p, const void *q, void *k_cache, void
         ap.k_new = (const uint8_t *)k_new;
         ap.v_new = (const uint8_t *)v_new;
         ap.seq_pos = seq_pos;
+        ap.rope_freqs = p->rope_freqs;
         ap.batch = p->batch;
         ap.q_len = p->q_len;
         ap.n_kv_heads = p->n_kv_heads;
         ap.max_seq = p->max_seq;
         (void)hipGetLastError();
-        hipError_t e = launch_kv_append(ap, p->batch * p->q_len * p->n_kv_heads * 16, s);
+        hipError_t e = launch_kv_append(ap, p->batch * p->q_len * p->n_kv_heads * 16, fp16, s);
         if (e == hipSuccess) e = launch_attn_valu(a, pl.items, fp16, s);
         if (e == hipSuccess) e = launch_attn_combine(a, fp16, out, s);
         return e == hipSuccess ? DA_OK : DA_ERR_HIP;

@@ -156,3 +156,11 @@ def make_layer(w: Workload, layer: int = 0, device="cpu"):
         kn[nm.to(device)] *= w.heavy_factor
     seq_pos = seq_pos.to(device)
     return {"q": q, "k_cache": kc, "v_cache": vc, "k_new": kn, "v_new": vn, "seq_pos": seq_pos}
+
+
+def rope_freqs(head_dim: int = 128, theta: float = 1.0e6, device="cpu") -> torch.Tensor:
+    """A rotary frequency table, theta^(-2j/head_dim) for j < head_dim/2, as float32: an
+    input of the step like the page's precomputed freqs table (theta 1e6 is Qwen3's
+    rope_theta, 1e4 Qwen1.5's)."""
+    j = torch.arange(0, head_dim, 2, dtype=torch.float64)
+    return (theta ** (-j / head_dim)).to(torch.float32).to(device)

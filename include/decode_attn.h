@@ -87,6 +87,17 @@ typedef struct {
                              takes at most 16 rows per KV head)                   */
     int32_t work_items;   /* balanced chunking: chunks to aim for over the whole
                              launch, 0 = automatic (a tuning override)            */
+    const float *rope_freqs; /* DEVICE pointer to head_dim/2 float32 rotary
+                             frequencies (16-byte aligned), or NULL.  With a table,
+                             the rotary embedding of the "Qwen MoE BringUp" page
+                             (Per-Layer IR Patterns, 2. Self-Attention, "Rotary
+                             Position Embeddings (RoPE)") is fused into the step: a
+                             row at position pos has each pair of dims (j, j + D/2)
+                             rotated by the angle pos * freqs[j], formed as a float32
+                             product; k_new rows are rotated at seq_pos[b] + i as
+                             they are appended, and q rows at seq_pos[b] + i before
+                             the scores (the cache holds rotated keys).  Evaluated
+                             in fp32 and rounded once to the 16-bit type.          */
 } da_problem;
 
 /*

@@ -148,6 +148,17 @@ def test_plan_fused_merge(shape, fused):
     assert pl["workspace_bytes"] >= units * pl["n_chunks"] * rows * (128 + 2) * 4 + units * 4
 
 
+def test_rope_table_must_be_aligned():
+    p = P()
+    p.rope_freqs = 0x1004  # never dereferenced: rejected before any launch
+    assert da.lib.da_plan_attention(ctypes.byref(p), ctypes.byref(da.Plan())) == da.DA_ERR_INVALID_ARG
+    p.rope_freqs = 0x1000
+    assert da.lib.da_plan_attention(ctypes.byref(p), ctypes.byref(da.Plan())) == da.DA_OK
+    p16 = P(n_q_heads=32, n_kv_heads=2, q_len=1, variant="valu")
+    p16.rope_freqs = 0x1000
+    assert da.lib.da_plan_attention(ctypes.byref(p16), ctypes.byref(da.Plan())) == da.DA_ERR_UNSUPPORTED
+
+
 def test_status_strings():
     for s in (0, -1, -2, -3, -4):
         assert da.status_str(s) and da.status_str(s) != "unknown status"
