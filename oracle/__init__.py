@@ -65,6 +65,10 @@ class Oracle:
         lib.oracle_encode_fp16.restype = ctypes.c_uint16
         lib.oracle_rope_rows.argtypes = [i32, i32, i32, p, p, p, p]
         lib.oracle_rope_rows.restype = ctypes.c_int
+        lib.oracle_gather_paged.argtypes = [i32] * 6 + [p] * 3
+        lib.oracle_gather_paged.restype = ctypes.c_int
+        lib.oracle_kv_append_paged.argtypes = [i32] * 7 + [p] * 6
+        lib.oracle_kv_append_paged.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
@@ -115,6 +119,31 @@ class Oracle:
         pos = _i32(seq_pos)[:, None, None] + np.arange(q_len, dtype=np.int32)[None, :, None]
         k_rot = self.rope_rows(kn, np.broadcast_to(pos, (B, q_len, Hkv)), freqs, dtype)
         return self.kv_append(k_cache, v_cache, k_rot, v_new, seq_pos)
+
+    def gather_paged(self, pool, block_table):
+        """Page pool [n_pages, Hkv, page_size, D] + block table [B, pages_per_seq] -> the
+        sequences' contiguous caches [B, Hkv, pages_per_seq * page_size, D]."""
+        pool = _u16(pool)
+        n_pages, Hkv, page_size, D = pool.shape
+        bt = _i32(block_table)
+        B, pps = bt.shape
+        out = np.empty((B, Hkv, pps * page_size, D), dtype=np.uint16)
+        if self.lib.oracle_gather_paged(B, Hkv, D, page_size, pps, n_pages, _ptr(bt), _ptr(pool), _ptr(out)):
+            raise ValueError("block table entry outside the pool")
+        return out
+
+    def kv_append_paged(self, k_pool, v_pool, k_new, v_new, seq_pos, block_table):
+        """The append into page pools; returns (k_pool', v_pool') as new arrays."""
+        kp, vp = _u16(k_pool).copy(), _u16(v_pool).copy()
+        n_pages, Hkv, page_size, D = kp.shape
+        kn, vn = _u16(k_new), _u16(v_new)
+        B, q_len = kn.shape[:2]
+        bt = _i32(block_table)
+        sp = _i32(seq_pos)
+        if self.lib.oracle_kv_append_paged(B, q_len, Hkv, D, page_size, bt.shape[1], n_pages, _ptr(bt), _ptr(sp),
+                                           _ptr(kn), _ptr(vn), _ptr(kp), _ptr(vp)):
+            raise ValueError("block table entry outside the pool, or seq_pos outside the pages")
+        return kp, vp
 
     def kv_append(self, k_cache, v_cache, k_new, v_new, seq_pos):
         """Returns (k_cache', v_cache') as new uint16 arrays; the inputs are not modified.
@@ -221,3 +250,11 @@ def rope_q(*args, **kw):
 
 def kv_append_rope(*args, **kw):
     return default().kv_append_rope(*args, **kw)
+
+
+def gather_paged(*args, **kw):
+    return default().gather_paged(*args, **kw)
+
+
+def kv_append_paged(*args, **kw):
+    return default().kv_append_paged(*args, **kw)

@@ -342,3 +342,65 @@ int oracle_rope_rows(int32_t dtype, int32_t n, int32_t D, const int32_t *pos, co
     }
     return 0;
 }
+
+/* ---- paged KV cache ----------------------------------------------------------
+ * "Architecture Diagram - Qwen3-30B-A3B (Extern Dispatch, 75 tok/s)", Paged
+ * Attention: the KV write goes to a page pool laid out [pages][KV heads][16
+ * tokens per page][head dim].  A per-sequence block table (int32
+ * [B][pages_per_seq]) names the pool page that holds logical page i of
+ * sequence b, i.e. tokens 16 i .. 16 i + 15.  The sequence's cache is the
+ * concatenation of its pages in block-table order; nothing else changes.
+ *
+ * gather: pool -> contiguous [B][Hkv][pages_per_seq * page_size][D].
+ * append: writes new[b][i][h][:] into the pool slot of token seq_pos[b] + i.
+ * Both return -1 (and write nothing) for a block-table entry outside the pool
+ * or a position outside the sequence's pages.
+ */
+static int check_pages(int32_t B, int32_t pages_per_seq, int32_t n_pages, const int32_t *block_table)
+{
+    for (int64_t k = 0; k < (int64_t)B * pages_per_seq; ++k)
+        if (block_table[k] < 0 || block_table[k] >= n_pages)
+            return -1;
+    return 0;
+}
+
+int oracle_gather_paged(int32_t B, int32_t Hkv, int32_t D, int32_t page_size, int32_t pages_per_seq,
+                        int32_t n_pages, const int32_t *block_table, const uint16_t *pool, uint16_t *out)
+{
+    if (check_pages(B, pages_per_seq, n_pages, block_table))
+        return -1;
+    const int64_t S = (int64_t)pages_per_seq * page_size;
+    for (int32_t b = 0; b < B; ++b)
+        for (int32_t h = 0; h < Hkv; ++h)
+            for (int64_t t = 0; t < S; ++t) {
+                const int32_t page = block_table[(int64_t)b * pages_per_seq + t / page_size];
+                const uint16_t *src = pool + (((int64_t)page * Hkv + h) * page_size + t % page_size) * D;
+                uint16_t *dst = out + (((int64_t)b * Hkv + h) * S + t) * D;
+                memcpy(dst, src, (size_t)D * sizeof(uint16_t));
+            }
+    return 0;
+}
+
+int oracle_kv_append_paged(int32_t B, int32_t q_len, int32_t Hkv, int32_t D, int32_t page_size,
+                           int32_t pages_per_seq, int32_t n_pages, const int32_t *block_table,
+                           const int32_t *seq_pos, const uint16_t *k_new, const uint16_t *v_new,
+                           uint16_t *k_pool, uint16_t *v_pool)
+{
+    if (check_pages(B, pages_per_seq, n_pages, block_table))
+        return -1;
+    const int64_t S = (int64_t)pages_per_seq * page_size;
+    for (int32_t b = 0; b < B; ++b)
+        if (seq_pos[b] < 0 || seq_pos[b] + q_len > S)
+            return -1;
+    for (int32_t b = 0; b < B; ++b)
+        for (int32_t i = 0; i < q_len; ++i)
+            for (int32_t h = 0; h < Hkv; ++h) {
+                const int64_t t = (int64_t)seq_pos[b] + i;
+                const int32_t page = block_table[(int64_t)b * pages_per_seq + t / page_size];
+                const size_t row = (((size_t)b * q_len + i) * Hkv + h) * D;
+                const size_t dst = (((size_t)page * Hkv + h) * page_size + (size_t)(t % page_size)) * D;
+                memcpy(k_pool + dst, k_new + row, (size_t)D * sizeof(uint16_t));
+                memcpy(v_pool + dst, v_new + row, (size_t)D * sizeof(uint16_t));
+            }
+    return 0;
+}

@@ -428,4 +428,66 @@ def pin_rope_append_and_query_positions(orc):
         assert np.array_equal(k2[b][:, untouched], k_plain[b][:, untouched])
 
 
+# ---------------------------------------------------------------- paged KV cache
+
+def pin_paged_pool_layout(orc):
+    """Hand-worked positions of the page pool layout (tests/golden/paged_pool_layout.json)."""
+    g = _golden("paged_pool_layout.json")
+    shape = tuple(g["pool_shape"])
+    pool = np.arange(np.prod(shape), dtype=np.uint16).reshape(shape)  # every element distinct
+    out = orc.gather_paged(pool, np.array(g["block_table"], np.int32))
+    for c in g["cases"]:
+        assert out[c["b"], c["h"], c["t"], c["d"]] == pool[tuple(c["pool"])], c
+
+
+def _paged_case(rng, B, Hkv, D, pps, n_pages):
+    pool_k = rng.integers(0, 1 << 16, (n_pages, Hkv, 16, D), dtype=np.uint32).astype(np.uint16) & 0xBFFF
+    pool_v = rng.integers(0, 1 << 16, (n_pages, Hkv, 16, D), dtype=np.uint32).astype(np.uint16) & 0xBFFF
+    bt = rng.permutation(n_pages)[:B * pps].reshape(B, pps).astype(np.int32)
+    return pool_k, pool_v, bt
+
+
+def pin_paged_append_commutes_with_contiguous(orc):
+    """Appending into the pool and then gathering equals gathering and then the (pinned)
+    contiguous append; no other pool byte changes."""
+    rng = np.random.default_rng(41)
+    B, Hkv, D, pps, n_pages, q_len = 3, 2, 8, 4, 16, 3
+    pk, pv, bt = _paged_case(rng, B, Hkv, D, pps, n_pages)
+    kn = rng.integers(0, 1 << 16, (B, q_len, Hkv, D), dtype=np.uint32).astype(np.uint16)
+    vn = rng.integers(0, 1 << 16, (B, q_len, Hkv, D), dtype=np.uint32).astype(np.uint16)
+    sp = np.array([0, 14, 61], np.int32)  # one crossing a page boundary, one at the end
+    pk2, pv2 = orc.kv_append_paged(pk, pv, kn, vn, sp, bt)
+    kc, vc = orc.kv_append(orc.gather_paged(pk, bt), orc.gather_paged(pv, bt), kn, vn, sp)
+    assert np.array_equal(orc.gather_paged(pk2, bt), kc)
+    assert np.array_equal(orc.gather_paged(pv2, bt), vc)
+    changed = np.argwhere((pk2 != pk).any(axis=(1, 3)))
+    for page, h, tok in [(int(a), int(b_), int(c)) for a, b_, c in np.argwhere((pk2 != pk).any(axis=3))]:
+        assert any(bt[b, (sp[b] + i) // 16] == page and (sp[b] + i) % 16 == tok
+                   for b in range(B) for i in range(q_len)), (page, h, tok)
+    assert len(changed) >= 1
+
+
+def pin_paged_page_relabelling(orc):
+    """Renumbering the pool's pages (and the block table with them) changes nothing."""
+    rng = np.random.default_rng(42)
+    pk, _, bt = _paged_case(rng, 2, 2, 8, 3, 10)
+    perm = rng.permutation(10)
+    pk_relabelled = np.empty_like(pk)
+    pk_relabelled[perm] = pk  # page p moves to slot perm[p]
+    assert np.array_equal(orc.gather_paged(pk_relabelled, perm[bt].astype(np.int32)), orc.gather_paged(pk, bt))
+
+
+def pin_paged_rejects_bad_pages(orc):
+    rng = np.random.default_rng(43)
+    pk, pv, bt = _paged_case(rng, 2, 2, 8, 2, 6)
+    bad = bt.copy()
+    bad[1, 1] = 6
+    try:
+        orc.gather_paged(pk, bad)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("a block-table entry outside the pool was accepted")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

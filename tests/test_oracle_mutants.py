@@ -48,6 +48,13 @@ MUTANTS = [
      "(double)(float)(pos[r] + 1) * (double)freqs[j]"),
     ("encode truncates", "double n = nearbyint(ax / quantum);", "double n = floor(ax / quantum);"),
     ("encode ties away from zero", "double n = nearbyint(ax / quantum);", "double n = round(ax / quantum);"),
+    ("paged pool token-major inside a page",
+     "const uint16_t *src = pool + (((int64_t)page * Hkv + h) * page_size + t % page_size) * D;",
+     "const uint16_t *src = pool + (((int64_t)page * page_size + t % page_size) * Hkv + h) * D;"),
+    ("paged block table row stride", "const int32_t page = block_table[(int64_t)b * pages_per_seq + t / page_size];\n                const uint16_t *src",
+     "const int32_t page = block_table[(int64_t)b + t / page_size];\n                const uint16_t *src"),
+    ("paged append into the next token", "const size_t dst = (((size_t)page * Hkv + h) * page_size + (size_t)(t % page_size)) * D;",
+     "const size_t dst = (((size_t)page * Hkv + h) * page_size + (size_t)((t + 1) % page_size)) * D;"),
     ("encode subnormal quantum", "e = emin;                   /* subnormals",
      "e = emin - 1;               /* subnormals"),
 ]
