@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--rope", type=float, default=0.0, metavar="THETA",
                     help="fuse the rotary embedding with this base (e.g. 1e6): the append rotates new K "
                          "rows and the attention rotates q")
+    ap.add_argument("--paged", action="store_true",
+                    help="paged caches: every layer's K/V cache becomes a pool of 16-token pages in a "
+                         "random order behind one block table")
     ap.add_argument("--graph", action="store_true",
                     help="capture one whole step (every layer) into a HIP graph and time its replays; the "
                          "kernel roofline then comes from an eager pass of the same steps afterwards")
@@ -86,7 +89,7 @@ def counters_for(kernel_tag, workload):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, layers_host_fn, n_layers, budget_s, freqs=None):
+def cpu_baseline(w, layers_host_fn, n_layers, budget_s, freqs=None, block_table=None):
     """The oracle (append + attention, fp64, OpenMP; with the rotary embedding when a
     table is given) on whole layers of the workload until about budget_s of CPU time is
     spent; returns the record for the JSON line."""
@@ -97,11 +100,15 @@ def cpu_baseline(w, layers_host_fn, n_layers, budget_s, freqs=None):
     for layer in range(n_layers):
         q, kc, vc, kn, vn, sp = layers_host_fn(layer)
         t = time.perf_counter()
-        if freqs is None:
+        if freqs is not None:
+            pos = sp[:, None, None] + np.arange(w.q_len, dtype=np.int32)[None, :, None]
+            kn = oracle.rope_rows(kn, np.broadcast_to(pos, kn.shape[:3]), freqs, dt)
+            q = oracle.rope_q(q, sp, freqs, dt)
+        if block_table is None:
             k2, v2 = oracle.kv_append(kc, vc, kn, vn, sp)
         else:
-            k2, v2 = oracle.kv_append_rope(kc, vc, kn, vn, sp, freqs, dt)
-            q = oracle.rope_q(q, sp, freqs, dt)
+            kp, vp = oracle.kv_append_paged(kc, vc, kn, vn, sp, block_table)
+            k2, v2 = oracle.gather_paged(kp, block_table), oracle.gather_paged(vp, block_table)
         oracle.gqa_decode(q, k2, v2, sp, dt)
         spent += time.perf_counter() - t
         done_bytes += algorithmic_bytes(w, sp)[1]
@@ -145,8 +152,24 @@ def main():
     layers = [make_layer(w, l, dev) for l in range(w.layers)]
     seq_pos = layers[0]["seq_pos"].cpu().numpy()
     freqs = rope_freqs(w.head_dim, args.rope, dev) if args.rope > 0 else None
+    block_table, n_pages = None, 0
+    if args.paged:
+        # pages of every (sequence, KV head) cache, shuffled into one pool per layer and cache
+        pps = w.max_seq // 16
+        n_pages = w.batch * pps
+        perm = torch.randperm(n_pages, generator=torch.Generator().manual_seed(7))
+        block_table = perm.view(w.batch, pps).to(torch.int32).to(dev)
+        inv = torch.empty_like(perm)
+        inv[perm] = torch.arange(n_pages)
+        for L in layers:
+            for key in ("k_cache", "v_cache"):
+                c = L[key].view(w.batch, w.n_kv_heads, pps, 16, w.head_dim).transpose(1, 2)
+                pages = c.reshape(n_pages, w.n_kv_heads, 16, w.head_dim)  # page b * pps + i
+                L[key] = pages[inv.to(dev)].contiguous()  # pool page perm[j] holds page j
+                del c, pages
+        torch.cuda.synchronize()
     p = da.problem(w.batch, w.q_len, w.n_q_heads, w.n_kv_heads, w.head_dim, w.max_seq, w.dtype,
-                   chunk_tokens=args.chunk, rope_freqs=freqs)
+                   chunk_tokens=args.chunk, rope_freqs=freqs, block_table=block_table, n_pages=n_pages)
     plan = da.plan_attention(p)
     ws = da.new_workspace(p)
     outs = [torch.empty_like(L["q"]) for L in layers]
@@ -236,6 +259,8 @@ def main():
     if args.path == "step":
         attn_bytes += 2 * w.batch * w.q_len * w.n_kv_heads * w.head_dim * 2 + q_bytes
         kernel_tag += "_step" if plan["fused_combine"] else "_step+attn_combine"
+    if args.paged:
+        kernel_tag = kernel_tag.replace("attn_split_" + plan["variant"], "attn_split_" + plan["variant"] + "_paged")
     if args.rope > 0:
         kernel_tag = kernel_tag.replace("attn_split_" + plan["variant"], "attn_split_" + plan["variant"] + "_rope")
     attn_gbs = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
@@ -260,7 +285,7 @@ def main():
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "context": int(seq_pos.max()) + w.q_len,
                    "max_seq": w.max_seq, "layers": w.layers, "chunk_tokens": plan["chunk_tokens"],
                    "variant": plan["variant"], "path": args.path, "graph": args.graph,
-                   "rope_theta": args.rope if args.rope > 0 else None,
+                   "rope_theta": args.rope if args.rope > 0 else None, "paged": args.paged,
                    "fused_merge": bool(plan["fused_combine"]) and args.path == "step",
                    "bytes_per_step": step_bytes,
                    "cold_cache_flush": flush},
@@ -282,7 +307,8 @@ def main():
             return (u16(L["q"]), u16(L["k_cache"]), u16(L["v_cache"]), u16(L["k_new"]),
                     u16(L["v_new"]), L["seq_pos"].cpu().numpy())
         rec["cpu_baseline"] = cpu_baseline(w, host_layer_fn, w.layers, args.cpu_seconds,
-                                           None if freqs is None else freqs.cpu().numpy())
+                                           None if freqs is None else freqs.cpu().numpy(),
+                                           None if block_table is None else block_table.cpu().numpy())
 
     print(json.dumps(rec), flush=True)
 

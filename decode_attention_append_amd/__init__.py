@@ -52,6 +52,10 @@ class Problem(ctypes.Structure):
         ("variant", ctypes.c_int32),
         ("work_items", ctypes.c_int32),
         ("rope_freqs", ctypes.c_void_p),
+        ("page_size", ctypes.c_int32),
+        ("pages_per_seq", ctypes.c_int32),
+        ("n_pages", ctypes.c_int32),
+        ("block_table", ctypes.c_void_p),
     ]
 
     def __repr__(self):
@@ -131,10 +135,13 @@ def status_str(status: int) -> str:
 
 
 def problem(batch, q_len, n_q_heads, n_kv_heads, head_dim, max_seq, dtype, scale=0.0,
-            chunk_tokens=0, variant=None, work_items=0, rope_freqs=None) -> Problem:
+            chunk_tokens=0, variant=None, work_items=0, rope_freqs=None, block_table=None,
+            n_pages=0, page_size=16) -> Problem:
     """variant: None (automatic), "valu" or "mfma"; chunk_tokens 0 = balanced chunks.
-    rope_freqs: None, or a float32 GPU tensor of head_dim/2 rotary frequencies (the
-    problem keeps a reference to it)."""
+    rope_freqs: None, or a float32 GPU tensor of head_dim/2 rotary frequencies.
+    block_table: None (contiguous caches), or an int32 GPU tensor [batch, pages_per_seq]
+    for paged caches (pools [n_pages, n_kv_heads, page_size, head_dim]; max_seq must be
+    pages_per_seq * page_size).  The problem keeps references to both tensors."""
     if isinstance(dtype, torch.dtype):
         dtype = _DTYPE_CODE[dtype]
     elif isinstance(dtype, str):
@@ -143,18 +150,31 @@ def problem(batch, q_len, n_q_heads, n_kv_heads, head_dim, max_seq, dtype, scale
     rp = None
     if rope_freqs is not None:
         rp = _dev(rope_freqs, "rope_freqs", (head_dim // 2,), torch.float32)
+    ps, pps, bt = 0, 0, None
+    if block_table is not None:
+        if block_table.dim() != 2 or block_table.shape[0] != batch:
+            raise ValueError("block_table must be [batch, pages_per_seq]")
+        pps = block_table.shape[1]
+        bt = _dev(block_table, "block_table", None, torch.int32)
+        ps = page_size
     pr = Problem(batch, q_len, n_q_heads, n_kv_heads, head_dim, max_seq, dtype, float(scale),
-                 chunk_tokens, v, work_items, rp)
-    pr._rope_ref = rope_freqs  # keeps the table alive as long as the problem
+                 chunk_tokens, v, work_items, rp, ps, pps, n_pages if ps else 0, bt)
+    pr._refs = (rope_freqs, block_table)  # keeps the tables alive as long as the problem
     return pr
 
 
 def problem_for(q: torch.Tensor, k_cache: torch.Tensor, scale=0.0, chunk_tokens=0,
-                variant=None, work_items=0, rope_freqs=None) -> Problem:
-    """The problem described by q [B, q_len, Hq, D] and a cache [B, Hkv, S, D]."""
+                variant=None, work_items=0, rope_freqs=None, block_table=None) -> Problem:
+    """The problem described by q [B, q_len, Hq, D] and a cache [B, Hkv, S, D], or with a
+    block table [B, pages_per_seq] a page pool [n_pages, Hkv, page_size, D]."""
     B, q_len, Hq, D = q.shape
-    _, Hkv, S, _ = k_cache.shape
-    return problem(B, q_len, Hq, Hkv, D, S, q.dtype, scale, chunk_tokens, variant, work_items, rope_freqs)
+    if block_table is None:
+        _, Hkv, S, _ = k_cache.shape
+        return problem(B, q_len, Hq, Hkv, D, S, q.dtype, scale, chunk_tokens, variant, work_items, rope_freqs)
+    n_pages, Hkv, page_size, _ = k_cache.shape
+    S = block_table.shape[1] * page_size
+    return problem(B, q_len, Hq, Hkv, D, S, q.dtype, scale, chunk_tokens, variant, work_items, rope_freqs,
+                   block_table, n_pages, page_size)
 
 
 def plan_attention(p: Problem) -> dict:
@@ -221,10 +241,16 @@ def _elem(p: Problem):
     return torch.float16 if p.dtype == DA_FP16 else torch.bfloat16
 
 
+def _cache_shape(p: Problem):
+    if p.page_size:
+        return (p.n_pages, p.n_kv_heads, p.page_size, p.head_dim)
+    return (p.batch, p.n_kv_heads, p.max_seq, p.head_dim)
+
+
 def kv_append(p: Problem, k_cache, v_cache, k_new, v_new, seq_pos, stream=None):
     """da_kv_append: k_cache[b, h, seq_pos[b] + i] = k_new[b, i, h] (and V), in place."""
     e = _elem(p)
-    cs = (p.batch, p.n_kv_heads, p.max_seq, p.head_dim)
+    cs = _cache_shape(p)
     ns = (p.batch, p.q_len, p.n_kv_heads, p.head_dim)
     st = _get_lib().da_kv_append(ctypes.byref(p), _dev(k_cache, "k_cache", cs, e), _dev(v_cache, "v_cache", cs, e),
                           _dev(k_new, "k_new", ns, e), _dev(v_new, "v_new", ns, e),
@@ -236,7 +262,7 @@ def kv_append(p: Problem, k_cache, v_cache, k_new, v_new, seq_pos, stream=None):
 def gqa_decode_attn(p: Problem, q, k_cache, v_cache, seq_pos, workspace, stream=None):
     """da_gqa_decode_attn: fp32 split-context partials into ``workspace``."""
     e = _elem(p)
-    cs = (p.batch, p.n_kv_heads, p.max_seq, p.head_dim)
+    cs = _cache_shape(p)
     st = _get_lib().da_gqa_decode_attn(ctypes.byref(p),
                                 _dev(q, "q", (p.batch, p.q_len, p.n_q_heads, p.head_dim), e),
                                 _dev(k_cache, "k_cache", cs, e), _dev(v_cache, "v_cache", cs, e),
@@ -269,7 +295,7 @@ def workspace_init(p: Problem, workspace, stream=None):
 def decode_step(p: Problem, q, k_cache, v_cache, k_new, v_new, seq_pos, workspace, out, stream=None):
     """da_decode_step: append + attention + combine, in one launch where the plan allows."""
     e = _elem(p)
-    cs = (p.batch, p.n_kv_heads, p.max_seq, p.head_dim)
+    cs = _cache_shape(p)
     ns = (p.batch, p.q_len, p.n_kv_heads, p.head_dim)
     qs = (p.batch, p.q_len, p.n_q_heads, p.head_dim)
     st = _get_lib().da_decode_step(

@@ -67,18 +67,37 @@ struct Tile {
     u32x4_t v[8];     // V: slot u, dims 8i .. 8i+7
 };
 
-// A whole 32-key tile inside the chunk: a few base addresses, immediate offsets.
-__device__ __forceinline__ void load_full(Tile &t, const uint8_t *kb, const uint8_t *vb, int tb, int l16, int q) {
-    const uint8_t *kr = kb + (size_t)(tb + l16) * kRowBytes + 16 * q;
+// The caches of one (sequence b, KV head h) seen from a chunk starting at key t0
+// (a multiple of 32): contiguous, or paged through the block table.  A 32-key
+// tile is two 16-token blocks, each one page of a paged cache.
+struct CacheView {
+    const uint8_t *k, *v;  // whole caches / pools
+    uint8_t *kw, *vw;      // the same, writable (one-launch step), or null
+    KvLayout L;
+    int b, h, n_kv_heads, max_seq, t0;
+    __device__ __forceinline__ size_t block(int j) const {  // 16-token block j of the chunk
+        return kv_block_off(L, b, h, n_kv_heads, max_seq, t0 / kPageTokens + j);
+    }
+    __device__ __forceinline__ size_t row(int key) const {
+        return kv_row_off(L, b, h, n_kv_heads, max_seq, t0 + key);
+    }
+    __device__ __forceinline__ bool writable(int key) const { return kv_row_writable(L, b, t0 + key); }
+};
+
+// A whole 32-key tile inside the chunk: two block bases, immediate offsets.
+__device__ __forceinline__ void load_full(Tile &t, const CacheView &cv, int tb, int l16, int q) {
+    const size_t blk[2] = {cv.block(tb / kPageTokens), cv.block(tb / kPageTokens + 1)};
 #pragma unroll
-    for (int kblk = 0; kblk < 2; ++kblk)
+    for (int kblk = 0; kblk < 2; ++kblk) {
+        const uint8_t *kr = cv.k + blk[kblk] + (size_t)l16 * kRowBytes + 16 * q;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) t.k[kblk][s] = ld16(kr + 16 * kRowBytes * kblk + 64 * s);
-    const uint8_t *v0 = vb + (size_t)(tb + 4 * q) * kRowBytes + 16 * l16;
+        for (int s = 0; s < 4; ++s) t.k[kblk][s] = ld16(kr + 64 * s);
+    }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        t.v[u] = ld16(v0 + u * kRowBytes);
-        t.v[u + 4] = ld16(v0 + (16 + u) * kRowBytes);
+    for (int half = 0; half < 2; ++half) {
+        const uint8_t *v0 = cv.v + blk[half] + (size_t)(4 * q) * kRowBytes + 16 * l16;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) t.v[4 * half + u] = ld16(v0 + u * kRowBytes);
     }
 }
 
@@ -90,7 +109,6 @@ __device__ __forceinline__ void load_full(Tile &t, const uint8_t *kb, const uint
 // k_new / v_new and, by `store`, appended to the cache.
 struct RowSource {
     const uint8_t *knew, *vnew;  // new rows of (b, h), row i at + i * stride
-    uint8_t *kw, *vw;            // writable cache of (b, h) at the chunk start
     size_t stride;
     int new_first;
     int t0;             // absolute position of local key 0
@@ -99,23 +117,23 @@ struct RowSource {
 };
 
 template <bool F16>
-__device__ __forceinline__ void load_rows(Tile &t, const uint8_t *kb, const uint8_t *vb, int tb, int last,
-                                          int l16, int q, const RowSource &rs) {
+__device__ __forceinline__ void load_rows(Tile &t, const CacheView &cv, int tb, int last, int l16, int q,
+                                          const RowSource &rs) {
 #pragma unroll
     for (int kblk = 0; kblk < 2; ++kblk) {
         const int key = min(tb + 16 * kblk + l16, last);
         const uint8_t *kr = key >= rs.new_first ? rs.knew + (size_t)(key - rs.new_first) * rs.stride + 16 * q
-                                                : kb + (size_t)key * kRowBytes + 16 * q;
+                                                : cv.k + cv.row(key) + 16 * q;
 #pragma unroll
         for (int s = 0; s < 4; ++s) t.k[kblk][s] = ld16(kr + 64 * s);
         if (rs.rope && key >= rs.new_first) {
             rope8<F16>(t.k[kblk][0], t.k[kblk][2], rs.t0 + key, rs.rope, 8 * q);
             rope8<F16>(t.k[kblk][1], t.k[kblk][3], rs.t0 + key, rs.rope, 32 + 8 * q);
         }
-        if (rs.store && key >= rs.new_first && tb + 16 * kblk + l16 <= last) {
+        if (rs.store && key >= rs.new_first && tb + 16 * kblk + l16 <= last && cv.writable(key)) {
+            uint8_t *kw = cv.kw + cv.row(key) + 16 * q;
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
-                *reinterpret_cast<u32x4_t *>(rs.kw + (size_t)key * kRowBytes + 16 * q + 64 * s) = t.k[kblk][s];
+            for (int s = 0; s < 4; ++s) *reinterpret_cast<u32x4_t *>(kw + 64 * s) = t.k[kblk][s];
         }
     }
 #pragma unroll
@@ -123,10 +141,10 @@ __device__ __forceinline__ void load_rows(Tile &t, const uint8_t *kb, const uint
         const int k_raw = tb + pv_key(q, u);
         const int key = min(k_raw, last);
         t.v[u] = ld16(key >= rs.new_first ? rs.vnew + (size_t)(key - rs.new_first) * rs.stride + 16 * l16
-                                          : vb + (size_t)key * kRowBytes + 16 * l16);
+                                          : cv.v + cv.row(key) + 16 * l16);
         if (k_raw > last) t.v[u] = u32x4_t{0u, 0u, 0u, 0u};
-        else if (rs.store && key >= rs.new_first)
-            *reinterpret_cast<u32x4_t *>(rs.vw + (size_t)key * kRowBytes + 16 * l16) = t.v[u];
+        else if (rs.store && key >= rs.new_first && cv.writable(key))
+            *reinterpret_cast<u32x4_t *>(cv.vw + cv.row(key) + 16 * l16) = t.v[u];
     }
 }
 
@@ -184,9 +202,17 @@ void attn_split_mfma_kernel(AttnParams p) {
         }
     }
 
-    const size_t head_off = ((size_t)bh * p.max_seq + t0) * kRowBytes;
-    const uint8_t *kb = p.k_cache + head_off;
-    const uint8_t *vb = p.v_cache + head_off;
+    CacheView cv;
+    cv.k = p.k_cache;
+    cv.v = p.v_cache;
+    cv.kw = p.k_cache_w;
+    cv.vw = p.v_cache_w;
+    cv.L = p.layout;
+    cv.b = b;
+    cv.h = h;
+    cv.n_kv_heads = p.n_kv_heads;
+    cv.max_seq = p.max_seq;
+    cv.t0 = t0;
 
     float m_run[RB], l_run[RB];
     f32x4_t oacc[RB][8];
@@ -274,29 +300,26 @@ void attn_split_mfma_kernel(AttnParams p) {
         const size_t noff = ((size_t)b * p.q_len * p.n_kv_heads + h) * kRowBytes;
         rs.knew = p.k_new + noff;
         rs.vnew = p.v_new + noff;
-        rs.kw = p.k_cache_w + head_off;
-        rs.vw = p.v_cache_w + head_off;
     } else {
         rs.knew = rs.vnew = nullptr;
-        rs.kw = rs.vw = nullptr;
     }
     const int n_all = (n_tok + 31) >> 5;
     const int nt = min(n_tok >> 5, max(rs.new_first, 0) >> 5);
     if (nt > 0) {
         Tile ta, tb_;
-        load_full(ta, kb, vb, 0, l16, q);
+        load_full(ta, cv, 0, l16, q);
         int i = 0;
         for (; i + 2 <= nt; i += 2) {
-            load_full(tb_, kb, vb, (i + 1) * 32, l16, q);
+            load_full(tb_, cv, (i + 1) * 32, l16, q);
             compute(ta, i);
-            load_full(ta, kb, vb, min(i + 2, nt - 1) * 32, l16, q);
+            load_full(ta, cv, min(i + 2, nt - 1) * 32, l16, q);
             compute(tb_, i + 1);
         }
         if (i < nt) compute(ta, i);
     }
     for (int i = nt; i < n_all; ++i) {
         Tile tt_;
-        load_rows<F16>(tt_, kb, vb, i * 32, last, l16, q, rs);
+        load_rows<F16>(tt_, cv, i * 32, last, l16, q, rs);
         compute(tt_, i);
     }
 

@@ -142,10 +142,17 @@ __global__ __launch_bounds__(256) void attn_split_valu_kernel(AttnParams p) {
         }
     }
 
-    const size_t head_off = ((size_t)bh * p.max_seq + t0) * kRowBytes + cq * 16;
-    const uint8_t *kb = p.k_cache + head_off;
-    const uint8_t *vb = p.v_cache + head_off;
     const int last = n_tok - 1;  // loads past the context re-read the last row (masked)
+    // Cache addresses of this lane's 16-byte column (contiguous or paged caches).
+    // Chunks start on multiples of 32 keys, so slab s (keys t0 + 16 s ..) is one
+    // 16-token block: one page of a paged cache.
+    const int lp0 = t0 / kPageTokens;
+    auto slab_ptr = [&](const uint8_t *cache, int s_) {
+        return cache + kv_block_off(p.layout, b, h, p.n_kv_heads, p.max_seq, lp0 + s_) + cq * 16;
+    };
+    auto row_ptr = [&](const uint8_t *cache, int t) {
+        return cache + kv_row_off(p.layout, b, h, p.n_kv_heads, p.max_seq, t0 + t) + cq * 16;
+    };
 
     // Slab loads: four 128-bit loads per lane cover 16 keys (1 KiB each).
     //  - Fast slabs (full, and below this step's new rows) use one base address
@@ -163,7 +170,7 @@ __global__ __launch_bounds__(256) void attn_split_valu_kernel(AttnParams p) {
     const size_t new_stride = (size_t)p.n_kv_heads * kRowBytes;
     const size_t new_off = ((size_t)b * p.q_len * p.n_kv_heads + h) * kRowBytes + cq * 16;
     auto load_fast = [&](u32x4_t (&buf)[4], const uint8_t *base, int s_) {
-        const uint8_t *r0 = base + (size_t)(s_ * 16 + gq) * kRowBytes;
+        const uint8_t *r0 = slab_ptr(base, s_) + (size_t)gq * kRowBytes;
 #pragma unroll
         for (int u = 0; u < 4; ++u) buf[u] = ld16(r0 + u * 4 * kRowBytes);
     };
@@ -172,7 +179,7 @@ __global__ __launch_bounds__(256) void attn_split_valu_kernel(AttnParams p) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int t = min(s_ * 16 + u * 4 + gq, last);
-            buf[u] = ld16(t >= new_first ? nbase + (size_t)(t - new_first) * new_stride : base + (size_t)t * kRowBytes);
+            buf[u] = ld16(t >= new_first ? nbase + (size_t)(t - new_first) * new_stride : row_ptr(base, t));
         }
         if (ROPE && rot) {
 #pragma unroll
@@ -185,7 +192,9 @@ __global__ __launch_bounds__(256) void attn_split_valu_kernel(AttnParams p) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int t = s_ * 16 + u * 4 + gq;
-                if (t >= new_first && t <= last) *reinterpret_cast<u32x4_t *>(wbase + (size_t)t * kRowBytes) = buf[u];
+                if (t >= new_first && t <= last && kv_row_writable(p.layout, b, t0 + t))
+                    *reinterpret_cast<u32x4_t *>(wbase + kv_row_off(p.layout, b, h, p.n_kv_heads, p.max_seq,
+                                                                    t0 + t) + cq * 16) = buf[u];
             }
         }
     };
@@ -215,9 +224,9 @@ __global__ __launch_bounds__(256) void attn_split_valu_kernel(AttnParams p) {
     // ---- pass 1: scores of the chunk into LDS ----------------------------------
     const uint8_t *knb = fused_append ? p.k_new + new_off : nullptr;
     const uint8_t *vnb = fused_append ? p.v_new + new_off : nullptr;
-    uint8_t *kwb = fused_append ? p.k_cache_w + head_off : nullptr;
-    uint8_t *vwb = fused_append ? p.v_cache_w + head_off : nullptr;
-    pass(kb, knb, kwb, fused_append, [&](u32x4_t (&cur)[4], int s_) {
+    uint8_t *kwb = fused_append ? p.k_cache_w : nullptr;
+    uint8_t *vwb = fused_append ? p.v_cache_w : nullptr;
+    pass(p.k_cache, knb, kwb, fused_append, [&](u32x4_t (&cur)[4], int s_) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int tl = s_ * 16 + u * 4 + gq;
@@ -266,7 +275,7 @@ __global__ __launch_bounds__(256) void attn_split_valu_kernel(AttnParams p) {
 #pragma unroll
         for (int d = 0; d < 8; ++d) acc[r][d] = 0.f;
     const int first_draft = sp - t0;  // local keys above this may be hidden from some rows
-    pass(vb, vnb, vwb, false, [&](u32x4_t (&cur)[4], int s_) {
+    pass(p.v_cache, vnb, vwb, false, [&](u32x4_t (&cur)[4], int s_) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int tl = s_ * 16 + u * 4 + gq;

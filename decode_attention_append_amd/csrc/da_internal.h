@@ -16,6 +16,43 @@ constexpr int kMaxQLen = 8;
 constexpr int kTokenTile = 64;    // chunk sizes are multiples of this
 constexpr int kMaxChunk = 2048;
 
+// ---- cache layout -----------------------------------------------------------
+// Contiguous: [B][Hkv][max_seq][D].  Paged ("Architecture Diagram - Qwen3-30B-A3B",
+// Paged Attention: a page pool [pages][KV heads][16 tokens][D]): token t of
+// sequence b is in pool page block_table[b][t / 16], slot t % 16, and max_seq =
+// pages_per_seq * 16.
+struct KvLayout {
+    const int32_t *block_table;  // [B][pages_per_seq], null for the contiguous layout
+    int32_t pages_per_seq, n_pages;
+};
+
+constexpr int kPageTokens = 16;
+
+// Pool page of logical page `lp` of sequence b; a block-table entry outside the
+// pool gives -1 (the caller's contract is broken: reads use page 0, writes are
+// dropped, so nothing outside the pool is touched).
+__device__ __forceinline__ int kv_page(const KvLayout &L, int b, int lp) {
+    const int pg = L.block_table[(size_t)b * L.pages_per_seq + lp];
+    return (unsigned)pg < (unsigned)L.n_pages ? pg : -1;
+}
+
+// Byte offset of the 16-token block holding tokens 16 * lp .. 16 * lp + 15 of
+// (b, h), and of token t.  Contiguous caches have no pages, but the same
+// arithmetic (blocks of 16 consecutive rows) applies.
+__device__ __forceinline__ size_t kv_block_off(const KvLayout &L, int b, int h, int n_kv_heads, int max_seq,
+                                               int lp) {
+    if (!L.block_table)
+        return (((size_t)b * n_kv_heads + h) * max_seq + (size_t)lp * kPageTokens) * kRowBytes;
+    const int pg = kv_page(L, b, lp);
+    return ((size_t)(pg < 0 ? 0 : pg) * n_kv_heads + h) * kPageTokens * kRowBytes;
+}
+__device__ __forceinline__ size_t kv_row_off(const KvLayout &L, int b, int h, int n_kv_heads, int max_seq, int t) {
+    return kv_block_off(L, b, h, n_kv_heads, max_seq, t / kPageTokens) + (size_t)(t % kPageTokens) * kRowBytes;
+}
+__device__ __forceinline__ bool kv_row_writable(const KvLayout &L, int b, int t) {
+    return !L.block_table || kv_page(L, b, t / kPageTokens) >= 0;
+}
+
 // ---- parameter blocks ------------------------------------------------------
 
 struct AppendParams {
@@ -25,6 +62,7 @@ struct AppendParams {
     const uint8_t *v_new;
     const int32_t *seq_pos;
     const float *rope_freqs;   // D/2 rotary frequencies, or null: k_new is copied as is
+    KvLayout layout;
     int32_t batch, q_len, n_kv_heads, max_seq;
 };
 
@@ -46,6 +84,7 @@ struct AttnParams {
     float scale_log2;      // softmax scale * log2(e): scores are kept in log2 units
     const float *rope_freqs;  // D/2 rotary frequencies, or null: q (and fused-appended
                               //   k_new rows) are used as given
+    KvLayout layout;          // contiguous or paged caches
     int32_t seq_chunk_cap; // balanced: at most this many chunks per sequence unless its
                            //   length needs more of max_chunk keys (0: no cap)
 

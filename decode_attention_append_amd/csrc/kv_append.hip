@@ -8,7 +8,8 @@
 // stores.  Without a rotary table it is a pure bit copy: no arithmetic touches
 // the data.  With one, each K row is rotated at its position seq_pos + i first
 // (the RoPE block of the same page; lanes c and c ^ 8 of a row hold the two
-// halves of each rotated pair and swap them with one shuffle).
+// halves of each rotated pair and swap them with one shuffle).  In a paged
+// cache the row's slot comes from the block table.
 #include "da_internal.h"
 
 namespace da {
@@ -24,13 +25,13 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p, int thre
     const int sp = p.seq_pos[b];
     // a sequence that breaks the contract is skipped (both lanes of every pair
     // belong to the same row, so they agree)
-    const bool ok = t < threads_total && sp >= 0 && sp <= p.max_seq - p.q_len;
+    const bool ok = t < threads_total && sp >= 0 && sp <= p.max_seq - p.q_len &&
+                    kv_row_writable(p.layout, b, sp + i);
     const size_t src = (size_t)min(row, threads_total / 16 - 1) * kRowBytes + piece * 16;
     u32x4_t k = ld16(p.k_new + src);
     if (p.rope_freqs) rope_row16<F16>(k, piece, sp + i, p.rope_freqs, ok);
     if (!ok) return;
-    const size_t dst = (((size_t)b * p.n_kv_heads + h) * p.max_seq + (size_t)(sp + i)) * kRowBytes +
-                       piece * 16;
+    const size_t dst = kv_row_off(p.layout, b, h, p.n_kv_heads, p.max_seq, sp + i) + piece * 16;
     const u32x4_t v = ld16(p.v_new + src);
     *reinterpret_cast<u32x4_t *>(p.k_cache + dst) = k;
     *reinterpret_cast<u32x4_t *>(p.v_cache + dst) = v;

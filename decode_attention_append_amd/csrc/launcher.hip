@@ -32,6 +32,12 @@ da_status check_problem(const da_problem *p) {
     if (p->variant < 0 || p->variant > DA_VARIANT_MFMA + 1) return DA_ERR_INVALID_ARG;
     if (p->work_items < 0 || p->work_items > (1 << 20)) return DA_ERR_INVALID_ARG;
     if (p->rope_freqs && !aligned16(p->rope_freqs)) return DA_ERR_INVALID_ARG;
+    if (p->page_size != 0) {
+        if (p->pages_per_seq <= 0 || p->n_pages <= 0 || !p->block_table || ((uintptr_t)p->block_table & 3u))
+            return DA_ERR_INVALID_ARG;
+        if ((int64_t)p->pages_per_seq * p->page_size != p->max_seq) return DA_ERR_INVALID_ARG;
+        if (p->page_size != kPageTokens) return DA_ERR_UNSUPPORTED;
+    }
     if (p->dtype != DA_BF16 && p->dtype != DA_FP16) return DA_ERR_UNSUPPORTED;
     if (p->head_dim != kHeadDim) return DA_ERR_UNSUPPORTED;
     if (p->q_len > kMaxQLen) return DA_ERR_UNSUPPORTED;
@@ -149,6 +155,14 @@ int32_t *counters_of(const da_problem *p, const da_plan &pl, void *workspace) {
                        align256(ws_ml_floats(bh, pl.n_chunks, pl.rows) * sizeof(float)));
 }
 
+KvLayout layout_of(const da_problem *p) {
+    KvLayout L;
+    L.block_table = p->page_size ? p->block_table : nullptr;
+    L.pages_per_seq = p->page_size ? p->pages_per_seq : 0;
+    L.n_pages = p->page_size ? p->n_pages : 0;
+    return L;
+}
+
 AttnParams attn_params(const da_problem *p, const da_plan &pl, const void *q, const void *k_cache,
                        const void *v_cache, const int32_t *seq_pos, const void *workspace) {
     AttnParams a;
@@ -175,6 +189,7 @@ AttnParams attn_params(const da_problem *p, const da_plan &pl, const void *q, co
     a.scale_log2 = (float)(scale * 1.4426950408889634);  // log2(e)
     a.seq_chunk_cap = 0;
     a.rope_freqs = p->rope_freqs;
+    a.layout = layout_of(p);
     a.k_cache_w = a.v_cache_w = nullptr;
     a.k_new = a.v_new = nullptr;
     a.counters = nullptr;
@@ -215,6 +230,7 @@ da_status da_kv_append(const da_problem *p, void *k_cache, void *v_cache, const 
     a.v_new = (const uint8_t *)v_new;
     a.seq_pos = seq_pos;
     a.rope_freqs = p->rope_freqs;
+    a.layout = layout_of(p);
     a.batch = p->batch;
     a.q_len = p->q_len;
     a.n_kv_heads = p->n_kv_heads;
@@ -299,6 +315,7 @@ da_status da_decode_step(const da_problem *p, const void *q, void *k_cache, void
         ap.v_new = (const uint8_t *)v_new;
         ap.seq_pos = seq_pos;
         ap.rope_freqs = p->rope_freqs;
+        ap.layout = layout_of(p);
         ap.batch = p->batch;
         ap.q_len = p->q_len;
         ap.n_kv_heads = p->n_kv_heads;

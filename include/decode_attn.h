@@ -98,6 +98,24 @@ typedef struct {
                              they are appended, and q rows at seq_pos[b] + i before
                              the scores (the cache holds rotated keys).  Evaluated
                              in fp32 and rounded once to the 16-bit type.          */
+    int32_t page_size;    /* 0: contiguous caches [B][Hkv][max_seq][D].  16: paged
+                             caches, the page pool of the "Qwen MoE BringUp" page
+                             ("Architecture Diagram - Qwen3-30B-A3B (Extern
+                             Dispatch, 75 tok/s)", Paged Attention: KV write to a
+                             page pool [pages][KV heads][16 tokens][head dim]):
+                             k_cache / v_cache are pools [n_pages][Hkv][16][D] and
+                             token t of sequence b lives in pool page
+                             block_table[b][t / 16], slot t % 16.  Other sizes:
+                             DA_ERR_UNSUPPORTED.                                   */
+    int32_t pages_per_seq;/* paged: block-table row length; max_seq must equal
+                             pages_per_seq * page_size                             */
+    int32_t n_pages;      /* paged: pages in each pool                             */
+    const int32_t *block_table; /* paged: DEVICE int32 [B][pages_per_seq], 4-byte
+                             aligned.  Entries outside [0, n_pages) break the
+                             contract: reads through them use page 0 and writes
+                             through them are dropped, so no kernel touches memory
+                             outside the pools; that sequence's results are
+                             unspecified.                                          */
 } da_problem;
 
 /*

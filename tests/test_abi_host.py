@@ -159,6 +159,21 @@ def test_rope_table_must_be_aligned():
     assert da.lib.da_plan_attention(ctypes.byref(p16), ctypes.byref(da.Plan())) == da.DA_ERR_UNSUPPORTED
 
 
+def test_paged_problem_checks():
+    p = P(max_seq=160)
+    pl = da.Plan()
+    p.page_size, p.pages_per_seq, p.n_pages, p.block_table = 16, 10, 50, 0x1000
+    assert da.lib.da_plan_attention(ctypes.byref(p), ctypes.byref(pl)) == da.DA_OK
+    p.block_table = 0x1002  # misaligned
+    assert da.lib.da_plan_attention(ctypes.byref(p), ctypes.byref(pl)) == da.DA_ERR_INVALID_ARG
+    p.block_table = None
+    assert da.lib.da_plan_attention(ctypes.byref(p), ctypes.byref(pl)) == da.DA_ERR_INVALID_ARG
+    p.block_table, p.pages_per_seq = 0x1000, 9  # max_seq != pages_per_seq * 16
+    assert da.lib.da_plan_attention(ctypes.byref(p), ctypes.byref(pl)) == da.DA_ERR_INVALID_ARG
+    p.pages_per_seq, p.page_size, p.max_seq = 5, 32, 160
+    assert da.lib.da_plan_attention(ctypes.byref(p), ctypes.byref(pl)) == da.DA_ERR_UNSUPPORTED
+
+
 def test_status_strings():
     for s in (0, -1, -2, -3, -4):
         assert da.status_str(s) and da.status_str(s) != "unknown status"
