@@ -75,8 +75,12 @@ struct CacheView {
     uint8_t *kw, *vw;      // the same, writable (one-launch step), or null
     KvLayout L;
     int b, h, n_kv_heads, max_seq, t0;
+    int pg_lane;  // paged: lane j holds the pool page of the chunk's block j (j < 64)
     __device__ __forceinline__ size_t block(int j) const {  // 16-token block j of the chunk
-        return kv_block_off(L, b, h, n_kv_heads, max_seq, t0 / kPageTokens + j);
+        if (!L.block_table || j >= 64) return kv_block_off(L, b, h, n_kv_heads, max_seq, t0 / kPageTokens + j);
+        int pg = __builtin_amdgcn_readlane(pg_lane, j);
+        pg = pg < 0 ? 0 : pg;  // outside the pool: read page 0
+        return ((size_t)pg * n_kv_heads + h) * kPageTokens * kRowBytes;
     }
     __device__ __forceinline__ size_t row(int key) const {
         return kv_row_off(L, b, h, n_kv_heads, max_seq, t0 + key);
@@ -177,6 +181,12 @@ void attn_split_mfma_kernel(AttnParams p) {
     const int l16 = lane & 15, q = lane >> 4;
 
     // B operand of S^T = K q^T: lane holds q[row][dims 64s + 16q .. +16 bytes), s = 0..3
+    // paged caches: lane j reads the pool page of the chunk's 16-token block j
+    // once, first, so its latency overlaps the query loads
+    int pg_lane = 0;
+    if (p.layout.block_table && lane < (n_tok + kPageTokens - 1) / kPageTokens)
+        pg_lane = kv_page(p.layout, b, t0 / kPageTokens + lane);
+
     u32x4_t qop[RB][4];
     int vis[RB];  // exclusive local key limit of this lane's row
 #pragma unroll
@@ -213,6 +223,7 @@ void attn_split_mfma_kernel(AttnParams p) {
     cv.n_kv_heads = p.n_kv_heads;
     cv.max_seq = p.max_seq;
     cv.t0 = t0;
+    cv.pg_lane = pg_lane;
 
     float m_run[RB], l_run[RB];
     f32x4_t oacc[RB][8];

@@ -108,6 +108,12 @@ __global__ __launch_bounds__(256) void attn_split_valu_kernel(AttnParams p) {
     const int gq = lane >> 4;  // which of the 4 keys of a 1 KiB load
     const int cq = lane & 15;  // 16-byte column: dims 8*cq .. 8*cq+7
 
+    // paged caches: the pool page of this wave's first slab is read first, so its
+    // latency overlaps the query loads (later slabs' entries come from the same
+    // cache lines)
+    const int lp0 = t0 / kPageTokens;
+    const int pg_first = p.layout.block_table && wave < n_slab ? kv_page(p.layout, b, lp0 + wave) : 0;
+
     // Query rows: r = i * group + g is query token i of query head h*group + g.
     uint32_t qr[RP][4];
     int vis[RP];  // exclusive limit of the visible local key indices of row r
@@ -146,8 +152,11 @@ __global__ __launch_bounds__(256) void attn_split_valu_kernel(AttnParams p) {
     // Cache addresses of this lane's 16-byte column (contiguous or paged caches).
     // Chunks start on multiples of 32 keys, so slab s (keys t0 + 16 s ..) is one
     // 16-token block: one page of a paged cache.
-    const int lp0 = t0 / kPageTokens;
     auto slab_ptr = [&](const uint8_t *cache, int s_) {
+        if (p.layout.block_table && s_ == wave) {
+            const int pg = pg_first < 0 ? 0 : pg_first;  // outside the pool: read page 0
+            return cache + ((size_t)pg * p.n_kv_heads + h) * kPageTokens * kRowBytes + cq * 16;
+        }
         return cache + kv_block_off(p.layout, b, h, p.n_kv_heads, p.max_seq, lp0 + s_) + cq * 16;
     };
     auto row_ptr = [&](const uint8_t *cache, int t) {
