@@ -63,8 +63,10 @@ class Oracle:
         lib.oracle_encode_bf16.restype = ctypes.c_uint16
         lib.oracle_encode_fp16.argtypes = [f64]
         lib.oracle_encode_fp16.restype = ctypes.c_uint16
-        lib.oracle_rope_rows.argtypes = [i32, i32, i32, p, p, p, p]
+        lib.oracle_rope_rows.argtypes = [i32, i32, i32, i32, p, p, p, p]
         lib.oracle_rope_rows.restype = ctypes.c_int
+        lib.oracle_output_gate.argtypes = [i32, ctypes.c_int64, p, p]
+        lib.oracle_output_gate.restype = None
         lib.oracle_gather_paged.argtypes = [i32] * 6 + [p] * 3
         lib.oracle_gather_paged.restype = ctypes.c_int
         lib.oracle_kv_append_paged.argtypes = [i32] * 7 + [p] * 6
@@ -90,19 +92,29 @@ class Oracle:
 
     def rope_rows(self, rows, positions, freqs, dtype: int) -> np.ndarray:
         """Rotary embedding of ``rows`` [..., D] (16-bit patterns) at ``positions`` (one per
-        row, shape rows.shape[:-1]) with the D/2 float32 ``freqs``; returns new patterns."""
+        row, shape rows.shape[:-1]) with the float32 ``freqs``: R/2 values rotate the first
+        R dims (R = D for full rotation); returns new patterns."""
         x = _u16(rows)
         D = x.shape[-1]
         pos = _i32(positions).reshape(-1)
         if pos.size * D != x.size:
             raise ValueError("one position per row")
-        f = np.ascontiguousarray(np.asarray(freqs, dtype=np.float32))
-        if f.shape != (D // 2,):
-            raise ValueError("freqs must hold D/2 values")
+        f = np.ascontiguousarray(np.asarray(freqs, dtype=np.float32).reshape(-1))
+        R = 2 * f.size
         out = np.empty_like(x)
-        if self.lib.oracle_rope_rows(dtype, pos.size, D, _ptr(pos), _ptr(f), _ptr(x), _ptr(out)) != 0:
-            raise ValueError("bad row length")
+        if self.lib.oracle_rope_rows(dtype, pos.size, D, R, _ptr(pos), _ptr(f), _ptr(x), _ptr(out)) != 0:
+            raise ValueError("bad row length or rotary width")
         return out
+
+    def output_gate(self, out, gate, dtype: int) -> np.ndarray:
+        """out (float64 attention output) times sigmoid(gate) elementwise; gate: 16-bit
+        patterns of the same shape.  Returns a new array."""
+        o = np.ascontiguousarray(np.array(out, dtype=np.float64))
+        g = _u16(gate)
+        if g.shape != o.shape:
+            raise ValueError("gate and output shapes differ")
+        self.lib.oracle_output_gate(dtype, o.size, _ptr(g), _ptr(o))
+        return o
 
     def rope_q(self, q, seq_pos, freqs, dtype: int) -> np.ndarray:
         """q [B, q_len, Hq, D] rotated at position seq_pos[b] + i (new patterns)."""
@@ -258,3 +270,7 @@ def gather_paged(*args, **kw):
 
 def kv_append_paged(*args, **kw):
     return default().kv_append_paged(*args, **kw)
+
+
+def output_gate(*args, **kw):
+    return default().output_gate(*args, **kw)

@@ -319,18 +319,24 @@ static uint16_t encode(int dtype, double x)
  * cos, sin and the rotation are evaluated in double here and the result is
  * rounded once to the row's 16-bit format.
  *
- * rows: n rows of D 16-bit elements; pos: n positions; freqs: D/2 floats.
+ * Partial rotation ("Architecture Diagram - Qwen3.5-35B-A3B", full-SDPA layers:
+ * partial RoPE over 25% of the dims): only the first R dims rotate, as above
+ * with R in place of D (pairs j and j + R/2); dims R .. D-1 pass unchanged.
+ *
+ * rows: n rows of D 16-bit elements; pos: n positions; freqs: R/2 floats.
  */
-int oracle_rope_rows(int32_t dtype, int32_t n, int32_t D, const int32_t *pos, const float *freqs,
+int oracle_rope_rows(int32_t dtype, int32_t n, int32_t D, int32_t R, const int32_t *pos, const float *freqs,
                      const uint16_t *in, uint16_t *out)
 {
-    if (D <= 0 || D % 2)
+    if (D <= 0 || R <= 0 || R > D || R % 2)
         return -1;
-    const int32_t half = D / 2;
+    const int32_t half = R / 2;
 #pragma omp parallel for schedule(static)
     for (int32_t r = 0; r < n; ++r) {
         const uint16_t *x = in + (size_t)r * D;
         uint16_t *y = out + (size_t)r * D;
+        for (int32_t j = R; j < D; ++j)
+            y[j] = x[j];
         for (int32_t j = 0; j < half; ++j) {
             /* the exact product of two floats fits a double; one rounding to float */
             const float a = (float)((double)(float)pos[r] * (double)freqs[j]);
@@ -403,4 +409,18 @@ int oracle_kv_append_paged(int32_t B, int32_t q_len, int32_t Hkv, int32_t D, int
                 memcpy(v_pool + dst, v_new + row, (size_t)D * sizeof(uint16_t));
             }
     return 0;
+}
+
+/* ---- sigmoid output gate ------------------------------------------------------
+ * "Qwen MoE BringUp", "Architecture Diagram - Qwen3.5-35B-A3B", full-SDPA
+ * layers: the query projection also yields a gate ("Q(->8192)+gate" for 16
+ * heads of 256 dims), and the attention output is multiplied elementwise by
+ * sigmoid(gate) ("sigmoid gate") before the output projection.
+ * out: n doubles (the attention output), multiplied in place by
+ * 1 / (1 + exp(-g)) with g the decoded 16-bit gate element.
+ */
+void oracle_output_gate(int32_t dtype, int64_t n, const uint16_t *gate, double *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] *= 1.0 / (1.0 + exp(-decode(dtype, gate[i])));
 }

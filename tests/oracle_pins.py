@@ -490,4 +490,54 @@ def pin_paged_rejects_bad_pages(orc):
         raise AssertionError("a block-table entry outside the pool was accepted")
 
 
+# ---------------------------------------------------------------- head_dim 256, partial rotation, gate
+
+def pin_partial_rope_256(orc):
+    """Rotating the first 64 of 256 dims: those equal the complex rotation of pairs
+    (j, j + 32), correctly rounded; dims 64..255 pass unchanged."""
+    rng = np.random.default_rng(51)
+    freqs = qwen_freqs(64, 1.0e7)
+    q, _, _, _, _, _ = rand_case(1, 1, 32, 1, 256, 1, [0], FP16, seed=52)
+    x = bits(q).reshape(-1, 256)
+    pos = rng.integers(0, 1 << 18, x.shape[0]).astype(np.int32)
+    got = orc.rope_rows(x, pos, freqs, FP16)
+    assert np.array_equal(got[:, 64:], x[:, 64:])
+    ref = _complex_rotation(orc.decode(x[:, :64], FP16), pos, freqs)
+    assert np.array_equal(got[:, :64], ref.astype(np.float16).view(np.uint16))
+
+
+def pin_output_gate_is_sigmoid(orc):
+    """Against scipy's logistic function; gate 0 halves exactly; -inf closes the gate."""
+    from scipy.special import expit
+    rng = np.random.default_rng(53)
+    for dtype in (BF16, FP16):
+        g = bits((torch.randn(4, 256, generator=torch.Generator().manual_seed(54)) * 3).to(_tdt(dtype)))
+        out = rng.standard_normal((4, 256))
+        got = orc.output_gate(out, g, dtype)
+        ref = out * expit(orc.decode(g, dtype))
+        assert np.allclose(got, ref, rtol=1e-14, atol=0)
+    half = orc.output_gate(np.array([3.0, -7.0]), np.zeros(2, np.uint16), BF16)
+    assert np.array_equal(half, np.array([1.5, -3.5]))
+    closed = orc.output_gate(np.array([2.0]), np.array([0xFF80], np.uint16), BF16)  # bf16 -inf
+    assert closed[0] == 0.0
+
+
+def pin_torch_sdpa_float64_d256(orc):
+    """Head dim 256, GQA 16:2, a 4-token causal window: torch's float64 SDPA with
+    enable_gqa and an explicit mask."""
+    B, q_len, Hq, Hkv, D, S = 2, 4, 16, 2, 256, 90
+    q, kc, vc, kn, vn, sp = rand_case(B, q_len, Hq, Hkv, D, S, [40, 86], BF16, seed=55)
+    k2, v2 = orc.kv_append(bits(kc), bits(vc), bits(kn), bits(vn), sp)
+    got = orc.gqa_decode(bits(q), k2, v2, sp, BF16)
+    qd = torch.from_numpy(orc.decode(bits(q), BF16)).permute(0, 2, 1, 3)
+    kd = torch.from_numpy(orc.decode(k2, BF16))
+    vd = torch.from_numpy(orc.decode(v2, BF16))
+    for b in range(B):
+        t = sp[b] + torch.arange(q_len)[:, None]
+        mask = torch.arange(S)[None, :] <= t
+        ref = torch.nn.functional.scaled_dot_product_attention(qd[b:b + 1], kd[b:b + 1], vd[b:b + 1],
+                                                               attn_mask=mask, enable_gqa=True)
+        assert np.allclose(got[b], ref[0].permute(1, 0, 2).numpy(), rtol=1e-10, atol=1e-12)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -55,6 +55,10 @@ MUTANTS = [
      "const int32_t page = block_table[(int64_t)b + t / page_size];\n                const uint16_t *src"),
     ("paged append into the next token", "const size_t dst = (((size_t)page * Hkv + h) * page_size + (size_t)(t % page_size)) * D;",
      "const size_t dst = (((size_t)page * Hkv + h) * page_size + (size_t)((t + 1) % page_size)) * D;"),
+    ("partial rope skips a pass-through dim", "for (int32_t j = R; j < D; ++j)",
+     "for (int32_t j = R + 1; j < D; ++j)"),
+    ("gate sign", "out[i] *= 1.0 / (1.0 + exp(-decode(dtype, gate[i])));",
+     "out[i] *= 1.0 / (1.0 + exp(decode(dtype, gate[i])));"),
     ("encode subnormal quantum", "e = emin;                   /* subnormals",
      "e = emin - 1;               /* subnormals"),
 ]
