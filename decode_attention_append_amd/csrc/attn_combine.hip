@@ -8,8 +8,9 @@
 //
 // One 256-lane workgroup per (sequence, KV head, query row).  Lane c computes
 // chunk c's weight (a block-wide max first), then the four waves split the
-// chunks, each lane owning two dims so a chunk's 512-byte partial is one
-// coalesced load per wave; the four wave sums are added in a fixed order.
+// chunks, each lane owning D/64 dims so a chunk's partial is one coalesced load
+// per wave; the four wave sums are added in a fixed order.  With an output gate
+// the result is multiplied by sigmoid(gate) before rounding.
 #include "da_internal.h"
 
 #include <math.h>
@@ -19,34 +20,33 @@ namespace da {
 constexpr int kCombineThreads = 256;
 constexpr int kCombineMaxChunks = 2048;  // whole weight table in LDS
 
-template <bool F16>
+template <bool F16, int D>
 __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnParams p, uint16_t *out) {
+    constexpr int NV = D / 64;  // dims per lane
     __shared__ float wts[kCombineMaxChunks];
-    __shared__ float red[4][2 * 64];
+    __shared__ float red[4][D];
     __shared__ float wmax[4], wsum[4];
 
     const int r = blockIdx.x % p.rows;
     const int bh = blockIdx.x / p.rows;
     const int b = bh / p.n_kv_heads;
     const int h = bh - b * p.n_kv_heads;
-    const int i = r / p.group, g = r - i * p.group;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    uint32_t *o = reinterpret_cast<uint32_t *>(
-                      out + (((size_t)b * p.q_len + i) * p.n_q_heads + (size_t)h * p.group + g) * kHeadDim) +
-                  lane;
+    const size_t o_off = out_row_off(p, b, h, r) + NV * lane;
     const SeqChunks sc = seq_chunks(p, b, p.fixed_chunk > 0 ? p.fixed_chunk : balanced_chunk(p));
     if (sc.n == 0) {  // seq_pos breaks the contract: flag the rows with NaN
         if (wave == 0) {
-            const uint32_t nan16 = F16 ? 0x7e00u : 0x7fc0u;
-            *o = nan16 | (nan16 << 16);
+            const uint16_t nan16 = F16 ? 0x7e00u : 0x7fc0u;
+#pragma unroll
+            for (int k = 0; k < NV; ++k) out[o_off + k] = nan16;
         }
         return;
     }
     const int n_live = sc.n;
     const size_t cstride_ml = (size_t)p.rows * 2;
-    const size_t cstride_acc = (size_t)p.rows * kHeadDim;
+    const size_t cstride_acc = (size_t)p.rows * D;
     const float *ml = p.ws_ml + ((size_t)bh * p.n_chunks * p.rows + r) * 2;
-    const float *acc = p.ws_acc + ((size_t)bh * p.n_chunks * p.rows + r) * kHeadDim + 2 * lane;
+    const float *acc = p.ws_acc + ((size_t)bh * p.n_chunks * p.rows + r) * D + NV * lane;
 
     // M = max over live chunks
     float m = -INFINITY;
@@ -70,46 +70,66 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnParam
     const float L = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
 
     // weighted sum of the partial V sums: wave w takes chunks w, w+4, ...
-    float a0 = 0.f, a1 = 0.f;
+    float a[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) a[k] = 0.f;
+    auto ld = [&](int c, float (&v)[NV]) {
+        if constexpr (NV == 2) {
+            const float2 x = *reinterpret_cast<const float2 *>(acc + (size_t)c * cstride_acc);
+            v[0] = x.x;
+            v[1] = x.y;
+        } else {
+            const float4 x = *reinterpret_cast<const float4 *>(acc + (size_t)c * cstride_acc);
+            v[0] = x.x;
+            v[1] = x.y;
+            v[2] = x.z;
+            v[3] = x.w;
+        }
+    };
     int c = wave;
     for (; c + 12 < n_live; c += 16) {  // four loads in flight per lane
-        const float2 v0 = *reinterpret_cast<const float2 *>(acc + (size_t)c * cstride_acc);
-        const float2 v1 = *reinterpret_cast<const float2 *>(acc + (size_t)(c + 4) * cstride_acc);
-        const float2 v2 = *reinterpret_cast<const float2 *>(acc + (size_t)(c + 8) * cstride_acc);
-        const float2 v3 = *reinterpret_cast<const float2 *>(acc + (size_t)(c + 12) * cstride_acc);
-        a0 = fmaf(wts[c], v0.x, a0);
-        a1 = fmaf(wts[c], v0.y, a1);
-        a0 = fmaf(wts[c + 4], v1.x, a0);
-        a1 = fmaf(wts[c + 4], v1.y, a1);
-        a0 = fmaf(wts[c + 8], v2.x, a0);
-        a1 = fmaf(wts[c + 8], v2.y, a1);
-        a0 = fmaf(wts[c + 12], v3.x, a0);
-        a1 = fmaf(wts[c + 12], v3.y, a1);
+        float v[4][NV];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) ld(c + 4 * u, v[u]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int k = 0; k < NV; ++k) a[k] = fmaf(wts[c + 4 * u], v[u][k], a[k]);
     }
     for (; c < n_live; c += 4) {
-        const float2 v = *reinterpret_cast<const float2 *>(acc + (size_t)c * cstride_acc);
-        a0 = fmaf(wts[c], v.x, a0);
-        a1 = fmaf(wts[c], v.y, a1);
+        float v[NV];
+        ld(c, v);
+#pragma unroll
+        for (int k = 0; k < NV; ++k) a[k] = fmaf(wts[c], v[k], a[k]);
     }
-    red[wave][2 * lane] = a0;
-    red[wave][2 * lane + 1] = a1;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) red[wave][NV * lane + k] = a[k];
     __syncthreads();
     if (wave == 0) {
-        const float s0 = (red[0][2 * lane] + red[1][2 * lane]) + (red[2][2 * lane] + red[3][2 * lane]);
-        const float s1 =
-            (red[0][2 * lane + 1] + red[1][2 * lane + 1]) + (red[2][2 * lane + 1] + red[3][2 * lane + 1]);
-        *o = (uint32_t)round16<F16>(s0 / L) | ((uint32_t)round16<F16>(s1 / L) << 16);
+        float o[NV];
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int d = NV * lane + k;
+            o[k] = ((red[0][d] + red[1][d]) + (red[2][d] + red[3][d])) / L;
+        }
+        store_out<F16, NV>(p, out, o_off, o);
     }
 }
 
 hipError_t launch_attn_combine(const AttnParams &p, bool fp16, void *out, hipStream_t s) {
     const int grid = p.batch * p.n_kv_heads * p.rows;
-    if (fp16)
-        hipLaunchKernelGGL(attn_combine_kernel<true>, dim3(grid), dim3(kCombineThreads), 0, s, p,
-                           (uint16_t *)out);
-    else
-        hipLaunchKernelGGL(attn_combine_kernel<false>, dim3(grid), dim3(kCombineThreads), 0, s, p,
-                           (uint16_t *)out);
+    uint16_t *o = (uint16_t *)out;
+    if (p.head_dim == 256) {
+        if (fp16)
+            hipLaunchKernelGGL((attn_combine_kernel<true, 256>), dim3(grid), dim3(kCombineThreads), 0, s, p, o);
+        else
+            hipLaunchKernelGGL((attn_combine_kernel<false, 256>), dim3(grid), dim3(kCombineThreads), 0, s, p, o);
+    } else {
+        if (fp16)
+            hipLaunchKernelGGL((attn_combine_kernel<true, 128>), dim3(grid), dim3(kCombineThreads), 0, s, p, o);
+        else
+            hipLaunchKernelGGL((attn_combine_kernel<false, 128>), dim3(grid), dim3(kCombineThreads), 0, s, p, o);
+    }
     return hipGetLastError();
 }
 

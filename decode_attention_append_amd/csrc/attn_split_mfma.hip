@@ -62,6 +62,19 @@ constexpr int kObufStride = kHeadDim + 4;
 // P V product consumes them: keys 4q..4q+3, then 16+4q..16+4q+3.
 __device__ __forceinline__ int pv_key(int q, int u) { return (u < 4 ? 4 * q + u : 16 + 4 * q + (u - 4)); }
 
+// Rotary embedding of one row held as this lane's four 16-byte pieces, dims
+// 8q + 32s .. +7 (s = 0..3): with the first R dims rotating (pairs j, j + R/2),
+// piece s < R/64 pairs with piece s + R/64 of the same lane.
+template <bool F16>
+__device__ __forceinline__ void rope_pieces(u32x4_t (&x)[4], int R, int pos, const float *freqs, int q) {
+    if (R == 128) {
+        rope8<F16>(x[0], x[2], pos, freqs, 8 * q);
+        rope8<F16>(x[1], x[3], pos, freqs, 32 + 8 * q);
+    } else {  // R == 64
+        rope8<F16>(x[0], x[1], pos, freqs, 8 * q);
+    }
+}
+
 struct Tile {
     u32x4_t k[2][4];  // K: key block kb (16 keys), k-step s (32 dims)
     u32x4_t v[8];     // V: slot u, dims 8i .. 8i+7
@@ -117,6 +130,7 @@ struct RowSource {
     int new_first;
     int t0;             // absolute position of local key 0
     const float *rope;  // rotary table: new K rows are rotated at t0 + key first
+    int rope_dim;
     bool store;
 };
 
@@ -130,10 +144,7 @@ __device__ __forceinline__ void load_rows(Tile &t, const CacheView &cv, int tb, 
                                                 : cv.k + cv.row(key) + 16 * q;
 #pragma unroll
         for (int s = 0; s < 4; ++s) t.k[kblk][s] = ld16(kr + 64 * s);
-        if (rs.rope && key >= rs.new_first) {
-            rope8<F16>(t.k[kblk][0], t.k[kblk][2], rs.t0 + key, rs.rope, 8 * q);
-            rope8<F16>(t.k[kblk][1], t.k[kblk][3], rs.t0 + key, rs.rope, 32 + 8 * q);
-        }
+        if (rs.rope && key >= rs.new_first) rope_pieces<F16>(t.k[kblk], rs.rope_dim, rs.t0 + key, rs.rope, q);
         if (rs.store && key >= rs.new_first && tb + 16 * kblk + l16 <= last && cv.writable(key)) {
             uint8_t *kw = cv.kw + cv.row(key) + 16 * q;
 #pragma unroll
@@ -198,12 +209,7 @@ void attn_split_mfma_kernel(AttnParams p) {
                 p.q + (((size_t)b * p.q_len + i) * p.n_q_heads + (size_t)h * p.group + g) * kRowBytes + 16 * q;
 #pragma unroll
             for (int s = 0; s < 4; ++s) qop[rb][s] = ld16(qp + 64 * s);
-            if (p.rope_freqs) {
-                // rotary embedding at seq_pos + i: this lane holds dims 8q + 32s .. +7,
-                // so pieces s and s + 2 are the two halves of the same pairs
-                rope8<F16>(qop[rb][0], qop[rb][2], sp + i, p.rope_freqs, 8 * q);
-                rope8<F16>(qop[rb][1], qop[rb][3], sp + i, p.rope_freqs, 32 + 8 * q);
-            }
+            if (p.rope_freqs) rope_pieces<F16>(qop[rb], p.rope_dim, sp + i, p.rope_freqs, q);
             vis[rb] = min(sp + i + 1 - t0, n_tok);
         } else {
 #pragma unroll
@@ -305,6 +311,7 @@ void attn_split_mfma_kernel(AttnParams p) {
     rs.new_first = p.k_new ? sp - t0 : n_tok;
     rs.t0 = t0;
     rs.rope = p.k_new ? p.rope_freqs : nullptr;
+    rs.rope_dim = p.rope_dim;
     rs.store = p.k_new != nullptr && rg == 0;
     rs.stride = (size_t)p.n_kv_heads * kRowBytes;
     if (p.k_new) {
@@ -372,7 +379,7 @@ void attn_split_mfma_kernel(AttnParams p) {
     // One-launch step: the wave whose partial arrives last for (b, h) merges all
     // its rows and resets the arrival counter for the next call.
     if (p.counters && last_arrival(&p.counters[bh], sc.n * RG, lane)) {
-        for (int r = 0; r < p.rows; ++r) merge_row_wave<F16>(p, p.out, bh, b, h, r, sc.n, lane);
+        for (int r = 0; r < p.rows; ++r) merge_row_wave<F16, kHeadDim>(p, p.out, bh, b, h, r, sc.n, lane);
         if (lane == 0) p.counters[bh] = 0;
     }
 }

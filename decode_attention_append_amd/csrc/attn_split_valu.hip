@@ -37,15 +37,15 @@ template <bool F16>
 __device__ void merge_rows_block(const AttnParams &p, float *red, int bh, int b, int h, int n, int tid) {
     const int lane = tid & 63, wave = tid >> 6;
     if (n <= 16 || p.rows >= 4) {
-        for (int r = wave; r < p.rows; r += 4) merge_row_wave<F16>(p, p.out, bh, b, h, r, n, lane);
+        for (int r = wave; r < p.rows; r += 4) merge_row_wave<F16, kHeadDim>(p, p.out, bh, b, h, r, n, lane);
         return;
     }
     float *wm = red + 4 * kHeadDim, *wl = wm + 4;
     const int c_lo = wave * n / 4, c_hi = (wave + 1) * n / 4;
     for (int r = 0; r < p.rows; ++r) {
-        const MergeState s = merge_range(p, (size_t)bh * p.n_chunks * p.rows + r, c_lo, c_hi, lane);
-        red[wave * kHeadDim + 2 * lane] = s.a0;
-        red[wave * kHeadDim + 2 * lane + 1] = s.a1;
+        const MergeState<kHeadDim> s = merge_range<kHeadDim>(p, (size_t)bh * p.n_chunks * p.rows + r, c_lo, c_hi, lane);
+        red[wave * kHeadDim + 2 * lane] = s.a[0];
+        red[wave * kHeadDim + 2 * lane + 1] = s.a[1];
         if (lane == 0) {
             wm[wave] = s.m;
             wl[wave] = s.l;
@@ -65,8 +65,7 @@ __device__ void merge_rows_block(const AttnParams &p, float *red, int bh, int b,
                         (f[2] * red[2 * kHeadDim + d] + f[3] * red[3 * kHeadDim + d])) /
                        L;
             }
-            out_row_words(p, p.out, b, h, r)[lane] =
-                (uint32_t)round16<F16>(o[0]) | ((uint32_t)round16<F16>(o[1]) << 16);
+            store_out<F16, 2>(p, p.out, out_row_off(p, b, h, r) + 2 * lane, o);
         }
         __syncthreads();
     }
@@ -140,7 +139,7 @@ __global__ __launch_bounds__(256) void attn_split_valu_kernel(AttnParams p) {
 #pragma unroll
         for (int r = 0; r < RP; ++r) {
             u32x4_t v = {qr[r][0], qr[r][1], qr[r][2], qr[r][3]};
-            rope_row16<F16>(v, cq, sp + r / p.group, p.rope_freqs, r < p.rows);
+            rope_row<F16>(v, cq, p.rope_dim, sp + r / p.group, p.rope_freqs, r < p.rows);
             qr[r][0] = v[0];
             qr[r][1] = v[1];
             qr[r][2] = v[2];
@@ -194,7 +193,7 @@ __global__ __launch_bounds__(256) void attn_split_valu_kernel(AttnParams p) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int t = min(s_ * 16 + u * 4 + gq, last);
-                rope_row16<F16>(buf[u], cq, t0 + t, p.rope_freqs, t >= new_first);
+                rope_row<F16>(buf[u], cq, p.rope_dim, t0 + t, p.rope_freqs, t >= new_first);
             }
         }
         if (fused_append) {

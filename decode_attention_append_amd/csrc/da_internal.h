@@ -9,8 +9,9 @@
 
 namespace da {
 
-constexpr int kHeadDim = 128;     // the only head_dim implemented
+constexpr int kHeadDim = 128;     // head_dim of the vector-ALU kernel and the 128 MFMA kernel
 constexpr int kRowBytes = kHeadDim * 2;
+constexpr int kMaxHeadDim = 256;  // the MFMA kernel also takes 256
 constexpr int kMaxRows = 32;      // (Hq/Hkv) * q_len limit
 constexpr int kMaxQLen = 8;
 constexpr int kTokenTile = 64;    // chunk sizes are multiples of this
@@ -24,6 +25,7 @@ constexpr int kMaxChunk = 2048;
 struct KvLayout {
     const int32_t *block_table;  // [B][pages_per_seq], null for the contiguous layout
     int32_t pages_per_seq, n_pages;
+    int32_t row_bytes;           // head_dim * 2
 };
 
 constexpr int kPageTokens = 16;
@@ -42,12 +44,12 @@ __device__ __forceinline__ int kv_page(const KvLayout &L, int b, int lp) {
 __device__ __forceinline__ size_t kv_block_off(const KvLayout &L, int b, int h, int n_kv_heads, int max_seq,
                                                int lp) {
     if (!L.block_table)
-        return (((size_t)b * n_kv_heads + h) * max_seq + (size_t)lp * kPageTokens) * kRowBytes;
+        return (((size_t)b * n_kv_heads + h) * max_seq + (size_t)lp * kPageTokens) * L.row_bytes;
     const int pg = kv_page(L, b, lp);
-    return ((size_t)(pg < 0 ? 0 : pg) * n_kv_heads + h) * kPageTokens * kRowBytes;
+    return ((size_t)(pg < 0 ? 0 : pg) * n_kv_heads + h) * kPageTokens * L.row_bytes;
 }
 __device__ __forceinline__ size_t kv_row_off(const KvLayout &L, int b, int h, int n_kv_heads, int max_seq, int t) {
-    return kv_block_off(L, b, h, n_kv_heads, max_seq, t / kPageTokens) + (size_t)(t % kPageTokens) * kRowBytes;
+    return kv_block_off(L, b, h, n_kv_heads, max_seq, t / kPageTokens) + (size_t)(t % kPageTokens) * L.row_bytes;
 }
 __device__ __forceinline__ bool kv_row_writable(const KvLayout &L, int b, int t) {
     return !L.block_table || kv_page(L, b, t / kPageTokens) >= 0;
@@ -61,9 +63,10 @@ struct AppendParams {
     const uint8_t *k_new;
     const uint8_t *v_new;
     const int32_t *seq_pos;
-    const float *rope_freqs;   // D/2 rotary frequencies, or null: k_new is copied as is
+    const float *rope_freqs;   // rope_dim/2 rotary frequencies, or null: k_new is copied as is
     KvLayout layout;
     int32_t batch, q_len, n_kv_heads, max_seq;
+    int32_t head_dim, rope_dim;
 };
 
 struct AttnParams {
@@ -71,9 +74,10 @@ struct AttnParams {
     const uint8_t *k_cache;
     const uint8_t *v_cache;
     const int32_t *seq_pos;
-    float *ws_acc;  // [B*Hkv][n_chunks][rows][D] unnormalised weighted V sums
+    float *ws_acc;  // [B*Hkv][n_chunks][rows][head_dim] unnormalised weighted V sums
     float *ws_ml;   // [B*Hkv][n_chunks][rows][2]  (running max in log2 units, sum)
     int32_t batch, q_len, n_q_heads, n_kv_heads, max_seq;
+    int32_t head_dim;  // 128 or 256 (256: MFMA kernel only)
     int32_t group;  // Hq / Hkv
     int32_t rows;   // group * q_len
     int32_t n_chunks;      // chunk slots per (sequence, KV head) in the workspace
@@ -82,9 +86,11 @@ struct AttnParams {
     int32_t min_chunk;     // balanced: smallest chunk (multiple of 32)
     int32_t max_chunk;     // largest chunk the kernel accepts (multiple of 32)
     float scale_log2;      // softmax scale * log2(e): scores are kept in log2 units
-    const float *rope_freqs;  // D/2 rotary frequencies, or null: q (and fused-appended
+    const float *rope_freqs;  // rope_dim/2 rotary frequencies, or null: q (and fused-appended
                               //   k_new rows) are used as given
+    int32_t rope_dim;         // rotated dims (the first rope_dim of each row)
     KvLayout layout;          // contiguous or paged caches
+    const uint16_t *out_gate; // [B][q_len][Hq][D] sigmoid output gate, or null
     int32_t seq_chunk_cap; // balanced: at most this many chunks per sequence unless its
                            //   length needs more of max_chunk keys (0: no cap)
 
@@ -173,8 +179,8 @@ __host__ __device__ inline bool locate(const AttnParams &p, int &w, int &b, int 
 }
 
 // Workspace carving, shared by the attention and the combine.
-inline size_t ws_acc_floats(int32_t bh, int32_t n_chunks, int32_t rows) {
-    return (size_t)bh * n_chunks * rows * kHeadDim;
+inline size_t ws_acc_floats(int32_t bh, int32_t n_chunks, int32_t rows, int32_t head_dim) {
+    return (size_t)bh * n_chunks * rows * head_dim;
 }
 inline size_t ws_ml_floats(int32_t bh, int32_t n_chunks, int32_t rows) {
     return (size_t)bh * n_chunks * rows * 2;
@@ -289,19 +295,22 @@ __device__ __forceinline__ void rope8(u32x4_t &lo, u32x4_t &hi, int pos, const f
     }
 }
 
-// The same when sixteen lanes hold one row, 16 bytes (dims 8c .. 8c+7) each:
-// lane c pairs with lane c ^ 8 of its group.  Every lane of the wave must call
-// it (it shuffles); `apply` says whether this lane's piece is rotated.
+// The same when consecutive lanes hold one row, 16 bytes (dims 8c .. 8c+7) each,
+// and the first R dims rotate (R = 64, 128 or 256): piece c < R/8 pairs with
+// piece c ^ (R/16), which is lane c ^ (R/16) of the row's lanes.  Every lane of
+// the wave must call it (it shuffles); `apply` says whether this lane's piece
+// is rotated.
 template <bool F16>
-__device__ __forceinline__ void rope_row16(u32x4_t &piece, int c, int pos, const float *freqs, bool apply) {
+__device__ __forceinline__ void rope_row(u32x4_t &piece, int c, int R, int pos, const float *freqs, bool apply) {
+    const int hl = R / 16;
     u32x4_t other;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) other[w] = (uint32_t)__shfl_xor((int)piece[w], 8);
-    if (!apply) return;
-    if (c < 8) {
+    for (int w = 0; w < 4; ++w) other[w] = (uint32_t)__shfl_xor((int)piece[w], hl);
+    if (!apply || c >= R / 8) return;
+    if (c < hl) {
         rope8<F16>(piece, other, pos, freqs, 8 * c);
     } else {
-        rope8<F16>(other, piece, pos, freqs, 8 * (c - 8));
+        rope8<F16>(other, piece, pos, freqs, 8 * (c - hl));
     }
 }
 
@@ -375,16 +384,32 @@ __device__ inline bool last_arrival(int32_t *counter, int arrivals, int lane) {
 }
 
 // Log-sum-exp merge state of one query row over some chunks: running maximum m
-// (log2 units), sum l = sum_c 2^(m_c - m) l_c and this lane's two dims of
+// (log2 units), sum l = sum_c 2^(m_c - m) l_c and this lane's D/64 dims of
 // sum_c 2^(m_c - m) acc_c.
+template <int D>
 struct MergeState {
-    float m, l, a0, a1;
+    static constexpr int NV = D / 64;
+    float m, l, a[NV];
 };
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
+template <int NV>
+__device__ __forceinline__ void buffer_load_dims(float (&out)[NV], __amdgpu_buffer_rsrc_t r, int voff, uint32_t soff) {
+    constexpr int kDevScope = 16;  // cache policy of the buffer loads: device scope
+    if constexpr (NV == 2) {
+        const f32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kDevScope);
+        out[0] = x.x;
+        out[1] = x.y;
+    } else {
+        const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kDevScope);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) out[k] = __uint_as_float(x[k]);
+    }
+}
+
 // Merge of chunks [c_lo, c_hi) of partial row `part` (= (b * Hkv + h) *
-// n_chunks * rows + r) by one wave; lane j takes dims 2j and 2j + 1.
+// n_chunks * rows + r) by one wave; lane j takes dims NV*j .. NV*j + NV-1.
 //  - Per group of up to 64 chunks, lane k loads chunk k's (m, l): one
 //    wave-wide max and sum give the group's weights w_k = 2^(m_k - M) and
 //    sum of w_k l_k at once.
@@ -394,16 +419,20 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 //    while (m, l) are reduced.  Each is weighted by w_k, read from lane k.
 // A chunk the row saw no key of (m_k = -inf) has weight 0.  Every load is
 // device-scope (the partials may come from other XCDs in the same launch).
-__device__ inline MergeState merge_range(const AttnParams &p, size_t part, int c_lo, int c_hi, int lane) {
+template <int D>
+__device__ inline MergeState<D> merge_range(const AttnParams &p, size_t part, int c_lo, int c_hi, int lane) {
+    constexpr int NV = D / 64;
     const float *ml = p.ws_ml + part * 2;
-    const uint32_t cs_ml = (uint32_t)p.rows * 2;             // floats between chunks
-    const uint32_t cs_acc = (uint32_t)p.rows * kHeadDim * 4;  // bytes between chunks
+    const uint32_t cs_ml = (uint32_t)p.rows * 2;      // floats between chunks
+    const uint32_t cs_acc = (uint32_t)p.rows * D * 4;  // bytes between chunks
     const __amdgpu_buffer_rsrc_t acc =
-        __builtin_amdgcn_make_buffer_rsrc(p.ws_acc + part * kHeadDim, 0, (int)(cs_acc * (uint32_t)p.n_chunks),
-                                          0x00020000);
-    constexpr int kDevScope = 16;  // cache policy of the buffer loads: device scope
-    const int voff = lane * 8;
-    MergeState s{-INFINITY, 0.f, 0.f, 0.f};
+        __builtin_amdgcn_make_buffer_rsrc(p.ws_acc + part * D, 0, (int)(cs_acc * (uint32_t)p.n_chunks), 0x00020000);
+    const int voff = lane * NV * 4;
+    MergeState<D> s;
+    s.m = -INFINITY;
+    s.l = 0.f;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) s.a[k] = 0.f;
     for (int g = c_lo; g < c_hi; g += 64) {
         const int cnt = min(64, c_hi - g);
         float m = -INFINITY, l = 0.f;
@@ -411,12 +440,17 @@ __device__ inline MergeState merge_range(const AttnParams &p, size_t part, int c
             m = ld_dev(ml + (size_t)(g + lane) * cs_ml);
             l = ld_dev(ml + (size_t)(g + lane) * cs_ml + 1);
         }
-        f32x2_t v[16];
+        float v[16][NV];
         auto load_batch = [&](int j) {
 #pragma unroll
-            for (int u = 0; u < 16; ++u)
-                v[u] = j + u < cnt ? __builtin_amdgcn_raw_buffer_load_b64(acc, voff, (g + j + u) * cs_acc, kDevScope)
-                                   : f32x2_t{0.f, 0.f};
+            for (int u = 0; u < 16; ++u) {
+                if (j + u < cnt) {
+                    buffer_load_dims<NV>(v[u], acc, voff, (g + j + u) * cs_acc);
+                } else {
+#pragma unroll
+                    for (int k = 0; k < NV; ++k) v[u][k] = 0.f;
+                }
+            }
         };
         load_batch(0);
         const float M = fmaxf(s.m, wave_max(m));
@@ -424,16 +458,16 @@ __device__ inline MergeState merge_range(const AttnParams &p, size_t part, int c
         const float f = s.m == -INFINITY ? 0.f : exp2_fast(s.m - M);
         const float w = m == -INFINITY ? 0.f : exp2_fast(m - M);
         s.l = fmaf(s.l, f, wave_sum(w * l));
-        s.a0 *= f;
-        s.a1 *= f;
+#pragma unroll
+        for (int k = 0; k < NV; ++k) s.a[k] *= f;
         s.m = M;
         for (int j = 0;;) {
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
                 if (j + u < cnt) {
                     const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j + u));
-                    s.a0 = fmaf(wu, v[u].x, s.a0);
-                    s.a1 = fmaf(wu, v[u].y, s.a1);
+#pragma unroll
+                    for (int k = 0; k < NV; ++k) s.a[k] = fmaf(wu, v[u][k], s.a[k]);
                 }
             }
             j += 16;
@@ -444,22 +478,49 @@ __device__ inline MergeState merge_range(const AttnParams &p, size_t part, int c
     return s;
 }
 
-// Output row r of (b, h) as 32-bit words (two 16-bit elements each).
-__device__ __forceinline__ uint32_t *out_row_words(const AttnParams &p, uint16_t *out, int b, int h, int r) {
+// Element offset of output row r of (b, h) (query token i, query head h*G + g).
+__device__ __forceinline__ size_t out_row_off(const AttnParams &p, int b, int h, int r) {
     const int i = r / p.group, g = r - i * p.group;
-    return reinterpret_cast<uint32_t *>(out +
-                                        (((size_t)b * p.q_len + i) * p.n_q_heads + (size_t)h * p.group + g) * kHeadDim);
+    return (((size_t)b * p.q_len + i) * p.n_q_heads + (size_t)h * p.group + g) * p.head_dim;
+}
+
+// sigmoid(g) of a 16-bit gate element, fp32: 1 / (1 + 2^(-g log2 e)).
+template <bool F16>
+__device__ __forceinline__ float sigmoid16(uint16_t g) {
+    float x, unused;
+    unpack2<F16>((uint32_t)g, x, unused);
+    return 1.f / (1.f + exp2_fast(-x * 1.4426950408889634f));
+}
+
+// Stores NV consecutive output values at element offset `off`, times the
+// sigmoid output gate when the problem has one ("Architecture Diagram -
+// Qwen3.5-35B-A3B", full-SDPA layers), rounded to nearest even.
+template <bool F16, int NV>
+__device__ __forceinline__ void store_out(const AttnParams &p, uint16_t *out, size_t off, const float (&x)[NV]) {
+    float y[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) y[k] = x[k];
+    if (p.out_gate) {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) y[k] *= sigmoid16<F16>(p.out_gate[off + k]);
+    }
+    uint32_t *o = reinterpret_cast<uint32_t *>(out + off);
+#pragma unroll
+    for (int k = 0; k < NV; k += 2) o[k / 2] = (uint32_t)round16<F16>(y[k]) | ((uint32_t)round16<F16>(y[k + 1]) << 16);
 }
 
 // Merge of query row r of (b, h) over its n chunks by one wave, written to out:
 //     out = (sum_c 2^(m_c - M) acc_c) / (sum_c 2^(m_c - M) l_c),  M = max_c m_c,
-// rounded to nearest even.
-template <bool F16>
+// (times the output gate), rounded to nearest even.
+template <bool F16, int D>
 __device__ inline void merge_row_wave(const AttnParams &p, uint16_t *out, int bh, int b, int h, int r, int n,
                                       int lane) {
-    const MergeState s = merge_range(p, (size_t)bh * p.n_chunks * p.rows + r, 0, n, lane);
-    out_row_words(p, out, b, h, r)[lane] =
-        (uint32_t)round16<F16>(s.a0 / s.l) | ((uint32_t)round16<F16>(s.a1 / s.l) << 16);
+    constexpr int NV = D / 64;
+    const MergeState<D> s = merge_range<D>(p, (size_t)bh * p.n_chunks * p.rows + r, 0, n, lane);
+    float x[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) x[k] = s.a[k] / s.l;
+    store_out<F16, NV>(p, out, out_row_off(p, b, h, r) + NV * lane, x);
 }
 
 // One-launch step: the output rows of sequence b, whose seq_pos breaks the
@@ -468,8 +529,8 @@ __device__ inline void merge_row_wave(const AttnParams &p, uint16_t *out, int bh
 template <bool F16>
 __device__ inline void flag_sequence_nan(const AttnParams &p, int b, int lane, int n_lanes) {
     const uint32_t nan16 = F16 ? 0x7e00u : 0x7fc0u;
-    uint32_t *o = reinterpret_cast<uint32_t *>(p.out + (size_t)b * p.q_len * p.n_q_heads * kHeadDim);
-    const int words = p.q_len * p.n_q_heads * (kHeadDim / 2);
+    uint32_t *o = reinterpret_cast<uint32_t *>(p.out + (size_t)b * p.q_len * p.n_q_heads * p.head_dim);
+    const int words = p.q_len * p.n_q_heads * (p.head_dim / 2);
     for (int x = lane; x < words; x += n_lanes) o[x] = nan16 | (nan16 << 16);
 }
 

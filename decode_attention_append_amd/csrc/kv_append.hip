@@ -4,8 +4,8 @@
 // Patterns, "KV Cache Update (EP rewrite: tensor.insert_slice)"; fix A5).
 //
 // One lane moves 16 bytes of K and 16 bytes of V: sixteen lanes cover one
-// 128-dim row, a wave covers four rows with fully coalesced 128-bit loads and
-// stores.  Without a rotary table it is a pure bit copy: no arithmetic touches
+// 128-dim row (32 a 256-dim row), a wave covers four (two) rows with fully
+// coalesced 128-bit loads and stores.  Without a rotary table it is a pure bit copy: no arithmetic touches
 // the data.  With one, each K row is rotated at its position seq_pos + i first
 // (the RoPE block of the same page; lanes c and c ^ 8 of a row hold the two
 // halves of each rotated pair and swap them with one shuffle).  In a paged
@@ -17,8 +17,9 @@ namespace da {
 template <bool F16>
 __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p, int threads_total) {
     const int t = blockIdx.x * blockDim.x + threadIdx.x;
-    const int piece = t & 15;         // 16-byte piece of the 256-byte row
-    const int row = t >> 4;           // (b, i, h) in k_new's [B][q_len][Hkv] order
+    const int lpr = p.head_dim / 8;   // lanes per row: 16 (head_dim 128) or 32 (256)
+    const int piece = t % lpr;        // 16-byte piece of the row
+    const int row = t / lpr;          // (b, i, h) in k_new's [B][q_len][Hkv] order
     const int h = row % p.n_kv_heads;
     const int i = (row / p.n_kv_heads) % p.q_len;
     const int b = min(row / (p.n_kv_heads * p.q_len), p.batch - 1);
@@ -27,9 +28,9 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p, int thre
     // belong to the same row, so they agree)
     const bool ok = t < threads_total && sp >= 0 && sp <= p.max_seq - p.q_len &&
                     kv_row_writable(p.layout, b, sp + i);
-    const size_t src = (size_t)min(row, threads_total / 16 - 1) * kRowBytes + piece * 16;
+    const size_t src = (size_t)min(row, threads_total / lpr - 1) * (p.head_dim * 2) + piece * 16;
     u32x4_t k = ld16(p.k_new + src);
-    if (p.rope_freqs) rope_row16<F16>(k, piece, sp + i, p.rope_freqs, ok);
+    if (p.rope_freqs) rope_row<F16>(k, piece, p.rope_dim, sp + i, p.rope_freqs, ok);
     if (!ok) return;
     const size_t dst = kv_row_off(p.layout, b, h, p.n_kv_heads, p.max_seq, sp + i) + piece * 16;
     const u32x4_t v = ld16(p.v_new + src);

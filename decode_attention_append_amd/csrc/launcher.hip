@@ -39,7 +39,13 @@ da_status check_problem(const da_problem *p) {
         if (p->page_size != kPageTokens) return DA_ERR_UNSUPPORTED;
     }
     if (p->dtype != DA_BF16 && p->dtype != DA_FP16) return DA_ERR_UNSUPPORTED;
-    if (p->head_dim != kHeadDim) return DA_ERR_UNSUPPORTED;
+    if (p->head_dim != kHeadDim && p->head_dim != kMaxHeadDim) return DA_ERR_UNSUPPORTED;
+    // head_dim 256 runs on the MFMA kernel only
+    if (p->head_dim != kHeadDim && p->variant == DA_VARIANT_VALU + 1) return DA_ERR_UNSUPPORTED;
+    if (p->rope_dim != 0 && (p->rope_dim > p->head_dim ||
+                             (p->rope_dim != 64 && p->rope_dim != 128 && p->rope_dim != 256)))
+        return DA_ERR_UNSUPPORTED;
+    if (p->out_gate && !aligned16(p->out_gate)) return DA_ERR_INVALID_ARG;
     if (p->q_len > kMaxQLen) return DA_ERR_UNSUPPORTED;
     if ((int64_t)(p->n_q_heads / p->n_kv_heads) * p->q_len > kMaxRows) return DA_ERR_UNSUPPORTED;
     if (p->max_seq > kMaxSeq) return DA_ERR_UNSUPPORTED;
@@ -104,7 +110,8 @@ bool one_launch_capable(int variant, int rows) { return variant == DA_VARIANT_MF
 
 void plan_of(const da_problem *p, da_plan *pl) {
     const int rows = (p->n_q_heads / p->n_kv_heads) * p->q_len;
-    const int variant = p->variant ? p->variant - 1 : (rows >= kMfmaRows ? DA_VARIANT_MFMA : DA_VARIANT_VALU);
+    const int variant = p->variant ? p->variant - 1
+                                   : (rows >= kMfmaRows || p->head_dim != kHeadDim ? DA_VARIANT_MFMA : DA_VARIANT_VALU);
     const int units = p->batch * p->n_kv_heads;
     pl->rows = rows;
     pl->variant = variant;
@@ -143,7 +150,7 @@ void plan_of(const da_problem *p, da_plan *pl) {
     pl->fused_combine = one_launch_capable(variant, rows) &&
                         nb_max * rows <= (variant == DA_VARIANT_MFMA ? kFusedMergeRowsWave : kFusedMergeRowsBlock);
     const int32_t bh = units;
-    pl->workspace_bytes = align256(ws_acc_floats(bh, pl->n_chunks, rows) * sizeof(float)) +
+    pl->workspace_bytes = align256(ws_acc_floats(bh, pl->n_chunks, rows, p->head_dim) * sizeof(float)) +
                           align256(ws_ml_floats(bh, pl->n_chunks, rows) * sizeof(float)) +
                           (size_t)bh * sizeof(int32_t);
 }
@@ -151,12 +158,14 @@ void plan_of(const da_problem *p, da_plan *pl) {
 // Arrival counters of the one-launch step: int32 [B * Hkv] after the partials.
 int32_t *counters_of(const da_problem *p, const da_plan &pl, void *workspace) {
     const int32_t bh = p->batch * p->n_kv_heads;
-    return (int32_t *)((uint8_t *)workspace + align256(ws_acc_floats(bh, pl.n_chunks, pl.rows) * sizeof(float)) +
+    return (int32_t *)((uint8_t *)workspace +
+                       align256(ws_acc_floats(bh, pl.n_chunks, pl.rows, p->head_dim) * sizeof(float)) +
                        align256(ws_ml_floats(bh, pl.n_chunks, pl.rows) * sizeof(float)));
 }
 
 KvLayout layout_of(const da_problem *p) {
     KvLayout L;
+    L.row_bytes = p->head_dim * 2;
     L.block_table = p->page_size ? p->block_table : nullptr;
     L.pages_per_seq = p->page_size ? p->pages_per_seq : 0;
     L.n_pages = p->page_size ? p->n_pages : 0;
@@ -172,7 +181,8 @@ AttnParams attn_params(const da_problem *p, const da_plan &pl, const void *q, co
     a.seq_pos = seq_pos;
     const int32_t bh = p->batch * p->n_kv_heads;
     a.ws_acc = (float *)workspace;
-    a.ws_ml = (float *)((uint8_t *)workspace + align256(ws_acc_floats(bh, pl.n_chunks, pl.rows) * sizeof(float)));
+    a.ws_ml = (float *)((uint8_t *)workspace +
+                        align256(ws_acc_floats(bh, pl.n_chunks, pl.rows, p->head_dim) * sizeof(float)));
     a.batch = p->batch;
     a.q_len = p->q_len;
     a.n_q_heads = p->n_q_heads;
@@ -189,7 +199,10 @@ AttnParams attn_params(const da_problem *p, const da_plan &pl, const void *q, co
     a.scale_log2 = (float)(scale * 1.4426950408889634);  // log2(e)
     a.seq_chunk_cap = 0;
     a.rope_freqs = p->rope_freqs;
+    a.rope_dim = p->rope_dim ? p->rope_dim : p->head_dim;
     a.layout = layout_of(p);
+    a.head_dim = p->head_dim;
+    a.out_gate = (const uint16_t *)p->out_gate;
     a.k_cache_w = a.v_cache_w = nullptr;
     a.k_new = a.v_new = nullptr;
     a.counters = nullptr;
@@ -231,11 +244,13 @@ da_status da_kv_append(const da_problem *p, void *k_cache, void *v_cache, const 
     a.seq_pos = seq_pos;
     a.rope_freqs = p->rope_freqs;
     a.layout = layout_of(p);
+    a.head_dim = p->head_dim;
+    a.rope_dim = p->rope_dim ? p->rope_dim : p->head_dim;
     a.batch = p->batch;
     a.q_len = p->q_len;
     a.n_kv_heads = p->n_kv_heads;
     a.max_seq = p->max_seq;
-    const int threads = p->batch * p->q_len * p->n_kv_heads * 16;
+    const int threads = p->batch * p->q_len * p->n_kv_heads * (p->head_dim / 8);
     (void)hipGetLastError();  // launch errors below are ours alone
     return launch_kv_append(a, threads, p->dtype == DA_FP16, (hipStream_t)stream) == hipSuccess ? DA_OK
                                                                                                   : DA_ERR_HIP;
@@ -316,12 +331,14 @@ da_status da_decode_step(const da_problem *p, const void *q, void *k_cache, void
         ap.seq_pos = seq_pos;
         ap.rope_freqs = p->rope_freqs;
         ap.layout = layout_of(p);
+        ap.head_dim = p->head_dim;
+        ap.rope_dim = p->rope_dim ? p->rope_dim : p->head_dim;
         ap.batch = p->batch;
         ap.q_len = p->q_len;
         ap.n_kv_heads = p->n_kv_heads;
         ap.max_seq = p->max_seq;
         (void)hipGetLastError();
-        hipError_t e = launch_kv_append(ap, p->batch * p->q_len * p->n_kv_heads * 16, fp16, s);
+        hipError_t e = launch_kv_append(ap, p->batch * p->q_len * p->n_kv_heads * (p->head_dim / 8), fp16, s);
         if (e == hipSuccess) e = launch_attn_valu(a, pl.items, fp16, s);
         if (e == hipSuccess) e = launch_attn_combine(a, fp16, out, s);
         return e == hipSuccess ? DA_OK : DA_ERR_HIP;

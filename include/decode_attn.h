@@ -76,7 +76,7 @@ typedef struct {
     int32_t q_len;        /* new tokens per sequence this step, 1..8 (verify batches) */
     int32_t n_q_heads;    /* Hq >= 1                                              */
     int32_t n_kv_heads;   /* Hkv >= 1, Hq % Hkv == 0, (Hq / Hkv) * q_len <= 32    */
-    int32_t head_dim;     /* D; only 128 is implemented                           */
+    int32_t head_dim;     /* D: 128, or 256 (on the MFMA kernel)                  */
     int32_t max_seq;      /* allocated cache length (slots per KV head)           */
     int32_t dtype;        /* da_dtype of q, caches, new rows and out              */
     float scale;          /* softmax scale; <= 0 selects 1 / sqrt(head_dim)       */
@@ -116,6 +116,15 @@ typedef struct {
                              through them are dropped, so no kernel touches memory
                              outside the pools; that sequence's results are
                              unspecified.                                          */
+    int32_t rope_dim;     /* with rope_freqs: rotate only the first rope_dim dims of
+                             each q / k row (pairs j and j + rope_dim/2; the table
+                             holds rope_dim/2 values); 0 = head_dim.  64, 128 or 256
+                             ("Architecture Diagram - Qwen3.5-35B-A3B": partial
+                             RoPE over 25% of the 256 dims)                       */
+    const void *out_gate; /* DEVICE [B][q_len][Hq][head_dim] in p->dtype, 16-byte
+                             aligned, or NULL: the output is multiplied elementwise
+                             by sigmoid(gate) before rounding (the same diagram's
+                             full-SDPA layers: "Q(->8192)+gate", "sigmoid gate")   */
 } da_problem;
 
 /*
