@@ -61,11 +61,12 @@ def parse():
 
 def algorithmic_bytes(w, seq_pos):
     """Bytes the step must move at least, per layer: K+V of the visible context read once,
-    q read, out written, new K/V read and written into the cache."""
+    q read, out written (and the output gate read, when gated), new K/V read and written
+    into the cache."""
     E, D = 2, w.head_dim
     ctx = [int(s) + w.q_len for s in seq_pos]
     kv = 2 * w.n_kv_heads * sum(ctx) * D * E
-    q_out = 2 * w.batch * w.q_len * w.n_q_heads * D * E
+    q_out = (3 if w.gated else 2) * w.batch * w.q_len * w.n_q_heads * D * E
     append = 2 * 2 * w.batch * w.q_len * w.n_kv_heads * D * E
     return kv, kv + q_out + append
 
@@ -91,14 +92,15 @@ def counters_for(kernel_tag, workload):
 
 def cpu_baseline(w, layers_host_fn, n_layers, budget_s, freqs=None, block_table=None):
     """The oracle (append + attention, fp64, OpenMP; with the rotary embedding when a
-    table is given) on whole layers of the workload until about budget_s of CPU time is
-    spent; returns the record for the JSON line."""
+    table is given, the output gate when the workload has one) on whole layers of the
+    workload until about budget_s of CPU time is spent; returns the record for the JSON
+    line."""
     import numpy as np
     import oracle
     dt = oracle.FP16 if w.dtype == "fp16" else oracle.BF16
     done_bytes, spent, n = 0, 0.0, 0
     for layer in range(n_layers):
-        q, kc, vc, kn, vn, sp = layers_host_fn(layer)
+        q, kc, vc, kn, vn, sp, gate = layers_host_fn(layer)
         t = time.perf_counter()
         if freqs is not None:
             pos = sp[:, None, None] + np.arange(w.q_len, dtype=np.int32)[None, :, None]
@@ -109,7 +111,9 @@ def cpu_baseline(w, layers_host_fn, n_layers, budget_s, freqs=None, block_table=
         else:
             kp, vp = oracle.kv_append_paged(kc, vc, kn, vn, sp, block_table)
             k2, v2 = oracle.gather_paged(kp, block_table), oracle.gather_paged(vp, block_table)
-        oracle.gqa_decode(q, k2, v2, sp, dt)
+        out = oracle.gqa_decode(q, k2, v2, sp, dt)
+        if gate is not None:
+            oracle.output_gate(out, gate, dt)
         spent += time.perf_counter() - t
         done_bytes += algorithmic_bytes(w, sp)[1]
         n += 1
@@ -151,7 +155,9 @@ def main():
 
     layers = [make_layer(w, l, dev) for l in range(w.layers)]
     seq_pos = layers[0]["seq_pos"].cpu().numpy()
-    freqs = rope_freqs(w.head_dim, args.rope, dev) if args.rope > 0 else None
+    theta = args.rope if args.rope > 0 else w.rope_theta
+    rope_dim = w.rope_dim or w.head_dim
+    freqs = rope_freqs(rope_dim, theta, dev) if theta > 0 else None
     block_table, n_pages = None, 0
     if args.paged:
         # pages of every (sequence, KV head) cache, shuffled into one pool per layer and cache
@@ -168,8 +174,12 @@ def main():
                 L[key] = pages[inv.to(dev)].contiguous()  # pool page perm[j] holds page j
                 del c, pages
         torch.cuda.synchronize()
-    p = da.problem(w.batch, w.q_len, w.n_q_heads, w.n_kv_heads, w.head_dim, w.max_seq, w.dtype,
-                   chunk_tokens=args.chunk, rope_freqs=freqs, block_table=block_table, n_pages=n_pages)
+    # one problem per layer: a gated problem carries its layer's gate tensor
+    probs = [da.problem(w.batch, w.q_len, w.n_q_heads, w.n_kv_heads, w.head_dim, w.max_seq, w.dtype,
+                        chunk_tokens=args.chunk, rope_freqs=freqs, block_table=block_table, n_pages=n_pages,
+                        rope_dim=rope_dim if freqs is not None else 0, out_gate=L.get("out_gate"))
+             for L in layers]
+    p = probs[0]
     plan = da.plan_attention(p)
     ws = da.new_workspace(p)
     outs = [torch.empty_like(L["q"]) for L in layers]
@@ -180,6 +190,7 @@ def main():
 
     def step_separate(events=None):
         for l, L in enumerate(layers):
+            p = probs[l]
             da.kv_append(p, L["k_cache"], L["v_cache"], L["k_new"], L["v_new"], L["seq_pos"], launch_stream[0])
             if events is not None:
                 events[l][0].record(stream)
@@ -192,7 +203,7 @@ def main():
         for l, L in enumerate(layers):
             if events is not None:
                 events[l][0].record(stream)
-            da.decode_step(p, L["q"], L["k_cache"], L["v_cache"], L["k_new"], L["v_new"], L["seq_pos"], ws,
+            da.decode_step(probs[l], L["q"], L["k_cache"], L["v_cache"], L["k_new"], L["v_new"], L["seq_pos"], ws,
                            outs[l], launch_stream[0])
             if events is not None:
                 events[l][1].record(stream)
@@ -250,19 +261,25 @@ def main():
 
     # dominant kernel: the split-context attention.  Its algorithmic bytes per launch are the
     # K+V of the visible context (512 bytes per visible key per KV head) plus q; in the
-    # one-launch step also the new rows' cache writes and, with the merge fused, the output.
-    # (There the new rows are read once, from k_new, as part of the visible context.)
+    # one-launch step also the new rows' cache writes and, with the merge fused, the output
+    # (and the gate).  (There the new rows are read once, from k_new, as part of the visible
+    # context.)
     attn_avg_ms = float(np.mean(attn_ms))
     q_bytes = w.batch * w.q_len * w.n_q_heads * w.head_dim * 2
     attn_bytes = kv_bytes + q_bytes
-    kernel_tag = "attn_split_" + plan["variant"]
-    if args.path == "step":
-        attn_bytes += 2 * w.batch * w.q_len * w.n_kv_heads * w.head_dim * 2 + q_bytes
-        kernel_tag += "_step" if plan["fused_combine"] else "_step+attn_combine"
+    kernel = "attn_split_" + plan["variant"] + ("256" if w.head_dim == 256 else "")
     if args.paged:
-        kernel_tag = kernel_tag.replace("attn_split_" + plan["variant"], "attn_split_" + plan["variant"] + "_paged")
-    if args.rope > 0:
-        kernel_tag = kernel_tag.replace("attn_split_" + plan["variant"], "attn_split_" + plan["variant"] + "_rope")
+        kernel += "_paged"
+    if freqs is not None:
+        kernel += "_rope"
+    if w.gated:
+        kernel += "_gate"
+    kernel_tag = kernel
+    if args.path == "step":
+        attn_bytes += 2 * w.batch * w.q_len * w.n_kv_heads * w.head_dim * 2
+        if plan["fused_combine"]:
+            attn_bytes += q_bytes * (2 if w.gated else 1)
+        kernel_tag += "_step" if plan["fused_combine"] else "_step+attn_combine"
     attn_gbs = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
     traffic = counters_for(kernel_tag, w.name) if "+" not in kernel_tag else None
 
@@ -285,7 +302,9 @@ def main():
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "context": int(seq_pos.max()) + w.q_len,
                    "max_seq": w.max_seq, "layers": w.layers, "chunk_tokens": plan["chunk_tokens"],
                    "variant": plan["variant"], "path": args.path, "graph": args.graph,
-                   "rope_theta": args.rope if args.rope > 0 else None, "paged": args.paged,
+                   "rope_theta": theta if freqs is not None else None,
+                   "rope_dim": rope_dim if freqs is not None else None, "output_gate": w.gated,
+                   "paged": args.paged,
                    "fused_merge": bool(plan["fused_combine"]) and args.path == "step",
                    "bytes_per_step": step_bytes,
                    "cold_cache_flush": flush},
@@ -305,7 +324,8 @@ def main():
             def u16(t):
                 return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
             return (u16(L["q"]), u16(L["k_cache"]), u16(L["v_cache"]), u16(L["k_new"]),
-                    u16(L["v_new"]), L["seq_pos"].cpu().numpy())
+                    u16(L["v_new"]), L["seq_pos"].cpu().numpy(),
+                    u16(L["out_gate"]) if "out_gate" in L else None)
         rec["cpu_baseline"] = cpu_baseline(w, host_layer_fn, w.layers, args.cpu_seconds,
                                            None if freqs is None else freqs.cpu().numpy(),
                                            None if block_table is None else block_table.cpu().numpy())

@@ -80,27 +80,6 @@ struct Tile {
     u32x4_t v[8];     // V: slot u, dims 8i .. 8i+7
 };
 
-// The caches of one (sequence b, KV head h) seen from a chunk starting at key t0
-// (a multiple of 32): contiguous, or paged through the block table.  A 32-key
-// tile is two 16-token blocks, each one page of a paged cache.
-struct CacheView {
-    const uint8_t *k, *v;  // whole caches / pools
-    uint8_t *kw, *vw;      // the same, writable (one-launch step), or null
-    KvLayout L;
-    int b, h, n_kv_heads, max_seq, t0;
-    int pg_lane;  // paged: lane j holds the pool page of the chunk's block j (j < 64)
-    __device__ __forceinline__ size_t block(int j) const {  // 16-token block j of the chunk
-        if (!L.block_table || j >= 64) return kv_block_off(L, b, h, n_kv_heads, max_seq, t0 / kPageTokens + j);
-        int pg = __builtin_amdgcn_readlane(pg_lane, j);
-        pg = pg < 0 ? 0 : pg;  // outside the pool: read page 0
-        return ((size_t)pg * n_kv_heads + h) * kPageTokens * kRowBytes;
-    }
-    __device__ __forceinline__ size_t row(int key) const {
-        return kv_row_off(L, b, h, n_kv_heads, max_seq, t0 + key);
-    }
-    __device__ __forceinline__ bool writable(int key) const { return kv_row_writable(L, b, t0 + key); }
-};
-
 // A whole 32-key tile inside the chunk: two block bases, immediate offsets.
 __device__ __forceinline__ void load_full(Tile &t, const CacheView &cv, int tb, int l16, int q) {
     const size_t blk[2] = {cv.block(tb / kPageTokens), cv.block(tb / kPageTokens + 1)};
@@ -399,6 +378,7 @@ static hipError_t launch_dtype(const AttnParams &p, int items, hipStream_t s) {
 }
 
 hipError_t launch_attn_mfma(const AttnParams &p, int grid, bool fp16, hipStream_t s) {
+    if (p.head_dim != kHeadDim) return launch_attn_mfma256(p, grid, fp16, s);
     return fp16 ? launch_dtype<true>(p, grid, s) : launch_dtype<false>(p, grid, s);
 }
 

@@ -1,0 +1,359 @@
+// Split-context attention partials on the matrix cores for head_dim 256: the
+// full-SDPA layers of "Architecture Diagram - Qwen3.5-35B-A3B" on the "Qwen MoE
+// BringUp" page (GQA 16Q:2KV, head_dim 256; "Attention Computation" of the same
+// page for what is computed).  Same contract and output as the head_dim-128
+// kernel: per (sequence b, KV head h, chunk c) and query row r, the fp32
+// partial (m, l, acc[256]) with scores in log2 units.
+//
+// Mapping on gfx950 (wave64).  A 256-dim key row is twice the bytes of a
+// 128-dim one, so a tile holds 16 keys instead of 32 and the registers per tile
+// stay the same:
+//  - S^T = K q^T with v_mfma_f32_16x16x32: 16 keys x 16 query rows, eight
+//    k-steps of 32 dims.  Lane (row l16, group q) holds q[row][32s + 8q .. +7]
+//    for s = 0..7, and the key tile the same pieces of key l16.  The result
+//    gives lane (l16, q) the scores of keys 4q .. 4q+3 of row l16;
+//  - O^T += V^T P^T with v_mfma_f32_16x16x16 (k = 16 keys).  The B operand is
+//    exactly those four weights of the lane (rounded to the 16-bit type, as on
+//    the 128 kernel); the A operand wants keys 4q .. 4q+3 of one dim per lane:
+//    lane (i, q) loads 16 bytes (dims 128 hh + 8i .. +7) of each of keys
+//    4q .. 4q+3, and v_perm pairs their 16-bit halves, so MFMA (hh, o) produces
+//    dims 128 hh + 8 (4q + v) + o of every row;
+//  - everything else (one wave per chunk, pairs of waves above 16 rows, two
+//    tile buffers used in turn, the per-row path for the chunk's last tile and
+//    this step's new rows, the fused append, rotary embedding, paged caches
+//    and the in-launch merge) follows the head_dim-128 kernel.
+#include "da_internal.h"
+
+#include <math.h>
+
+namespace da {
+namespace {
+
+constexpr int kD = 256;
+constexpr int kRow = kD * 2;  // bytes per row
+constexpr int kWaves = 4;     // waves per workgroup
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 h16x4_t __attribute__((ext_vector_type(4)));
+
+template <bool F16>
+__device__ __forceinline__ f32x4_t mfma_k32(u32x4_t a, u32x4_t b, f32x4_t c) {
+    if constexpr (F16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+template <bool F16>
+__device__ __forceinline__ f32x4_t mfma_k16(u32x2_t a, u32x2_t b, f32x4_t c) {
+    if constexpr (F16)
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h16x4_t, a),
+                                                     __builtin_bit_cast(h16x4_t, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
+                                                         __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
+}
+
+template <bool F16>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    return (uint32_t)round16<F16>(lo) | ((uint32_t)round16<F16>(hi) << 16);
+}
+
+// Rotary embedding of a row held as this lane's eight pieces (dims 32s + 8q ..
+// +7): with the first R dims rotating, piece s < R/64 pairs with s + R/64.
+template <bool F16>
+__device__ __forceinline__ void rope_pieces8(u32x4_t (&x)[8], int R, int pos, const float *freqs, int q) {
+    if (R == 256) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) rope8<F16>(x[s], x[s + 4], pos, freqs, 32 * s + 8 * q);
+    } else if (R == 128) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) rope8<F16>(x[s], x[s + 2], pos, freqs, 32 * s + 8 * q);
+    } else {  // R == 64
+        rope8<F16>(x[0], x[1], pos, freqs, 8 * q);
+    }
+}
+
+struct Tile16 {
+    u32x4_t k[8];     // K of key l16: dims 32s + 8q .. +7
+    u32x4_t v[2][4];  // V of key 4q + u: dims 128 hh + 8 l16 .. +7
+};
+
+// A whole 16-key tile: one 16-token block (one page of a paged cache).
+__device__ __forceinline__ void load_full16(Tile16 &t, const CacheView &cv, int tb, int l16, int q) {
+    const size_t blk = cv.block(tb / kPageTokens);
+    const uint8_t *kr = cv.k + blk + (size_t)l16 * kRow + 16 * q;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) t.k[s] = ld16(kr + 64 * s);
+    const uint8_t *vr = cv.v + blk + (size_t)(4 * q) * kRow + 16 * l16;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) t.v[hh][u] = ld16(vr + u * kRow + 256 * hh);
+}
+
+// Where rows come from when a tile is not all plain cache rows: keys past
+// `last` re-read row `last` (scores masked, value rows zeroed), and this step's
+// new rows (local keys from new_first on) come from k_new / v_new, rotated (K)
+// and, by `store`, appended to the cache.
+struct RowSource16 {
+    const uint8_t *knew, *vnew;  // new rows of (b, h), row i at + i * stride
+    size_t stride;
+    int new_first;
+    int t0;
+    const float *rope;
+    int rope_dim;
+    bool store;
+};
+
+template <bool F16>
+__device__ __forceinline__ void load_rows16(Tile16 &t, const CacheView &cv, int tb, int last, int l16, int q,
+                                            const RowSource16 &rs) {
+    {
+        const int key = min(tb + l16, last);
+        const uint8_t *kr = key >= rs.new_first ? rs.knew + (size_t)(key - rs.new_first) * rs.stride + 16 * q
+                                                : cv.k + cv.row(key) + 16 * q;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) t.k[s] = ld16(kr + 64 * s);
+        if (rs.rope && key >= rs.new_first) rope_pieces8<F16>(t.k, rs.rope_dim, rs.t0 + key, rs.rope, q);
+        if (rs.store && key >= rs.new_first && tb + l16 <= last && cv.writable(key)) {
+            uint8_t *kw = cv.kw + cv.row(key) + 16 * q;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) *reinterpret_cast<u32x4_t *>(kw + 64 * s) = t.k[s];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int k_raw = tb + 4 * q + u;
+        const int key = min(k_raw, last);
+        const bool fresh = key >= rs.new_first;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            t.v[hh][u] = ld16(fresh ? rs.vnew + (size_t)(key - rs.new_first) * rs.stride + 256 * hh + 16 * l16
+                                    : cv.v + cv.row(key) + 256 * hh + 16 * l16);
+            if (k_raw > last) t.v[hh][u] = u32x4_t{0u, 0u, 0u, 0u};
+            else if (rs.store && fresh && cv.writable(key))
+                *reinterpret_cast<u32x4_t *>(cv.vw + cv.row(key) + 256 * hh + 16 * l16) = t.v[hh][u];
+        }
+    }
+}
+
+template <bool F16, int RG>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_split_mfma256_kernel(AttnParams p) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rg = wave % RG;
+    const int item = blockIdx.x * (kWaves / RG) + wave / RG;
+
+    int b, h, c;
+    SeqChunks sc;
+    int rest = item;
+    if (!locate(p, rest, b, h, c, sc)) {  // past the last chunk of the launch
+        if (p.out && rg == 0 && rest < p.batch && !seq_pos_ok(p, p.seq_pos[rest]))
+            flag_sequence_nan<F16>(p, rest, lane, 64);
+        return;
+    }
+    const int bh = b * p.n_kv_heads + h;
+    const int sp = p.seq_pos[b];
+    const int t0 = c * sc.len;
+    const int n_tok = min(sc.len, sc.ctx - t0);
+    const int last = n_tok - 1;
+    const int l16 = lane & 15, q = lane >> 4;
+
+    // paged caches: lane j reads the pool page of the chunk's block j first
+    int pg_lane = 0;
+    if (p.layout.block_table && lane < (n_tok + kPageTokens - 1) / kPageTokens)
+        pg_lane = kv_page(p.layout, b, t0 / kPageTokens + lane);
+
+    // B operand of S^T = K q^T: q[row][32s + 8q .. +7] for s = 0..7.  The 16 rows
+    // live in this wave's LDS slice (row stride padded by 16 bytes against bank
+    // conflicts) rather than in 32 registers the key tiles need; each tile reads
+    // them back.
+    __shared__ u32x4_t qsh[kWaves][16][33];
+    int vis;  // exclusive local key limit of this lane's row
+    const int row = rg * 16 + l16;
+    {
+        u32x4_t qop[8];
+        if (row < p.rows) {
+            const int i = row / p.group, g = row - i * p.group;
+            const uint8_t *qp =
+                p.q + (((size_t)b * p.q_len + i) * p.n_q_heads + (size_t)h * p.group + g) * kRow + 16 * q;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) qop[s] = ld16(qp + 64 * s);
+            if (p.rope_freqs) rope_pieces8<F16>(qop, p.rope_dim, sp + i, p.rope_freqs, q);
+            vis = min(sp + i + 1 - t0, n_tok);
+        } else {
+#pragma unroll
+            for (int s = 0; s < 8; ++s) qop[s] = u32x4_t{0u, 0u, 0u, 0u};
+            vis = 0;
+        }
+#pragma unroll
+        for (int s = 0; s < 8; ++s) qsh[wave][l16][4 * s + q] = qop[s];
+        // the wave reads back what other lanes of it wrote
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+
+    CacheView cv;
+    cv.k = p.k_cache;
+    cv.v = p.v_cache;
+    cv.kw = p.k_cache_w;
+    cv.vw = p.v_cache_w;
+    cv.L = p.layout;
+    cv.b = b;
+    cv.h = h;
+    cv.n_kv_heads = p.n_kv_heads;
+    cv.max_seq = p.max_seq;
+    cv.t0 = t0;
+    cv.pg_lane = pg_lane;
+
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4_t oacc[2][8];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int o = 0; o < 8; ++o) oacc[hh][o] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // One 16-key tile: S^T, online softmax, O^T += V^T P^T.
+    auto compute = [&](Tile16 &t, int tt) {
+        const int tb = tt * 16;
+        asm volatile("" ::: "memory");  // keep the q reads inside the loop (no hoisting into registers)
+        f32x4_t st = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) st = mfma_k32<F16>(t.k[s], qsh[wave][l16][4 * s + q], st);
+        float x[4];
+        float mt = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            x[v] = tb + 4 * q + v < vis ? st[v] * p.scale_log2 : -INFINITY;
+            mt = fmaxf(mt, x[v]);
+        }
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = (m_run == -INFINITY) ? 0.f : exp2_fast(m_run - m_new);
+        float pw[4];
+        float psum = 0.f;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            pw[v] = (m_new == -INFINITY) ? 0.f : round_trip16<F16>(exp2_fast(x[v] - m_new));
+            psum += pw[v];
+        }
+        if (__any(m_new != m_run)) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int o = 0; o < 8; ++o) oacc[hh][o] *= alpha;
+        }
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+
+        const u32x2_t pop = {pack2<F16>(pw[0], pw[1]), pack2<F16>(pw[2], pw[3])};
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int o = 0; o < 8; ++o) {
+                const int w = o >> 1;
+                const uint32_t sel = (o & 1) ? 0x07060302u : 0x05040100u;
+                const u32x2_t vop = {__builtin_amdgcn_perm(t.v[hh][1][w], t.v[hh][0][w], sel),
+                                     __builtin_amdgcn_perm(t.v[hh][3][w], t.v[hh][2][w], sel)};
+                oacc[hh][o] = mfma_k16<F16>(vop, pop, oacc[hh][o]);
+            }
+    };
+
+    RowSource16 rs;
+    rs.new_first = p.k_new ? sp - t0 : n_tok;
+    rs.t0 = t0;
+    rs.rope = p.k_new ? p.rope_freqs : nullptr;
+    rs.rope_dim = p.rope_dim;
+    rs.store = p.k_new != nullptr && rg == 0;
+    rs.stride = (size_t)p.n_kv_heads * kRow;
+    if (p.k_new) {
+        const size_t noff = ((size_t)b * p.q_len * p.n_kv_heads + h) * kRow;
+        rs.knew = p.k_new + noff;
+        rs.vnew = p.v_new + noff;
+    } else {
+        rs.knew = rs.vnew = nullptr;
+    }
+    // full tiles below the new rows through two buffers used in turn, then the rest row by row
+    const int n_all = (n_tok + 15) >> 4;
+    const int nt = min(n_tok >> 4, max(rs.new_first, 0) >> 4);
+    if (nt > 0) {
+        Tile16 ta, tb_;
+        load_full16(ta, cv, 0, l16, q);
+        int i = 0;
+        for (; i + 2 <= nt; i += 2) {
+            load_full16(tb_, cv, (i + 1) * 16, l16, q);
+            compute(ta, i);
+            load_full16(ta, cv, min(i + 2, nt - 1) * 16, l16, q);
+            compute(tb_, i + 1);
+        }
+        if (i < nt) compute(ta, i);
+    }
+    for (int i = nt; i < n_all; ++i) {
+        Tile16 tt_;
+        load_rows16<F16>(tt_, cv, i * 16, last, l16, q, rs);
+        compute(tt_, i);
+    }
+
+    // ---- this wave's partial: row l16, dims 128 hh + 8 (4q + v) + o ------------
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+    if (row < p.rows) {
+        const size_t part = ((size_t)bh * p.n_chunks + c) * p.rows + row;
+        float *wa = p.ws_acc + part * kD;
+        const bool dev = p.counters != nullptr;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+#pragma unroll
+                for (int o = 0; o < 8; o += 4) {
+                    float *dst = wa + 128 * hh + 8 * (4 * q + v) + o;
+                    if (dev) {
+                        st_dev4(dst, oacc[hh][o][v], oacc[hh][o + 1][v], oacc[hh][o + 2][v], oacc[hh][o + 3][v]);
+                    } else {
+                        *reinterpret_cast<float4 *>(dst) =
+                            make_float4(oacc[hh][o][v], oacc[hh][o + 1][v], oacc[hh][o + 2][v], oacc[hh][o + 3][v]);
+                    }
+                }
+        if (q == 0) {
+            if (dev) {
+                st_dev(p.ws_ml + part * 2 + 0, m_run);
+                st_dev(p.ws_ml + part * 2 + 1, l_run);
+            } else {
+                p.ws_ml[part * 2 + 0] = m_run;
+                p.ws_ml[part * 2 + 1] = l_run;
+            }
+        }
+    }
+
+    if (p.counters && last_arrival(&p.counters[bh], sc.n * RG, lane)) {
+        for (int r = 0; r < p.rows; ++r) merge_row_wave<F16, kD>(p, p.out, bh, b, h, r, sc.n, lane);
+        if (lane == 0) p.counters[bh] = 0;
+    }
+}
+
+template <bool F16>
+hipError_t launch_dtype256(const AttnParams &p, int items, hipStream_t s) {
+    if (p.rows <= 16) {
+        const int grid = (items + kWaves - 1) / kWaves;
+        hipLaunchKernelGGL((attn_split_mfma256_kernel<F16, 1>), dim3(grid), dim3(64 * kWaves), 0, s, p);
+    } else {
+        const int grid = (items + kWaves / 2 - 1) / (kWaves / 2);
+        hipLaunchKernelGGL((attn_split_mfma256_kernel<F16, 2>), dim3(grid), dim3(64 * kWaves), 0, s, p);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_mfma256(const AttnParams &p, int items, bool fp16, hipStream_t s) {
+    return fp16 ? launch_dtype256<true>(p, items, s) : launch_dtype256<false>(p, items, s);
+}
+
+}  // namespace da

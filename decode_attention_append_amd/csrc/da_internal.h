@@ -55,6 +55,27 @@ __device__ __forceinline__ bool kv_row_writable(const KvLayout &L, int b, int t)
     return !L.block_table || kv_page(L, b, t / kPageTokens) >= 0;
 }
 
+// The caches of one (sequence b, KV head h) seen from a chunk starting at key t0
+// (a multiple of 32): contiguous, or paged through the block table.  A 16-token
+// block is one page of a paged cache.
+struct CacheView {
+    const uint8_t *k, *v;  // whole caches / pools
+    uint8_t *kw, *vw;      // the same, writable (one-launch step), or null
+    KvLayout L;
+    int b, h, n_kv_heads, max_seq, t0;
+    int pg_lane;  // paged: lane j holds the pool page of the chunk's block j (j < 64)
+    __device__ __forceinline__ size_t block(int j) const {  // 16-token block j of the chunk
+        if (!L.block_table || j >= 64) return kv_block_off(L, b, h, n_kv_heads, max_seq, t0 / kPageTokens + j);
+        int pg = __builtin_amdgcn_readlane(pg_lane, j);
+        pg = pg < 0 ? 0 : pg;  // outside the pool: read page 0
+        return ((size_t)pg * n_kv_heads + h) * kPageTokens * L.row_bytes;
+    }
+    __device__ __forceinline__ size_t row(int key) const {
+        return kv_row_off(L, b, h, n_kv_heads, max_seq, t0 + key);
+    }
+    __device__ __forceinline__ bool writable(int key) const { return kv_row_writable(L, b, t0 + key); }
+};
+
 // ---- parameter blocks ------------------------------------------------------
 
 struct AppendParams {
@@ -192,6 +213,7 @@ hipError_t launch_kv_append(const AppendParams &p, int threads_total, bool fp16,
 hipError_t launch_fill_zero(int32_t *x, int n, hipStream_t s);
 hipError_t launch_attn_valu(const AttnParams &p, int items, bool fp16, hipStream_t s);
 hipError_t launch_attn_mfma(const AttnParams &p, int items, bool fp16, hipStream_t s);
+hipError_t launch_attn_mfma256(const AttnParams &p, int items, bool fp16, hipStream_t s);
 hipError_t launch_attn_combine(const AttnParams &p, bool fp16, void *out, hipStream_t s);
 
 // ---- device helpers --------------------------------------------------------
@@ -292,6 +314,9 @@ __device__ __forceinline__ void rope8(u32x4_t &lo, u32x4_t &hi, int pos, const f
         rope_pair(x1, y1, pos, fb);
         lo[w] = (uint32_t)round16<F16>(x0) | ((uint32_t)round16<F16>(x1) << 16);
         hi[w] = (uint32_t)round16<F16>(y0) | ((uint32_t)round16<F16>(y1) << 16);
+        // one word at a time: interleaving all eight pairs' double-precision
+        // reductions costs registers the callers' tiles need
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 

@@ -12,6 +12,7 @@ per layer as ``seed * 1000 + layer``, in this order):
   v_cache  [B, Hkv, S, D]         same
   k_new    [B, q_len, Hkv, D]     same
   v_new    [B, q_len, Hkv, D]     same
+  out_gate [B, q_len, Hq, D]      N(0,1), unscaled (gated workloads only; drawn last)
 
 Integer draws come from a separate CPU generator seeded with ``seed``:
 per-sequence context lengths (or positions) first, then the heavy-row mask
@@ -19,10 +20,13 @@ per-sequence context lengths (or positions) first, then the heavy-row mask
 multiplied by ``heavy_factor``).  value_scale and heavy_factor are powers of
 two, so scaling is exact in bf16/fp16.
 
-The five decode workloads restate the attention shapes of the Qwen decodes the
+The decode workloads restate the attention shapes of the Qwen decodes the
 pages profile (Qwen3-0.6B 16:8 heads, Qwen1.5-MoE-A2.7B 16 MHA heads, a GQA-8
-long context, a 4-token speculative verify); no trained weights or prompts are
-involved, all values are synthetic.
+long context, a 4-token speculative verify, and the full-attention layers of
+Qwen3.5-35B-A3B: 16:2 heads of 256 dims, rotary on a quarter of the dims and a
+sigmoid output gate); no trained weights or prompts are involved, all values
+are synthetic.  A workload with a rotary width takes its frequency table from
+``rope_freqs`` at ``rope_theta``.
 """
 from dataclasses import dataclass, field
 from typing import Optional, Tuple
@@ -50,6 +54,9 @@ class Workload:
     pos_range: Optional[Tuple[int, int]] = None   # inclusive, seq_pos of the first new token
     heavy_fraction: float = 0.0
     heavy_factor: float = 8.0
+    rope_dim: int = 0            # rotated leading dims (0: no rotary embedding in the step)
+    rope_theta: float = 0.0
+    gated: bool = False          # out *= sigmoid(out_gate)
     note: str = field(default="", compare=False)
 
     @property
@@ -91,6 +98,11 @@ WORKLOADS = {
                  n_kv_heads=4, head_dim=128, dtype="bf16", max_seq=8192, layers=1,
                  seed=1005, pos_range=(2048, 8188), heavy_fraction=0.01, heavy_factor=8.0,
                  note="speculative verify of 4 draft tokens, causal inside the window"),
+        Workload("qwen35_gqa16x2_d256_gated_b16_ctx8192_10l", batch=16, q_len=1, n_q_heads=16,
+                 n_kv_heads=2, head_dim=256, dtype="fp16", max_seq=8192, layers=10, seed=1006,
+                 ctx_range=(6144, 8192), rope_dim=64, rope_theta=1.0e7, gated=True,
+                 note="Qwen3.5-35B-A3B full-attention layers: 16:2 heads of 256 dims, partial "
+                      "rotary (64 dims), sigmoid output gate, ragged contexts"),
     ]
 }
 
@@ -125,8 +137,9 @@ def draw_seq_pos(w: Workload) -> torch.Tensor:
 
 
 def make_tensors(batch, q_len, n_q_heads, n_kv_heads, head_dim, max_seq, dtype, seed,
-                 device="cpu", value_scale=1.0):
-    """q, k_cache, v_cache, k_new, v_new drawn N(0,1)*value_scale in ``dtype``."""
+                 device="cpu", value_scale=1.0, gate=False):
+    """q, k_cache, v_cache, k_new, v_new drawn N(0,1)*value_scale in ``dtype``; with
+    ``gate`` also an N(0,1) out_gate like q, drawn after them."""
     tdt = DTYPES[dtype] if isinstance(dtype, str) else dtype
     g = torch.Generator(device=device)
     g.manual_seed(seed)
@@ -142,25 +155,31 @@ def make_tensors(batch, q_len, n_q_heads, n_kv_heads, head_dim, max_seq, dtype, 
     v_cache = draw(batch, n_kv_heads, max_seq, head_dim)
     k_new = draw(batch, q_len, n_kv_heads, head_dim)
     v_new = draw(batch, q_len, n_kv_heads, head_dim)
+    if gate:
+        return q, k_cache, v_cache, k_new, v_new, torch.randn(q.shape, generator=g, device=device, dtype=tdt)
     return q, k_cache, v_cache, k_new, v_new
 
 
 def make_layer(w: Workload, layer: int = 0, device="cpu"):
     """All inputs of one layer of a workload: dict of tensors on ``device``."""
-    q, kc, vc, kn, vn = make_tensors(w.batch, w.q_len, w.n_q_heads, w.n_kv_heads, w.head_dim,
-                                     w.max_seq, w.dtype, w.seed * 1000 + layer, device,
-                                     w.value_scale)
+    t = make_tensors(w.batch, w.q_len, w.n_q_heads, w.n_kv_heads, w.head_dim, w.max_seq,
+                     w.dtype, w.seed * 1000 + layer, device, w.value_scale, gate=w.gated)
+    q, kc, vc, kn, vn = t[:5]
     seq_pos, km, nm = _integer_draws(w)
     if km is not None:
         kc[km.to(device)] *= w.heavy_factor
         kn[nm.to(device)] *= w.heavy_factor
     seq_pos = seq_pos.to(device)
-    return {"q": q, "k_cache": kc, "v_cache": vc, "k_new": kn, "v_new": vn, "seq_pos": seq_pos}
+    out = {"q": q, "k_cache": kc, "v_cache": vc, "k_new": kn, "v_new": vn, "seq_pos": seq_pos}
+    if w.gated:
+        out["out_gate"] = t[5]
+    return out
 
 
 def rope_freqs(head_dim: int = 128, theta: float = 1.0e6, device="cpu") -> torch.Tensor:
     """A rotary frequency table, theta^(-2j/head_dim) for j < head_dim/2, as float32: an
     input of the step like the page's precomputed freqs table (theta 1e6 is Qwen3's
-    rope_theta, 1e4 Qwen1.5's)."""
+    rope_theta, 1e4 Qwen1.5's).  For a partial rotary embedding pass the rotated width
+    as ``head_dim``: the table then holds rope_dim/2 values theta^(-2j/rope_dim)."""
     j = torch.arange(0, head_dim, 2, dtype=torch.float64)
     return (theta ** (-j / head_dim)).to(torch.float32).to(device)

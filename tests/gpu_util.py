@@ -88,8 +88,91 @@ def check_layer(p, inp, rows=None, stream=None, paths=PATHS):
 
 
 def make_case(B, q_len, Hq, Hkv, S, seq_pos, dtype=torch.bfloat16, seed=0, scale=1.0,
-              device="cuda"):
+              device="cuda", head_dim=128, gate=False):
     from decode_attention_append_amd.workloads import make_tensors
-    q, kc, vc, kn, vn = make_tensors(B, q_len, Hq, Hkv, 128, S, dtype, seed, device, scale)
+    t = make_tensors(B, q_len, Hq, Hkv, head_dim, S, dtype, seed, device, scale, gate=gate)
     sp = torch.as_tensor(np.asarray(seq_pos, dtype=np.int32)).to(device)
-    return {"q": q, "k_cache": kc, "v_cache": vc, "k_new": kn, "v_new": vn, "seq_pos": sp}
+    out = {"q": t[0], "k_cache": t[1], "v_cache": t[2], "k_new": t[3], "v_new": t[4], "seq_pos": sp}
+    if gate:
+        out["out_gate"] = t[5]
+    return out
+
+
+def _ulp(ref, dt):
+    mbits, emin = (10, -14) if dt == oracle.FP16 else (7, -126)
+    return np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** emin))) - mbits)
+
+
+def appended_rows(kshape, sp, q_len, block_table=None):
+    """Mask over the cache's (or pool's) rows [.., .., 16 or S] that the step appends."""
+    m = np.zeros(kshape[:3], bool)
+    for b, s in enumerate(sp):
+        for i in range(q_len):
+            if block_table is None:
+                m[b, :, s + i] = True
+            else:
+                m[block_table[b, (s + i) // 16], :, (s + i) % 16] = True
+    return m
+
+
+def check_full(p, inp, freqs=None, rows=None, stream=None, paths=PATHS, ws=None):
+    """check_layer for every feature of the step: optional rotary table (rope_dim from
+    the table's length), paged caches (inp["block_table"]) and output gate
+    (inp["out_gate"]; ``p`` must carry the same tensors).  V caches bit for bit; K
+    caches bit for bit without a rotary table, else within one ulp in the appended
+    rows (at most 1% of their elements off by that ulp) and bit for bit elsewhere."""
+    dt = odt(inp["q"].dtype)
+    sp = inp["seq_pos"].cpu().numpy()
+    kc0, vc0 = bits(inp["k_cache"]), bits(inp["v_cache"])
+    kn, vn, qb = bits(inp["k_new"]), bits(inp["v_new"]), bits(inp["q"])
+    bt = inp.get("block_table")
+    bt = None if bt is None else bt.cpu().numpy()
+    if freqs is not None:
+        fr = freqs.cpu().numpy()
+        pos = sp[:, None, None] + np.arange(p.q_len, dtype=np.int32)[None, :, None]
+        kn = oracle.rope_rows(kn, np.broadcast_to(pos, kn.shape[:3]), fr, dt)
+        qb = oracle.rope_q(qb, sp, fr, dt)
+    if bt is None:
+        k_ref, v_ref = oracle.kv_append(kc0, vc0, kn, vn, sp)
+        kc, vc = k_ref, v_ref
+    else:
+        k_ref, v_ref = oracle.kv_append_paged(kc0, vc0, kn, vn, sp, bt)
+        kc, vc = oracle.gather_paged(k_ref, bt), oracle.gather_paged(v_ref, bt)
+    del kc0, vc0
+    scale = p.scale if p.scale > 0 else None
+    gate = inp.get("out_gate")
+    gb = None if gate is None else bits(gate)
+    if rows is None:
+        ref = oracle.gqa_decode(qb, kc, vc, sp, dt, scale=scale)
+    else:
+        rows = np.asarray(rows, dtype=np.int32).reshape(-1, 3)
+        ref = oracle.gqa_decode_rows(qb, kc, vc, sp, rows, dt, scale=scale)
+        if gb is not None:
+            gb = np.ascontiguousarray(gb[rows[:, 0], rows[:, 1], rows[:, 2]])
+    if gb is not None:
+        ref = oracle.output_gate(ref, gb, dt)
+    new = appended_rows(k_ref.shape, sp, p.q_len, bt)
+    stats = {}
+    for n, path in enumerate(paths):
+        last = n == len(paths) - 1
+        run = inp if last else dict(inp, k_cache=inp["k_cache"].clone(), v_cache=inp["v_cache"].clone())
+        out = run_step(p, run, stream, path, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(run["v_cache"]), v_ref), f"{path}: v cache differs from the oracle's append"
+        kg = bits(run["k_cache"])
+        d = kg != k_ref
+        if freqs is None:
+            assert not d.any(), f"{path}: k cache differs from the oracle's append"
+        else:
+            assert not d[~new].any(), f"{path}: k cache differs outside the appended rows"
+            a, r = oracle.decode(kg[new], dt), oracle.decode(k_ref[new], dt)
+            assert (np.abs(a - r) <= _ulp(r, dt)).all(), f"{path}: rotated K more than one ulp off"
+            assert d[new].mean() <= 0.01, f"{path}: {d[new].mean():.4f} of rotated K off by an ulp"
+        if rows is None:
+            stats[path] = compare_out(out, ref, f"{path}: all rows")
+        else:
+            o = out.cpu()
+            got = torch.stack([o[b, i, hq] for b, i, hq in rows])
+            stats[path] = compare_out(got, ref, f"{path}: sampled rows")
+        del run, out
+    return stats

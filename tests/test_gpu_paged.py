@@ -23,24 +23,30 @@ def _say(*a):
     print("[case]", *a, flush=True)
 
 
-def make_paged(B, q_len, Hq, Hkv, pps, seq_pos, dtype=torch.bfloat16, seed=0, spare=5, scale=1.0):
+def make_paged(B, q_len, Hq, Hkv, pps, seq_pos, dtype=torch.bfloat16, seed=0, spare=5, scale=1.0,
+               head_dim=128, gate=False):
     """Pools of B * pps + spare pages; sequence pages are a random permutation; spare pages
-    are poisoned."""
+    are poisoned.  With ``gate`` the case also holds an out_gate."""
     n_pages = B * pps + spare
-    _, kp, vp, _, _ = make_tensors(1, 1, Hkv, Hkv, 128, n_pages * 16, dtype, seed, "cuda", scale)
-    q, _, _, kn, vn = make_tensors(B, q_len, Hq, Hkv, 128, 16, dtype, seed + 1, "cuda", scale)
+    D = head_dim
+    _, kp, vp, _, _ = make_tensors(1, 1, Hkv, Hkv, D, n_pages * 16, dtype, seed, "cuda", scale)
+    t = make_tensors(B, q_len, Hq, Hkv, D, 16, dtype, seed + 1, "cuda", scale, gate=gate)
+    q, kn, vn = t[0], t[3], t[4]
     # the [1, Hkv, n_pages * 16, D] draw regrouped as [n_pages, Hkv, 16, D] pages
-    kp = kp.reshape(Hkv, n_pages, 16, 128).transpose(0, 1).contiguous()
-    vp = vp.reshape(Hkv, n_pages, 16, 128).transpose(0, 1).contiguous()
+    kp = kp.reshape(Hkv, n_pages, 16, D).transpose(0, 1).contiguous()
+    vp = vp.reshape(Hkv, n_pages, 16, D).transpose(0, 1).contiguous()
     rng = np.random.default_rng(seed)
     perm = rng.permutation(n_pages).astype(np.int32)
     bt = perm[:B * pps].reshape(B, pps)
     for pg in perm[B * pps:]:
         kp[pg] = float("nan")
         vp[pg] = float("inf")
-    return {"q": q, "k_cache": kp, "v_cache": vp, "k_new": kn, "v_new": vn,
-            "seq_pos": torch.as_tensor(np.asarray(seq_pos, np.int32)).cuda(),
-            "block_table": torch.as_tensor(bt).cuda()}
+    out = {"q": q, "k_cache": kp, "v_cache": vp, "k_new": kn, "v_new": vn,
+           "seq_pos": torch.as_tensor(np.asarray(seq_pos, np.int32)).cuda(),
+           "block_table": torch.as_tensor(bt).cuda()}
+    if gate:
+        out["out_gate"] = t[5]
+    return out
 
 
 def check_paged(p, inp, path, freqs=None, rows=None):
