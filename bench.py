@@ -35,6 +35,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--chunk", type=int, default=0, help="chunk_tokens override (0 = automatic)")
+    ap.add_argument("--items", type=int, default=0,
+                    help="balanced chunking: chunks to aim for over the launch (0 = the library's default)")
     ap.add_argument("--path", choices=["step", "separate"], default="step",
                     help="step: one da_decode_step per layer; separate: the three calls per layer")
     ap.add_argument("--rope", type=float, default=0.0, metavar="THETA",
@@ -176,7 +178,7 @@ def main():
         torch.cuda.synchronize()
     # one problem per layer: a gated problem carries its layer's gate tensor
     probs = [da.problem(w.batch, w.q_len, w.n_q_heads, w.n_kv_heads, w.head_dim, w.max_seq, w.dtype,
-                        chunk_tokens=args.chunk, rope_freqs=freqs, block_table=block_table, n_pages=n_pages,
+                        chunk_tokens=args.chunk, work_items=args.items, rope_freqs=freqs, block_table=block_table, n_pages=n_pages,
                         rope_dim=rope_dim if freqs is not None else 0, out_gate=L.get("out_gate"))
              for L in layers]
     p = probs[0]
@@ -301,6 +303,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "q_len": w.q_len, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "context": int(seq_pos.max()) + w.q_len,
                    "max_seq": w.max_seq, "layers": w.layers, "chunk_tokens": plan["chunk_tokens"],
+                   "target_items": plan["target_items"],
                    "variant": plan["variant"], "path": args.path, "graph": args.graph,
                    "rope_theta": theta if freqs is not None else None,
                    "rope_dim": rope_dim if freqs is not None else None, "output_gate": w.gated,

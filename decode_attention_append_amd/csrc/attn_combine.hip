@@ -33,7 +33,7 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnParam
     const int h = bh - b * p.n_kv_heads;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const size_t o_off = out_row_off(p, b, h, r) + NV * lane;
-    const SeqChunks sc = seq_chunks(p, b, p.fixed_chunk > 0 ? p.fixed_chunk : balanced_chunk(p));
+    const SeqChunks sc = seq_chunks(p, b, p.fixed_chunk > 0 ? p.fixed_chunk : balanced_chunk_wave(p, lane));
     if (sc.n == 0) {  // seq_pos breaks the contract: flag the rows with NaN
         if (wave == 0) {
             const uint16_t nan16 = F16 ? 0x7e00u : 0x7fc0u;

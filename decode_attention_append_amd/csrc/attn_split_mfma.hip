@@ -157,13 +157,13 @@ void attn_split_mfma_kernel(AttnParams p) {
     int b, h, c;
     SeqChunks sc;
     int rest = item;
-    if (!locate(p, rest, b, h, c, sc)) {  // past the last chunk of the launch
+    int sp;
+    if (!locate_wave(p, rest, b, h, c, sc, sp, lane)) {  // past the last chunk of the launch
         if (p.out && rg == 0 && rest < p.batch && !seq_pos_ok(p, p.seq_pos[rest]))
             flag_sequence_nan<F16>(p, rest, lane, 64);
         return;
     }
     const int bh = b * p.n_kv_heads + h;
-    const int sp = p.seq_pos[b];
     const int ctx = sc.ctx;
     const int t0 = c * sc.len;
     const int n_tok = min(sc.len, ctx - t0);

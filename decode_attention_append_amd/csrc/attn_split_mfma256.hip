@@ -143,21 +143,20 @@ __device__ __forceinline__ void load_rows16(Tile16 &t, const CacheView &cv, int 
 template <bool F16, int RG>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_split_mfma256_kernel(AttnParams p) {
+    constexpr int KS = kWaves / RG;  // waves sharing one row group's tiles
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int rg = wave % RG;
-    const int item = blockIdx.x * (kWaves / RG) + wave / RG;
+    const int rg = wave % RG, kw = wave / RG;
 
     int b, h, c;
     SeqChunks sc;
-    int rest = item;
-    if (!locate(p, rest, b, h, c, sc)) {  // past the last chunk of the launch
-        if (p.out && rg == 0 && rest < p.batch && !seq_pos_ok(p, p.seq_pos[rest]))
-            flag_sequence_nan<F16>(p, rest, lane, 64);
+    int rest = blockIdx.x;
+    int sp;
+    if (!locate_wave(p, rest, b, h, c, sc, sp, lane)) {  // past the last chunk of the launch
+        if (p.out && rest < p.batch && !seq_pos_ok(p, p.seq_pos[rest])) flag_sequence_nan<F16>(p, rest, tid, 64 * kWaves);
         return;
     }
     const int bh = b * p.n_kv_heads + h;
-    const int sp = p.seq_pos[b];
     const int t0 = c * sc.len;
     const int n_tok = min(sc.len, sc.ctx - t0);
     const int last = n_tok - 1;
@@ -168,11 +167,35 @@ void attn_split_mfma256_kernel(AttnParams p) {
     if (p.layout.block_table && lane < (n_tok + kPageTokens - 1) / kPageTokens)
         pg_lane = kv_page(p.layout, b, t0 / kPageTokens + lane);
 
+    CacheView cv;
+    cv.k = p.k_cache;
+    cv.v = p.v_cache;
+    cv.kw = p.k_cache_w;
+    cv.vw = p.v_cache_w;
+    cv.L = p.layout;
+    cv.b = b;
+    cv.h = h;
+    cv.n_kv_heads = p.n_kv_heads;
+    cv.max_seq = p.max_seq;
+    cv.t0 = t0;
+    cv.pg_lane = pg_lane;
+
+    // Tiles 0 .. nt-1 hold old cache rows only and load whole; this wave takes
+    // tiles kw, kw + KS, ... of them, the first already in flight while q loads.
+    const int new_first = p.k_new ? sp - t0 : n_tok;
+    const int n_all = (n_tok + 15) >> 4;
+    const int nt = min(n_tok >> 4, max(new_first, 0) >> 4);
+    const int nj = kw < nt ? (nt - kw + KS - 1) / KS : 0;
+    Tile16 ta, tb_;
+    if (nj > 0) load_full16(ta, cv, kw * 16, l16, q);
+
     // B operand of S^T = K q^T: q[row][32s + 8q .. +7] for s = 0..7.  The 16 rows
     // live in this wave's LDS slice (row stride padded by 16 bytes against bank
     // conflicts) rather than in 32 registers the key tiles need; each tile reads
-    // them back.
+    // them back.  After the last tile the same memory serves the waves' merge.
     __shared__ u32x4_t qsh[kWaves][16][33];
+    __shared__ float mlsh[kWaves][16][2];
+    __shared__ int s_last;
     int vis;  // exclusive local key limit of this lane's row
     const int row = rg * 16 + l16;
     {
@@ -197,19 +220,6 @@ void attn_split_mfma256_kernel(AttnParams p) {
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-
-    CacheView cv;
-    cv.k = p.k_cache;
-    cv.v = p.v_cache;
-    cv.kw = p.k_cache_w;
-    cv.vw = p.v_cache_w;
-    cv.L = p.layout;
-    cv.b = b;
-    cv.h = h;
-    cv.n_kv_heads = p.n_kv_heads;
-    cv.max_seq = p.max_seq;
-    cv.t0 = t0;
-    cv.pg_lane = pg_lane;
 
     float m_run = -INFINITY, l_run = 0.f;
     f32x4_t oacc[2][8];
@@ -265,8 +275,22 @@ void attn_split_mfma256_kernel(AttnParams p) {
             }
     };
 
+    // full tiles through two buffers used in turn
+    if (nj > 0) {
+        int j = 0;
+        for (; j + 2 <= nj; j += 2) {
+            load_full16(tb_, cv, (kw + KS * (j + 1)) * 16, l16, q);
+            compute(ta, kw + KS * j);
+            if (j + 2 < nj) load_full16(ta, cv, (kw + KS * (j + 2)) * 16, l16, q);
+            compute(tb_, kw + KS * (j + 1));
+        }
+        if (j < nj) compute(ta, kw + KS * j);
+    }
+
+    // the rest row by row (the chunk's last partial tile, this step's new rows),
+    // tile i by wave i mod KS of the row group
     RowSource16 rs;
-    rs.new_first = p.k_new ? sp - t0 : n_tok;
+    rs.new_first = new_first;
     rs.t0 = t0;
     rs.rope = p.k_new ? p.rope_freqs : nullptr;
     rs.rope_dim = p.rope_dim;
@@ -279,31 +303,63 @@ void attn_split_mfma256_kernel(AttnParams p) {
     } else {
         rs.knew = rs.vnew = nullptr;
     }
-    // full tiles below the new rows through two buffers used in turn, then the rest row by row
-    const int n_all = (n_tok + 15) >> 4;
-    const int nt = min(n_tok >> 4, max(rs.new_first, 0) >> 4);
-    if (nt > 0) {
-        Tile16 ta, tb_;
-        load_full16(ta, cv, 0, l16, q);
-        int i = 0;
-        for (; i + 2 <= nt; i += 2) {
-            load_full16(tb_, cv, (i + 1) * 16, l16, q);
-            compute(ta, i);
-            load_full16(ta, cv, min(i + 2, nt - 1) * 16, l16, q);
-            compute(tb_, i + 1);
-        }
-        if (i < nt) compute(ta, i);
-    }
     for (int i = nt; i < n_all; ++i) {
+        if (i % KS != kw) continue;
         Tile16 tt_;
         load_rows16<F16>(tt_, cv, i * 16, last, l16, q, rs);
         compute(tt_, i);
     }
 
-    // ---- this wave's partial: row l16, dims 128 hh + 8 (4q + v) + o ------------
+    // ---- merge of the KS waves of a row group, then one partial per chunk ------
+    // rows l16: dims 128 hh + 8 (4q + v) + o in oacc[hh][o][v]
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
-    if (row < p.rows) {
+    if (q == 0) {
+        mlsh[wave][l16][0] = m_run;
+        mlsh[wave][l16][1] = l_run;
+    }
+    __syncthreads();  // every wave is past its last tile: qsh is free
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) M = fmaxf(M, mlsh[rg + RG * k][l16][0]);
+    float L = 0.f;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+        const float mk = mlsh[rg + RG * k][l16][0];
+        L += mk == -INFINITY ? 0.f : exp2_fast(mk - M) * mlsh[rg + RG * k][l16][1];
+    }
+    {
+        const float f = m_run == -INFINITY ? 0.f : exp2_fast(m_run - M);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int o = 0; o < 8; ++o) oacc[hh][o] *= f;
+    }
+    // two slots of 16 rows x 256 floats in the q memory; lane-private layout
+    f32x4_t *red = reinterpret_cast<f32x4_t *>(&qsh[0][0][0]);
+    auto put = [&](int slot) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) red[(slot * 16 + e) * 64 + lane] = oacc[e >> 3][e & 7];
+    };
+    auto add = [&](int slot) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[e >> 3][e & 7] += red[(slot * 16 + e) * 64 + lane];
+    };
+    if constexpr (KS == 4) {  // (0 + 2) + (1 + 3)
+        if (kw >= 2) put(kw - 2);
+        __syncthreads();
+        if (kw < 2) add(kw);
+        __syncthreads();
+        if (kw == 1) put(0);
+        __syncthreads();
+        if (kw == 0) add(0);
+    } else {
+        if (kw == 1) put(rg);
+        __syncthreads();
+        if (kw == 0) add(rg);
+    }
+
+    if (kw == 0 && row < p.rows) {
         const size_t part = ((size_t)bh * p.n_chunks + c) * p.rows + row;
         float *wa = p.ws_acc + part * kD;
         const bool dev = p.counters != nullptr;
@@ -323,30 +379,39 @@ void attn_split_mfma256_kernel(AttnParams p) {
                 }
         if (q == 0) {
             if (dev) {
-                st_dev(p.ws_ml + part * 2 + 0, m_run);
-                st_dev(p.ws_ml + part * 2 + 1, l_run);
+                st_dev(p.ws_ml + part * 2 + 0, M);
+                st_dev(p.ws_ml + part * 2 + 1, L);
             } else {
-                p.ws_ml[part * 2 + 0] = m_run;
-                p.ws_ml[part * 2 + 1] = l_run;
+                p.ws_ml[part * 2 + 0] = M;
+                p.ws_ml[part * 2 + 1] = L;
             }
         }
     }
 
-    if (p.counters && last_arrival(&p.counters[bh], sc.n * RG, lane)) {
-        for (int r = 0; r < p.rows; ++r) merge_row_wave<F16, kD>(p, p.out, bh, b, h, r, sc.n, lane);
-        if (lane == 0) p.counters[bh] = 0;
+    // One-launch step: the workgroup that stores the last partial of (b, h)
+    // merges its rows (one wave per row) and resets the arrival counter.
+    if (p.counters) {
+        wait_mem();       // this wave's partial stores are complete
+        __syncthreads();  // and so are the other waves'
+        if (tid == 0)
+            s_last = __hip_atomic_fetch_add(&p.counters[bh], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                     sc.n - 1;
+        __syncthreads();
+        if (s_last) {
+            for (int r = wave; r < p.rows; r += kWaves) merge_row_wave<F16, kD>(p, p.out, bh, b, h, r, sc.n, lane);
+            if (tid == 0) p.counters[bh] = 0;
+        }
     }
 }
 
+// `items` = chunks in the launch (an upper bound), one workgroup each: four
+// waves over the chunk's tiles (up to 16 rows), or two pairs (17..32 rows).
 template <bool F16>
 hipError_t launch_dtype256(const AttnParams &p, int items, hipStream_t s) {
-    if (p.rows <= 16) {
-        const int grid = (items + kWaves - 1) / kWaves;
-        hipLaunchKernelGGL((attn_split_mfma256_kernel<F16, 1>), dim3(grid), dim3(64 * kWaves), 0, s, p);
-    } else {
-        const int grid = (items + kWaves / 2 - 1) / (kWaves / 2);
-        hipLaunchKernelGGL((attn_split_mfma256_kernel<F16, 2>), dim3(grid), dim3(64 * kWaves), 0, s, p);
-    }
+    if (p.rows <= 16)
+        hipLaunchKernelGGL((attn_split_mfma256_kernel<F16, 1>), dim3(items), dim3(64 * kWaves), 0, s, p);
+    else
+        hipLaunchKernelGGL((attn_split_mfma256_kernel<F16, 2>), dim3(items), dim3(64 * kWaves), 0, s, p);
     return hipGetLastError();
 }
 

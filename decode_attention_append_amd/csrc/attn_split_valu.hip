@@ -90,13 +90,13 @@ __global__ __launch_bounds__(256) void attn_split_valu_kernel(AttnParams p) {
     int b, h, c;
     SeqChunks sc;
     int item = blockIdx.x;
-    if (!locate(p, item, b, h, c, sc)) {  // past the last chunk of the launch
+    int sp;
+    if (!locate_wave(p, item, b, h, c, sc, sp, threadIdx.x & 63)) {  // past the last chunk of the launch
         if (kOneLaunch && p.out && item < p.batch && !seq_pos_ok(p, p.seq_pos[item]))
             flag_sequence_nan<F16>(p, item, threadIdx.x, 256);
         return;
     }
     const int bh = b * p.n_kv_heads + h;
-    const int sp = p.seq_pos[b];
     const int ctx = sc.ctx;
     const int t0 = c * sc.len;
     const int n_tok = min(sc.len, ctx - t0);

@@ -148,21 +148,26 @@ __host__ __device__ inline bool seq_pos_ok(const AttnParams &p, int sp) {
     return sp >= 0 && sp <= p.max_seq - p.q_len;
 }
 
-__host__ __device__ inline int balanced_chunk(const AttnParams &p) {
-    int64_t total = 0;
-    for (int b = 0; b < p.batch; ++b) {
-        const int sp = p.seq_pos[b];
-        if (seq_pos_ok(p, sp)) total += sp + p.q_len;
-    }
+// Balanced chunk length for `total` visible keys over all sequences.
+__host__ __device__ inline int balanced_len(const AttnParams &p, int64_t total) {
     const int64_t want = (total * p.n_kv_heads + p.target_wg - 1) / p.target_wg;
     int t = (int)(want < p.max_chunk ? want : p.max_chunk);
     t = round_up32(t);
     return t < p.min_chunk ? p.min_chunk : (t > p.max_chunk ? p.max_chunk : t);
 }
 
-__host__ __device__ inline SeqChunks seq_chunks(const AttnParams &p, int b, int T) {
+__host__ __device__ inline int balanced_chunk(const AttnParams &p) {
+    int64_t total = 0;
+    for (int b = 0; b < p.batch; ++b) {
+        const int sp = p.seq_pos[b];
+        if (seq_pos_ok(p, sp)) total += sp + p.q_len;
+    }
+    return balanced_len(p, total);
+}
+
+// Chunks of a sequence whose first new token sits at `sp`, for chunk length T.
+__host__ __device__ inline SeqChunks seq_chunks_at(const AttnParams &p, int sp, int T) {
     SeqChunks s{0, 0, 0};
-    const int sp = p.seq_pos[b];
     if (!seq_pos_ok(p, sp)) return s;
     s.ctx = sp + p.q_len;
     if (p.fixed_chunk > 0) {
@@ -180,6 +185,10 @@ __host__ __device__ inline SeqChunks seq_chunks(const AttnParams &p, int b, int 
     s.len = round_up32(ceil_div(s.ctx, n));
     s.n = ceil_div(s.ctx, s.len);  // rounding the length up may leave the last chunk empty
     return s;
+}
+
+__host__ __device__ inline SeqChunks seq_chunks(const AttnParams &p, int b, int T) {
+    return seq_chunks_at(p, p.seq_pos[b], T);
 }
 
 // Which (b, h, c) work item `w` is; false if w is past the last chunk, and then
@@ -356,6 +365,72 @@ __device__ __forceinline__ float wave_max(float x) {
 __device__ __forceinline__ float wave_sum(float x) {
     for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
     return x;
+}
+
+__device__ __forceinline__ int wave_sum_i(int x) {
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d);
+        if (lane >= d) x += y;
+    }
+    return x;
+}
+
+// The chunk plan's per-launch values, computed by a whole wave: lane j of each
+// pass holds sequence (pass + j), so the positions arrive in one vector load
+// per 64 sequences instead of a chain of dependent scalar loads (every wave of
+// the launch reads them while the cache streams, and a serial chain there costs
+// microseconds).  Same results as balanced_chunk / locate.
+__device__ inline int balanced_chunk_wave(const AttnParams &p, int lane) {
+    int64_t total = 0;
+    for (int b0 = 0; b0 < p.batch; b0 += 64) {
+        const int b = b0 + lane;
+        const int sp = b < p.batch ? p.seq_pos[b] : -1;
+        total += wave_sum_i(seq_pos_ok(p, sp) ? sp + p.q_len : 0);
+    }
+    return balanced_len(p, total);
+}
+
+// locate() by a whole wave; also returns the sequence's seq_pos.  Every lane
+// gets the same (uniform) results.
+__device__ inline bool locate_wave(const AttnParams &p, int &w, int &b, int &h, int &c, SeqChunks &sc, int &sp,
+                                   int lane) {
+    int sp0 = lane < p.batch ? p.seq_pos[lane] : -1;  // the first 64 sequences, kept for the walk
+    int T = p.fixed_chunk;
+    if (T <= 0) {
+        int64_t total = wave_sum_i(seq_pos_ok(p, sp0) ? sp0 + p.q_len : 0);
+        for (int b0 = 64; b0 < p.batch; b0 += 64) {
+            const int bb = b0 + lane;
+            const int s1 = bb < p.batch ? p.seq_pos[bb] : -1;
+            total += wave_sum_i(seq_pos_ok(p, s1) ? s1 + p.q_len : 0);
+        }
+        T = balanced_len(p, total);
+    }
+    for (int b0 = 0; b0 < p.batch; b0 += 64) {
+        const int bb = b0 + lane;
+        const int s1 = b0 == 0 ? sp0 : (bb < p.batch ? p.seq_pos[bb] : -1);
+        const SeqChunks s = seq_chunks_at(p, s1, T);
+        const int here = s.n * p.n_kv_heads;
+        const int incl = wave_incl_scan(here, lane);
+        const int tot = __builtin_amdgcn_readlane(incl, 63);
+        if (w < tot) {
+            const int L = __ffsll((unsigned long long)__ballot(incl > w)) - 1;
+            w -= __builtin_amdgcn_readlane(incl - here, L);
+            b = b0 + L;
+            sc.n = __builtin_amdgcn_readlane(s.n, L);
+            sc.len = __builtin_amdgcn_readlane(s.len, L);
+            sc.ctx = __builtin_amdgcn_readlane(s.ctx, L);
+            sp = __builtin_amdgcn_readlane(s1, L);
+            h = w / sc.n;
+            c = w - h * sc.n;
+            return true;
+        }
+        w -= tot;
+    }
+    return false;
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }

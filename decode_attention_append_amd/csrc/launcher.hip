@@ -66,10 +66,15 @@ da_status check_problem(const da_problem *p) {
 
 // Chunks to aim for in balanced mode, per kernel: a few per compute unit (256
 // on MI355X) at the kernel's occupancy.  A vector-ALU chunk is a 4-wave
-// workgroup (about 7 fit per compute unit); an MFMA chunk is one wave, or a
-// pair of waves above 16 rows (8 waves fit per compute unit).
-int default_target(int variant, int rows) {
-    if (variant == DA_VARIANT_MFMA) return rows > 16 ? 1024 : 2048;
+// workgroup (about 7 fit per compute unit); a head_dim-128 MFMA chunk is one
+// wave, or a pair of waves above 16 rows (8 waves fit per compute unit); a
+// head_dim-256 MFMA chunk is a 4-wave workgroup (2 fit), two per compute unit
+// so that every wave streams long runs of tiles.
+int default_target(int variant, int rows, int head_dim) {
+    if (variant == DA_VARIANT_MFMA) {
+        if (head_dim != kHeadDim) return 512;
+        return rows > 16 ? 1024 : 2048;
+    }
     return 1024;
 }
 
@@ -97,6 +102,13 @@ constexpr int kMfmaRows = 8;
 // combine launch, with a workgroup per row, finishes sooner.
 constexpr int kFusedMergeRowsWave = 64;
 constexpr int kFusedMergeRowsBlock = 512;
+
+// The head_dim-256 MFMA kernel merges in the last workgroup of a (sequence,
+// KV head), one wave per row: four times the one-wave budget.
+int fused_merge_rows(int variant, int head_dim) {
+    if (variant != DA_VARIANT_MFMA) return kFusedMergeRowsBlock;
+    return head_dim != kHeadDim ? 4 * kFusedMergeRowsWave : kFusedMergeRowsWave;
+}
 
 // Chunks per sequence (balanced mode) when the one-launch step merges in the
 // launch: every chunk counts its arrival on one atomic per (sequence, KV
@@ -129,7 +141,7 @@ void plan_of(const da_problem *p, da_plan *pl) {
         // keeps ceil(ctx / max_chunk) within them, so no chunk exceeds max_chunk
         const int slots = (p->max_seq + kMinChunk - 1) / kMinChunk;
         pl->n_chunks = slots < kMaxChunks ? slots : kMaxChunks;
-        pl->target_items = p->work_items > 0 ? p->work_items : default_target(variant, rows);
+        pl->target_items = p->work_items > 0 ? p->work_items : default_target(variant, rows, p->head_dim);
         // at most target + one rounding chunk per (sequence, head), or every
         // sequence in chunks of max_chunk keys when the target is too few
         const int64_t a = (int64_t)pl->target_items + units;
@@ -148,7 +160,7 @@ void plan_of(const da_problem *p, da_plan *pl) {
         if (bound < nb_max) nb_max = bound;
     }
     pl->fused_combine = one_launch_capable(variant, rows) &&
-                        nb_max * rows <= (variant == DA_VARIANT_MFMA ? kFusedMergeRowsWave : kFusedMergeRowsBlock);
+                        nb_max * rows <= fused_merge_rows(variant, p->head_dim);
     const int32_t bh = units;
     pl->workspace_bytes = align256(ws_acc_floats(bh, pl->n_chunks, rows, p->head_dim) * sizeof(float)) +
                           align256(ws_ml_floats(bh, pl->n_chunks, rows) * sizeof(float)) +

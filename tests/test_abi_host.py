@@ -136,6 +136,10 @@ def test_decode_step_rejects_before_launch():
     (dict(batch=8, q_len=4, n_q_heads=32, n_kv_heads=4, max_seq=8192), False),  # MFMA, 32 rows
     (dict(batch=1, n_q_heads=64, n_kv_heads=8, max_seq=512), True),      # MFMA, 8 chunks at most
     (dict(batch=1, n_q_heads=16, n_kv_heads=1, max_seq=65536, variant="valu"), False),
+    # head_dim 256: the last workgroup merges, up to 256 chunk-rows
+    (dict(batch=16, n_q_heads=16, n_kv_heads=2, head_dim=256, max_seq=8192, dtype="fp16"), True),
+    (dict(batch=4, q_len=2, n_q_heads=16, n_kv_heads=2, head_dim=256, max_seq=8192), True),
+    (dict(batch=4, q_len=4, n_q_heads=16, n_kv_heads=2, head_dim=256, max_seq=8192), False),
 ])
 def test_plan_fused_merge(shape, fused):
     """The one-launch step merges inside the attention launch only when every
@@ -145,7 +149,17 @@ def test_plan_fused_merge(shape, fused):
     units = shape["batch"] * shape.get("n_kv_heads", 8)
     # the counters sit after the partials
     rows = pl["rows"]
-    assert pl["workspace_bytes"] >= units * pl["n_chunks"] * rows * (128 + 2) * 4 + units * 4
+    D = shape.get("head_dim", 128)
+    assert pl["workspace_bytes"] >= units * pl["n_chunks"] * rows * (D + 2) * 4 + units * 4
+
+
+def test_plan_head_dim_256():
+    """head_dim 256 always takes the MFMA kernel, one 4-wave workgroup per chunk, aiming
+    at 512 chunks."""
+    for rows in (1, 8, 32):
+        pl = da.plan_attention(P(head_dim=256, n_q_heads=2 * rows, n_kv_heads=2, batch=16))
+        assert pl["variant"] == "mfma" and pl["target_items"] == 512
+    assert da.workspace_bytes(P(head_dim=256, variant="valu")) == 0
 
 
 def test_rope_table_must_be_aligned():

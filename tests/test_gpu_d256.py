@@ -128,11 +128,12 @@ def test_d256_contract_breaking_seq_pos(S, path):
     gu.compare_out(out[good], ref)
 
 
-@pytest.mark.parametrize("S,fused", [(512, True), (4096, False)])
-def test_d256_decode_loop(S, fused):
-    """Consecutive steps through one workspace with fresh q, gate and new rows."""
-    B, q_len, Hq, Hkv = 2, 1, 16, 2
-    sp = np.asarray([S - 6, S // 3], np.int32)
+@pytest.mark.parametrize("q_len,S,fused", [(1, 512, True), (1, 4096, True), (4, 4096, False)])
+def test_d256_decode_loop(q_len, S, fused):
+    """Consecutive steps through one workspace with fresh q, gate and new rows; the
+    merge inside the attention launch, or (32 rows x 16 chunks) the separate one."""
+    B, Hq, Hkv = 2, 16, 2
+    sp = np.asarray([S - 4 * q_len - 2, S // 3], np.int32)
     inp = gu.make_case(B, q_len, Hq, Hkv, S, sp, torch.float16, seed=S, head_dim=256, gate=True)
     freqs = rope_freqs(64, 1.0e7, "cuda")
     p = _problem(inp, freqs, 64)
@@ -140,7 +141,7 @@ def test_d256_decode_loop(S, fused):
     ws = da.new_workspace(p)
     gen = torch.Generator(device="cpu").manual_seed(S)
     for it in range(4):
-        _say("d256 loop", S, it, sp.tolist())
+        _say("d256 loop", q_len, S, it, sp.tolist())
         if it:
             for k in ("q", "k_new", "v_new", "out_gate"):
                 inp[k].copy_(torch.randn(inp[k].shape, generator=gen).to(torch.float16))
