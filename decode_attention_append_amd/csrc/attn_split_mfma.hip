@@ -358,7 +358,11 @@ void attn_split_mfma_kernel(AttnParams p) {
     // One-launch step: the wave whose partial arrives last for (b, h) merges all
     // its rows and resets the arrival counter for the next call.
     if (p.counters && last_arrival(&p.counters[bh], sc.n * RG, lane)) {
-        for (int r = 0; r < p.rows; ++r) merge_row_wave<F16, kHeadDim>(p, p.out, bh, b, h, r, sc.n, lane);
+        if (sc.n <= 16) {
+            for (int r = 0; r < p.rows; r += 2) merge_two_rows_wave<F16, kHeadDim>(p, bh, b, h, r, 1, sc.n, lane);
+        } else {
+            for (int r = 0; r < p.rows; ++r) merge_row_wave<F16, kHeadDim>(p, p.out, bh, b, h, r, sc.n, lane);
+        }
         if (lane == 0) p.counters[bh] = 0;
     }
 }

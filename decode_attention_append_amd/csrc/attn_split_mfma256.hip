@@ -389,7 +389,8 @@ void attn_split_mfma256_kernel(AttnParams p) {
     }
 
     // One-launch step: the workgroup that stores the last partial of (b, h)
-    // merges its rows (one wave per row) and resets the arrival counter.
+    // merges its rows (wave w takes rows w, w + 4, ..., two at a time) and
+    // resets the arrival counter.
     if (p.counters) {
         wait_mem();       // this wave's partial stores are complete
         __syncthreads();  // and so are the other waves'
@@ -398,7 +399,11 @@ void attn_split_mfma256_kernel(AttnParams p) {
                      sc.n - 1;
         __syncthreads();
         if (s_last) {
-            for (int r = wave; r < p.rows; r += kWaves) merge_row_wave<F16, kD>(p, p.out, bh, b, h, r, sc.n, lane);
+            if (sc.n <= 16) {
+                for (int r = wave; r < p.rows; r += 2 * kWaves) merge_two_rows_wave<F16, kD>(p, bh, b, h, r, kWaves, sc.n, lane);
+            } else {
+                for (int r = wave; r < p.rows; r += kWaves) merge_row_wave<F16, kD>(p, p.out, bh, b, h, r, sc.n, lane);
+            }
             if (tid == 0) p.counters[bh] = 0;
         }
     }

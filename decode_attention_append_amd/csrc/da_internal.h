@@ -623,6 +623,79 @@ __device__ inline void merge_row_wave(const AttnParams &p, uint16_t *out, int bh
     store_out<F16, NV>(p, out, out_row_off(p, b, h, r) + NV * lane, x);
 }
 
+// sigmoid(gate) of the NV output elements at `off` (1 without a gate).
+template <bool F16, int NV>
+__device__ __forceinline__ void gate_factors(const AttnParams &p, size_t off, float (&g)[NV]) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) g[k] = 1.f;
+    if (p.out_gate) {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) g[k] = sigmoid16<F16>(p.out_gate[off + k]);
+    }
+}
+
+// Merge of query rows r0 and r0 + r_step (when below p.rows) of (b, h) over their
+// n <= 16 chunks by one wave, with every load of both rows in flight at once:
+// the (m, l) pairs, the partial sums and the gate.  Same arithmetic as
+// merge_row_wave.
+template <bool F16, int D>
+__device__ inline void merge_two_rows_wave(const AttnParams &p, int bh, int b, int h, int r0, int r_step, int n,
+                                           int lane) {
+    constexpr int NV = D / 64;
+    const int r1 = r0 + r_step < p.rows ? r0 + r_step : r0;  // a missing second row repeats the first
+    const uint32_t cs_ml = (uint32_t)p.rows * 2;
+    const uint32_t cs_acc = (uint32_t)p.rows * D * 4;
+    const int voff = lane * NV * 4;
+    float m[2], l[2], v[2][16][NV], g[2][NV];
+    size_t off[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int r = j ? r1 : r0;
+        const size_t part = (size_t)bh * p.n_chunks * p.rows + r;
+        m[j] = -INFINITY;
+        l[j] = 0.f;
+        if (lane < n) {
+            m[j] = ld_dev(p.ws_ml + part * 2 + (size_t)lane * cs_ml);
+            l[j] = ld_dev(p.ws_ml + part * 2 + (size_t)lane * cs_ml + 1);
+        }
+        const __amdgpu_buffer_rsrc_t acc =
+            __builtin_amdgcn_make_buffer_rsrc(p.ws_acc + part * D, 0, (int)(cs_acc * (uint32_t)p.n_chunks), 0x00020000);
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            if (u < n) {
+                buffer_load_dims<NV>(v[j][u], acc, voff, u * cs_acc);
+            } else {
+#pragma unroll
+                for (int k = 0; k < NV; ++k) v[j][u][k] = 0.f;
+            }
+        }
+        off[j] = out_row_off(p, b, h, r) + NV * lane;
+        gate_factors<F16, NV>(p, off[j], g[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        if (j == 1 && r1 == r0) break;
+        const float M = wave_max(m[j]);
+        const float w = m[j] == -INFINITY ? 0.f : exp2_fast(m[j] - M);
+        const float L = wave_sum(w * l[j]);
+        float a[NV];
+#pragma unroll
+        for (int k = 0; k < NV; ++k) a[k] = 0.f;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            if (u < n) {
+                const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), u));
+#pragma unroll
+                for (int k = 0; k < NV; ++k) a[k] = fmaf(wu, v[j][u][k], a[k]);
+            }
+        }
+        uint32_t *o = reinterpret_cast<uint32_t *>(p.out + off[j]);
+#pragma unroll
+        for (int k = 0; k < NV; k += 2)
+            o[k / 2] = (uint32_t)round16<F16>(a[k] / L * g[j][k]) | ((uint32_t)round16<F16>(a[k + 1] / L * g[j][k + 1]) << 16);
+    }
+}
+
 // One-launch step: the output rows of sequence b, whose seq_pos breaks the
 // contract (it has no chunks), are flagged with NaN, as the separate combine
 // does.  Written by `n_lanes` lanes starting at `lane`.

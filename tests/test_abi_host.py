@@ -155,10 +155,10 @@ def test_plan_fused_merge(shape, fused):
 
 def test_plan_head_dim_256():
     """head_dim 256 always takes the MFMA kernel, one 4-wave workgroup per chunk, aiming
-    at 512 chunks."""
+    at 256 chunks."""
     for rows in (1, 8, 32):
         pl = da.plan_attention(P(head_dim=256, n_q_heads=2 * rows, n_kv_heads=2, batch=16))
-        assert pl["variant"] == "mfma" and pl["target_items"] == 512
+        assert pl["variant"] == "mfma" and pl["target_items"] == 256
     assert da.workspace_bytes(P(head_dim=256, variant="valu")) == 0
 
 
