@@ -10,14 +10,21 @@ The default workload is batched GQA decode with Hq 16 / Hkv 8 / head_dim 128,
 batch 32, context 8192, 28 layers (bf16, synthetic N(0,1)*0.5 inputs resident
 in HBM before timing starts).
 
+One whole step (every layer) is captured into a HIP graph once, after the
+warm-up steps, and the timed steps are its replays: each replay runs every
+layer's kernels on the same inputs, exactly as an eager step does (the graph
+tests check replays against eager steps bit for bit), without the host launch
+gaps between layers.  --eager times eagerly launched steps instead.
+
 Prints ONE JSON line: KV GB/s (algorithmic bytes per step / step time), ms per
 step, the attention kernel's roofline fraction against the 8 TB/s HBM peak
-(its average duration measured with HIP events on the launch stream during
-the timed steps), and the fp64 CPU oracle's rate on a bounded sample of the
-same workload.
+(its average duration measured with HIP events on the launch stream around
+every attention launch of K eagerly launched steps, right after the timed
+replays; with --eager, of the timed steps themselves), and the fp64 CPU
+oracle's rate on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--path step|separate]
-                    [--no-cpu-baseline]
+                    [--eager] [--no-cpu-baseline]
 """
 import argparse
 import json
@@ -45,9 +52,9 @@ def parse():
     ap.add_argument("--paged", action="store_true",
                     help="paged caches: every layer's K/V cache becomes a pool of 16-token pages in a "
                          "random order behind one block table")
-    ap.add_argument("--graph", action="store_true",
-                    help="capture one whole step (every layer) into a HIP graph and time its replays; the "
-                         "kernel roofline then comes from an eager pass of the same steps afterwards")
+    ap.add_argument("--eager", action="store_true",
+                    help="time eagerly launched steps instead of replays of the step captured into a HIP "
+                         "graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle sample")
@@ -243,7 +250,7 @@ def main():
         torch.cuda.synchronize()
         return sum(a.elapsed_time(b) for a, b in marks)
 
-    if args.graph:
+    if not args.eager:
         graph = torch.cuda.CUDAGraph()
         launch_stream[0] = None
         with torch.cuda.graph(graph):
@@ -304,7 +311,7 @@ def main():
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "context": int(seq_pos.max()) + w.q_len,
                    "max_seq": w.max_seq, "layers": w.layers, "chunk_tokens": plan["chunk_tokens"],
                    "target_items": plan["target_items"],
-                   "variant": plan["variant"], "path": args.path, "graph": args.graph,
+                   "variant": plan["variant"], "path": args.path, "graph": not args.eager,
                    "rope_theta": theta if freqs is not None else None,
                    "rope_dim": rope_dim if freqs is not None else None, "output_gate": w.gated,
                    "paged": args.paged,

@@ -10,15 +10,15 @@
 // workspace for the combine kernel.
 //
 // Mapping on gfx950 (wave64, v_mfma_f32_16x16x32_{bf16,f16}):
-//  - every wave owns one (b, h, chunk) and writes that chunk's partial
-//    itself: no barrier, no LDS and no cross-wave merge, so a wave never
-//    waits for its neighbours and keeps its loads in flight until its chunk
-//    ends.  Query rows come in RG groups of 16 (RG = 1 for up to 16 rows, 2
-//    for up to 32); with two groups a pair of waves shares one chunk, each
-//    computing its 16 rows from the same tiles (the second read of a tile is
-//    served by the compute unit's caches, not by HBM).  A wave streams its
-//    32-key tiles through two register buffers in turn, so its next tile is
-//    in flight while it computes the current one;
+//  - a 4-wave workgroup owns one (b, h, chunk).  Query rows come in RG
+//    groups of 16 (RG = 1 for up to 16 rows, 2 for up to 32); the 4 / RG
+//    waves of a row group take the chunk's 32-key tiles in turn (tile i by
+//    wave i mod 4/RG), each streaming its tiles through two register buffers
+//    so its next tile is in flight while it computes the current one.  With
+//    two groups every tile is read by two waves (the second read is served by
+//    the compute unit's caches, not by HBM).  At the end the waves' (m, l,
+//    acc) are merged through LDS in a fixed order and one partial per chunk is
+//    stored: a quarter of the partial traffic of one chunk per wave;
 //  - scores come out transposed, S^T[key][row] = K q^T, so lane l holds 8
 //    scores of ONE query row (row = l % 16) and that row's running max, sum
 //    and rescale factor stay in the lane; the scores then feed P V as its B
@@ -55,8 +55,6 @@ template <bool F16>
 __device__ __forceinline__ uint32_t pack16(float lo, float hi) {
     return (uint32_t)round16<F16>(lo) | ((uint32_t)round16<F16>(hi) << 16);
 }
-
-constexpr int kObufStride = kHeadDim + 4;
 
 // Key of slot u (0..7) of lane group q inside a 32-key tile, in the order the
 // P V product consumes them: keys 4q..4q+3, then 16+4q..16+4q+3.
@@ -142,60 +140,35 @@ __device__ __forceinline__ void load_rows(Tile &t, const CacheView &cv, int tb, 
     }
 }
 
-constexpr int kMfmaWaves = 4;  // waves per workgroup (independent chunks or pairs)
+constexpr int kMfmaWaves = 4;  // waves per workgroup, all on one chunk
 
 template <bool F16, int RG>
 __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_split_mfma_kernel(AttnParams p) {
-    constexpr int RB = 1;  // row blocks per wave
+    constexpr int KS = kMfmaWaves / RG;  // waves sharing one row group's tiles
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
-    const int rg = wave % RG;                                   // this wave's 16-row group
-    const int item = blockIdx.x * (kMfmaWaves / RG) + wave / RG;
+    const int rg = wave % RG, kw = wave / RG;                   // 16-row group, tile phase
 
-    const int n_chunks = p.n_chunks;
     int b, h, c;
     SeqChunks sc;
-    int rest = item;
+    int rest = blockIdx.x;
     int sp;
     if (!locate_wave(p, rest, b, h, c, sc, sp, lane)) {  // past the last chunk of the launch
-        if (p.out && rg == 0 && rest < p.batch && !seq_pos_ok(p, p.seq_pos[rest]))
-            flag_sequence_nan<F16>(p, rest, lane, 64);
+        if (p.out && rest < p.batch && !seq_pos_ok(p, p.seq_pos[rest]))
+            flag_sequence_nan<F16>(p, rest, tid, 64 * kMfmaWaves);
         return;
     }
     const int bh = b * p.n_kv_heads + h;
-    const int ctx = sc.ctx;
     const int t0 = c * sc.len;
-    const int n_tok = min(sc.len, ctx - t0);
+    const int n_tok = min(sc.len, sc.ctx - t0);
     const int last = n_tok - 1;
     const int l16 = lane & 15, q = lane >> 4;
 
-    // B operand of S^T = K q^T: lane holds q[row][dims 64s + 16q .. +16 bytes), s = 0..3
     // paged caches: lane j reads the pool page of the chunk's 16-token block j
-    // once, first, so its latency overlaps the query loads
     int pg_lane = 0;
     if (p.layout.block_table && lane < (n_tok + kPageTokens - 1) / kPageTokens)
         pg_lane = kv_page(p.layout, b, t0 / kPageTokens + lane);
-
-    u32x4_t qop[RB][4];
-    int vis[RB];  // exclusive local key limit of this lane's row
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        const int row = rg * 16 + l16;
-        if (row < p.rows) {
-            const int i = row / p.group, g = row - i * p.group;
-            const uint8_t *qp =
-                p.q + (((size_t)b * p.q_len + i) * p.n_q_heads + (size_t)h * p.group + g) * kRowBytes + 16 * q;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) qop[rb][s] = ld16(qp + 64 * s);
-            if (p.rope_freqs) rope_pieces<F16>(qop[rb], p.rope_dim, sp + i, p.rope_freqs, q);
-            vis[rb] = min(sp + i + 1 - t0, n_tok);
-        } else {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) qop[rb][s] = u32x4_t{0u, 0u, 0u, 0u};
-            vis[rb] = 0;
-        }
-    }
 
     CacheView cv;
     cv.k = p.k_cache;
@@ -210,84 +183,111 @@ void attn_split_mfma_kernel(AttnParams p) {
     cv.t0 = t0;
     cv.pg_lane = pg_lane;
 
-    float m_run[RB], l_run[RB];
-    f32x4_t oacc[RB][8];
+    // Tiles 0 .. nt-1 hold old cache rows only and load whole; this wave takes
+    // tiles kw, kw + KS, ... of them, the first already in flight while q loads.
+    const int new_first = p.k_new ? sp - t0 : n_tok;
+    const int n_all = (n_tok + 31) >> 5;
+    const int nt = min(n_tok >> 5, max(new_first, 0) >> 5);
+    const int nj = kw < nt ? (nt - kw + KS - 1) / KS : 0;
+    Tile ta, tb_;
+    if (nj > 0) load_full(ta, cv, kw * 32, l16, q);
+
+    // B operand of S^T = K q^T: lane holds q[row][dims 32s + 8q .. +7], s = 0..3
+    u32x4_t qop[4];
+    int vis;  // exclusive local key limit of this lane's row
+    const int row = rg * 16 + l16;
+    if (row < p.rows) {
+        const int i = row / p.group, g = row - i * p.group;
+        const uint8_t *qp =
+            p.q + (((size_t)b * p.q_len + i) * p.n_q_heads + (size_t)h * p.group + g) * kRowBytes + 16 * q;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        m_run[rb] = -INFINITY;
-        l_run[rb] = 0.f;
+        for (int s = 0; s < 4; ++s) qop[s] = ld16(qp + 64 * s);
+        if (p.rope_freqs) rope_pieces<F16>(qop, p.rope_dim, sp + i, p.rope_freqs, q);
+        vis = min(sp + i + 1 - t0, n_tok);
+    } else {
 #pragma unroll
-        for (int o = 0; o < 8; ++o) oacc[rb][o] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < 4; ++s) qop[s] = u32x4_t{0u, 0u, 0u, 0u};
+        vis = 0;
     }
 
-    const int n_tile = (n_tok + 31) >> 5;
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4_t oacc[8];
+#pragma unroll
+    for (int o = 0; o < 8; ++o) oacc[o] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     // One 32-key tile: S^T, online softmax, O^T += V^T P^T.
     auto compute = [&](Tile &t, int tt) {
         const int tb = tt * 32;
+        // S^T for the two 16-key blocks: lane holds keys tb + 16*kblk + 4q + v of its row
+        f32x4_t st[2];
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            // S^T for the two 16-key blocks: lane holds keys tb + 16*kblk + 4q + v of its row
-            f32x4_t st[2];
+        for (int kblk = 0; kblk < 2; ++kblk) {
+            st[kblk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kblk = 0; kblk < 2; ++kblk) {
-                st[kblk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < 4; ++s) st[kblk] = mfma16<F16>(t.k[kblk][s], qop[s], st[kblk]);
+        }
+        float s2[8];
+        float mt = -INFINITY;
 #pragma unroll
-                for (int s = 0; s < 4; ++s) st[kblk] = mfma16<F16>(t.k[kblk][s], qop[rb][s], st[kblk]);
+        for (int kblk = 0; kblk < 2; ++kblk)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int key = tb + 16 * kblk + 4 * q + v;
+                const float x = key < vis ? st[kblk][v] * p.scale_log2 : -INFINITY;
+                s2[4 * kblk + v] = x;
+                mt = fmaxf(mt, x);
             }
-            float s2[8];
-            float mt = -INFINITY;
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = (m_run == -INFINITY) ? 0.f : exp2_fast(m_run - m_new);
+        float pv[8];
+        float psum = 0.f;
 #pragma unroll
-            for (int kblk = 0; kblk < 2; ++kblk)
+        for (int u = 0; u < 8; ++u) {
+            pv[u] = (m_new == -INFINITY) ? 0.f : round_trip16<F16>(exp2_fast(s2[u] - m_new));
+            psum += pv[u];
+        }
+        if (__any(m_new != m_run)) {
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int key = tb + 16 * kblk + 4 * q + v;
-                    const float x = key < vis[rb] ? st[kblk][v] * p.scale_log2 : -INFINITY;
-                    s2[4 * kblk + v] = x;
-                    mt = fmaxf(mt, x);
-                }
-            mt = fmaxf(mt, __shfl_xor(mt, 16));
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
-            const float m_new = fmaxf(m_run[rb], mt);
-            const float alpha = (m_run[rb] == -INFINITY) ? 0.f : exp2_fast(m_run[rb] - m_new);
-            float pv[8];
-            float psum = 0.f;
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                pv[u] = (m_new == -INFINITY) ? 0.f : round_trip16<F16>(exp2_fast(s2[u] - m_new));
-                psum += pv[u];
-            }
-            if (__any(m_new != m_run[rb])) {
-#pragma unroll
-                for (int o = 0; o < 8; ++o) oacc[rb][o] *= alpha;
-            }
-            l_run[rb] = l_run[rb] * alpha + psum;
-            m_run[rb] = m_new;
+            for (int o = 0; o < 8; ++o) oacc[o] *= alpha;
+        }
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
 
-            // B operand of O^T: P^T, slot u <-> key pv_key(q, u) = s2 index u
-            u32x4_t pop;
+        // B operand of O^T: P^T, slot u <-> key pv_key(q, u) = s2 index u
+        u32x4_t pop;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) pop[j] = pack16<F16>(pv[2 * j], pv[2 * j + 1]);
+        for (int j = 0; j < 4; ++j) pop[j] = pack16<F16>(pv[2 * j], pv[2 * j + 1]);
 #pragma unroll
-            for (int o = 0; o < 8; ++o) {
-                const int word = o >> 1;
-                const uint32_t sel = (o & 1) ? 0x07060302u : 0x05040100u;
-                u32x4_t vop;
+        for (int o = 0; o < 8; ++o) {
+            const int word = o >> 1;
+            const uint32_t sel = (o & 1) ? 0x07060302u : 0x05040100u;
+            u32x4_t vop;
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    vop[j] = __builtin_amdgcn_perm(t.v[2 * j + 1][word], t.v[2 * j][word], sel);
-                oacc[rb][o] = mfma16<F16>(vop, pop, oacc[rb][o]);
-            }
+            for (int j = 0; j < 4; ++j) vop[j] = __builtin_amdgcn_perm(t.v[2 * j + 1][word], t.v[2 * j][word], sel);
+            oacc[o] = mfma16<F16>(vop, pop, oacc[o]);
         }
     };
 
-    // Full tiles below this step's new rows go through two register buffers used
-    // in turn, with no copy between them, so the wave waits only for the older
-    // tile while the newer one is in flight.  When their count is even the last
-    // prefetch re-reads the final tile (from cache) and is not used.  The tiles
-    // that hold new rows or run past the chunk take the per-row path.
+    // full tiles through two register buffers used in turn, with no copy
+    // between them, so the wave waits only for the older tile while the newer
+    // one is in flight
+    if (nj > 0) {
+        int j = 0;
+        for (; j + 2 <= nj; j += 2) {
+            load_full(tb_, cv, (kw + KS * (j + 1)) * 32, l16, q);
+            compute(ta, kw + KS * j);
+            if (j + 2 < nj) load_full(ta, cv, (kw + KS * (j + 2)) * 32, l16, q);
+            compute(tb_, kw + KS * (j + 1));
+        }
+        if (j < nj) compute(ta, kw + KS * j);
+    }
+
+    // The tiles that hold new rows or run past the chunk take the per-row path,
+    // tile i by wave i mod KS of the row group.
     RowSource rs;
-    rs.new_first = p.k_new ? sp - t0 : n_tok;
+    rs.new_first = new_first;
     rs.t0 = t0;
     rs.rope = p.k_new ? p.rope_freqs : nullptr;
     rs.rope_dim = p.rope_dim;
@@ -300,35 +300,66 @@ void attn_split_mfma_kernel(AttnParams p) {
     } else {
         rs.knew = rs.vnew = nullptr;
     }
-    const int n_all = (n_tok + 31) >> 5;
-    const int nt = min(n_tok >> 5, max(rs.new_first, 0) >> 5);
-    if (nt > 0) {
-        Tile ta, tb_;
-        load_full(ta, cv, 0, l16, q);
-        int i = 0;
-        for (; i + 2 <= nt; i += 2) {
-            load_full(tb_, cv, (i + 1) * 32, l16, q);
-            compute(ta, i);
-            load_full(ta, cv, min(i + 2, nt - 1) * 32, l16, q);
-            compute(tb_, i + 1);
-        }
-        if (i < nt) compute(ta, i);
-    }
     for (int i = nt; i < n_all; ++i) {
+        if (i % KS != kw) continue;
         Tile tt_;
         load_rows<F16>(tt_, cv, i * 32, last, l16, q, rs);
         compute(tt_, i);
     }
 
-    // ---- this wave's partial: O^T (lane: row l16, dims 8*(4q+v)+o), m, l ---------
+    // ---- merge of the KS waves of a row group, then one partial per chunk ------
+    // lane: row l16, dims 8 (4q + v) + o in oacc[o][v]
+    __shared__ float mlsh[kMfmaWaves][16][2];
+    __shared__ f32x4_t red[2][8][64];  // two slots, lane-private layout
+    __shared__ int s_last;
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+    if (q == 0) {
+        mlsh[wave][l16][0] = m_run;
+        mlsh[wave][l16][1] = l_run;
+    }
+    __syncthreads();
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) M = fmaxf(M, mlsh[rg + RG * k][l16][0]);
+    float L = 0.f;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+        const float mk = mlsh[rg + RG * k][l16][0];
+        L += mk == -INFINITY ? 0.f : exp2_fast(mk - M) * mlsh[rg + RG * k][l16][1];
+    }
+    {
+        const float f = m_run == -INFINITY ? 0.f : exp2_fast(m_run - M);
+#pragma unroll
+        for (int o = 0; o < 8; ++o) oacc[o] *= f;
+    }
+    auto put = [&](int slot) {
+#pragma unroll
+        for (int o = 0; o < 8; ++o) red[slot][o][lane] = oacc[o];
+    };
+    auto add = [&](int slot) {
+#pragma unroll
+        for (int o = 0; o < 8; ++o) oacc[o] += red[slot][o][lane];
+    };
+    if constexpr (KS == 4) {  // (0 + 2) + (1 + 3)
+        if (kw >= 2) put(kw - 2);
+        __syncthreads();
+        if (kw < 2) add(kw);
+        __syncthreads();
+        if (kw == 1) put(0);
+        __syncthreads();
+        if (kw == 0) add(0);
+    } else {
+        if (kw == 1) put(rg);
+        __syncthreads();
+        if (kw == 0) add(rg);
+    }
+
     // When the one-launch step merges in this launch, device-scope stores (the
     // merge may read them from another XCD); else plain stores, which the L2
     // gathers into whole lines (a lane's 16-byte pieces are scattered).
-    l_run[0] += __shfl_xor(l_run[0], 16);
-    l_run[0] += __shfl_xor(l_run[0], 32);
-    const int row = rg * 16 + l16;
-    if (row < p.rows) {
-        const size_t part = ((size_t)bh * n_chunks + c) * p.rows + row;
+    if (kw == 0 && row < p.rows) {
+        const size_t part = ((size_t)bh * p.n_chunks + c) * p.rows + row;
         float *wa = p.ws_acc + part * kHeadDim;
         const bool dev = p.counters != nullptr;
 #pragma unroll
@@ -338,46 +369,53 @@ void attn_split_mfma_kernel(AttnParams p) {
                 // dims 8*(4q+v) + o .. +3 are four consecutive floats of this lane
                 float *dst = wa + 8 * (4 * q + v) + o;
                 if (dev) {
-                    st_dev4(dst, oacc[0][o][v], oacc[0][o + 1][v], oacc[0][o + 2][v], oacc[0][o + 3][v]);
+                    st_dev4(dst, oacc[o][v], oacc[o + 1][v], oacc[o + 2][v], oacc[o + 3][v]);
                 } else {
-                    *reinterpret_cast<float4 *>(dst) =
-                        make_float4(oacc[0][o][v], oacc[0][o + 1][v], oacc[0][o + 2][v], oacc[0][o + 3][v]);
+                    *reinterpret_cast<float4 *>(dst) = make_float4(oacc[o][v], oacc[o + 1][v], oacc[o + 2][v], oacc[o + 3][v]);
                 }
             }
         if (q == 0) {
             if (dev) {
-                st_dev(p.ws_ml + part * 2 + 0, m_run[0]);
-                st_dev(p.ws_ml + part * 2 + 1, l_run[0]);
+                st_dev(p.ws_ml + part * 2 + 0, M);
+                st_dev(p.ws_ml + part * 2 + 1, L);
             } else {
-                p.ws_ml[part * 2 + 0] = m_run[0];
-                p.ws_ml[part * 2 + 1] = l_run[0];
+                p.ws_ml[part * 2 + 0] = M;
+                p.ws_ml[part * 2 + 1] = L;
             }
         }
     }
 
-    // One-launch step: the wave whose partial arrives last for (b, h) merges all
-    // its rows and resets the arrival counter for the next call.
-    if (p.counters && last_arrival(&p.counters[bh], sc.n * RG, lane)) {
-        if (sc.n <= 16) {
-            for (int r = 0; r < p.rows; r += 2) merge_two_rows_wave<F16, kHeadDim>(p, bh, b, h, r, 1, sc.n, lane);
-        } else {
-            for (int r = 0; r < p.rows; ++r) merge_row_wave<F16, kHeadDim>(p, p.out, bh, b, h, r, sc.n, lane);
+    // One-launch step: the workgroup that stores the last partial of (b, h)
+    // merges its rows (wave w takes rows w, w + 4, ..., two at a time) and
+    // resets the arrival counter for the next call.
+    if (p.counters) {
+        wait_mem();       // this wave's partial stores are complete
+        __syncthreads();  // and so are the other waves'
+        if (tid == 0)
+            s_last = __hip_atomic_fetch_add(&p.counters[bh], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                     sc.n - 1;
+        __syncthreads();
+        if (s_last) {
+            if (sc.n <= 16) {
+                for (int r = wave; r < p.rows; r += 2 * kMfmaWaves)
+                    merge_two_rows_wave<F16, kHeadDim>(p, bh, b, h, r, kMfmaWaves, sc.n, lane);
+            } else {
+                for (int r = wave; r < p.rows; r += kMfmaWaves)
+                    merge_row_wave<F16, kHeadDim>(p, p.out, bh, b, h, r, sc.n, lane);
+            }
+            if (tid == 0) p.counters[bh] = 0;
         }
-        if (lane == 0) p.counters[bh] = 0;
     }
 }
 
-// `items` = chunks in the launch (an upper bound); a workgroup takes 4 of them
-// (16-row problems) or 2 wave pairs (17..32 rows).
+// `items` = chunks in the launch (an upper bound), one workgroup each: four
+// waves over the chunk's tiles (up to 16 rows), or two pairs (17..32 rows).
 template <bool F16>
 static hipError_t launch_dtype(const AttnParams &p, int items, hipStream_t s) {
-    if (p.rows <= 16) {
-        const int grid = (items + kMfmaWaves - 1) / kMfmaWaves;
-        hipLaunchKernelGGL((attn_split_mfma_kernel<F16, 1>), dim3(grid), dim3(64 * kMfmaWaves), 0, s, p);
-    } else {
-        const int grid = (items + kMfmaWaves / 2 - 1) / (kMfmaWaves / 2);
-        hipLaunchKernelGGL((attn_split_mfma_kernel<F16, 2>), dim3(grid), dim3(64 * kMfmaWaves), 0, s, p);
-    }
+    if (p.rows <= 16)
+        hipLaunchKernelGGL((attn_split_mfma_kernel<F16, 1>), dim3(items), dim3(64 * kMfmaWaves), 0, s, p);
+    else
+        hipLaunchKernelGGL((attn_split_mfma_kernel<F16, 2>), dim3(items), dim3(64 * kMfmaWaves), 0, s, p);
     return hipGetLastError();
 }
 

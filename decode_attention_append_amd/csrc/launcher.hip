@@ -66,17 +66,14 @@ da_status check_problem(const da_problem *p) {
 
 // Chunks to aim for in balanced mode, per kernel: a few per compute unit (256
 // on MI355X) at the kernel's occupancy.  A vector-ALU chunk is a 4-wave
-// workgroup (about 7 fit per compute unit); a head_dim-128 MFMA chunk is one
-// wave, or a pair of waves above 16 rows (8 waves fit per compute unit); a
-// head_dim-256 MFMA chunk is a 4-wave workgroup, one per compute unit, so that
-// every wave streams long runs of tiles (measured on 16 x 2 KV heads at 8k
-// context: 52.8 us at 256 chunks, 55.3 us at 512, 56.2 us at 1024).
-int default_target(int variant, int rows, int head_dim) {
-    if (variant == DA_VARIANT_MFMA) {
-        if (head_dim != kHeadDim) return 256;
-        return rows > 16 ? 1024 : 2048;
-    }
-    return 1024;
+// workgroup (about 7 fit per compute unit).  An MFMA chunk is a 4-wave
+// workgroup too, whose waves share the chunk's tiles: one per compute unit
+// keeps every wave streaming long runs of tiles.  Measured (attention launch,
+// separate path): GQA-8 at 12k-16k context 50.0 / 49.7 / 52.1 us and the
+// 4-token verify 27.6 / 28.7 / 34.6 us at 256 / 512 / 1024 chunks; head_dim 256
+// on 16 x 2 KV heads at 8k context 52.8 / 55.3 / 56.2 us.
+int default_target(int variant) {
+    return variant == DA_VARIANT_MFMA ? 256 : 1024;
 }
 
 // Longest chunk a kernel accepts: the vector-ALU kernel keeps the chunk's
@@ -97,18 +94,16 @@ constexpr int kMinChunk = 64;
 constexpr int kMfmaRows = 8;
 
 // Most chunk-rows (chunks x query rows) one (sequence, KV head) may have for
-// the one-launch step to merge them inside the attention launch: one wave
-// merges them on the MFMA kernel (eight chunk loads in flight), a whole
-// workgroup on the vector-ALU kernel (32 in flight).  Beyond that the separate
-// combine launch, with a workgroup per row, finishes sooner.
-constexpr int kFusedMergeRowsWave = 64;
-constexpr int kFusedMergeRowsBlock = 512;
+// the one-launch step to merge them inside the attention launch, where the
+// last workgroup of the (sequence, KV head) merges: on the MFMA kernels its
+// four waves take two rows at a time with every load in flight, on the
+// vector-ALU kernel the workgroup splits rows or chunks.  Beyond that the
+// separate combine launch, with a workgroup per row, finishes sooner.
+constexpr int kFusedMergeRowsMfma = 256;
+constexpr int kFusedMergeRowsValu = 512;
 
-// The head_dim-256 MFMA kernel merges in the last workgroup of a (sequence,
-// KV head), one wave per row: four times the one-wave budget.
-int fused_merge_rows(int variant, int head_dim) {
-    if (variant != DA_VARIANT_MFMA) return kFusedMergeRowsBlock;
-    return head_dim != kHeadDim ? 4 * kFusedMergeRowsWave : kFusedMergeRowsWave;
+int fused_merge_rows(int variant) {
+    return variant == DA_VARIANT_MFMA ? kFusedMergeRowsMfma : kFusedMergeRowsValu;
 }
 
 // Chunks per sequence (balanced mode) when the one-launch step merges in the
@@ -142,7 +137,7 @@ void plan_of(const da_problem *p, da_plan *pl) {
         // keeps ceil(ctx / max_chunk) within them, so no chunk exceeds max_chunk
         const int slots = (p->max_seq + kMinChunk - 1) / kMinChunk;
         pl->n_chunks = slots < kMaxChunks ? slots : kMaxChunks;
-        pl->target_items = p->work_items > 0 ? p->work_items : default_target(variant, rows, p->head_dim);
+        pl->target_items = p->work_items > 0 ? p->work_items : default_target(variant);
         // at most target + one rounding chunk per (sequence, head), or every
         // sequence in chunks of max_chunk keys when the target is too few
         const int64_t a = (int64_t)pl->target_items + units;
@@ -161,7 +156,7 @@ void plan_of(const da_problem *p, da_plan *pl) {
         if (bound < nb_max) nb_max = bound;
     }
     pl->fused_combine = one_launch_capable(variant, rows) &&
-                        nb_max * rows <= fused_merge_rows(variant, p->head_dim);
+                        nb_max * rows <= fused_merge_rows(variant);
     const int32_t bh = units;
     pl->workspace_bytes = align256(ws_acc_floats(bh, pl->n_chunks, rows, p->head_dim) * sizeof(float)) +
                           align256(ws_ml_floats(bh, pl->n_chunks, rows) * sizeof(float)) +

@@ -132,9 +132,10 @@ def test_decode_step_rejects_before_launch():
     (dict(batch=32, n_q_heads=16, n_kv_heads=8, max_seq=8192), True),    # vector ALU, 2 rows
     (dict(batch=1, n_q_heads=16, n_kv_heads=16, max_seq=4096, dtype="fp16"), True),  # MHA
     (dict(batch=1, max_seq=512), True),
-    (dict(batch=4, n_q_heads=64, n_kv_heads=8, max_seq=16384), False),   # MFMA, 8 rows, long
+    (dict(batch=4, n_q_heads=64, n_kv_heads=8, max_seq=16384), True),    # MFMA, 8 rows x 16 chunks
     (dict(batch=8, q_len=4, n_q_heads=32, n_kv_heads=4, max_seq=8192), False),  # MFMA, 32 rows
     (dict(batch=1, n_q_heads=64, n_kv_heads=8, max_seq=512), True),      # MFMA, 8 chunks at most
+    (dict(batch=1, n_q_heads=64, n_kv_heads=2, max_seq=65536), False),   # MFMA, 32 rows x 16 chunks
     (dict(batch=1, n_q_heads=16, n_kv_heads=1, max_seq=65536, variant="valu"), False),
     # head_dim 256: the last workgroup merges, up to 256 chunk-rows
     (dict(batch=16, n_q_heads=16, n_kv_heads=2, head_dim=256, max_seq=8192, dtype="fp16"), True),
@@ -155,7 +156,8 @@ def test_plan_fused_merge(shape, fused):
 
 def test_plan_head_dim_256():
     """head_dim 256 always takes the MFMA kernel, one 4-wave workgroup per chunk, aiming
-    at 256 chunks."""
+    at 256 chunks like the head_dim-128 MFMA kernel."""
+    assert da.plan_attention(P(n_q_heads=64))["target_items"] == 256
     for rows in (1, 8, 32):
         pl = da.plan_attention(P(head_dim=256, n_q_heads=2 * rows, n_kv_heads=2, batch=16))
         assert pl["variant"] == "mfma" and pl["target_items"] == 256

@@ -21,8 +21,8 @@ def _say(*a):
 
 @pytest.mark.parametrize("B,q_len,Hq,Hkv,S,seq_pos,variant", [
     (2, 1, 16, 8, 700, [699, 345], None),                  # vector ALU, merge in the launch
-    (2, 1, 64, 8, 3000, [2999, 1537], None),               # MFMA, separate merge: two launches
-    (2, 4, 32, 4, 2100, [2096, 777], None),                # MFMA, 32 rows, causal
+    (2, 1, 64, 8, 3000, [2999, 1537], None),               # MFMA, merge in the launch
+    (2, 4, 32, 4, 2100, [2096, 777], None),                # MFMA, 32 rows, causal, separate merge: two launches
     (2, 2, 32, 4, 900, [898, 250], "valu"),                # forced 16-row VALU: three launches
 ])
 def test_graph_replays_match_eager(B, q_len, Hq, Hkv, S, seq_pos, variant):

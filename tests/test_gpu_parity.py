@@ -277,7 +277,7 @@ def test_kernel_reads_caller_data():
 @pytest.mark.parametrize("B,q_len,Hq,Hkv,S,sp0,fused", [
     (3, 1, 16, 8, 3000, [2990, 100, 1500], True),      # vector ALU, merge in the launch
     (1, 1, 64, 8, 512, [500], True),                   # MFMA, 8 rows, merge in the launch
-    (4, 1, 64, 8, 16384, [15000, 12288, 16380, 13000], False),  # MFMA, separate merge
+    (4, 1, 64, 8, 16384, [15000, 12288, 16380, 13000], True),   # MFMA, 8 rows x 16 chunks merged in the launch
     (2, 4, 32, 4, 2100, [2000, 60], False),            # MFMA, 32 rows, separate merge
     (2, 4, 8, 8, 700, [600, 61], True),                # vector ALU, 4 draft tokens
 ])
