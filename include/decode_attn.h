@@ -63,7 +63,7 @@ extern "C" {
 typedef enum {
     DA_OK = 0,
     DA_ERR_INVALID_ARG = -1, /* null or misaligned pointer, non-positive size, Hq % Hkv != 0 */
-    DA_ERR_UNSUPPORTED = -2, /* valid but not implemented: head_dim != 128, q_len > 8, ... */
+    DA_ERR_UNSUPPORTED = -2, /* valid but not implemented: head_dim other than 128 / 256, q_len > 8, ... */
     DA_ERR_WORKSPACE = -3,   /* workspace smaller than da_workspace_bytes() */
     DA_ERR_HIP = -4          /* the HIP runtime refused a launch */
 } da_status;
@@ -119,12 +119,14 @@ typedef struct {
     int32_t rope_dim;     /* with rope_freqs: rotate only the first rope_dim dims of
                              each q / k row (pairs j and j + rope_dim/2; the table
                              holds rope_dim/2 values); 0 = head_dim.  64, 128 or 256
-                             ("Architecture Diagram - Qwen3.5-35B-A3B": partial
-                             RoPE over 25% of the 256 dims)                       */
+                             ("Qwen MoE BringUp", Model Architectures table and
+                             "Architecture Diagram - Qwen3.5-35B-A3B": the rotary
+                             embedding covers a quarter of the 256 dims)          */
     const void *out_gate; /* DEVICE [B][q_len][Hq][head_dim] in p->dtype, 16-byte
                              aligned, or NULL: the output is multiplied elementwise
-                             by sigmoid(gate) before rounding (the same diagram's
-                             full-SDPA layers: "Q(->8192)+gate", "sigmoid gate")   */
+                             by sigmoid(gate) in fp32 before rounding (the same
+                             diagram's full-SDPA layers, whose Q projection also
+                             yields a gate applied through a sigmoid)             */
 } da_problem;
 
 /*
@@ -136,9 +138,8 @@ typedef struct {
  * `target_items` chunks in all), never longer than `chunk_tokens` (the plan's
  * maximum) and never shorter than 64 keys.  With an explicit chunk_tokens every
  * chunk has that length.  Either way the attention and the combine derive the
- * same chunks from the same seq_pos.  A chunk is the work of one workgroup on
- * the vector-ALU kernel and of one wave (a pair of waves above 16 rows) on the
- * MFMA kernel.
+ * same chunks from the same seq_pos.  A chunk is the work of one 4-wave
+ * workgroup on every kernel.
  */
 typedef struct {
     int32_t chunk_tokens;    /* longest chunk (fixed mode: every chunk)          */
@@ -159,7 +160,8 @@ enum { DA_VARIANT_VALU = 0, DA_VARIANT_MFMA = 1 };
  * Plans the attention of *p: chunking, kernel variant, workspace size.  The
  * automatic variant is the MFMA kernel when rows >= 8 (Q K^T and P V are then
  * small matrix products, and on the vector ALU they would cost more issue
- * slots than streaming the keys from HBM), the vector-ALU kernel otherwise.
+ * slots than streaming the keys from HBM) and always for head_dim 256, the
+ * vector-ALU kernel otherwise.
  * Returns DA_OK, DA_ERR_INVALID_ARG or DA_ERR_UNSUPPORTED.  Host only.
  */
 da_status da_plan_attention(const da_problem *p, da_plan *plan);
