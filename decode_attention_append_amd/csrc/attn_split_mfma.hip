@@ -310,7 +310,7 @@ void attn_split_mfma_kernel(AttnParams p) {
     // ---- merge of the KS waves of a row group, then one partial per chunk ------
     // lane: row l16, dims 8 (4q + v) + o in oacc[o][v]
     __shared__ float mlsh[kMfmaWaves][16][2];
-    __shared__ f32x4_t red[2][8][64];  // two slots, lane-private layout
+    __shared__ f32x4_t red[3][8][64];  // three slots, lane-private layout
     __shared__ int s_last;
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
@@ -333,26 +333,28 @@ void attn_split_mfma_kernel(AttnParams p) {
 #pragma unroll
         for (int o = 0; o < 8; ++o) oacc[o] *= f;
     }
-    auto put = [&](int slot) {
+    // waves 1.. of a row group write their sums, one barrier, wave 0 adds them
+    // in a fixed order: (0 + 1) + (2 + 3), or 0 + 1 with two row groups
+    if constexpr (KS == 4) {
+        if (kw > 0) {
 #pragma unroll
-        for (int o = 0; o < 8; ++o) red[slot][o][lane] = oacc[o];
-    };
-    auto add = [&](int slot) {
+            for (int o = 0; o < 8; ++o) red[kw - 1][o][lane] = oacc[o];
+        }
+        __syncthreads();
+        if (kw == 0) {
 #pragma unroll
-        for (int o = 0; o < 8; ++o) oacc[o] += red[slot][o][lane];
-    };
-    if constexpr (KS == 4) {  // (0 + 2) + (1 + 3)
-        if (kw >= 2) put(kw - 2);
-        __syncthreads();
-        if (kw < 2) add(kw);
-        __syncthreads();
-        if (kw == 1) put(0);
-        __syncthreads();
-        if (kw == 0) add(0);
+            for (int o = 0; o < 8; ++o) oacc[o] = (oacc[o] + red[0][o][lane]) + (red[1][o][lane] + red[2][o][lane]);
+        }
     } else {
-        if (kw == 1) put(rg);
+        if (kw == 1) {
+#pragma unroll
+            for (int o = 0; o < 8; ++o) red[rg][o][lane] = oacc[o];
+        }
         __syncthreads();
-        if (kw == 0) add(rg);
+        if (kw == 0) {
+#pragma unroll
+            for (int o = 0; o < 8; ++o) oacc[o] += red[rg][o][lane];
+        }
     }
 
     // When the one-launch step merges in this launch, device-scope stores (the

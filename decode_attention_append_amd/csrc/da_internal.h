@@ -114,6 +114,9 @@ struct AttnParams {
     const uint16_t *out_gate; // [B][q_len][Hq][D] sigmoid output gate, or null
     int32_t seq_chunk_cap; // balanced: at most this many chunks per sequence unless its
                            //   length needs more of max_chunk keys (0: no cap)
+    int32_t chunk_align;   // balanced: a sequence whose chunks would be at least half
+                           //   this long gets lengths rounded up to a multiple of it
+                           //   (a multiple of 32; 32: no effect)
 
     // One-launch step (all null for the separate entry points):
     uint8_t *k_cache_w;        // k_cache as writable: the fused append stores new rows here
@@ -182,7 +185,10 @@ __host__ __device__ inline SeqChunks seq_chunks_at(const AttnParams &p, int sp, 
     if (n < 1) n = 1;
     if (n > p.n_chunks) n = p.n_chunks;
     s.n = n;
-    s.len = round_up32(ceil_div(s.ctx, n));
+    const int raw = round_up32(ceil_div(s.ctx, n));
+    const int a = p.chunk_align;
+    s.len = a > 32 && 2 * raw >= a ? (raw + a - 1) / a * a : raw;
+    if (s.len > p.max_chunk) s.len = p.max_chunk;  // raw <= max_chunk: no chunk is shorter than raw
     s.n = ceil_div(s.ctx, s.len);  // rounding the length up may leave the last chunk empty
     return s;
 }

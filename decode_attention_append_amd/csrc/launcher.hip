@@ -86,6 +86,23 @@ int max_chunk_of(int variant, int rows) {
 
 constexpr int kMinChunk = 64;
 
+// Balanced chunk lengths on the head_dim-128 MFMA kernel are rounded up to whole
+// multiples of 512 KiB of K (and V) rows, 2048 keys, when a chunk would be at
+// least half that long, so chunks start on 512 KiB boundaries of a (sequence,
+// KV head) stream.  Measured with the attention launch alone on the GQA-8
+// long-context workload (contexts 12k-16k): 47.8-48.2 us against 50.1-50.6 us
+// with 32-key rounding (256 KiB: 47.5-48.2 us, but it lengthens the 4-token
+// verify's chunks and costs it 24%).  On the head_dim-256 kernel the same
+// rounding slows the one-launch step by 1.6%, so there chunks keep 32-key
+// rounding; the vector-ALU kernel's chunks are already whole 2048-key runs on
+// full-length batches.
+constexpr int kMfma128ChunkAlignBytes = 512 * 1024;
+
+int chunk_align_of(int variant, int head_dim) {
+    if (variant != DA_VARIANT_MFMA || head_dim != kHeadDim) return 32;
+    return kMfma128ChunkAlignBytes / (head_dim * 2);
+}
+
 // Rows per KV head from which the matrix-core kernel is used.  Below 8 rows the
 // vector-ALU kernel is memory-bound (its dot products cost about 4 wave
 // instructions per key and row); at 8 rows it needs some 34 wave instructions
@@ -206,6 +223,7 @@ AttnParams attn_params(const da_problem *p, const da_plan &pl, const void *q, co
     const double scale = p->scale > 0.f ? (double)p->scale : 1.0 / sqrt((double)p->head_dim);
     a.scale_log2 = (float)(scale * 1.4426950408889634);  // log2(e)
     a.seq_chunk_cap = 0;
+    a.chunk_align = chunk_align_of(pl.variant, p->head_dim);
     a.rope_freqs = p->rope_freqs;
     a.rope_dim = p->rope_dim ? p->rope_dim : p->head_dim;
     a.layout = layout_of(p);

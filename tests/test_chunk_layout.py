@@ -85,3 +85,31 @@ def test_fixed_chunks_match_override():
     p = da.problem(2, 1, 16, 8, 128, 2500, "bf16", chunk_tokens=256)
     _, lay, _ = check_layout(p, np.array([2499, 1300], np.int32))
     assert lay == [(10, 256), (6, 256)]
+
+
+def test_mfma128_chunks_start_on_512k_boundaries():
+    """On the head_dim-128 MFMA kernel a balanced chunk that would be at least 1024 keys
+    long is rounded up to a multiple of 2048 keys (512 KiB of K or V rows), so every
+    chunk of such a sequence starts on a 512 KiB boundary of its stream; shorter chunks
+    keep 32-key rounding, and head_dim 256 is not rounded."""
+    rng = np.random.default_rng(5)
+    p = da.problem(4, 1, 64, 8, 128, 16384, "bf16")
+    assert da.plan_attention(p)["variant"] == "mfma"
+    sp = rng.integers(12287, 16384, 4).astype(np.int32)
+    _, lay, total = check_layout(p, sp)
+    assert all(ln % 2048 == 0 for _, ln in lay)
+    assert total <= 256
+    # short contexts: chunks under 1024 keys stay 32-key multiples
+    sp = np.array([3000, 2000, 5000, 4000], np.int32)
+    _, lay, _ = check_layout(p, sp)
+    assert any(ln % 2048 for _, ln in lay)
+    # head_dim 256 keeps 32-key rounding
+    p = da.problem(16, 1, 16, 2, 256, 8192, "fp16")
+    sp = rng.integers(6143, 8192, 16).astype(np.int32)
+    _, lay, _ = check_layout(p, sp)
+    assert any(ln % 1024 for _, ln in lay)
+    # the vector-ALU kernel is unaffected
+    p = da.problem(4, 1, 16, 8, 128, 16384, "bf16")
+    sp = rng.integers(12287, 16384, 4).astype(np.int32)
+    _, lay, _ = check_layout(p, sp)
+    assert any(ln % 2048 for _, ln in lay)
