@@ -10,15 +10,15 @@
 // workspace for the combine kernel.
 //
 // Mapping on gfx950 (wave64, v_mfma_f32_16x16x32_{bf16,f16}):
-//  - a 4-wave workgroup owns one (b, h, chunk).  Query rows come in RG
-//    groups of 16 (RG = 1 for up to 16 rows, 2 for up to 32); the 4 / RG
-//    waves of a row group take the chunk's 32-key tiles in turn (tile i by
-//    wave i mod 4/RG), each streaming its tiles through two register buffers
-//    so its next tile is in flight while it computes the current one.  With
-//    two groups every tile is read by two waves (the second read is served by
-//    the compute unit's caches, not by HBM).  At the end the waves' (m, l,
-//    acc) are merged through LDS in a fixed order and one partial per chunk is
-//    stored: a quarter of the partial traffic of one chunk per wave;
+//  - a 4-wave workgroup owns one (b, h, chunk); its waves take the chunk's
+//    32-key tiles in turn (tile i by wave i mod 4), each streaming its tiles
+//    through two register buffers so its next tile is in flight while it
+//    computes the current one.  Every wave computes every query row of the
+//    KV head: rows come in blocks of 16 (one block up to 16 rows, held in
+//    registers; two up to 32, whose q rows sit in LDS), so each tile is read
+//    from memory once.  At
+//    the end the waves' (m, l, acc) are merged through LDS in a fixed order
+//    and one partial per chunk is stored;
 //  - scores come out transposed, S^T[key][row] = K q^T, so lane l holds 8
 //    scores of ONE query row (row = l % 16) and that row's running max, sum
 //    and rescale factor stay in the lane; the scores then feed P V as its B
@@ -142,13 +142,12 @@ __device__ __forceinline__ void load_rows(Tile &t, const CacheView &cv, int tb, 
 
 constexpr int kMfmaWaves = 4;  // waves per workgroup, all on one chunk
 
-template <bool F16, int RG>
+template <bool F16, int RB>
 __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_split_mfma_kernel(AttnParams p) {
-    constexpr int KS = kMfmaWaves / RG;  // waves sharing one row group's tiles
+    constexpr int KS = kMfmaWaves;  // waves taking the chunk's tiles in turn
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
-    const int rg = wave % RG, kw = wave / RG;                   // 16-row group, tile phase
+    const int kw = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
 
     int b, h, c;
     SeqChunks sc;
@@ -192,73 +191,110 @@ void attn_split_mfma_kernel(AttnParams p) {
     Tile ta, tb_;
     if (nj > 0) load_full(ta, cv, kw * 32, l16, q);
 
-    // B operand of S^T = K q^T: lane holds q[row][dims 32s + 8q .. +7], s = 0..3
-    u32x4_t qop[4];
-    int vis;  // exclusive local key limit of this lane's row
-    const int row = rg * 16 + l16;
-    if (row < p.rows) {
-        const int i = row / p.group, g = row - i * p.group;
-        const uint8_t *qp =
-            p.q + (((size_t)b * p.q_len + i) * p.n_q_heads + (size_t)h * p.group + g) * kRowBytes + 16 * q;
+    // B operand of S^T = K q^T for row block rb: q[rb*16 + l16][dims 32s + 8q .. +7],
+    // s = 0..3.  One row block stays in this wave's registers; two live in LDS,
+    // shared by the four waves (row stride padded by 16 bytes against bank
+    // conflicts): wave rb loads and rotates row block rb, and every tile reads
+    // them back.
+    int vis[RB];  // exclusive local key limit of this lane's row in each row block
 #pragma unroll
-        for (int s = 0; s < 4; ++s) qop[s] = ld16(qp + 64 * s);
-        if (p.rope_freqs) rope_pieces<F16>(qop, p.rope_dim, sp + i, p.rope_freqs, q);
-        vis = min(sp + i + 1 - t0, n_tok);
+    for (int rb = 0; rb < RB; ++rb) {
+        const int row = rb * 16 + l16;
+        const int i = row / p.group;
+        vis[rb] = row < p.rows ? min(sp + i + 1 - t0, n_tok) : 0;
+    }
+    auto load_q = [&](u32x4_t (&qop)[4], int rb) {
+        const int row = rb * 16 + l16;
+        if (row < p.rows) {
+            const int i = row / p.group, g = row - i * p.group;
+            const uint8_t *qp =
+                p.q + (((size_t)b * p.q_len + i) * p.n_q_heads + (size_t)h * p.group + g) * kRowBytes + 16 * q;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) qop[s] = ld16(qp + 64 * s);
+            if (p.rope_freqs) rope_pieces<F16>(qop, p.rope_dim, sp + i, p.rope_freqs, q);
+        } else {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) qop[s] = u32x4_t{0u, 0u, 0u, 0u};
+        }
+    };
+    u32x4_t qreg[4];
+    __shared__ u32x4_t qsh[RB > 1 ? RB : 1][16][17];
+    if constexpr (RB == 1) {
+        load_q(qreg, 0);
     } else {
+        if (kw < RB) {
+            u32x4_t qop[4];
+            load_q(qop, kw);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) qop[s] = u32x4_t{0u, 0u, 0u, 0u};
-        vis = 0;
+            for (int s = 0; s < 4; ++s) qsh[kw][l16][4 * s + q] = qop[s];
+        }
+        __syncthreads();
+    }
+    auto qpiece = [&](int rb, int s) -> u32x4_t {
+        if constexpr (RB == 1)
+            return qreg[s];
+        else
+            return qsh[rb][l16][4 * s + q];
+    };
+
+    float m_run[RB], l_run[RB];
+    f32x4_t oacc[RB][8];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        m_run[rb] = -INFINITY;
+        l_run[rb] = 0.f;
+#pragma unroll
+        for (int o = 0; o < 8; ++o) oacc[rb][o] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    float m_run = -INFINITY, l_run = 0.f;
-    f32x4_t oacc[8];
-#pragma unroll
-    for (int o = 0; o < 8; ++o) oacc[o] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    // One 32-key tile: S^T, online softmax, O^T += V^T P^T.
+    // One 32-key tile: S^T and the online softmax of every row block, then
+    // O^T += V^T P^T with each V operand serving every row block.
     auto compute = [&](Tile &t, int tt) {
         const int tb = tt * 32;
-        // S^T for the two 16-key blocks: lane holds keys tb + 16*kblk + 4q + v of its row
-        f32x4_t st[2];
+        if constexpr (RB > 1) asm volatile("" ::: "memory");  // keep the q reads inside the loop
+        u32x4_t pop[RB];
 #pragma unroll
-        for (int kblk = 0; kblk < 2; ++kblk) {
-            st[kblk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int rb = 0; rb < RB; ++rb) {
+            // S^T for the two 16-key blocks: lane holds keys tb + 16*kblk + 4q + v of its row
+            f32x4_t st[2];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) st[kblk] = mfma16<F16>(t.k[kblk][s], qop[s], st[kblk]);
-        }
-        float s2[8];
-        float mt = -INFINITY;
+            for (int kblk = 0; kblk < 2; ++kblk) {
+                st[kblk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kblk = 0; kblk < 2; ++kblk)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int key = tb + 16 * kblk + 4 * q + v;
-                const float x = key < vis ? st[kblk][v] * p.scale_log2 : -INFINITY;
-                s2[4 * kblk + v] = x;
-                mt = fmaxf(mt, x);
+                for (int s = 0; s < 4; ++s) st[kblk] = mfma16<F16>(t.k[kblk][s], qpiece(rb, s), st[kblk]);
             }
-        mt = fmaxf(mt, __shfl_xor(mt, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = (m_run == -INFINITY) ? 0.f : exp2_fast(m_run - m_new);
-        float pv[8];
-        float psum = 0.f;
+            float s2[8];
+            float mt = -INFINITY;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            pv[u] = (m_new == -INFINITY) ? 0.f : round_trip16<F16>(exp2_fast(s2[u] - m_new));
-            psum += pv[u];
+            for (int kblk = 0; kblk < 2; ++kblk)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int key = tb + 16 * kblk + 4 * q + v;
+                    const float x = key < vis[rb] ? st[kblk][v] * p.scale_log2 : -INFINITY;
+                    s2[4 * kblk + v] = x;
+                    mt = fmaxf(mt, x);
+                }
+            mt = fmaxf(mt, __shfl_xor(mt, 16));
+            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            const float m_new = fmaxf(m_run[rb], mt);
+            const float alpha = (m_run[rb] == -INFINITY) ? 0.f : exp2_fast(m_run[rb] - m_new);
+            float pv[8];
+            float psum = 0.f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                pv[u] = (m_new == -INFINITY) ? 0.f : round_trip16<F16>(exp2_fast(s2[u] - m_new));
+                psum += pv[u];
+            }
+            if (__any(m_new != m_run[rb])) {
+#pragma unroll
+                for (int o = 0; o < 8; ++o) oacc[rb][o] *= alpha;
+            }
+            l_run[rb] = l_run[rb] * alpha + psum;
+            m_run[rb] = m_new;
+            // B operand of O^T: P^T, slot u <-> key pv_key(q, u) = s2 index u
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pop[rb][j] = pack16<F16>(pv[2 * j], pv[2 * j + 1]);
         }
-        if (__any(m_new != m_run)) {
-#pragma unroll
-            for (int o = 0; o < 8; ++o) oacc[o] *= alpha;
-        }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-
-        // B operand of O^T: P^T, slot u <-> key pv_key(q, u) = s2 index u
-        u32x4_t pop;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) pop[j] = pack16<F16>(pv[2 * j], pv[2 * j + 1]);
 #pragma unroll
         for (int o = 0; o < 8; ++o) {
             const int word = o >> 1;
@@ -266,32 +302,42 @@ void attn_split_mfma_kernel(AttnParams p) {
             u32x4_t vop;
 #pragma unroll
             for (int j = 0; j < 4; ++j) vop[j] = __builtin_amdgcn_perm(t.v[2 * j + 1][word], t.v[2 * j][word], sel);
-            oacc[o] = mfma16<F16>(vop, pop, oacc[o]);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) oacc[rb][o] = mfma16<F16>(vop, pop[rb], oacc[rb][o]);
         }
     };
 
-    // full tiles through two register buffers used in turn, with no copy
-    // between them, so the wave waits only for the older tile while the newer
-    // one is in flight
-    if (nj > 0) {
-        int j = 0;
-        for (; j + 2 <= nj; j += 2) {
-            load_full(tb_, cv, (kw + KS * (j + 1)) * 32, l16, q);
-            compute(ta, kw + KS * j);
-            if (j + 2 < nj) load_full(ta, cv, (kw + KS * (j + 2)) * 32, l16, q);
-            compute(tb_, kw + KS * (j + 1));
+    // Full tiles: with one row block through two register buffers used in
+    // turn, with no copy between them, so the wave waits only for the older
+    // tile while the newer one is in flight; with two row blocks (whose second
+    // accumulator takes the registers of the second buffer) one tile at a time,
+    // the workgroup's other waves keeping the compute unit's loads in flight.
+    if constexpr (RB == 1) {
+        if (nj > 0) {
+            int j = 0;
+            for (; j + 2 <= nj; j += 2) {
+                load_full(tb_, cv, (kw + KS * (j + 1)) * 32, l16, q);
+                compute(ta, kw + KS * j);
+                if (j + 2 < nj) load_full(ta, cv, (kw + KS * (j + 2)) * 32, l16, q);
+                compute(tb_, kw + KS * (j + 1));
+            }
+            if (j < nj) compute(ta, kw + KS * j);
         }
-        if (j < nj) compute(ta, kw + KS * j);
+    } else {
+        for (int j = 0; j < nj; ++j) {
+            if (j > 0) load_full(ta, cv, (kw + KS * j) * 32, l16, q);
+            compute(ta, kw + KS * j);
+        }
     }
 
     // The tiles that hold new rows or run past the chunk take the per-row path,
-    // tile i by wave i mod KS of the row group.
+    // tile i by wave i mod KS (which also appends its new rows).
     RowSource rs;
     rs.new_first = new_first;
     rs.t0 = t0;
     rs.rope = p.k_new ? p.rope_freqs : nullptr;
     rs.rope_dim = p.rope_dim;
-    rs.store = p.k_new != nullptr && rg == 0;
+    rs.store = p.k_new != nullptr;
     rs.stride = (size_t)p.n_kv_heads * kRowBytes;
     if (p.k_new) {
         const size_t noff = ((size_t)b * p.q_len * p.n_kv_heads + h) * kRowBytes;
@@ -307,82 +353,82 @@ void attn_split_mfma_kernel(AttnParams p) {
         compute(tt_, i);
     }
 
-    // ---- merge of the KS waves of a row group, then one partial per chunk ------
-    // lane: row l16, dims 8 (4q + v) + o in oacc[o][v]
-    __shared__ float mlsh[kMfmaWaves][16][2];
-    __shared__ f32x4_t red[3][8][64];  // three slots, lane-private layout
+    // ---- merge of the four waves, then one partial per chunk --------------------
+    // lane: row rb*16 + l16, dims 8 (4q + v) + o in oacc[rb][o][v]
+    __shared__ float mlsh[kMfmaWaves][RB][16][2];
+    __shared__ f32x4_t red[3][RB][8][64];  // three slots, lane-private layout
     __shared__ int s_last;
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
-    if (q == 0) {
-        mlsh[wave][l16][0] = m_run;
-        mlsh[wave][l16][1] = l_run;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        l_run[rb] += __shfl_xor(l_run[rb], 16);
+        l_run[rb] += __shfl_xor(l_run[rb], 32);
+        if (q == 0) {
+            mlsh[kw][rb][l16][0] = m_run[rb];
+            mlsh[kw][rb][l16][1] = l_run[rb];
+        }
     }
     __syncthreads();
-    float M = -INFINITY;
+    float M[RB], L[RB];
 #pragma unroll
-    for (int k = 0; k < KS; ++k) M = fmaxf(M, mlsh[rg + RG * k][l16][0]);
-    float L = 0.f;
+    for (int rb = 0; rb < RB; ++rb) {
+        M[rb] = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < KS; ++k) {
-        const float mk = mlsh[rg + RG * k][l16][0];
-        L += mk == -INFINITY ? 0.f : exp2_fast(mk - M) * mlsh[rg + RG * k][l16][1];
+        for (int k = 0; k < KS; ++k) M[rb] = fmaxf(M[rb], mlsh[k][rb][l16][0]);
+        L[rb] = 0.f;
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+            const float mk = mlsh[k][rb][l16][0];
+            L[rb] += mk == -INFINITY ? 0.f : exp2_fast(mk - M[rb]) * mlsh[k][rb][l16][1];
+        }
+        const float f = m_run[rb] == -INFINITY ? 0.f : exp2_fast(m_run[rb] - M[rb]);
+#pragma unroll
+        for (int o = 0; o < 8; ++o) oacc[rb][o] *= f;
     }
-    {
-        const float f = m_run == -INFINITY ? 0.f : exp2_fast(m_run - M);
+    // waves 1..3 write their sums, one barrier, wave 0 adds them in a fixed
+    // order: (0 + 1) + (2 + 3)
+    if (kw > 0) {
 #pragma unroll
-        for (int o = 0; o < 8; ++o) oacc[o] *= f;
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int o = 0; o < 8; ++o) red[kw - 1][rb][o][lane] = oacc[rb][o];
     }
-    // waves 1.. of a row group write their sums, one barrier, wave 0 adds them
-    // in a fixed order: (0 + 1) + (2 + 3), or 0 + 1 with two row groups
-    if constexpr (KS == 4) {
-        if (kw > 0) {
-#pragma unroll
-            for (int o = 0; o < 8; ++o) red[kw - 1][o][lane] = oacc[o];
-        }
-        __syncthreads();
-        if (kw == 0) {
-#pragma unroll
-            for (int o = 0; o < 8; ++o) oacc[o] = (oacc[o] + red[0][o][lane]) + (red[1][o][lane] + red[2][o][lane]);
-        }
-    } else {
-        if (kw == 1) {
-#pragma unroll
-            for (int o = 0; o < 8; ++o) red[rg][o][lane] = oacc[o];
-        }
-        __syncthreads();
-        if (kw == 0) {
-#pragma unroll
-            for (int o = 0; o < 8; ++o) oacc[o] += red[rg][o][lane];
-        }
-    }
+    __syncthreads();
 
     // When the one-launch step merges in this launch, device-scope stores (the
     // merge may read them from another XCD); else plain stores, which the L2
     // gathers into whole lines (a lane's 16-byte pieces are scattered).
-    if (kw == 0 && row < p.rows) {
-        const size_t part = ((size_t)bh * p.n_chunks + c) * p.rows + row;
-        float *wa = p.ws_acc + part * kHeadDim;
+    if (kw == 0) {
         const bool dev = p.counters != nullptr;
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
+        for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-            for (int o = 0; o < 8; o += 4) {
-                // dims 8*(4q+v) + o .. +3 are four consecutive floats of this lane
-                float *dst = wa + 8 * (4 * q + v) + o;
-                if (dev) {
-                    st_dev4(dst, oacc[o][v], oacc[o + 1][v], oacc[o + 2][v], oacc[o + 3][v]);
-                } else {
-                    *reinterpret_cast<float4 *>(dst) = make_float4(oacc[o][v], oacc[o + 1][v], oacc[o + 2][v], oacc[o + 3][v]);
+            for (int o = 0; o < 8; ++o)
+                oacc[rb][o] = (oacc[rb][o] + red[0][rb][o][lane]) + (red[1][rb][o][lane] + red[2][rb][o][lane]);
+            const int row = rb * 16 + l16;
+            if (row >= p.rows) continue;
+            const size_t part = ((size_t)bh * p.n_chunks + c) * p.rows + row;
+            float *wa = p.ws_acc + part * kHeadDim;
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+#pragma unroll
+                for (int o = 0; o < 8; o += 4) {
+                    // dims 8*(4q+v) + o .. +3 are four consecutive floats of this lane
+                    float *dst = wa + 8 * (4 * q + v) + o;
+                    if (dev) {
+                        st_dev4(dst, oacc[rb][o][v], oacc[rb][o + 1][v], oacc[rb][o + 2][v], oacc[rb][o + 3][v]);
+                    } else {
+                        *reinterpret_cast<float4 *>(dst) =
+                            make_float4(oacc[rb][o][v], oacc[rb][o + 1][v], oacc[rb][o + 2][v], oacc[rb][o + 3][v]);
+                    }
                 }
-            }
-        if (q == 0) {
-            if (dev) {
-                st_dev(p.ws_ml + part * 2 + 0, M);
-                st_dev(p.ws_ml + part * 2 + 1, L);
-            } else {
-                p.ws_ml[part * 2 + 0] = M;
-                p.ws_ml[part * 2 + 1] = L;
+            if (q == 0) {
+                if (dev) {
+                    st_dev(p.ws_ml + part * 2 + 0, M[rb]);
+                    st_dev(p.ws_ml + part * 2 + 1, L[rb]);
+                } else {
+                    p.ws_ml[part * 2 + 0] = M[rb];
+                    p.ws_ml[part * 2 + 1] = L[rb];
+                }
             }
         }
     }
@@ -399,10 +445,10 @@ void attn_split_mfma_kernel(AttnParams p) {
         __syncthreads();
         if (s_last) {
             if (sc.n <= 16) {
-                for (int r = wave; r < p.rows; r += 2 * kMfmaWaves)
+                for (int r = kw; r < p.rows; r += 2 * kMfmaWaves)
                     merge_two_rows_wave<F16, kHeadDim>(p, bh, b, h, r, kMfmaWaves, sc.n, lane);
             } else {
-                for (int r = wave; r < p.rows; r += kMfmaWaves)
+                for (int r = kw; r < p.rows; r += kMfmaWaves)
                     merge_row_wave<F16, kHeadDim>(p, p.out, bh, b, h, r, sc.n, lane);
             }
             if (tid == 0) p.counters[bh] = 0;
@@ -411,7 +457,8 @@ void attn_split_mfma_kernel(AttnParams p) {
 }
 
 // `items` = chunks in the launch (an upper bound), one workgroup each: four
-// waves over the chunk's tiles (up to 16 rows), or two pairs (17..32 rows).
+// waves over the chunk's tiles, each computing every row (one 16-row block up
+// to 16 rows, two up to 32).
 template <bool F16>
 static hipError_t launch_dtype(const AttnParams &p, int items, hipStream_t s) {
     if (p.rows <= 16)
