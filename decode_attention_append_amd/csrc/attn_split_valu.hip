@@ -27,21 +27,34 @@
 
 namespace da {
 
+// Sum of f(0) .. f(NW-1) as a fixed pairwise tree: ((0 + 1) + (2 + 3)) + ...
+template <int NW, typename F>
+__device__ __forceinline__ float tree_sum(F &&f) {
+    float v[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) v[w] = f(w);
+#pragma unroll
+    for (int st = 1; st < NW; st *= 2)
+#pragma unroll
+        for (int w = 0; w < NW; w += 2 * st) v[w] = v[w] + v[w + st];
+    return v[0];
+}
+
 // The one-launch step's merge of every query row of (b, h) over its n chunks,
-// by the whole workgroup.  With at most 16 chunks, or 4 rows or more, each wave
-// merges whole rows (r = wave, wave + 4, ...); otherwise the four waves split
-// each row's chunks into four consecutive ranges and their merge states are
-// combined in LDS in a fixed order.  `red` is LDS of at least 4 * 128 + 8
-// floats.  Uniform across the workgroup (it has barriers).
-template <bool F16>
+// by the whole workgroup of NW waves.  With at most 16 chunks, or 4 rows or
+// more, each wave merges whole rows (r = wave, wave + NW, ...); otherwise the
+// waves split each row's chunks into NW consecutive ranges and their merge
+// states are combined in LDS in a fixed order.  `red` is LDS of at least
+// NW * 128 + 2 * NW floats.  Uniform across the workgroup (it has barriers).
+template <bool F16, int NW>
 __device__ void merge_rows_block(const AttnParams &p, float *red, int bh, int b, int h, int n, int tid) {
     const int lane = tid & 63, wave = tid >> 6;
     if (n <= 16 || p.rows >= 4) {
-        for (int r = wave; r < p.rows; r += 4) merge_row_wave<F16, kHeadDim>(p, p.out, bh, b, h, r, n, lane);
+        for (int r = wave; r < p.rows; r += NW) merge_row_wave<F16, kHeadDim>(p, p.out, bh, b, h, r, n, lane);
         return;
     }
-    float *wm = red + 4 * kHeadDim, *wl = wm + 4;
-    const int c_lo = wave * n / 4, c_hi = (wave + 1) * n / 4;
+    float *wm = red + NW * kHeadDim, *wl = wm + NW;
+    const int c_lo = wave * n / NW, c_hi = (wave + 1) * n / NW;
     for (int r = 0; r < p.rows; ++r) {
         const MergeState<kHeadDim> s = merge_range<kHeadDim>(p, (size_t)bh * p.n_chunks * p.rows + r, c_lo, c_hi, lane);
         red[wave * kHeadDim + 2 * lane] = s.a[0];
@@ -52,18 +65,18 @@ __device__ void merge_rows_block(const AttnParams &p, float *red, int bh, int b,
         }
         __syncthreads();
         if (wave == 0) {
-            const float M = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
-            float f[4];
+            float M = -INFINITY;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) f[w] = wm[w] == -INFINITY ? 0.f : exp2_fast(wm[w] - M);
-            const float L = (f[0] * wl[0] + f[1] * wl[1]) + (f[2] * wl[2] + f[3] * wl[3]);
+            for (int w = 0; w < NW; ++w) M = fmaxf(M, wm[w]);
+            float f[NW];
+#pragma unroll
+            for (int w = 0; w < NW; ++w) f[w] = wm[w] == -INFINITY ? 0.f : exp2_fast(wm[w] - M);
+            const float L = tree_sum<NW>([&](int w) { return f[w] * wl[w]; });
             float o[2];
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
                 const int d = 2 * lane + k;
-                o[k] = ((f[0] * red[d] + f[1] * red[kHeadDim + d]) +
-                        (f[2] * red[2 * kHeadDim + d] + f[3] * red[3 * kHeadDim + d])) /
-                       L;
+                o[k] = tree_sum<NW>([&](int w) { return f[w] * red[w * kHeadDim + d]; }) / L;
             }
             store_out<F16, 2>(p, p.out, out_row_off(p, b, h, r) + 2 * lane, o);
         }
@@ -79,12 +92,14 @@ constexpr int kValuOneLaunchRows = 8;
 
 // ROPE: the problem has a rotary table (a separate instantiation, so that the
 // rotation's registers never weigh on the kernel without one).
-template <bool F16, int RP, bool ROPE>
-__global__ __launch_bounds__(256) void attn_split_valu_kernel(AttnParams p) {
+// NW: waves per workgroup, 4 (chunks of up to 2048 keys) or 16 (up to 8192).
+template <bool F16, int RP, bool ROPE, int NW>
+__global__ __launch_bounds__(64 * NW) void attn_split_valu_kernel(AttnParams p) {
     constexpr bool kOneLaunch = RP <= kValuOneLaunchRows;
     static_assert(!ROPE || kOneLaunch, "the rotary embedding is compiled up to 8 rows");
-    extern __shared__ float lds[];  // scores [chunk][RP], later the wave sums [4][RP][128]
+    extern __shared__ float lds[];  // scores [chunk][RP], later the wave sums [NW][RP][128]
     __shared__ float row_m[RP], row_l[RP];
+    __shared__ float wpart[NW > 4 ? NW : 1][RP];  // per-wave maxima, then sums (NW > 4)
 
     const int n_chunks = p.n_chunks;
     int b, h, c;
@@ -93,7 +108,7 @@ __global__ __launch_bounds__(256) void attn_split_valu_kernel(AttnParams p) {
     int sp;
     if (!locate_wave(p, item, b, h, c, sc, sp, threadIdx.x & 63)) {  // past the last chunk of the launch
         if (kOneLaunch && p.out && item < p.batch && !seq_pos_ok(p, p.seq_pos[item]))
-            flag_sequence_nan<F16>(p, item, threadIdx.x, 256);
+            flag_sequence_nan<F16>(p, item, threadIdx.x, 64 * NW);
         return;
     }
     const int bh = b * p.n_kv_heads + h;
@@ -206,23 +221,25 @@ __global__ __launch_bounds__(256) void attn_split_valu_kernel(AttnParams p) {
             }
         }
     };
-    // This wave's slabs are wave, wave + 4, ...
-    const int nf = wave < n_fast ? (n_fast - 1 - wave) / 4 + 1 : 0;
-    const int first_slow = n_fast + (((wave - n_fast) % 4) + 4) % 4;
-    auto pass = [&](const uint8_t *base, const uint8_t *nbase, uint8_t *wbase, bool rot, auto &&body) {
+    // This wave's slabs are wave, wave + NW, ...
+    const int nf = wave < n_fast ? (n_fast - 1 - wave) / NW + 1 : 0;
+    const int first_slow = n_fast + (((wave - n_fast) % NW) + NW) % NW;
+    // b0 holds the wave's first fast slab when `preloaded` (issued early by the caller).
+    auto pass = [&](const uint8_t *base, const uint8_t *nbase, uint8_t *wbase, bool rot, u32x4_t (&b0)[4],
+                    bool preloaded, auto &&body) {
         if (nf > 0) {
-            u32x4_t b0[4], b1[4];
-            load_fast(b0, base, wave);
+            u32x4_t b1[4];
+            if (!preloaded) load_fast(b0, base, wave);
             int i = 0;
             for (; i + 2 <= nf; i += 2) {
-                load_fast(b1, base, wave + (i + 1) * 4);
-                body(b0, wave + i * 4);
-                load_fast(b0, base, wave + min(i + 2, nf - 1) * 4);
-                body(b1, wave + (i + 1) * 4);
+                load_fast(b1, base, wave + (i + 1) * NW);
+                body(b0, wave + i * NW);
+                load_fast(b0, base, wave + min(i + 2, nf - 1) * NW);
+                body(b1, wave + (i + 1) * NW);
             }
-            if (i < nf) body(b0, wave + i * 4);
+            if (i < nf) body(b0, wave + i * NW);
         }
-        for (int s_ = first_slow; s_ < n_slab; s_ += 4) {
+        for (int s_ = first_slow; s_ < n_slab; s_ += NW) {
             u32x4_t b0[4];
             load_rows(b0, base, nbase, wbase, rot, s_);
             body(b0, s_);
@@ -234,7 +251,8 @@ __global__ __launch_bounds__(256) void attn_split_valu_kernel(AttnParams p) {
     const uint8_t *vnb = fused_append ? p.v_new + new_off : nullptr;
     uint8_t *kwb = fused_append ? p.k_cache_w : nullptr;
     uint8_t *vwb = fused_append ? p.v_cache_w : nullptr;
-    pass(p.k_cache, knb, kwb, fused_append, [&](u32x4_t (&cur)[4], int s_) {
+    u32x4_t kb0[4], vb0[4];
+    pass(p.k_cache, knb, kwb, fused_append, kb0, false, [&](u32x4_t (&cur)[4], int s_) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int tl = s_ * 16 + u * 4 + gq;
@@ -254,24 +272,63 @@ __global__ __launch_bounds__(256) void attn_split_valu_kernel(AttnParams p) {
             }
         }
     });
+    // The V pass's first slab does not depend on the weights: issue it now, so
+    // its latency overlaps the other waves' last K slabs and the softmax.
+    if (nf > 0) load_fast(vb0, p.v_cache, wave);
     __syncthreads();
 
     // ---- chunk maximum and weights p = 2^(s - m), sum l ------------------------
     const int n_pad = n_slab * 16;
-    for (int r = wave; r < RP; r += 4) {
-        float m = -INFINITY;
-        for (int t = lane; t < n_pad; t += 64) m = fmaxf(m, lds[t * RP + r]);
-        m = wave_max(m);
-        float l = 0.f;
-        for (int t = lane; t < n_pad; t += 64) {
-            const float e = (m == -INFINITY) ? 0.f : exp2_fast(lds[t * RP + r] - m);
-            lds[t * RP + r] = e;
-            l += e;
+    if constexpr (NW == 4) {  // a wave per row
+        for (int r = wave; r < RP; r += 4) {
+            float m = -INFINITY;
+            for (int t = lane; t < n_pad; t += 64) m = fmaxf(m, lds[t * RP + r]);
+            m = wave_max(m);
+            float l = 0.f;
+            for (int t = lane; t < n_pad; t += 64) {
+                const float e = (m == -INFINITY) ? 0.f : exp2_fast(lds[t * RP + r] - m);
+                lds[t * RP + r] = e;
+                l += e;
+            }
+            l = wave_sum(l);
+            if (lane == 0) {
+                row_m[r] = m;
+                row_l[r] = l;
+            }
         }
-        l = wave_sum(l);
-        if (lane == 0) {
-            row_m[r] = m;
-            row_l[r] = l;
+    } else {  // every wave takes keys wave*64 + lane, + NW*64, ... of every row
+        float mr[RP];
+#pragma unroll
+        for (int r = 0; r < RP; ++r) {
+            float m = -INFINITY;
+            for (int t = wave * 64 + lane; t < n_pad; t += NW * 64) m = fmaxf(m, lds[t * RP + r]);
+            m = wave_max(m);
+            if (lane == 0) wpart[wave][r] = m;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < RP; ++r) {
+            float m = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) m = fmaxf(m, wpart[w][r]);
+            mr[r] = m;
+        }
+        __syncthreads();  // every wave has read the maxima
+#pragma unroll
+        for (int r = 0; r < RP; ++r) {
+            float l = 0.f;
+            for (int t = wave * 64 + lane; t < n_pad; t += NW * 64) {
+                const float e = (mr[r] == -INFINITY) ? 0.f : exp2_fast(lds[t * RP + r] - mr[r]);
+                lds[t * RP + r] = e;
+                l += e;
+            }
+            l = wave_sum(l);
+            if (lane == 0) wpart[wave][r] = l;
+        }
+        __syncthreads();
+        if (tid < RP) {
+            row_m[tid] = mr[tid];
+            row_l[tid] = tree_sum<NW>([&](int w) { return wpart[w][tid]; });
         }
     }
     __syncthreads();
@@ -283,7 +340,7 @@ __global__ __launch_bounds__(256) void attn_split_valu_kernel(AttnParams p) {
 #pragma unroll
         for (int d = 0; d < 8; ++d) acc[r][d] = 0.f;
     const int first_draft = sp - t0;  // local keys above this may be hidden from some rows
-    pass(p.v_cache, vnb, vwb, false, [&](u32x4_t (&cur)[4], int s_) {
+    pass(p.v_cache, vnb, vwb, false, vb0, true, [&](u32x4_t (&cur)[4], int s_) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int tl = s_ * 16 + u * 4 + gq;
@@ -320,7 +377,7 @@ __global__ __launch_bounds__(256) void attn_split_valu_kernel(AttnParams p) {
             acc[r][d] += __shfl_xor(acc[r][d], 32);
         }
     __syncthreads();  // every wave is done with the scores
-    float *red = lds;  // [4][RP][128]
+    float *red = lds;  // [NW][RP][128]
     if (gq == 0) {
 #pragma unroll
         for (int r = 0; r < RP; ++r)
@@ -329,13 +386,28 @@ __global__ __launch_bounds__(256) void attn_split_valu_kernel(AttnParams p) {
     }
     __syncthreads();
 
+    auto wave_sum_of = [&](int r, int d) {
+        return tree_sum<NW>([&](int w) { return red[(w * RP + r) * kHeadDim + d]; });
+    };
+
+    // One-launch step, a sequence whose context is this one chunk: the output
+    // rows are this chunk's acc / l (what the merge would compute from one
+    // partial), written here; no partial, no arrival.
+    if (kOneLaunch && p.counters && sc.n == 1) {
+        for (int idx = tid; idx < p.rows * (kHeadDim / 2); idx += 64 * NW) {
+            const int r = idx / (kHeadDim / 2), d = 2 * (idx - r * (kHeadDim / 2));
+            const float x[2] = {wave_sum_of(r, d) / row_l[r], wave_sum_of(r, d + 1) / row_l[r]};
+            store_out<F16, 2>(p, p.out, out_row_off(p, b, h, r) + d, x);
+        }
+        return;
+    }
+
     const size_t part = (size_t)bh * n_chunks + c;
     float *wa = p.ws_acc + part * p.rows * kHeadDim;
     // device-scope stores: the one-launch step's merge may read them from another XCD
-    for (int idx = tid; idx < p.rows * kHeadDim; idx += 256) {
+    for (int idx = tid; idx < p.rows * kHeadDim; idx += 64 * NW) {
         const int r = idx >> 7, d = idx & (kHeadDim - 1);
-        st_dev(wa + idx, (red[(0 * RP + r) * kHeadDim + d] + red[(1 * RP + r) * kHeadDim + d]) +
-                             (red[(2 * RP + r) * kHeadDim + d] + red[(3 * RP + r) * kHeadDim + d]));
+        st_dev(wa + idx, wave_sum_of(r, d));
     }
     if (tid < p.rows) {
         st_dev(p.ws_ml + (part * p.rows + tid) * 2 + 0, row_m[tid]);
@@ -353,26 +425,42 @@ __global__ __launch_bounds__(256) void attn_split_valu_kernel(AttnParams p) {
                      sc.n - 1;
         __syncthreads();
         if (s_last) {
-            merge_rows_block<F16>(p, lds, bh, b, h, sc.n, tid);
+            merge_rows_block<F16, NW>(p, lds, bh, b, h, sc.n, tid);
             if (tid == 0) p.counters[bh] = 0;
         }
     }
 }
 
-template <bool F16, int RP>
-static hipError_t launch_rp(const AttnParams &p, int grid, hipStream_t s) {
+// LDS: the scores of the longest chunk, and at least the wave sums
+// [NW][RP][128] and the fused merge's NW * 128 + 2 * NW floats.
+template <int RP, int NW>
+static size_t lds_bytes_of(const AttnParams &p) {
+    size_t f = (size_t)RP * p.max_chunk;
+    const size_t sums = (size_t)NW * RP * kHeadDim, merge = (size_t)NW * kHeadDim + 2 * NW;
+    if (f < sums) f = sums;
+    if (f < merge) f = merge;
+    return f * sizeof(float);
+}
+
+template <bool F16, int RP, int NW>
+static hipError_t launch_nw(const AttnParams &p, int grid, hipStream_t s) {
+    const size_t lds = lds_bytes_of<RP, NW>(p);
     if constexpr (RP <= kValuOneLaunchRows) {
         if (p.rope_freqs) {
-            const size_t lds = (size_t)RP * (p.max_chunk > 520 ? p.max_chunk : 520) * sizeof(float);
-            hipLaunchKernelGGL((attn_split_valu_kernel<F16, RP, true>), dim3(grid), dim3(256), lds, s, p);
+            hipLaunchKernelGGL((attn_split_valu_kernel<F16, RP, true, NW>), dim3(grid), dim3(64 * NW), lds, s, p);
             return hipGetLastError();
         }
     }
-    // scores of the longest chunk; at least the wave sums [4][RP][128] and the
-    // fused merge's 4 * 128 + 8 floats
-    const size_t lds_bytes = (size_t)RP * (p.max_chunk > 520 ? p.max_chunk : 520) * sizeof(float);
-    hipLaunchKernelGGL((attn_split_valu_kernel<F16, RP, false>), dim3(grid), dim3(256), lds_bytes, s, p);
+    hipLaunchKernelGGL((attn_split_valu_kernel<F16, RP, false, NW>), dim3(grid), dim3(64 * NW), lds, s, p);
     return hipGetLastError();
+}
+
+template <bool F16, int RP>
+static hipError_t launch_rp(const AttnParams &p, int grid, hipStream_t s) {
+    if constexpr (RP <= 2) {
+        if (p.valu_waves == 16) return launch_nw<F16, RP, 16>(p, grid, s);
+    }
+    return launch_nw<F16, RP, 4>(p, grid, s);
 }
 
 template <bool F16>

@@ -72,14 +72,27 @@ da_status check_problem(const da_problem *p) {
 // separate path): GQA-8 at 12k-16k context 50.0 / 49.7 / 52.1 us and the
 // 4-token verify 27.6 / 28.7 / 34.6 us at 256 / 512 / 1024 chunks; head_dim 256
 // on 16 x 2 KV heads at 8k context 52.8 / 55.3 / 56.2 us.
-int default_target(int variant) {
-    return variant == DA_VARIANT_MFMA ? 256 : 1024;
+// With 16-wave workgroups (below) the vector-ALU kernel also aims at one chunk
+// per compute unit.
+int default_target(int variant, int valu_waves) {
+    return variant == DA_VARIANT_MFMA || valu_waves == 16 ? 256 : 1024;
+}
+
+// Waves per workgroup of the vector-ALU kernel.  Up to 2 rows, when there are
+// at least 128 (sequence, KV head) units, a 16-wave workgroup takes chunks of
+// up to 8192 keys: the same 16 waves per compute unit as four 4-wave
+// workgroups, but a (sequence, KV head) of up to 8192 keys is one chunk, whose
+// workgroup writes the output itself in the one-launch step: no partials, no
+// arrival and no merge.
+int valu_waves_of(int variant, int rows, int units) {
+    return variant == DA_VARIANT_VALU && rows <= 2 && units >= 128 ? 16 : 4;
 }
 
 // Longest chunk a kernel accepts: the vector-ALU kernel keeps the chunk's
 // scores in LDS (rows x chunk floats, at most 64 KiB).
-int max_chunk_of(int variant, int rows) {
+int max_chunk_of(int variant, int rows, int valu_waves) {
     if (variant == DA_VARIANT_MFMA) return 4096;
+    if (valu_waves == 16) return 8192;
     const int rp = rows <= 1 ? 1 : rows <= 2 ? 2 : rows <= 4 ? 4 : rows <= 8 ? 8 : 16;
     return rp <= 8 ? 2048 : 1024;
 }
@@ -147,14 +160,14 @@ void plan_of(const da_problem *p, da_plan *pl) {
         pl->target_items = units * pl->n_chunks;
         pl->items = units * pl->n_chunks;
     } else {
-        const int max_chunk = max_chunk_of(variant, rows);
+        const int max_chunk = max_chunk_of(variant, rows, valu_waves_of(variant, rows, units));
         pl->balanced = 1;
         pl->chunk_tokens = max_chunk;
         // slots for the most chunks a sequence can get; max_seq <= 2048 * max_chunk
         // keeps ceil(ctx / max_chunk) within them, so no chunk exceeds max_chunk
         const int slots = (p->max_seq + kMinChunk - 1) / kMinChunk;
         pl->n_chunks = slots < kMaxChunks ? slots : kMaxChunks;
-        pl->target_items = p->work_items > 0 ? p->work_items : default_target(variant);
+        pl->target_items = p->work_items > 0 ? p->work_items : default_target(variant, valu_waves_of(variant, rows, units));
         // at most target + one rounding chunk per (sequence, head), or every
         // sequence in chunks of max_chunk keys when the target is too few
         const int64_t a = (int64_t)pl->target_items + units;
@@ -224,6 +237,7 @@ AttnParams attn_params(const da_problem *p, const da_plan &pl, const void *q, co
     a.scale_log2 = (float)(scale * 1.4426950408889634);  // log2(e)
     a.seq_chunk_cap = 0;
     a.chunk_align = chunk_align_of(pl.variant, p->head_dim);
+    a.valu_waves = valu_waves_of(pl.variant, pl.rows, p->batch * p->n_kv_heads);
     a.rope_freqs = p->rope_freqs;
     a.rope_dim = p->rope_dim ? p->rope_dim : p->head_dim;
     a.layout = layout_of(p);
