@@ -63,14 +63,32 @@ __device__ __forceinline__ int pv_key(int q, int u) { return (u < 4 ? 4 * q + u 
 // Rotary embedding of one row held as this lane's four 16-byte pieces, dims
 // 8q + 32s .. +7 (s = 0..3): with the first R dims rotating (pairs j, j + R/2),
 // piece s < R/64 pairs with piece s + R/64 of the same lane.
+// The frequencies those pieces use, freqs[8q .. 8q+7] and, when R = 128,
+// freqs[32+8q .. 32+8q+7], loaded ahead of the rotation.
+__device__ __forceinline__ void piece_freqs(f32x4_t (&f)[4], int R, const float *freqs, int q) {
+    f[0] = *reinterpret_cast<const f32x4_t *>(freqs + 8 * q);
+    f[1] = *reinterpret_cast<const f32x4_t *>(freqs + 8 * q + 4);
+    if (R == 128) {
+        f[2] = *reinterpret_cast<const f32x4_t *>(freqs + 32 + 8 * q);
+        f[3] = *reinterpret_cast<const f32x4_t *>(freqs + 36 + 8 * q);
+    } else {
+        f[2] = f[3] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+}
+template <bool F16>
+__device__ __forceinline__ void rope_pieces_with(u32x4_t (&x)[4], int R, int pos, const f32x4_t (&f)[4]) {
+    if (R == 128) {
+        rope8_with<F16>(x[0], x[2], pos, f[0], f[1]);
+        rope8_with<F16>(x[1], x[3], pos, f[2], f[3]);
+    } else {  // R == 64
+        rope8_with<F16>(x[0], x[1], pos, f[0], f[1]);
+    }
+}
 template <bool F16>
 __device__ __forceinline__ void rope_pieces(u32x4_t (&x)[4], int R, int pos, const float *freqs, int q) {
-    if (R == 128) {
-        rope8<F16>(x[0], x[2], pos, freqs, 8 * q);
-        rope8<F16>(x[1], x[3], pos, freqs, 32 + 8 * q);
-    } else {  // R == 64
-        rope8<F16>(x[0], x[1], pos, freqs, 8 * q);
-    }
+    f32x4_t f[4];
+    piece_freqs(f, R, freqs, q);
+    rope_pieces_with<F16>(x, R, pos, f);
 }
 
 struct Tile {
@@ -142,7 +160,7 @@ __device__ __forceinline__ void load_rows(Tile &t, const CacheView &cv, int tb, 
 
 constexpr int kMfmaWaves = 4;  // waves per workgroup, all on one chunk
 
-template <bool F16, int RB>
+template <bool F16, int RB, bool ROPE>
 __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_split_mfma_kernel(AttnParams p) {
     constexpr int KS = kMfmaWaves;  // waves taking the chunk's tiles in turn
@@ -183,13 +201,11 @@ void attn_split_mfma_kernel(AttnParams p) {
     cv.pg_lane = pg_lane;
 
     // Tiles 0 .. nt-1 hold old cache rows only and load whole; this wave takes
-    // tiles kw, kw + KS, ... of them, the first already in flight while q loads.
+    // tiles kw, kw + KS, ... of them.
     const int new_first = p.k_new ? sp - t0 : n_tok;
     const int n_all = (n_tok + 31) >> 5;
     const int nt = min(n_tok >> 5, max(new_first, 0) >> 5);
     const int nj = kw < nt ? (nt - kw + KS - 1) / KS : 0;
-    Tile ta, tb_;
-    if (nj > 0) load_full(ta, cv, kw * 32, l16, q);
 
     // B operand of S^T = K q^T for row block rb: q[rb*16 + l16][dims 32s + 8q .. +7],
     // s = 0..3.  One row block stays in this wave's registers; two live in LDS,
@@ -203,7 +219,7 @@ void attn_split_mfma_kernel(AttnParams p) {
         const int i = row / p.group;
         vis[rb] = row < p.rows ? min(sp + i + 1 - t0, n_tok) : 0;
     }
-    auto load_q = [&](u32x4_t (&qop)[4], int rb) {
+    auto issue_q = [&](u32x4_t (&qop)[4], int rb) {
         const int row = rb * 16 + l16;
         if (row < p.rows) {
             const int i = row / p.group, g = row - i * p.group;
@@ -211,22 +227,33 @@ void attn_split_mfma_kernel(AttnParams p) {
                 p.q + (((size_t)b * p.q_len + i) * p.n_q_heads + (size_t)h * p.group + g) * kRowBytes + 16 * q;
 #pragma unroll
             for (int s = 0; s < 4; ++s) qop[s] = ld16(qp + 64 * s);
-            if (p.rope_freqs) rope_pieces<F16>(qop, p.rope_dim, sp + i, p.rope_freqs, q);
         } else {
 #pragma unroll
             for (int s = 0; s < 4; ++s) qop[s] = u32x4_t{0u, 0u, 0u, 0u};
         }
     };
+    // q (and its rotation's frequencies) are issued first, then the wave's
+    // first tile, and only then is q rotated or stored: the tile's loads are in
+    // flight while q arrives, and nothing waits for the tile before the first
+    // compute.  The rotation is a separate instantiation, so that without a
+    // table no conditional load sits between the two.
     u32x4_t qreg[4];
     __shared__ u32x4_t qsh[RB > 1 ? RB : 1][16][17];
-    if constexpr (RB == 1) {
-        load_q(qreg, 0);
-    } else {
+    const bool loads_q = RB == 1 || kw < RB;
+    if (loads_q) issue_q(qreg, RB == 1 ? 0 : kw);
+    f32x4_t qfreq[4];
+    if (ROPE && loads_q) piece_freqs(qfreq, p.rope_dim, p.rope_freqs, q);
+    auto rotate_q = [&](u32x4_t (&qop)[4], int rb) {
+        const int row = rb * 16 + l16;
+        if (ROPE && row < p.rows) rope_pieces_with<F16>(qop, p.rope_dim, sp + row / p.group, qfreq);
+    };
+    Tile ta, tb_;
+    if (nj > 0) load_full(ta, cv, kw * 32, l16, q);
+    if (loads_q) rotate_q(qreg, RB == 1 ? 0 : kw);
+    if constexpr (RB > 1) {
         if (kw < RB) {
-            u32x4_t qop[4];
-            load_q(qop, kw);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) qsh[kw][l16][4 * s + q] = qop[s];
+            for (int s = 0; s < 4; ++s) qsh[kw][l16][4 * s + q] = qreg[s];
         }
         __syncthreads();
     }
@@ -335,7 +362,7 @@ void attn_split_mfma_kernel(AttnParams p) {
     RowSource rs;
     rs.new_first = new_first;
     rs.t0 = t0;
-    rs.rope = p.k_new ? p.rope_freqs : nullptr;
+    rs.rope = ROPE && p.k_new ? p.rope_freqs : nullptr;
     rs.rope_dim = p.rope_dim;
     rs.store = p.k_new != nullptr;
     rs.stride = (size_t)p.n_kv_heads * kRowBytes;
@@ -461,10 +488,18 @@ void attn_split_mfma_kernel(AttnParams p) {
 // to 16 rows, two up to 32).
 template <bool F16>
 static hipError_t launch_dtype(const AttnParams &p, int items, hipStream_t s) {
-    if (p.rows <= 16)
-        hipLaunchKernelGGL((attn_split_mfma_kernel<F16, 1>), dim3(items), dim3(64 * kMfmaWaves), 0, s, p);
-    else
-        hipLaunchKernelGGL((attn_split_mfma_kernel<F16, 2>), dim3(items), dim3(64 * kMfmaWaves), 0, s, p);
+    const dim3 grid(items), block(64 * kMfmaWaves);
+    if (p.rope_freqs) {
+        if (p.rows <= 16)
+            hipLaunchKernelGGL((attn_split_mfma_kernel<F16, 1, true>), grid, block, 0, s, p);
+        else
+            hipLaunchKernelGGL((attn_split_mfma_kernel<F16, 2, true>), grid, block, 0, s, p);
+    } else {
+        if (p.rows <= 16)
+            hipLaunchKernelGGL((attn_split_mfma_kernel<F16, 1, false>), grid, block, 0, s, p);
+        else
+            hipLaunchKernelGGL((attn_split_mfma_kernel<F16, 2, false>), grid, block, 0, s, p);
+    }
     return hipGetLastError();
 }
 

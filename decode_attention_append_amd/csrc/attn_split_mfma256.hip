@@ -63,17 +63,25 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 
 // Rotary embedding of a row held as this lane's eight pieces (dims 32s + 8q ..
 // +7): with the first R dims rotating, piece s < R/64 pairs with s + R/64.
+// f0, f1 are freqs[8q .. 8q+7], which every R uses, loaded ahead by the caller.
+template <bool F16>
+__device__ __forceinline__ void rope_pieces8(u32x4_t (&x)[8], int R, int pos, const float *freqs, int q, f32x4_t f0,
+                                             f32x4_t f1) {
+    if (R == 256) {
+        rope8_with<F16>(x[0], x[4], pos, f0, f1);
+#pragma unroll
+        for (int s = 1; s < 4; ++s) rope8<F16>(x[s], x[s + 4], pos, freqs, 32 * s + 8 * q);
+    } else if (R == 128) {
+        rope8_with<F16>(x[0], x[2], pos, f0, f1);
+        rope8<F16>(x[1], x[3], pos, freqs, 32 + 8 * q);
+    } else {  // R == 64
+        rope8_with<F16>(x[0], x[1], pos, f0, f1);
+    }
+}
 template <bool F16>
 __device__ __forceinline__ void rope_pieces8(u32x4_t (&x)[8], int R, int pos, const float *freqs, int q) {
-    if (R == 256) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) rope8<F16>(x[s], x[s + 4], pos, freqs, 32 * s + 8 * q);
-    } else if (R == 128) {
-#pragma unroll
-        for (int s = 0; s < 2; ++s) rope8<F16>(x[s], x[s + 2], pos, freqs, 32 * s + 8 * q);
-    } else {  // R == 64
-        rope8<F16>(x[0], x[1], pos, freqs, 8 * q);
-    }
+    rope_pieces8<F16>(x, R, pos, freqs, q, *reinterpret_cast<const f32x4_t *>(freqs + 8 * q),
+                      *reinterpret_cast<const f32x4_t *>(freqs + 8 * q + 4));
 }
 
 struct Tile16 {
@@ -140,7 +148,7 @@ __device__ __forceinline__ void load_rows16(Tile16 &t, const CacheView &cv, int 
     }
 }
 
-template <bool F16, int RG>
+template <bool F16, int RG, bool ROPE>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_split_mfma256_kernel(AttnParams p) {
     constexpr int KS = kWaves / RG;  // waves sharing one row group's tiles
@@ -181,45 +189,49 @@ void attn_split_mfma256_kernel(AttnParams p) {
     cv.pg_lane = pg_lane;
 
     // Tiles 0 .. nt-1 hold old cache rows only and load whole; this wave takes
-    // tiles kw, kw + KS, ... of them, the first already in flight while q loads.
+    // tiles kw, kw + KS, ... of them.
     const int new_first = p.k_new ? sp - t0 : n_tok;
     const int n_all = (n_tok + 15) >> 4;
     const int nt = min(n_tok >> 4, max(new_first, 0) >> 4);
     const int nj = kw < nt ? (nt - kw + KS - 1) / KS : 0;
-    Tile16 ta, tb_;
-    if (nj > 0) load_full16(ta, cv, kw * 16, l16, q);
 
     // B operand of S^T = K q^T: q[row][32s + 8q .. +7] for s = 0..7.  The 16 rows
     // live in this wave's LDS slice (row stride padded by 16 bytes against bank
     // conflicts) rather than in 32 registers the key tiles need; each tile reads
     // them back.  After the last tile the same memory serves the waves' merge.
+    //
+    // q (and the first rotation frequencies) are issued first, with no branch,
+    // then the wave's first tile; the rotation and the LDS store follow, so the
+    // tile's loads are in flight while q arrives.  Rows past p.rows re-read the
+    // last row: all their keys are hidden (vis 0) and nothing of theirs is stored.
     __shared__ u32x4_t qsh[kWaves][16][33];
     __shared__ float mlsh[kWaves][16][2];
     __shared__ int s_last;
-    int vis;  // exclusive local key limit of this lane's row
     const int row = rg * 16 + l16;
+    const int qrow = min(row, p.rows - 1);
+    const int qi = qrow / p.group, qg = qrow - qi * p.group;
+    const int vis = row < p.rows ? min(sp + qi + 1 - t0, n_tok) : 0;  // exclusive local key limit of this row
+    u32x4_t qop[8];
     {
-        u32x4_t qop[8];
-        if (row < p.rows) {
-            const int i = row / p.group, g = row - i * p.group;
-            const uint8_t *qp =
-                p.q + (((size_t)b * p.q_len + i) * p.n_q_heads + (size_t)h * p.group + g) * kRow + 16 * q;
+        const uint8_t *qp =
+            p.q + (((size_t)b * p.q_len + qi) * p.n_q_heads + (size_t)h * p.group + qg) * kRow + 16 * q;
 #pragma unroll
-            for (int s = 0; s < 8; ++s) qop[s] = ld16(qp + 64 * s);
-            if (p.rope_freqs) rope_pieces8<F16>(qop, p.rope_dim, sp + i, p.rope_freqs, q);
-            vis = min(sp + i + 1 - t0, n_tok);
-        } else {
-#pragma unroll
-            for (int s = 0; s < 8; ++s) qop[s] = u32x4_t{0u, 0u, 0u, 0u};
-            vis = 0;
-        }
-#pragma unroll
-        for (int s = 0; s < 8; ++s) qsh[wave][l16][4 * s + q] = qop[s];
-        // the wave reads back what other lanes of it wrote
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        for (int s = 0; s < 8; ++s) qop[s] = ld16(qp + 64 * s);
     }
+    f32x4_t qf0, qf1;
+    if (ROPE) {
+        qf0 = *reinterpret_cast<const f32x4_t *>(p.rope_freqs + 8 * q);
+        qf1 = *reinterpret_cast<const f32x4_t *>(p.rope_freqs + 8 * q + 4);
+    }
+    Tile16 ta, tb_;
+    if (nj > 0) load_full16(ta, cv, kw * 16, l16, q);
+    if (ROPE && row < p.rows) rope_pieces8<F16>(qop, p.rope_dim, sp + qi, p.rope_freqs, q, qf0, qf1);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qsh[wave][l16][4 * s + q] = qop[s];
+    // the wave reads back what other lanes of it wrote
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     float m_run = -INFINITY, l_run = 0.f;
     f32x4_t oacc[2][8];
@@ -292,7 +304,7 @@ void attn_split_mfma256_kernel(AttnParams p) {
     RowSource16 rs;
     rs.new_first = new_first;
     rs.t0 = t0;
-    rs.rope = p.k_new ? p.rope_freqs : nullptr;
+    rs.rope = ROPE && p.k_new ? p.rope_freqs : nullptr;
     rs.rope_dim = p.rope_dim;
     rs.store = p.k_new != nullptr && rg == 0;
     rs.stride = (size_t)p.n_kv_heads * kRow;
@@ -413,10 +425,18 @@ void attn_split_mfma256_kernel(AttnParams p) {
 // waves over the chunk's tiles (up to 16 rows), or two pairs (17..32 rows).
 template <bool F16>
 hipError_t launch_dtype256(const AttnParams &p, int items, hipStream_t s) {
-    if (p.rows <= 16)
-        hipLaunchKernelGGL((attn_split_mfma256_kernel<F16, 1>), dim3(items), dim3(64 * kWaves), 0, s, p);
-    else
-        hipLaunchKernelGGL((attn_split_mfma256_kernel<F16, 2>), dim3(items), dim3(64 * kWaves), 0, s, p);
+    const dim3 grid(items), block(64 * kWaves);
+    if (p.rope_freqs) {
+        if (p.rows <= 16)
+            hipLaunchKernelGGL((attn_split_mfma256_kernel<F16, 1, true>), grid, block, 0, s, p);
+        else
+            hipLaunchKernelGGL((attn_split_mfma256_kernel<F16, 2, true>), grid, block, 0, s, p);
+    } else {
+        if (p.rows <= 16)
+            hipLaunchKernelGGL((attn_split_mfma256_kernel<F16, 1, false>), grid, block, 0, s, p);
+        else
+            hipLaunchKernelGGL((attn_split_mfma256_kernel<F16, 2, false>), grid, block, 0, s, p);
+    }
     return hipGetLastError();
 }
 

@@ -131,24 +131,22 @@ __global__ __launch_bounds__(64 * NW) void attn_split_valu_kernel(AttnParams p) 
     // Query rows: r = i * group + g is query token i of query head h*group + g.
     uint32_t qr[RP][4];
     int vis[RP];  // exclusive limit of the visible local key indices of row r
+    // Every row's load is issued unconditionally (no branch between them and
+    // the first cache loads, so none waits for another): rows past p.rows
+    // re-read the last row; their keys are all hidden (vis 0) and nothing of
+    // theirs is stored.
 #pragma unroll
     for (int r = 0; r < RP; ++r) {
-        if (r < p.rows) {
-            const int i = r / p.group, g = r - i * p.group;
-            const uint8_t *qp = p.q +
-                                (((size_t)b * p.q_len + i) * p.n_q_heads + (size_t)h * p.group + g) *
-                                    kRowBytes +
-                                cq * 16;
-            const u32x4_t v = ld16(qp);
-            qr[r][0] = v[0];
-            qr[r][1] = v[1];
-            qr[r][2] = v[2];
-            qr[r][3] = v[3];
-            vis[r] = min(sp + i + 1 - t0, n_tok);
-        } else {
-            qr[r][0] = qr[r][1] = qr[r][2] = qr[r][3] = 0u;
-            vis[r] = 0;
-        }
+        const int rr = min(r, p.rows - 1);
+        const int i = rr / p.group, g = rr - i * p.group;
+        const uint8_t *qp =
+            p.q + (((size_t)b * p.q_len + i) * p.n_q_heads + (size_t)h * p.group + g) * kRowBytes + cq * 16;
+        const u32x4_t v = ld16(qp);
+        qr[r][0] = v[0];
+        qr[r][1] = v[1];
+        qr[r][2] = v[2];
+        qr[r][3] = v[3];
+        vis[r] = r < p.rows ? min(sp + i + 1 - t0, n_tok) : 0;
     }
     if (ROPE) {  // rotary embedding of the query rows at seq_pos + i
 #pragma unroll

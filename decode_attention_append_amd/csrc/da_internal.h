@@ -315,10 +315,10 @@ __device__ __forceinline__ void rope_pair(float &x, float &y, int pos, float fre
 
 // Rotates eight pairs held as 16-bit elements: `lo` holds dims j0 .. j0+7, `hi`
 // dims j0+64 .. j0+71 (head_dim 128).
+// rope8_with takes the eight frequencies already loaded (f0, f1 = freqs[j0 ..
+// j0+7]), so a caller can issue their loads early.
 template <bool F16>
-__device__ __forceinline__ void rope8(u32x4_t &lo, u32x4_t &hi, int pos, const float *freqs, int j0) {
-    const f32x4_t f0 = *reinterpret_cast<const f32x4_t *>(freqs + j0);
-    const f32x4_t f1 = *reinterpret_cast<const f32x4_t *>(freqs + j0 + 4);
+__device__ __forceinline__ void rope8_with(u32x4_t &lo, u32x4_t &hi, int pos, f32x4_t f0, f32x4_t f1) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
         float x0, x1, y0, y1;
@@ -334,6 +334,11 @@ __device__ __forceinline__ void rope8(u32x4_t &lo, u32x4_t &hi, int pos, const f
         // reductions costs registers the callers' tiles need
         __builtin_amdgcn_sched_barrier(0);
     }
+}
+template <bool F16>
+__device__ __forceinline__ void rope8(u32x4_t &lo, u32x4_t &hi, int pos, const float *freqs, int j0) {
+    rope8_with<F16>(lo, hi, pos, *reinterpret_cast<const f32x4_t *>(freqs + j0),
+                    *reinterpret_cast<const f32x4_t *>(freqs + j0 + 4));
 }
 
 // The same when consecutive lanes hold one row, 16 bytes (dims 8c .. 8c+7) each,
