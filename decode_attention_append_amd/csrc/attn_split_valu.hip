@@ -244,13 +244,56 @@ __global__ __launch_bounds__(64 * NW) void attn_split_valu_kernel(AttnParams p) 
         }
     };
 
+    // With 16 waves, the K pass's fast slabs after each wave's first are
+    // claimed from a workgroup counter in LDS, so waves the memory system
+    // serves faster take more slabs and none idles at the end of the pass
+    // (every score still lands in its own slot: the result does not depend on
+    // which wave took a slab).  The V pass keeps the fixed assignment, whose
+    // per-wave sums are added in a fixed order.
+    __shared__ int k_claim;
+    if constexpr (NW == 16) {
+        if (tid == 0) k_claim = 0;
+        __syncthreads();
+    }
+    auto claim = [&]() {
+        int r = 0;
+        if (lane == 0) r = atomicAdd(&k_claim, 1);
+        return NW + __builtin_amdgcn_readfirstlane(r);
+    };
+    auto pass_claimed = [&](const uint8_t *base, const uint8_t *nbase, uint8_t *wbase, bool rot, u32x4_t (&b0)[4],
+                            auto &&body) {
+        int i0 = wave < n_fast ? wave : n_fast;
+        if (i0 < n_fast) {
+            u32x4_t b1[4];
+            load_fast(b0, base, i0);
+            int i1 = claim();
+            while (true) {
+                if (i1 < n_fast) load_fast(b1, base, i1);
+                const int i2 = i1 < n_fast ? claim() : n_fast;
+                body(b0, i0);
+                if (i1 >= n_fast) break;
+                if (i2 < n_fast) load_fast(b0, base, i2);
+                const int i3 = i2 < n_fast ? claim() : n_fast;
+                body(b1, i1);
+                if (i2 >= n_fast) break;
+                i0 = i2;
+                i1 = i3;
+            }
+        }
+        for (int s_ = first_slow; s_ < n_slab; s_ += NW) {
+            u32x4_t c0[4];
+            load_rows(c0, base, nbase, wbase, rot, s_);
+            body(c0, s_);
+        }
+    };
+
     // ---- pass 1: scores of the chunk into LDS ----------------------------------
     const uint8_t *knb = fused_append ? p.k_new + new_off : nullptr;
     const uint8_t *vnb = fused_append ? p.v_new + new_off : nullptr;
     uint8_t *kwb = fused_append ? p.k_cache_w : nullptr;
     uint8_t *vwb = fused_append ? p.v_cache_w : nullptr;
     u32x4_t kb0[4], vb0[4];
-    pass(p.k_cache, knb, kwb, fused_append, kb0, false, [&](u32x4_t (&cur)[4], int s_) {
+    auto score_slab = [&](u32x4_t (&cur)[4], int s_) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int tl = s_ * 16 + u * 4 + gq;
@@ -269,7 +312,11 @@ __global__ __launch_bounds__(64 * NW) void attn_split_valu_kernel(AttnParams p) 
                     lds[tl * RP + r] = tl < vis[r] ? score[r] * p.scale_log2 : -INFINITY;
             }
         }
-    });
+    };
+    if constexpr (NW == 16)
+        pass_claimed(p.k_cache, knb, kwb, fused_append, kb0, score_slab);
+    else
+        pass(p.k_cache, knb, kwb, fused_append, kb0, false, score_slab);
     // The V pass's first slab does not depend on the weights: issue it now, so
     // its latency overlaps the other waves' last K slabs and the softmax.
     if (nf > 0) load_fast(vb0, p.v_cache, wave);
