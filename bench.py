@@ -231,24 +231,23 @@ def main():
     # timed region: K steps, HIP events around every attention launch on the launch stream
     ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
            for _ in range(w.layers)] for _ in range(args.steps)]
+    # one event pair per step (back to back when there is no flush), so the
+    # spread of the step time is reported beside its mean
     marks = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-             for _ in range(args.steps if flush else 1)]
+             for _ in range(args.steps)]
     torch.cuda.synchronize()
+    step_ms = []
 
     def timed(run):
-        if flush:
-            for k in range(args.steps):
+        for k in range(args.steps):
+            if flush:
                 flush_buf.sum(dtype=torch.float32)  # outside the timed span of the step
-                marks[k][0].record(stream)
-                run(k)
-                marks[k][1].record(stream)
-        else:
-            marks[0][0].record(stream)
-            for k in range(args.steps):
-                run(k)
-            marks[0][1].record(stream)
+            marks[k][0].record(stream)
+            run(k)
+            marks[k][1].record(stream)
         torch.cuda.synchronize()
-        return sum(a.elapsed_time(b) for a, b in marks)
+        step_ms[:] = [a.elapsed_time(b) for a, b in marks]
+        return sum(step_ms)
 
     if not args.eager:
         graph = torch.cuda.CUDAGraph()
@@ -260,7 +259,9 @@ def main():
         graph.replay()
         torch.cuda.synchronize()
         ms_total = timed(lambda k: graph.replay())
+        replay_ms = list(step_ms)
         timed(lambda k: step(ev[k]))  # eager pass for the kernel's own duration
+        step_ms[:] = replay_ms
     else:
         ms_total = timed(lambda k: step(ev[k]))
     attn_ms = [e0.elapsed_time(e1) for evk in ev for (e0, e1) in evk]
@@ -301,6 +302,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
         "us_per_step": round(ms_per_step * 1e3, 2),
+        "us_per_step_p10_p50_p90": [round(float(np.percentile(step_ms, q)) * 1e3, 2) for q in (10, 50, 90)],
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -320,7 +322,9 @@ def main():
                    "cold_cache_flush": flush},
         "roofline": {"bound": "hbm", "kernel": kernel_tag, "achieved": round(attn_gbs, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
-                     "avg_launch_us": round(attn_avg_ms * 1e3, 3), "bytes_per_launch": attn_bytes,
+                     "avg_launch_us": round(attn_avg_ms * 1e3, 3),
+                     "launch_us_p10_p50_p90": [round(float(np.percentile(attn_ms, q)) * 1e3, 2) for q in (10, 50, 90)],
+                     "bytes_per_launch": attn_bytes,
                      "traffic": traffic},
         "cpu_baseline": None,
     }
