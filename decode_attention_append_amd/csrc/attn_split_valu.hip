@@ -12,15 +12,18 @@
 // and (m, l, acc) is written to the workspace.  The combine kernel merges the
 // chunks.  A key j is visible to query token i iff j <= seq_pos + i.
 //
-// Mapping on gfx950: one 256-lane workgroup per (b, h, chunk), serving every
-// query row of KV head h, so each K/V byte is read once.  Sixteen lanes hold
+// Mapping on gfx950: one workgroup per (b, h, chunk), serving every query row
+// of KV head h, so each K/V byte is read once: 4 waves, or 16 (chunks of up to
+// 8192 keys, one workgroup per compute unit) for up to 2 rows per KV head and
+// at least 128 (b, h) pairs.  Sixteen lanes hold
 // one 256-byte row (16 bytes each): a wave's 128-bit load covers four
 // consecutive keys, 1 KiB contiguous.  Q.K partial dots use the packed
 // dot2 (bf16/fp16 pair -> fp32) instruction, then a 16-lane DPP butterfly.
 // The chunk's scores go to LDS; the chunk is two-pass (all scores, then the
 // maximum, then P.V), so no running rescale is needed inside a chunk.  Each
 // wave streams its 16-key slabs through two register buffers in turn, so the
-// next slab is in flight while the current one is computed.
+// next slab is in flight while the current one is computed; with 16 waves the
+// K pass's slabs after each wave's first are claimed from an LDS counter.
 #include "da_internal.h"
 
 #include <math.h>

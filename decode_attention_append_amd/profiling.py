@@ -8,25 +8,35 @@
 FETCH_SIZE, one with WRITE_SIZE), takes the average per dispatch of the named kernel,
 and scales both by what the same counter reads for the plain 1 GiB device copy the
 bench runs first (the three largest copy-kernel dispatches), so the result is HBM
-bytes per launch.  It records a hash of the kernel's sources, so a later change to
-the kernel makes the numbers stale (bench.py then reports traffic as null).
+bytes per launch.  It records a hash of the kernel's sources (comments and
+whitespace aside), so a later change to the kernel makes the numbers stale
+(bench.py then reports traffic as null).
 """
 import csv
 import glob
 import hashlib
 import json
 import os
+import re
 import sys
 
 COPY_BYTES = 1 << 30
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 
+def code_text(text: str) -> str:
+    """The source without comments and with whitespace runs collapsed: what the
+    compiler sees, so that editing a comment does not mark the counters stale."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_hash(source: str) -> str:
     h = hashlib.sha256()
     for name in (source, "da_internal.h"):
-        with open(os.path.join(HERE, "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(HERE, "csrc", name)) as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()
 
 

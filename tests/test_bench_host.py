@@ -40,3 +40,13 @@ def test_algorithmic_bytes_gated_head_dim_256():
     ctx = sum(s + 1 for s in sp)
     kv = 2 * ctx * 2 * 256 * 2
     assert bench.algorithmic_bytes(w, sp) == (kv, kv + 3 * 16 * 16 * 256 * 2 + 4 * 16 * 2 * 256 * 2)
+
+
+def test_counter_staleness_ignores_comments_only():
+    """The counters' source hash changes with the code, not with its comments."""
+    from decode_attention_append_amd import profiling
+    a = "int f(int x) {  // doubles\n    return 2 * x; /* plain */\n}\n"
+    b = "// a new comment\nint f(int x) {\n  return 2 * x;\n}\n"
+    c = "int f(int x) {\n    return 3 * x;\n}\n"
+    assert profiling.code_text(a) == profiling.code_text(b)
+    assert profiling.code_text(a) != profiling.code_text(c)
