@@ -182,10 +182,11 @@ void attn_split_mfma_kernel(AttnParams p) {
     const int last = n_tok - 1;
     const int l16 = lane & 15, q = lane >> 4;
 
-    // paged caches: lane j reads the pool page of the chunk's 16-token block j
-    int pg_lane = 0;
-    if (p.layout.block_table && lane < (n_tok + kPageTokens - 1) / kPageTokens)
-        pg_lane = kv_page(p.layout, b, t0 / kPageTokens + lane);
+    // Paged caches: the chunk's pool pages, one per thread (chunks have at most
+    // 4096 keys, 256 blocks), issued before the query loads and kept in LDS, so
+    // that no tile waits on a block-table load.
+    static_assert(4096 / kPageTokens <= 64 * kMfmaWaves, "one block-table entry per thread");
+    __shared__ int pg_tab[64 * kMfmaWaves];
 
     CacheView cv;
     cv.k = p.k_cache;
@@ -198,7 +199,7 @@ void attn_split_mfma_kernel(AttnParams p) {
     cv.n_kv_heads = p.n_kv_heads;
     cv.max_seq = p.max_seq;
     cv.t0 = t0;
-    cv.pg_lane = pg_lane;
+    cv.pg_tab = pg_tab;
 
     // Tiles 0 .. nt-1 hold old cache rows only and load whole; this wave takes
     // tiles kw, kw + KS, ... of them.
@@ -219,18 +220,16 @@ void attn_split_mfma_kernel(AttnParams p) {
         const int i = row / p.group;
         vis[rb] = row < p.rows ? min(sp + i + 1 - t0, n_tok) : 0;
     }
+    // Rows past p.rows re-read the last row (no branch between these loads and
+    // the first tile's): all their keys are hidden (vis 0) and nothing of
+    // theirs is stored.
     auto issue_q = [&](u32x4_t (&qop)[4], int rb) {
-        const int row = rb * 16 + l16;
-        if (row < p.rows) {
-            const int i = row / p.group, g = row - i * p.group;
-            const uint8_t *qp =
-                p.q + (((size_t)b * p.q_len + i) * p.n_q_heads + (size_t)h * p.group + g) * kRowBytes + 16 * q;
+        const int row = min(rb * 16 + l16, p.rows - 1);
+        const int i = row / p.group, g = row - i * p.group;
+        const uint8_t *qp =
+            p.q + (((size_t)b * p.q_len + i) * p.n_q_heads + (size_t)h * p.group + g) * kRowBytes + 16 * q;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) qop[s] = ld16(qp + 64 * s);
-        } else {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) qop[s] = u32x4_t{0u, 0u, 0u, 0u};
-        }
+        for (int s = 0; s < 4; ++s) qop[s] = ld16(qp + 64 * s);
     };
     // q (and its rotation's frequencies) are issued first, then the wave's
     // first tile, and only then is q rotated or stored: the tile's loads are in
@@ -241,6 +240,10 @@ void attn_split_mfma_kernel(AttnParams p) {
     __shared__ u32x4_t qsh[RB > 1 ? RB : 1][16][17];
     const bool loads_q = RB == 1 || kw < RB;
     if (loads_q) issue_q(qreg, RB == 1 ? 0 : kw);
+    if (p.layout.block_table) {  // the load and its use in one branch: no load left pending past it
+        store_chunk_page(p.layout, pg_tab, load_chunk_page(p.layout, b, t0, n_tok, tid), n_tok, tid);
+        __syncthreads();
+    }
     f32x4_t qfreq[4];
     if (ROPE && loads_q) piece_freqs(qfreq, p.rope_dim, p.rope_freqs, q);
     auto rotate_q = [&](u32x4_t (&qop)[4], int rb) {

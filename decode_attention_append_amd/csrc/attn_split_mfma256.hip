@@ -170,10 +170,10 @@ void attn_split_mfma256_kernel(AttnParams p) {
     const int last = n_tok - 1;
     const int l16 = lane & 15, q = lane >> 4;
 
-    // paged caches: lane j reads the pool page of the chunk's block j first
-    int pg_lane = 0;
-    if (p.layout.block_table && lane < (n_tok + kPageTokens - 1) / kPageTokens)
-        pg_lane = kv_page(p.layout, b, t0 / kPageTokens + lane);
+    // Paged caches: the chunk's pool pages, one per thread (chunks have at most
+    // 4096 keys, 256 blocks), issued before the query loads and kept in LDS.
+    static_assert(4096 / kPageTokens <= 64 * kWaves, "one block-table entry per thread");
+    __shared__ int pg_tab[64 * kWaves];
 
     CacheView cv;
     cv.k = p.k_cache;
@@ -186,7 +186,7 @@ void attn_split_mfma256_kernel(AttnParams p) {
     cv.n_kv_heads = p.n_kv_heads;
     cv.max_seq = p.max_seq;
     cv.t0 = t0;
-    cv.pg_lane = pg_lane;
+    cv.pg_tab = pg_tab;
 
     // Tiles 0 .. nt-1 hold old cache rows only and load whole; this wave takes
     // tiles kw, kw + KS, ... of them.
@@ -222,6 +222,10 @@ void attn_split_mfma256_kernel(AttnParams p) {
     if (ROPE) {
         qf0 = *reinterpret_cast<const f32x4_t *>(p.rope_freqs + 8 * q);
         qf1 = *reinterpret_cast<const f32x4_t *>(p.rope_freqs + 8 * q + 4);
+    }
+    if (p.layout.block_table) {  // the load and its use in one branch: no load left pending past it
+        store_chunk_page(p.layout, pg_tab, load_chunk_page(p.layout, b, t0, n_tok, tid), n_tok, tid);
+        __syncthreads();
     }
     Tile16 ta, tb_;
     if (nj > 0) load_full16(ta, cv, kw * 16, l16, q);

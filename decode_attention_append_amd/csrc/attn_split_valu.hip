@@ -125,11 +125,15 @@ __global__ __launch_bounds__(64 * NW) void attn_split_valu_kernel(AttnParams p) 
     const int gq = lane >> 4;  // which of the 4 keys of a 1 KiB load
     const int cq = lane & 15;  // 16-byte column: dims 8*cq .. 8*cq+7
 
-    // paged caches: the pool page of this wave's first slab is read first, so its
-    // latency overlaps the query loads (later slabs' entries come from the same
-    // cache lines)
+    // Paged caches: the pool page of every 16-token block of the chunk is read
+    // once, one entry per thread (a chunk has at most 64 * NW blocks), issued
+    // before the query loads and kept in LDS.  A block-table load per slab
+    // would be a vector load whose wait also waits for the slabs in flight.
     const int lp0 = t0 / kPageTokens;
-    const int pg_first = p.layout.block_table && wave < n_slab ? kv_page(p.layout, b, lp0 + wave) : 0;
+    const bool paged = p.layout.block_table != nullptr;
+    __shared__ int pg_tab[64 * NW];
+    int pg_mine = 0;  // checked against the pool when stored, after the query loads are issued
+    if (paged && tid < n_slab) pg_mine = p.layout.block_table[(size_t)b * p.layout.pages_per_seq + lp0 + tid];
 
     // Query rows: r = i * group + g is query token i of query head h*group + g.
     uint32_t qr[RP][4];
@@ -163,20 +167,27 @@ __global__ __launch_bounds__(64 * NW) void attn_split_valu_kernel(AttnParams p) 
         }
     }
 
+    if (paged) {
+        if (tid < n_slab) pg_tab[tid] = (unsigned)pg_mine < (unsigned)p.layout.n_pages ? pg_mine : -1;
+        __syncthreads();
+    }
+
     const int last = n_tok - 1;  // loads past the context re-read the last row (masked)
     // Cache addresses of this lane's 16-byte column (contiguous or paged caches).
     // Chunks start on multiples of 32 keys, so slab s (keys t0 + 16 s ..) is one
-    // 16-token block: one page of a paged cache.
-    auto slab_ptr = [&](const uint8_t *cache, int s_) {
-        if (p.layout.block_table && s_ == wave) {
-            const int pg = pg_first < 0 ? 0 : pg_first;  // outside the pool: read page 0
-            return cache + ((size_t)pg * p.n_kv_heads + h) * kPageTokens * kRowBytes + cq * 16;
+    // 16-token block: one page of a paged cache.  A block-table entry outside
+    // the pool (-1) reads page 0 and drops writes.
+    auto block_off = [&](int s_) {
+        if (paged) {
+            const int pg = pg_tab[s_];
+            return ((size_t)(pg < 0 ? 0 : pg) * p.n_kv_heads + h) * kPageTokens * kRowBytes;
         }
-        return cache + kv_block_off(p.layout, b, h, p.n_kv_heads, p.max_seq, lp0 + s_) + cq * 16;
+        return kv_block_off(p.layout, b, h, p.n_kv_heads, p.max_seq, lp0 + s_);
     };
-    auto row_ptr = [&](const uint8_t *cache, int t) {
-        return cache + kv_row_off(p.layout, b, h, p.n_kv_heads, p.max_seq, t0 + t) + cq * 16;
-    };
+    auto row_off = [&](int t) { return block_off(t >> 4) + (size_t)(t & 15) * kRowBytes + cq * 16; };
+    auto slab_ptr = [&](const uint8_t *cache, int s_) { return cache + block_off(s_) + cq * 16; };
+    auto row_ptr = [&](const uint8_t *cache, int t) { return cache + row_off(t); };
+    auto row_writable = [&](int t) { return !paged || pg_tab[t >> 4] >= 0; };
 
     // Slab loads: four 128-bit loads per lane cover 16 keys (1 KiB each).
     //  - Fast slabs (full, and below this step's new rows) use one base address
@@ -216,9 +227,8 @@ __global__ __launch_bounds__(64 * NW) void attn_split_valu_kernel(AttnParams p) 
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int t = s_ * 16 + u * 4 + gq;
-                if (t >= new_first && t <= last && kv_row_writable(p.layout, b, t0 + t))
-                    *reinterpret_cast<u32x4_t *>(wbase + kv_row_off(p.layout, b, h, p.n_kv_heads, p.max_seq,
-                                                                    t0 + t) + cq * 16) = buf[u];
+                if (t >= new_first && t <= last && row_writable(t))
+                    *reinterpret_cast<u32x4_t *>(wbase + row_off(t)) = buf[u];
             }
         }
     };

@@ -63,18 +63,37 @@ struct CacheView {
     uint8_t *kw, *vw;      // the same, writable (one-launch step), or null
     KvLayout L;
     int b, h, n_kv_heads, max_seq, t0;
-    int pg_lane;  // paged: lane j holds the pool page of the chunk's block j (j < 64)
-    __device__ __forceinline__ size_t block(int j) const {  // 16-token block j of the chunk
-        if (!L.block_table || j >= 64) return kv_block_off(L, b, h, n_kv_heads, max_seq, t0 / kPageTokens + j);
-        int pg = __builtin_amdgcn_readlane(pg_lane, j);
-        pg = pg < 0 ? 0 : pg;  // outside the pool: read page 0
-        return ((size_t)pg * n_kv_heads + h) * kPageTokens * L.row_bytes;
+    const int *pg_tab;  // paged: the pool page of the chunk's block j (-1 outside the pool), in LDS
+    // byte offset of the chunk's 16-token block j; a page outside the pool reads page 0
+    __device__ __forceinline__ size_t block_of_page(int pg) const {
+        return ((size_t)(pg < 0 ? 0 : pg) * n_kv_heads + h) * kPageTokens * L.row_bytes;
     }
-    __device__ __forceinline__ size_t row(int key) const {
-        return kv_row_off(L, b, h, n_kv_heads, max_seq, t0 + key);
+    __device__ __forceinline__ size_t block(int j) const {  // j wave-uniform
+        if (!L.block_table) return kv_block_off(L, b, h, n_kv_heads, max_seq, t0 / kPageTokens + j);
+        return block_of_page(__builtin_amdgcn_readfirstlane(pg_tab[j]));
     }
-    __device__ __forceinline__ bool writable(int key) const { return kv_row_writable(L, b, t0 + key); }
+    __device__ __forceinline__ size_t row(int key) const {  // key may differ per lane
+        if (!L.block_table) return kv_row_off(L, b, h, n_kv_heads, max_seq, t0 + key);
+        return block_of_page(pg_tab[key / kPageTokens]) + (size_t)(key % kPageTokens) * L.row_bytes;
+    }
+    __device__ __forceinline__ bool writable(int key) const {
+        return !L.block_table || pg_tab[key / kPageTokens] >= 0;
+    }
 };
+
+// Paged caches: the pool pages of a chunk's 16-token blocks, one per thread of a
+// workgroup (a chunk has at most `n_threads` blocks).  load_chunk_pages issues the
+// raw block-table load early; store_chunk_pages checks it against the pool and
+// writes it to `tab` in LDS (the caller then synchronises the workgroup).
+__device__ __forceinline__ int load_chunk_page(const KvLayout &L, int b, int t0, int n_tok, int tid) {
+    int pg = 0;
+    if (L.block_table && tid < (n_tok + kPageTokens - 1) / kPageTokens)
+        pg = L.block_table[(size_t)b * L.pages_per_seq + t0 / kPageTokens + tid];
+    return pg;
+}
+__device__ __forceinline__ void store_chunk_page(const KvLayout &L, int *tab, int pg, int n_tok, int tid) {
+    if (tid < (n_tok + kPageTokens - 1) / kPageTokens) tab[tid] = (unsigned)pg < (unsigned)L.n_pages ? pg : -1;
+}
 
 // ---- parameter blocks ------------------------------------------------------
 
