@@ -166,6 +166,10 @@ struct SeqChunks {
 
 __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 __host__ __device__ inline int round_up32(int a) { return (a + 31) & ~31; }
+__host__ __device__ inline bool pow2(int a) { return a > 0 && (a & (a - 1)) == 0; }
+// ceil(a / b) for b a power of two: a shift (the chunk-finding arithmetic runs
+// at the start of every workgroup, before its first cache load)
+__host__ __device__ inline int ceil_div_pow2(int a, int b) { return (a + b - 1) >> __builtin_ctz((unsigned)b); }
 
 __host__ __device__ inline bool seq_pos_ok(const AttnParams &p, int sp) {
     return sp >= 0 && sp <= p.max_seq - p.q_len;
@@ -173,8 +177,17 @@ __host__ __device__ inline bool seq_pos_ok(const AttnParams &p, int sp) {
 
 // Balanced chunk length for `total` visible keys over all sequences.
 __host__ __device__ inline int balanced_len(const AttnParams &p, int64_t total) {
-    const int64_t want = (total * p.n_kv_heads + p.target_wg - 1) / p.target_wg;
-    int t = (int)(want < p.max_chunk ? want : p.max_chunk);
+    // ceil(total * Hkv / target_wg) clamped to max_chunk, with a 32-bit division
+    // whenever the clamp does not decide it (a 64-bit division is a long
+    // instruction sequence on this GPU)
+    const int64_t x = total * p.n_kv_heads;
+    int t;
+    if (x >= (int64_t)p.target_wg * p.max_chunk)
+        t = p.max_chunk;
+    else if (x + p.target_wg <= (int64_t)0xffffffffu)
+        t = (int)(((uint32_t)x + (uint32_t)p.target_wg - 1u) / (uint32_t)p.target_wg);
+    else
+        t = (int)((x + p.target_wg - 1) / p.target_wg);
     t = round_up32(t);
     return t < p.min_chunk ? p.min_chunk : (t > p.max_chunk ? p.max_chunk : t);
 }
@@ -200,16 +213,16 @@ __host__ __device__ inline SeqChunks seq_chunks_at(const AttnParams &p, int sp, 
     }
     int n = (2 * s.ctx + T) / (2 * T);  // round(ctx / T)
     if (p.seq_chunk_cap > 0 && n > p.seq_chunk_cap) n = p.seq_chunk_cap;
-    const int n_cap = ceil_div(s.ctx, p.max_chunk);
+    const int n_cap = pow2(p.max_chunk) ? ceil_div_pow2(s.ctx, p.max_chunk) : ceil_div(s.ctx, p.max_chunk);
     if (n < n_cap) n = n_cap;
     if (n < 1) n = 1;
     if (n > p.n_chunks) n = p.n_chunks;
     s.n = n;
     const int raw = round_up32(ceil_div(s.ctx, n));
     const int a = p.chunk_align;
-    s.len = a > 32 && 2 * raw >= a ? (raw + a - 1) / a * a : raw;
+    s.len = a > 32 && 2 * raw >= a ? (pow2(a) ? (raw + a - 1) & -a : (raw + a - 1) / a * a) : raw;
     if (s.len > p.max_chunk) s.len = p.max_chunk;  // raw <= max_chunk: no chunk is shorter than raw
-    s.n = ceil_div(s.ctx, s.len);  // rounding the length up may leave the last chunk empty
+    s.n = pow2(s.len) ? ceil_div_pow2(s.ctx, s.len) : ceil_div(s.ctx, s.len);  // rounding the length up may leave the last chunk empty
     return s;
 }
 
@@ -398,16 +411,22 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
-__device__ __forceinline__ int wave_sum_i(int x) {
-    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+// Inclusive prefix sum over the wave's 64 lanes with DPP moves (no LDS round
+// trips): shifts by 1, 2, 4 and 8 lanes within each 16-lane row (lanes shifted
+// in from outside the row add 0), then lane 15's row total broadcast into rows
+// 1 and 3 and lane 31's into rows 2 and 3.  These run at the start of every
+// workgroup, before its first cache load.
+__device__ __forceinline__ int wave_incl_scan(int x, int /*lane*/) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
     return x;
 }
-__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
-    for (int d = 1; d < 64; d <<= 1) {
-        const int y = __shfl_up(x, d);
-        if (lane >= d) x += y;
-    }
-    return x;
+__device__ __forceinline__ int wave_sum_i(int x) {
+    return __builtin_amdgcn_readlane(wave_incl_scan(x, 0), 63);
 }
 
 // The chunk plan's per-launch values, computed by a whole wave: lane j of each
