@@ -304,8 +304,7 @@ void attn_split_mfma_kernel(AttnParams p) {
                     s2[4 * kblk + v] = x;
                     mt = fmaxf(mt, x);
                 }
-            mt = fmaxf(mt, __shfl_xor(mt, 16));
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            mt = xor32(xor16(mt, FMax{}), FMax{});
             const float m_new = fmaxf(m_run[rb], mt);
             const float alpha = (m_run[rb] == -INFINITY) ? 0.f : exp2_fast(m_run[rb] - m_new);
             float pv[8];
@@ -390,8 +389,7 @@ void attn_split_mfma_kernel(AttnParams p) {
     __shared__ int s_last;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-        l_run[rb] += __shfl_xor(l_run[rb], 16);
-        l_run[rb] += __shfl_xor(l_run[rb], 32);
+        l_run[rb] = xor32(xor16(l_run[rb], FAdd{}), FAdd{});
         if (q == 0) {
             mlsh[kw][rb][l16][0] = m_run[rb];
             mlsh[kw][rb][l16][1] = l_run[rb];

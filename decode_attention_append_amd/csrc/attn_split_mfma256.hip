@@ -258,8 +258,7 @@ void attn_split_mfma256_kernel(AttnParams p) {
             x[v] = tb + 4 * q + v < vis ? st[v] * p.scale_log2 : -INFINITY;
             mt = fmaxf(mt, x[v]);
         }
-        mt = fmaxf(mt, __shfl_xor(mt, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        mt = xor32(xor16(mt, FMax{}), FMax{});
         const float m_new = fmaxf(m_run, mt);
         const float alpha = (m_run == -INFINITY) ? 0.f : exp2_fast(m_run - m_new);
         float pw[4];
@@ -328,8 +327,7 @@ void attn_split_mfma256_kernel(AttnParams p) {
 
     // ---- merge of the KS waves of a row group, then one partial per chunk ------
     // rows l16: dims 128 hh + 8 (4q + v) + o in oacc[hh][o][v]
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
+    l_run = xor32(xor16(l_run, FAdd{}), FAdd{});
     if (q == 0) {
         mlsh[wave][l16][0] = m_run;
         mlsh[wave][l16][1] = l_run;

@@ -431,8 +431,7 @@ __global__ __launch_bounds__(64 * NW) void attn_split_valu_kernel(AttnParams p) 
     for (int r = 0; r < RP; ++r)
 #pragma unroll
         for (int d = 0; d < 8; ++d) {
-            acc[r][d] += __shfl_xor(acc[r][d], 16);
-            acc[r][d] += __shfl_xor(acc[r][d], 32);
+            acc[r][d] = xor32(xor16(acc[r][d], FAdd{}), FAdd{});
         }
     __syncthreads();  // every wave is done with the scores
     float *red = lds;  // [NW][RP][128]

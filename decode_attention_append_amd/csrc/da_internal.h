@@ -402,14 +402,45 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
+// x combined with lane l ^ 16 (xor16) or l ^ 32 (xor32) through gfx950's VALU
+// lane swaps instead of LDS permutes.  v_permlane16_swap exchanges the odd
+// 16-lane rows of its first register with the even rows of its second, and
+// v_permlane32_swap the upper half of the first with the lower half of the
+// second; with x in both, every lane ends up with its pair's two values, the
+// lower lane's first, so both lanes compute the same bits.  The instructions
+// are written out: this compiler folds the builtins' two results into one
+// (as if the swap were lane-local), which loses the partner's value.  The
+// s_nop before each gives the swap the wait states the compiler puts after a
+// VALU write of its operands.
+template <class Op>
+__device__ __forceinline__ float xor16(float x, Op op) {
+    uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+    return op(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+template <class Op>
+__device__ __forceinline__ float xor32(float x, Op op) {
+    uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+    return op(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+struct FMax {
+    __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+struct FAdd {
+    __device__ float operator()(float a, float b) const { return a + b; }
+};
+
+// Over all 64 lanes (every lane gets the result): the 16-lane rows by DPP, then
+// the rows by lane swaps.
 __device__ __forceinline__ float wave_max(float x) {
-    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-    return x;
+    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false)));
+    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false)));
+    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false)));
+    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false)));
+    return xor32(xor16(x, FMax{}), FMax{});
 }
-__device__ __forceinline__ float wave_sum(float x) {
-    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-    return x;
-}
+__device__ __forceinline__ float wave_sum(float x) { return xor32(xor16(row16_sum(x), FAdd{}), FAdd{}); }
 
 // Inclusive prefix sum over the wave's 64 lanes with DPP moves (no LDS round
 // trips): shifts by 1, 2, 4 and 8 lanes within each 16-lane row (lanes shifted
