@@ -279,9 +279,6 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u32x4_t ld16(const uint8_t *p) {
     return *reinterpret_cast<const u32x4_t *>(p);
 }
-__device__ __forceinline__ u32x2_t ld8(const uint8_t *p) {
-    return *reinterpret_cast<const u32x2_t *>(p);
-}
 
 // fp32 sum of a.lo*b.lo + a.hi*b.hi + c over packed 16-bit pairs.
 template <bool F16>
@@ -544,25 +541,9 @@ __device__ __forceinline__ void st_dev4(float *p, float a, float b, float c, flo
 __device__ __forceinline__ float ld_dev(const float *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float2 ld_dev2(const float *p) {
-    const uint64_t x =
-        __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return make_float2(__uint_as_float((uint32_t)x), __uint_as_float((uint32_t)(x >> 32)));
-}
 // Wait until every memory access this wave issued is complete; also a compiler
 // barrier, so no access moves across it.
 __device__ __forceinline__ void wait_mem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// Counts one arrival on `counter` once this wave's partial stores are complete.
-// True for the last of `arrivals` arrivals per (b, h): that wave then merges
-// every row and resets the counter for the next call.
-__device__ inline bool last_arrival(int32_t *counter, int arrivals, int lane) {
-    wait_mem();
-    int prev = 0;
-    if (lane == 0) prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    prev = __shfl(prev, 0);
-    return prev == arrivals - 1;
-}
 
 // Log-sum-exp merge state of one query row over some chunks: running maximum m
 // (log2 units), sum l = sum_c 2^(m_c - m) l_c and this lane's D/64 dims of
