@@ -385,7 +385,7 @@ void attn_split_mfma_kernel(AttnParams p) {
     // ---- merge of the four waves, then one partial per chunk --------------------
     // lane: row rb*16 + l16, dims 8 (4q + v) + o in oacc[rb][o][v]
     __shared__ float mlsh[kMfmaWaves][RB][16][2];
-    __shared__ f32x4_t red[3][RB][8][64];  // three slots, lane-private layout
+    __shared__ f32x4_t red[kMfmaWaves][RB][8][64];  // one slot per wave, lane-private layout
     __shared__ int s_last;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -412,44 +412,46 @@ void attn_split_mfma_kernel(AttnParams p) {
 #pragma unroll
         for (int o = 0; o < 8; ++o) oacc[rb][o] *= f;
     }
-    // waves 1..3 write their sums, one barrier, wave 0 adds them in a fixed
-    // order: (0 + 1) + (2 + 3)
-    if (kw > 0) {
+    // Every wave writes its rescaled sums; after one barrier wave w adds output
+    // slots o = 2w, 2w + 1 of all four in a fixed order, (0 + 1) + (2 + 3), and
+    // stores them, so the adds and the stores are shared by the four waves.
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-            for (int o = 0; o < 8; ++o) red[kw - 1][rb][o][lane] = oacc[rb][o];
-    }
+        for (int o = 0; o < 8; ++o) red[kw][rb][o][lane] = oacc[rb][o];
     __syncthreads();
 
     // When the one-launch step merges in this launch, device-scope stores (the
     // merge may read them from another XCD); else plain stores, which the L2
-    // gathers into whole lines (a lane's 16-byte pieces are scattered).
-    if (kw == 0) {
+    // gathers into whole lines (a lane's 8-byte pieces are scattered).
+    {
         const bool dev = p.counters != nullptr;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
+            f32x4_t sum[2];
 #pragma unroll
-            for (int o = 0; o < 8; ++o)
-                oacc[rb][o] = (oacc[rb][o] + red[0][rb][o][lane]) + (red[1][rb][o][lane] + red[2][rb][o][lane]);
+            for (int j = 0; j < 2; ++j) {
+                const int o = 2 * kw + j;
+                sum[j] = (red[0][rb][o][lane] + red[1][rb][o][lane]) + (red[2][rb][o][lane] + red[3][rb][o][lane]);
+            }
             const int row = rb * 16 + l16;
             if (row >= p.rows) continue;
             const size_t part = ((size_t)bh * p.n_chunks + c) * p.rows + row;
             float *wa = p.ws_acc + part * kHeadDim;
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-#pragma unroll
-                for (int o = 0; o < 8; o += 4) {
-                    // dims 8*(4q+v) + o .. +3 are four consecutive floats of this lane
-                    float *dst = wa + 8 * (4 * q + v) + o;
-                    if (dev) {
-                        st_dev4(dst, oacc[rb][o][v], oacc[rb][o + 1][v], oacc[rb][o + 2][v], oacc[rb][o + 3][v]);
-                    } else {
-                        *reinterpret_cast<float4 *>(dst) =
-                            make_float4(oacc[rb][o][v], oacc[rb][o + 1][v], oacc[rb][o + 2][v], oacc[rb][o + 3][v]);
-                    }
+            for (int v = 0; v < 4; ++v) {
+                // dims 8*(4q+v) + 2w and + 1: two consecutive floats of this lane
+                float *dst = wa + 8 * (4 * q + v) + 2 * kw;
+                if (dev) {
+                    __hip_atomic_store(reinterpret_cast<uint64_t *>(dst),
+                                       (uint64_t)__float_as_uint(sum[0][v]) |
+                                           ((uint64_t)__float_as_uint(sum[1][v]) << 32),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                } else {
+                    *reinterpret_cast<float2 *>(dst) = make_float2(sum[0][v], sum[1][v]);
                 }
-            if (q == 0) {
+            }
+            if (kw == 0 && q == 0) {
                 if (dev) {
                     st_dev(p.ws_ml + part * 2 + 0, M[rb]);
                     st_dev(p.ws_ml + part * 2 + 1, L[rb]);

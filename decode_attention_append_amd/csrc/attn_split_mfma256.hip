@@ -204,7 +204,11 @@ void attn_split_mfma256_kernel(AttnParams p) {
     // then the wave's first tile; the rotation and the LDS store follow, so the
     // tile's loads are in flight while q arrives.  Rows past p.rows re-read the
     // last row: all their keys are hidden (vis 0) and nothing of theirs is stored.
-    __shared__ u32x4_t qsh[kWaves][16][33];
+    // q rows while the tiles stream; then the same memory holds the four waves'
+    // sums for the merge (16 rows x 256 floats each)
+    __shared__ f32x4_t lds_q_red[kWaves * 16 * 64];
+    static_assert(sizeof(u32x4_t) * kWaves * 16 * 33 <= sizeof(lds_q_red), "q rows fit the merge slots");
+    auto &qsh = *reinterpret_cast<u32x4_t (*)[kWaves][16][33]>(lds_q_red);
     __shared__ float mlsh[kWaves][16][2];
     __shared__ int s_last;
     const int row = rg * 16 + l16;
@@ -349,49 +353,45 @@ void attn_split_mfma256_kernel(AttnParams p) {
 #pragma unroll
             for (int o = 0; o < 8; ++o) oacc[hh][o] *= f;
     }
-    // two slots of 16 rows x 256 floats in the q memory; lane-private layout
-    f32x4_t *red = reinterpret_cast<f32x4_t *>(&qsh[0][0][0]);
-    auto put = [&](int slot) {
+    // Every wave writes its sums to its own slot (16 rows x 256 floats in the q
+    // memory, lane-private layout); after one barrier the waves of a row group
+    // split the output slots and add the group's sums in a fixed order, with
+    // four waves per group (0 + 2) + (1 + 3), and store them.
+    f32x4_t *red = lds_q_red;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) red[(slot * 16 + e) * 64 + lane] = oacc[e >> 3][e & 7];
-    };
-    auto add = [&](int slot) {
+    for (int e = 0; e < 16; ++e) red[(wave * 16 + e) * 64 + lane] = oacc[e >> 3][e & 7];
+    __syncthreads();
+    constexpr int kE = 16 / KS;  // output slots per wave: hh = e / 8, o = e % 8
+    const int e0 = kw * kE;
+    f32x4_t sum[kE];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[e >> 3][e & 7] += red[(slot * 16 + e) * 64 + lane];
-    };
-    if constexpr (KS == 4) {  // (0 + 2) + (1 + 3)
-        if (kw >= 2) put(kw - 2);
-        __syncthreads();
-        if (kw < 2) add(kw);
-        __syncthreads();
-        if (kw == 1) put(0);
-        __syncthreads();
-        if (kw == 0) add(0);
-    } else {
-        if (kw == 1) put(rg);
-        __syncthreads();
-        if (kw == 0) add(rg);
+    for (int j = 0; j < kE; ++j) {
+        const int e = e0 + j;
+        auto slot = [&](int k) { return red[((rg + RG * k) * 16 + e) * 64 + lane]; };
+        if constexpr (KS == 4)
+            sum[j] = (slot(0) + slot(2)) + (slot(1) + slot(3));
+        else
+            sum[j] = slot(0) + slot(1);
     }
 
-    if (kw == 0 && row < p.rows) {
+    if (row < p.rows) {
         const size_t part = ((size_t)bh * p.n_chunks + c) * p.rows + row;
         float *wa = p.ws_acc + part * kD;
         const bool dev = p.counters != nullptr;
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
+        for (int j = 0; j < kE; j += 4) {
+            const int hh = (e0 + j) >> 3, o = (e0 + j) & 7;  // four consecutive o of one hh
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-#pragma unroll
-                for (int o = 0; o < 8; o += 4) {
-                    float *dst = wa + 128 * hh + 8 * (4 * q + v) + o;
-                    if (dev) {
-                        st_dev4(dst, oacc[hh][o][v], oacc[hh][o + 1][v], oacc[hh][o + 2][v], oacc[hh][o + 3][v]);
-                    } else {
-                        *reinterpret_cast<float4 *>(dst) =
-                            make_float4(oacc[hh][o][v], oacc[hh][o + 1][v], oacc[hh][o + 2][v], oacc[hh][o + 3][v]);
-                    }
+            for (int v = 0; v < 4; ++v) {
+                float *dst = wa + 128 * hh + 8 * (4 * q + v) + o;
+                if (dev) {
+                    st_dev4(dst, sum[j][v], sum[j + 1][v], sum[j + 2][v], sum[j + 3][v]);
+                } else {
+                    *reinterpret_cast<float4 *>(dst) = make_float4(sum[j][v], sum[j + 1][v], sum[j + 2][v], sum[j + 3][v]);
                 }
-        if (q == 0) {
+            }
+        }
+        if (kw == 0 && q == 0) {
             if (dev) {
                 st_dev(p.ws_ml + part * 2 + 0, M);
                 st_dev(p.ws_ml + part * 2 + 1, L);
