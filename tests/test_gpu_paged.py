@@ -113,6 +113,27 @@ def test_paged_pages_across_chunks(chunk, variant, path):
 
 
 @pytest.mark.parametrize("path", gu.PATHS)
+@pytest.mark.parametrize("B,Hq,Hkv,D,pps,seq_pos,chunk,pages", [
+    (2, 64, 8, 128, 257, [4095, 2600], 4096, 256),     # MFMA: one page per thread
+    (2, 16, 2, 256, 257, [4095, 2600], 4096, 256),     # head_dim 256
+    (2, 16, 8, 128, 257, [4095, 2600], 2048, 128),     # vector ALU, 4 waves
+    (16, 16, 8, 128, 400, [6300] + [211 * i + 5 for i in range(15)], 6304, 394),  # 16 waves
+])
+def test_paged_long_chunks(B, Hq, Hkv, D, pps, seq_pos, chunk, pages, path):
+    """Chunks of up to one page per thread of the workgroup: each workgroup reads its
+    chunk's page list into LDS once and takes every tile's or slab's page from there.
+    One requested work item gives every sequence its fewest, longest chunks."""
+    _say("paged long chunks", B, Hq, Hkv, D, pps, chunk, path)
+    inp = make_paged(B, 1, Hq, Hkv, pps, seq_pos, head_dim=D, seed=pps + D)
+    p = da.problem_for(inp["q"], inp["k_cache"], block_table=inp["block_table"], work_items=1)
+    assert max(ln for _, ln in da.chunk_layout(p, seq_pos)) == chunk
+    assert -(-chunk // 16) == pages
+    rng = np.random.default_rng(pps)
+    rows = [(b, 0, int(h)) for b in range(min(B, 4)) for h in rng.choice(Hq, 4, replace=False)]
+    check_paged(p, inp, path, rows=rows)
+
+
+@pytest.mark.parametrize("path", gu.PATHS)
 @pytest.mark.parametrize("Hq,Hkv,q_len", [(16, 8, 1), (32, 4, 4)])
 def test_paged_with_rope(Hq, Hkv, q_len, path):
     _say("paged rope", Hq, Hkv, q_len, path)
