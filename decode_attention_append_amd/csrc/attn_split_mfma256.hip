@@ -213,7 +213,7 @@ void attn_split_mfma256_kernel(AttnParams p) {
     __shared__ int s_last;
     const int row = rg * 16 + l16;
     const int qrow = min(row, p.rows - 1);
-    const int qi = qrow / p.group, qg = qrow - qi * p.group;
+    const int qi = div_small(qrow, p.group), qg = qrow - qi * p.group;
     const int vis = row < p.rows ? min(sp + qi + 1 - t0, n_tok) : 0;  // exclusive local key limit of this row
     u32x4_t qop[8];
     {

@@ -145,7 +145,7 @@ __global__ __launch_bounds__(64 * NW) void attn_split_valu_kernel(AttnParams p) 
 #pragma unroll
     for (int r = 0; r < RP; ++r) {
         const int rr = min(r, p.rows - 1);
-        const int i = rr / p.group, g = rr - i * p.group;
+        const int i = div_small(rr, p.group), g = rr - i * p.group;
         const uint8_t *qp =
             p.q + (((size_t)b * p.q_len + i) * p.n_q_heads + (size_t)h * p.group + g) * kRowBytes + cq * 16;
         const u32x4_t v = ld16(qp);
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(64 * NW) void attn_split_valu_kernel(AttnParams p) 
 #pragma unroll
         for (int r = 0; r < RP; ++r) {
             u32x4_t v = {qr[r][0], qr[r][1], qr[r][2], qr[r][3]};
-            rope_row<F16>(v, cq, p.rope_dim, sp + r / p.group, p.rope_freqs, r < p.rows);
+            rope_row<F16>(v, cq, p.rope_dim, sp + div_small(r, p.group), p.rope_freqs, r < p.rows);
             qr[r][0] = v[0];
             qr[r][1] = v[1];
             qr[r][2] = v[2];

@@ -164,12 +164,26 @@ struct SeqChunks {
     int ctx;    // visible keys
 };
 
-__host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+// a / b for 0 <= a <= 2^22 and 1 <= b (every quotient of the chunk plan:
+// contexts are at most 2^21 keys).  On the device the float quotient
+// a * rcp(b) is within 0.75 of a / b at these sizes (rcp is within one ulp,
+// the product within half an ulp: 1.5 * 2^-23 relative), so its truncation is
+// the integer quotient or one off either way, and the remainder's sign and
+// size correct it: about ten instructions where the generic division takes
+// some thirty.  The chunk plan runs at the start of every workgroup, before
+// its first cache load, so it is kept short and free of branches.
+__host__ __device__ inline int div_small(int a, int b) {
+#ifdef __HIP_DEVICE_COMPILE__
+    int q = (int)((float)a * __builtin_amdgcn_rcpf((float)b));
+    const int r = a - q * b;
+    return q + (r >= b) - (r < 0);
+#else
+    return a / b;
+#endif
+}
+__host__ __device__ inline int ceil_small(int a, int b) { return div_small(a + b - 1, b); }
 __host__ __device__ inline int round_up32(int a) { return (a + 31) & ~31; }
 __host__ __device__ inline bool pow2(int a) { return a > 0 && (a & (a - 1)) == 0; }
-// ceil(a / b) for b a power of two: a shift (the chunk-finding arithmetic runs
-// at the start of every workgroup, before its first cache load)
-__host__ __device__ inline int ceil_div_pow2(int a, int b) { return (a + b - 1) >> __builtin_ctz((unsigned)b); }
 
 __host__ __device__ inline bool seq_pos_ok(const AttnParams &p, int sp) {
     return sp >= 0 && sp <= p.max_seq - p.q_len;
@@ -184,6 +198,8 @@ __host__ __device__ inline int balanced_len(const AttnParams &p, int64_t total) 
     int t;
     if (x >= (int64_t)p.target_wg * p.max_chunk)
         t = p.max_chunk;
+    else if (__builtin_expect(pow2(p.target_wg), 1))  // the automatic targets: a shift
+        t = (int)((x + p.target_wg - 1) >> __builtin_ctz((unsigned)p.target_wg));
     else if (x + p.target_wg <= (int64_t)0xffffffffu)
         t = (int)(((uint32_t)x + (uint32_t)p.target_wg - 1u) / (uint32_t)p.target_wg);
     else
@@ -201,29 +217,27 @@ __host__ __device__ inline int balanced_chunk(const AttnParams &p) {
     return balanced_len(p, total);
 }
 
-// Chunks of a sequence whose first new token sits at `sp`, for chunk length T.
+// Chunks of a sequence whose first new token sits at `sp`, for chunk length T
+// (straight-line code: an out-of-range sp runs on a one-key context and is
+// zeroed at the end).
 __host__ __device__ inline SeqChunks seq_chunks_at(const AttnParams &p, int sp, int T) {
-    SeqChunks s{0, 0, 0};
-    if (!seq_pos_ok(p, sp)) return s;
-    s.ctx = sp + p.q_len;
+    const bool ok = seq_pos_ok(p, sp);
+    const int ctx = ok ? sp + p.q_len : 1;
+    int len;
     if (p.fixed_chunk > 0) {
-        s.len = p.fixed_chunk;
-        s.n = ceil_div(s.ctx, s.len);
-        return s;
+        len = p.fixed_chunk;
+    } else {
+        int n = div_small(ctx + (T >> 1), T);  // round(ctx / T); T is a multiple of 32
+        if (p.seq_chunk_cap > 0 && n > p.seq_chunk_cap) n = p.seq_chunk_cap;
+        n = max(n, ceil_small(ctx, p.max_chunk));
+        n = min(max(n, 1), p.n_chunks);
+        const int raw = round_up32(ceil_small(ctx, n));
+        const int a = p.chunk_align;
+        len = a > 32 && 2 * raw >= a ? ceil_small(raw, a) * a : raw;
+        len = min(len, p.max_chunk);  // raw <= max_chunk: no chunk is shorter than raw
     }
-    int n = (2 * s.ctx + T) / (2 * T);  // round(ctx / T)
-    if (p.seq_chunk_cap > 0 && n > p.seq_chunk_cap) n = p.seq_chunk_cap;
-    const int n_cap = pow2(p.max_chunk) ? ceil_div_pow2(s.ctx, p.max_chunk) : ceil_div(s.ctx, p.max_chunk);
-    if (n < n_cap) n = n_cap;
-    if (n < 1) n = 1;
-    if (n > p.n_chunks) n = p.n_chunks;
-    s.n = n;
-    const int raw = round_up32(ceil_div(s.ctx, n));
-    const int a = p.chunk_align;
-    s.len = a > 32 && 2 * raw >= a ? (pow2(a) ? (raw + a - 1) & -a : (raw + a - 1) / a * a) : raw;
-    if (s.len > p.max_chunk) s.len = p.max_chunk;  // raw <= max_chunk: no chunk is shorter than raw
-    s.n = pow2(s.len) ? ceil_div_pow2(s.ctx, s.len) : ceil_div(s.ctx, s.len);  // rounding the length up may leave the last chunk empty
-    return s;
+    // rounding the length up may leave the last chunk empty: n from the length
+    return ok ? SeqChunks{ceil_small(ctx, len), len, ctx} : SeqChunks{0, 0, 0};
 }
 
 __host__ __device__ inline SeqChunks seq_chunks(const AttnParams &p, int b, int T) {
@@ -473,20 +487,25 @@ __device__ inline int balanced_chunk_wave(const AttnParams &p, int lane) {
 }
 
 // locate() by a whole wave; also returns the sequence's seq_pos.  Every lane
-// gets the same (uniform) results.
+// gets the same (uniform) results.  The loops run once per 64 sequences and
+// are not unrolled: one copy of the chunk arithmetic.
 __device__ inline bool locate_wave(const AttnParams &p, int &w, int &b, int &h, int &c, SeqChunks &sc, int &sp,
                                    int lane) {
-    int sp0 = lane < p.batch ? p.seq_pos[lane] : -1;  // the first 64 sequences, kept for the walk
+    const int sp0 = lane < p.batch ? p.seq_pos[lane] : -1;  // the first 64 sequences
     int T = p.fixed_chunk;
     if (T <= 0) {
         int64_t total = wave_sum_i(seq_pos_ok(p, sp0) ? sp0 + p.q_len : 0);
-        for (int b0 = 64; b0 < p.batch; b0 += 64) {
+#pragma unroll 1
+        for (int b0 = 64; __builtin_expect(b0 < p.batch, 0); b0 += 64) {
             const int bb = b0 + lane;
             const int s1 = bb < p.batch ? p.seq_pos[bb] : -1;
             total += wave_sum_i(seq_pos_ok(p, s1) ? s1 + p.q_len : 0);
         }
         T = balanced_len(p, total);
     }
+    // lane j holds sequence b0 + j, which has `here` items; the item is in the
+    // sequence where the inclusive count first passes w
+#pragma unroll 1
     for (int b0 = 0; b0 < p.batch; b0 += 64) {
         const int bb = b0 + lane;
         const int s1 = b0 == 0 ? sp0 : (bb < p.batch ? p.seq_pos[bb] : -1);
@@ -502,7 +521,7 @@ __device__ inline bool locate_wave(const AttnParams &p, int &w, int &b, int &h, 
             sc.len = __builtin_amdgcn_readlane(s.len, L);
             sc.ctx = __builtin_amdgcn_readlane(s.ctx, L);
             sp = __builtin_amdgcn_readlane(s1, L);
-            h = w / sc.n;
+            h = w <= (1 << 22) ? div_small(w, sc.n) : w / sc.n;
             c = w - h * sc.n;
             return true;
         }
