@@ -25,6 +25,9 @@ FLAGS = [
     "-I", INCLUDE, "-I", CSRC,
     # Packed fp32 instructions stay off: no v_pk_{add,mul,fma}_f32 in this library.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # The first three dwords of a kernel's scalar leading arguments (the attention
+    # kernels' seq_pos pointer and batch) are preloaded into registers at wave start.
+    "-mllvm", "-amdgpu-kernarg-preload-count=3",
 ]
 
 

@@ -162,7 +162,8 @@ constexpr int kMfmaWaves = 4;  // waves per workgroup, all on one chunk
 
 template <bool F16, int RB, bool ROPE>
 __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void attn_split_mfma_kernel(AttnParams p) {
+void attn_split_mfma_kernel(const int32_t *__restrict__ seq_pos, int32_t batch, AttnParams p) {
+    const int sp_first = first_seq_pos(seq_pos, batch, threadIdx.x & 63);
     constexpr int KS = kMfmaWaves;  // waves taking the chunk's tiles in turn
     const int tid = threadIdx.x, lane = tid & 63;
     const int kw = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
@@ -171,7 +172,7 @@ void attn_split_mfma_kernel(AttnParams p) {
     SeqChunks sc;
     int rest = blockIdx.x;
     int sp;
-    if (!locate_wave(p, rest, b, h, c, sc, sp, lane)) {  // past the last chunk of the launch
+    if (!locate_wave(p, seq_pos, batch, sp_first, rest, b, h, c, sc, sp, lane)) {  // past the last chunk of the launch
         if (p.out && rest < p.batch && !seq_pos_ok(p, p.seq_pos[rest]))
             flag_sequence_nan<F16>(p, rest, tid, 64 * kMfmaWaves);
         return;
@@ -231,11 +232,11 @@ void attn_split_mfma_kernel(AttnParams p) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) qop[s] = ld16(qp + 64 * s);
     };
-    // q (and its rotation's frequencies) are issued first, then the wave's
-    // first tile, and only then is q rotated or stored: the tile's loads are in
-    // flight while q arrives, and nothing waits for the tile before the first
-    // compute.  The rotation is a separate instantiation, so that without a
-    // table no conditional load sits between the two.
+    // q (and its rotation's frequencies) are issued first.  With one row block
+    // the wave's first tile follows at once and q is rotated after it: the
+    // tile's loads are in flight while q arrives.  The rotation is a separate
+    // instantiation, so that without a table no conditional load sits between
+    // the two.
     u32x4_t qreg[4];
     __shared__ u32x4_t qsh[RB > 1 ? RB : 1][16][17];
     const bool loads_q = RB == 1 || kw < RB;
@@ -251,14 +252,22 @@ void attn_split_mfma_kernel(AttnParams p) {
         if (ROPE && row < p.rows) rope_pieces_with<F16>(qop, p.rope_dim, sp + row / p.group, qfreq);
     };
     Tile ta, tb_;
-    if (nj > 0) load_full(ta, cv, kw * 32, l16, q);
-    if (loads_q) rotate_q(qreg, RB == 1 ? 0 : kw);
     if constexpr (RB > 1) {
+        // The row blocks are stored before the wave's first tile is issued.
+        // Stored after it, the store (on one side of a branch) made the compiler
+        // wait for the tile's loads too, and the first compute then waited for
+        // the whole tile instead of its first quarter: 1.1 us more on the
+        // 32-row verify workload.
         if (kw < RB) {
+            rotate_q(qreg, kw);
 #pragma unroll
             for (int s = 0; s < 4; ++s) qsh[kw][l16][4 * s + q] = qreg[s];
         }
+        if (nj > 0) load_full(ta, cv, kw * 32, l16, q);
         __syncthreads();
+    } else {
+        if (nj > 0) load_full(ta, cv, kw * 32, l16, q);
+        rotate_q(qreg, 0);
     }
     auto qpiece = [&](int rb, int s) -> u32x4_t {
         if constexpr (RB == 1)
@@ -494,14 +503,14 @@ static hipError_t launch_dtype(const AttnParams &p, int items, hipStream_t s) {
     const dim3 grid(items), block(64 * kMfmaWaves);
     if (p.rope_freqs) {
         if (p.rows <= 16)
-            hipLaunchKernelGGL((attn_split_mfma_kernel<F16, 1, true>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((attn_split_mfma_kernel<F16, 1, true>), grid, block, 0, s, p.seq_pos, p.batch, p);
         else
-            hipLaunchKernelGGL((attn_split_mfma_kernel<F16, 2, true>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((attn_split_mfma_kernel<F16, 2, true>), grid, block, 0, s, p.seq_pos, p.batch, p);
     } else {
         if (p.rows <= 16)
-            hipLaunchKernelGGL((attn_split_mfma_kernel<F16, 1, false>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((attn_split_mfma_kernel<F16, 1, false>), grid, block, 0, s, p.seq_pos, p.batch, p);
         else
-            hipLaunchKernelGGL((attn_split_mfma_kernel<F16, 2, false>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((attn_split_mfma_kernel<F16, 2, false>), grid, block, 0, s, p.seq_pos, p.batch, p);
     }
     return hipGetLastError();
 }

@@ -150,7 +150,8 @@ __device__ __forceinline__ void load_rows16(Tile16 &t, const CacheView &cv, int 
 
 template <bool F16, int RG, bool ROPE>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void attn_split_mfma256_kernel(AttnParams p) {
+void attn_split_mfma256_kernel(const int32_t *__restrict__ seq_pos, int32_t batch, AttnParams p) {
+    const int sp_first = first_seq_pos(seq_pos, batch, threadIdx.x & 63);
     constexpr int KS = kWaves / RG;  // waves sharing one row group's tiles
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -160,7 +161,7 @@ void attn_split_mfma256_kernel(AttnParams p) {
     SeqChunks sc;
     int rest = blockIdx.x;
     int sp;
-    if (!locate_wave(p, rest, b, h, c, sc, sp, lane)) {  // past the last chunk of the launch
+    if (!locate_wave(p, seq_pos, batch, sp_first, rest, b, h, c, sc, sp, lane)) {  // past the last chunk of the launch
         if (p.out && rest < p.batch && !seq_pos_ok(p, p.seq_pos[rest])) flag_sequence_nan<F16>(p, rest, tid, 64 * kWaves);
         return;
     }
@@ -430,14 +431,14 @@ hipError_t launch_dtype256(const AttnParams &p, int items, hipStream_t s) {
     const dim3 grid(items), block(64 * kWaves);
     if (p.rope_freqs) {
         if (p.rows <= 16)
-            hipLaunchKernelGGL((attn_split_mfma256_kernel<F16, 1, true>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((attn_split_mfma256_kernel<F16, 1, true>), grid, block, 0, s, p.seq_pos, p.batch, p);
         else
-            hipLaunchKernelGGL((attn_split_mfma256_kernel<F16, 2, true>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((attn_split_mfma256_kernel<F16, 2, true>), grid, block, 0, s, p.seq_pos, p.batch, p);
     } else {
         if (p.rows <= 16)
-            hipLaunchKernelGGL((attn_split_mfma256_kernel<F16, 1, false>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((attn_split_mfma256_kernel<F16, 1, false>), grid, block, 0, s, p.seq_pos, p.batch, p);
         else
-            hipLaunchKernelGGL((attn_split_mfma256_kernel<F16, 2, false>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((attn_split_mfma256_kernel<F16, 2, false>), grid, block, 0, s, p.seq_pos, p.batch, p);
     }
     return hipGetLastError();
 }

@@ -97,7 +97,8 @@ constexpr int kValuOneLaunchRows = 8;
 // rotation's registers never weigh on the kernel without one).
 // NW: waves per workgroup, 4 (chunks of up to 2048 keys) or 16 (up to 8192).
 template <bool F16, int RP, bool ROPE, int NW>
-__global__ __launch_bounds__(64 * NW) void attn_split_valu_kernel(AttnParams p) {
+__global__ __launch_bounds__(64 * NW) void attn_split_valu_kernel(const int32_t *__restrict__ seq_pos, int32_t batch, AttnParams p) {
+    const int sp_first = first_seq_pos(seq_pos, batch, threadIdx.x & 63);
     constexpr bool kOneLaunch = RP <= kValuOneLaunchRows;
     static_assert(!ROPE || kOneLaunch, "the rotary embedding is compiled up to 8 rows");
     extern __shared__ float lds[];  // scores [chunk][RP], later the wave sums [NW][RP][128]
@@ -109,7 +110,7 @@ __global__ __launch_bounds__(64 * NW) void attn_split_valu_kernel(AttnParams p) 
     SeqChunks sc;
     int item = blockIdx.x;
     int sp;
-    if (!locate_wave(p, item, b, h, c, sc, sp, threadIdx.x & 63)) {  // past the last chunk of the launch
+    if (!locate_wave(p, seq_pos, batch, sp_first, item, b, h, c, sc, sp, threadIdx.x & 63)) {  // past the last chunk of the launch
         if (kOneLaunch && p.out && item < p.batch && !seq_pos_ok(p, p.seq_pos[item]))
             flag_sequence_nan<F16>(p, item, threadIdx.x, 64 * NW);
         return;
@@ -504,11 +505,11 @@ static hipError_t launch_nw(const AttnParams &p, int grid, hipStream_t s) {
     const size_t lds = lds_bytes_of<RP, NW>(p);
     if constexpr (RP <= kValuOneLaunchRows) {
         if (p.rope_freqs) {
-            hipLaunchKernelGGL((attn_split_valu_kernel<F16, RP, true, NW>), dim3(grid), dim3(64 * NW), lds, s, p);
+            hipLaunchKernelGGL((attn_split_valu_kernel<F16, RP, true, NW>), dim3(grid), dim3(64 * NW), lds, s, p.seq_pos, p.batch, p);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((attn_split_valu_kernel<F16, RP, false, NW>), dim3(grid), dim3(64 * NW), lds, s, p);
+    hipLaunchKernelGGL((attn_split_valu_kernel<F16, RP, false, NW>), dim3(grid), dim3(64 * NW), lds, s, p.seq_pos, p.batch, p);
     return hipGetLastError();
 }
 

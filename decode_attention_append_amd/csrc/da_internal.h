@@ -486,19 +486,30 @@ __device__ inline int balanced_chunk_wave(const AttnParams &p, int lane) {
     return balanced_len(p, total);
 }
 
+// Lane j's position for the chunk plan, sequence min(j, batch - 1): the first
+// memory access of every attention kernel, issued from the preloaded arguments
+// with nothing to wait for.  locate_wave takes it raw and masks the lanes past
+// the batch where it first uses it.
+__device__ __forceinline__ int first_seq_pos(const int32_t *__restrict__ seq_pos, int batch, int lane) {
+    return seq_pos[min(lane, batch - 1)];
+}
+
 // locate() by a whole wave; also returns the sequence's seq_pos.  Every lane
-// gets the same (uniform) results.  The loops run once per 64 sequences and
+// gets the same (uniform) results.  `seq_pos` and `batch` are p's, passed as
+// the kernel's leading arguments: scalar arguments there are preloaded into
+// registers when the wave starts, so the positions' load is issued before the
+// parameter block's scalar loads return.  The loops run once per 64 sequences and
 // are not unrolled: one copy of the chunk arithmetic.
-__device__ inline bool locate_wave(const AttnParams &p, int &w, int &b, int &h, int &c, SeqChunks &sc, int &sp,
-                                   int lane) {
-    const int sp0 = lane < p.batch ? p.seq_pos[lane] : -1;  // the first 64 sequences
+__device__ inline bool locate_wave(const AttnParams &p, const int32_t *__restrict__ seq_pos, int batch,
+                                   int sp_first, int &w, int &b, int &h, int &c, SeqChunks &sc, int &sp, int lane) {
+    const int sp0 = lane < batch ? sp_first : -1;  // the first 64 sequences
     int T = p.fixed_chunk;
     if (T <= 0) {
         int64_t total = wave_sum_i(seq_pos_ok(p, sp0) ? sp0 + p.q_len : 0);
 #pragma unroll 1
-        for (int b0 = 64; __builtin_expect(b0 < p.batch, 0); b0 += 64) {
+        for (int b0 = 64; __builtin_expect(b0 < batch, 0); b0 += 64) {
             const int bb = b0 + lane;
-            const int s1 = bb < p.batch ? p.seq_pos[bb] : -1;
+            const int s1 = bb < batch ? seq_pos[bb] : -1;
             total += wave_sum_i(seq_pos_ok(p, s1) ? s1 + p.q_len : 0);
         }
         T = balanced_len(p, total);
@@ -506,9 +517,9 @@ __device__ inline bool locate_wave(const AttnParams &p, int &w, int &b, int &h, 
     // lane j holds sequence b0 + j, which has `here` items; the item is in the
     // sequence where the inclusive count first passes w
 #pragma unroll 1
-    for (int b0 = 0; b0 < p.batch; b0 += 64) {
+    for (int b0 = 0; b0 < batch; b0 += 64) {
         const int bb = b0 + lane;
-        const int s1 = b0 == 0 ? sp0 : (bb < p.batch ? p.seq_pos[bb] : -1);
+        const int s1 = b0 == 0 ? sp0 : (bb < batch ? seq_pos[bb] : -1);
         const SeqChunks s = seq_chunks_at(p, s1, T);
         const int here = s.n * p.n_kv_heads;
         const int incl = wave_incl_scan(here, lane);
