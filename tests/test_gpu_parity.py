@@ -335,6 +335,43 @@ def test_contract_breaking_seq_pos(q_len, Hq, Hkv, S, path):
     gu.compare_out(out[good], ref)
 
 
+@pytest.mark.parametrize("path", gu.PATHS)
+@pytest.mark.parametrize("Hq,Hkv,D,work_items", [
+    (64, 8, 128, 0),      # MFMA, 8 rows
+    (32, 8, 128, 0),      # vector ALU, 4 rows
+    (16, 2, 256, 0),      # head_dim 256
+    (64, 8, 128, 77),     # a chunk target that is not a power of two
+    (32, 8, 128, 1000),   # many short chunks
+])
+def test_many_sequences(Hq, Hkv, D, work_items, path):
+    """130 sequences: every workgroup walks three 64-sequence groups of positions to find
+    its chunk, with ragged contexts and three contract-breaking positions (their caches
+    untouched, their rows NaN)."""
+    B, S = 130, 400
+    rng = np.random.default_rng(D + Hq + work_items)
+    sp = rng.integers(0, S, B).astype(np.int32)
+    sp[[3, 64, 129]] = [-1, S, S + 7]
+    sp[[0, 63, 65, 128]] = [S - 1, 0, S - 1, 1]
+    _say("many sequences", Hq, Hkv, D, work_items, path)
+    inp = gu.make_case(B, 1, Hq, Hkv, S, sp, seed=29, head_dim=D)
+    kc0, vc0 = bits(inp["k_cache"]), bits(inp["v_cache"])
+    p = da.problem_for(inp["q"], inp["k_cache"], work_items=work_items)
+    out = gu.run_step(p, inp, path=path)
+    torch.cuda.synchronize()
+    kc, vc = bits(inp["k_cache"]), bits(inp["v_cache"])
+    bad = [3, 64, 129]
+    for b in bad:
+        assert np.array_equal(kc[b], kc0[b]) and np.array_equal(vc[b], vc0[b])
+        assert torch.isnan(out[b].float()).all()
+    good = [b for b in range(B) if b not in bad]
+    sub = lambda x: np.ascontiguousarray(x[good])  # noqa: E731
+    spg = sp[good]
+    k_ref, v_ref = gu.oracle.kv_append(sub(kc0), sub(vc0), sub(bits(inp["k_new"])), sub(bits(inp["v_new"])), spg)
+    assert np.array_equal(kc[good], k_ref) and np.array_equal(vc[good], v_ref)
+    ref = gu.oracle.gqa_decode(sub(bits(inp["q"])), k_ref, v_ref, spg, gu.oracle.BF16)
+    gu.compare_out(out[good], ref)
+
+
 def test_decode_step_errors_launch_nothing():
     import ctypes
     inp = gu.make_case(2, 1, 16, 8, 256, [10, 20], seed=17)
