@@ -21,7 +21,9 @@ constexpr int kCombineThreads = 256;
 constexpr int kCombineMaxChunks = 2048;  // whole weight table in LDS
 
 template <bool F16, int D>
-__global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnParams p, uint16_t *out) {
+__global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const int32_t *__restrict__ seq_pos,
+                                                                         int32_t batch, AttnParams p, uint16_t *out) {
+    const int sp_first = first_seq_pos(seq_pos, batch, threadIdx.x & 63);
     constexpr int NV = D / 64;  // dims per lane
     __shared__ float wts[kCombineMaxChunks];
     __shared__ float red[4][D];
@@ -33,7 +35,8 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnParam
     const int h = bh - b * p.n_kv_heads;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const size_t o_off = out_row_off(p, b, h, r) + NV * lane;
-    const SeqChunks sc = seq_chunks(p, b, p.fixed_chunk > 0 ? p.fixed_chunk : balanced_chunk_wave(p, lane));
+    const int T = p.fixed_chunk > 0 ? p.fixed_chunk : balanced_chunk_wave(p, seq_pos, batch, sp_first, lane);
+    const SeqChunks sc = seq_chunks_at(p, b < 64 ? __builtin_amdgcn_readlane(sp_first, b) : seq_pos[b], T);
     if (sc.n == 0) {  // seq_pos breaks the contract: flag the rows with NaN
         if (wave == 0) {
             const uint16_t nan16 = F16 ? 0x7e00u : 0x7fc0u;
@@ -121,14 +124,14 @@ hipError_t launch_attn_combine(const AttnParams &p, bool fp16, void *out, hipStr
     uint16_t *o = (uint16_t *)out;
     if (p.head_dim == 256) {
         if (fp16)
-            hipLaunchKernelGGL((attn_combine_kernel<true, 256>), dim3(grid), dim3(kCombineThreads), 0, s, p, o);
+            hipLaunchKernelGGL((attn_combine_kernel<true, 256>), dim3(grid), dim3(kCombineThreads), 0, s, p.seq_pos, p.batch, p, o);
         else
-            hipLaunchKernelGGL((attn_combine_kernel<false, 256>), dim3(grid), dim3(kCombineThreads), 0, s, p, o);
+            hipLaunchKernelGGL((attn_combine_kernel<false, 256>), dim3(grid), dim3(kCombineThreads), 0, s, p.seq_pos, p.batch, p, o);
     } else {
         if (fp16)
-            hipLaunchKernelGGL((attn_combine_kernel<true, 128>), dim3(grid), dim3(kCombineThreads), 0, s, p, o);
+            hipLaunchKernelGGL((attn_combine_kernel<true, 128>), dim3(grid), dim3(kCombineThreads), 0, s, p.seq_pos, p.batch, p, o);
         else
-            hipLaunchKernelGGL((attn_combine_kernel<false, 128>), dim3(grid), dim3(kCombineThreads), 0, s, p, o);
+            hipLaunchKernelGGL((attn_combine_kernel<false, 128>), dim3(grid), dim3(kCombineThreads), 0, s, p.seq_pos, p.batch, p, o);
     }
     return hipGetLastError();
 }

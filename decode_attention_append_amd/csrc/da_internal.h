@@ -471,27 +471,30 @@ __device__ __forceinline__ int wave_sum_i(int x) {
     return __builtin_amdgcn_readlane(wave_incl_scan(x, 0), 63);
 }
 
-// The chunk plan's per-launch values, computed by a whole wave: lane j of each
-// pass holds sequence (pass + j), so the positions arrive in one vector load
-// per 64 sequences instead of a chain of dependent scalar loads (every wave of
-// the launch reads them while the cache streams, and a serial chain there costs
-// microseconds).  Same results as balanced_chunk / locate.
-__device__ inline int balanced_chunk_wave(const AttnParams &p, int lane) {
-    int64_t total = 0;
-    for (int b0 = 0; b0 < p.batch; b0 += 64) {
-        const int b = b0 + lane;
-        const int sp = b < p.batch ? p.seq_pos[b] : -1;
-        total += wave_sum_i(seq_pos_ok(p, sp) ? sp + p.q_len : 0);
-    }
-    return balanced_len(p, total);
-}
-
 // Lane j's position for the chunk plan, sequence min(j, batch - 1): the first
-// memory access of every attention kernel, issued from the preloaded arguments
+// memory access of the attention and combine kernels, issued from the preloaded arguments
 // with nothing to wait for.  locate_wave takes it raw and masks the lanes past
 // the batch where it first uses it.
 __device__ __forceinline__ int first_seq_pos(const int32_t *__restrict__ seq_pos, int batch, int lane) {
     return seq_pos[min(lane, batch - 1)];
+}
+
+// The chunk plan's per-launch values, computed by a whole wave: lane j of each
+// pass holds sequence (pass + j), so the positions arrive in one vector load
+// per 64 sequences instead of a chain of dependent scalar loads (every wave of
+// the launch reads them while the cache streams, and a serial chain there costs
+// microseconds).  Same results as balanced_chunk / locate.  `sp_first` is
+// first_seq_pos()'s value for this lane (the first 64 sequences).
+__device__ inline int balanced_chunk_wave(const AttnParams &p, const int32_t *__restrict__ seq_pos, int batch,
+                                          int sp_first, int lane) {
+    int64_t total = wave_sum_i(lane < batch && seq_pos_ok(p, sp_first) ? sp_first + p.q_len : 0);
+#pragma unroll 1
+    for (int b0 = 64; __builtin_expect(b0 < batch, 0); b0 += 64) {
+        const int b = b0 + lane;
+        const int sp = b < batch ? seq_pos[b] : -1;
+        total += wave_sum_i(seq_pos_ok(p, sp) ? sp + p.q_len : 0);
+    }
+    return balanced_len(p, total);
 }
 
 // locate() by a whole wave; also returns the sequence's seq_pos.  Every lane
