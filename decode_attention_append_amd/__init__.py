@@ -15,7 +15,6 @@ Names follow the C entry points without their ``da_`` prefix:
 three separate calls in order.
 """
 import ctypes
-import math
 import os
 
 import torch
@@ -325,7 +324,3 @@ def decode_step_separate(p: Problem, q, k_cache, v_cache, k_new, v_new, seq_pos,
     kv_append(p, k_cache, v_cache, k_new, v_new, seq_pos, stream)
     gqa_decode_attn(p, q, k_cache, v_cache, seq_pos, workspace, stream)
     gqa_decode_attn_combine(p, workspace, seq_pos, out, stream)
-
-
-def default_scale(head_dim: int) -> float:
-    return 1.0 / math.sqrt(head_dim)

@@ -18,10 +18,15 @@
 //    lane (i, q) loads 16 bytes (dims 128 hh + 8i .. +7) of each of keys
 //    4q .. 4q+3, and v_perm pairs their 16-bit halves, so MFMA (hh, o) produces
 //    dims 128 hh + 8 (4q + v) + o of every row;
-//  - everything else (one wave per chunk, pairs of waves above 16 rows, two
-//    tile buffers used in turn, the per-row path for the chunk's last tile and
-//    this step's new rows, the fused append, rotary embedding, paged caches
-//    and the in-launch merge) follows the head_dim-128 kernel.
+//  - one 4-wave workgroup per chunk.  Up to 16 query rows every wave computes
+//    every row and the four waves take the chunk's tiles in turn (tile i by
+//    wave i mod 4); above 16 rows the waves form two pairs, one per 16-row
+//    group, and the two waves of a pair take the tiles in turn, so each tile
+//    is read once per row group;
+//  - everything else follows the head_dim-128 kernel: two tile buffers used
+//    in turn, the per-row path for the chunk's last tile and this step's new
+//    rows, the fused append, rotary embedding, paged caches and the in-launch
+//    merge.
 #include "da_internal.h"
 
 #include <math.h>
