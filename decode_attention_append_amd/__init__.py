@@ -10,7 +10,8 @@ the library has not been built.
 
 Names follow the C entry points without their ``da_`` prefix:
 ``kv_append``, ``gqa_decode_attn``, ``gqa_decode_attn_combine``,
-``decode_step`` (the one-launch step), ``workspace_init``,
+``decode_step`` (the one-launch step), ``decode_step_static`` (the same without
+a workspace), ``workspace_init``,
 ``workspace_bytes``, ``plan_attention``.  ``decode_step_separate`` runs the
 three separate calls in order.
 """
@@ -25,6 +26,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdecode_attn.so")
 
 DA_OK, DA_ERR_INVALID_ARG, DA_ERR_UNSUPPORTED, DA_ERR_WORKSPACE, DA_ERR_HIP = 0, -1, -2, -3, -4
+DA_ERR_SCRATCH_LIMIT = -5
 DA_BF16, DA_FP16 = 0, 1
 VARIANTS = {0: "valu", 1: "mfma"}
 _DTYPE_CODE = {torch.bfloat16: DA_BF16, torch.float16: DA_FP16}
@@ -80,8 +82,8 @@ class Plan(ctypes.Structure):
 
 
 EXPORTS = ("da_plan_attention", "da_workspace_bytes", "da_kv_append", "da_gqa_decode_attn",
-           "da_gqa_decode_attn_combine", "da_workspace_init", "da_decode_step", "da_chunk_layout",
-           "da_status_str")
+           "da_gqa_decode_attn_combine", "da_workspace_init", "da_decode_step", "da_decode_step_static",
+           "da_chunk_layout", "da_status_str")
 
 
 def _load():
@@ -106,6 +108,8 @@ def _load():
     lib.da_workspace_init.restype = ctypes.c_int
     lib.da_decode_step.argtypes = [pp, vp, vp, vp, vp, vp, i32p, vp, sz, vp, vp]
     lib.da_decode_step.restype = ctypes.c_int
+    lib.da_decode_step_static.argtypes = [pp, vp, vp, vp, vp, vp, i32p, vp, vp]
+    lib.da_decode_step_static.restype = ctypes.c_int
     lib.da_chunk_layout.argtypes = [pp, vp, vp, vp]
     lib.da_chunk_layout.restype = ctypes.c_int
     lib.da_status_str.argtypes = [ctypes.c_int]
@@ -316,6 +320,21 @@ def decode_step(p: Problem, q, k_cache, v_cache, k_new, v_new, seq_pos, workspac
         _dev(out, "out", qs, e), _stream(stream))
     if st != DA_OK:
         raise DecodeAttnError(st, "da_decode_step")
+
+
+def decode_step_static(p: Problem, q, k_cache, v_cache, k_new, v_new, seq_pos, out, stream=None):
+    """da_decode_step_static: da_decode_step with the library's own scratch instead of a
+    workspace (nothing is allocated; calls on one GPU must not overlap)."""
+    e = _elem(p)
+    cs = _cache_shape(p)
+    ns = (p.batch, p.q_len, p.n_kv_heads, p.head_dim)
+    qs = (p.batch, p.q_len, p.n_q_heads, p.head_dim)
+    st = _get_lib().da_decode_step_static(
+        ctypes.byref(p), _dev(q, "q", qs, e), _dev(k_cache, "k_cache", cs, e), _dev(v_cache, "v_cache", cs, e),
+        _dev(k_new, "k_new", ns, e), _dev(v_new, "v_new", ns, e),
+        _dev(seq_pos, "seq_pos", (p.batch,), torch.int32), _dev(out, "out", qs, e), _stream(stream))
+    if st != DA_OK:
+        raise DecodeAttnError(st, "da_decode_step_static")
 
 
 def decode_step_separate(p: Problem, q, k_cache, v_cache, k_new, v_new, seq_pos, workspace, out,

@@ -6,6 +6,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 namespace {
 
 using namespace da;
@@ -201,6 +203,20 @@ int32_t *counters_of(const da_problem *p, const da_plan &pl, void *workspace) {
                        align256(ws_ml_floats(bh, pl.n_chunks, pl.rows) * sizeof(float)));
 }
 
+// Chunk slots per (sequence, KV head) the one-launch step with the fused merge
+// can use: balanced chunking caps a sequence there at kOneLaunchSeqChunks
+// chunks unless its length needs more of the longest chunk (the same bound
+// plan_of checks), so the chunking itself is the same as with n_chunks slots.
+int32_t fused_slots(const da_problem *p, const da_plan &pl) {
+    int64_t nb_max = pl.n_chunks;
+    if (pl.balanced) {
+        const int64_t need = (p->max_seq + pl.chunk_tokens - 1) / pl.chunk_tokens;
+        const int64_t bound = need > kOneLaunchSeqChunks ? need : kOneLaunchSeqChunks;
+        if (bound < nb_max) nb_max = bound;
+    }
+    return (int32_t)nb_max;
+}
+
 KvLayout layout_of(const da_problem *p) {
     KvLayout L;
     L.row_bytes = p->head_dim * 2;
@@ -248,6 +264,101 @@ AttnParams attn_params(const da_problem *p, const da_plan &pl, const void *q, co
     a.counters = nullptr;
     a.out = nullptr;
     return a;
+}
+
+bool step_pointers_ok(const void *q, const void *k_cache, const void *v_cache, const void *k_new, const void *v_new,
+                      const int32_t *seq_pos, const void *out) {
+    if (!q || !k_cache || !v_cache || !k_new || !v_new || !seq_pos || !out) return false;
+    return aligned16(q) && aligned16(k_cache) && aligned16(v_cache) && aligned16(k_new) && aligned16(v_new) &&
+           aligned16(out) && ((uintptr_t)seq_pos & 3u) == 0;
+}
+
+// The one-launch step (or, where the plan does not fuse, its two or three
+// launches) with the partials at acc / ml (`slots` chunk slots per (sequence,
+// KV head)) and the arrival counters at `counters` (zero between calls).
+da_status decode_step_on(const da_problem *p, const da_plan &pl, const void *q, void *k_cache, void *v_cache,
+                         const void *k_new, const void *v_new, const int32_t *seq_pos, float *acc, float *ml,
+                         int32_t slots, int32_t *counters, void *out, hipStream_t s) {
+    const bool fp16 = p->dtype == DA_FP16;
+    AttnParams a = attn_params(p, pl, q, k_cache, v_cache, seq_pos, nullptr);
+    a.ws_acc = acc;
+    a.ws_ml = ml;
+    a.n_chunks = slots;
+    if (!one_launch_capable(pl.variant, pl.rows)) {  // append, attention, combine
+        AppendParams ap;
+        ap.k_cache = (uint8_t *)k_cache;
+        ap.v_cache = (uint8_t *)v_cache;
+        ap.k_new = (const uint8_t *)k_new;
+        ap.v_new = (const uint8_t *)v_new;
+        ap.seq_pos = seq_pos;
+        ap.rope_freqs = p->rope_freqs;
+        ap.layout = layout_of(p);
+        ap.head_dim = p->head_dim;
+        ap.rope_dim = p->rope_dim ? p->rope_dim : p->head_dim;
+        ap.batch = p->batch;
+        ap.q_len = p->q_len;
+        ap.n_kv_heads = p->n_kv_heads;
+        ap.max_seq = p->max_seq;
+        (void)hipGetLastError();
+        hipError_t e = launch_kv_append(ap, p->batch * p->q_len * p->n_kv_heads * (p->head_dim / 8), fp16, s);
+        if (e == hipSuccess) e = launch_attn_valu(a, pl.items, fp16, s);
+        if (e == hipSuccess) e = launch_attn_combine(a, fp16, out, s);
+        return e == hipSuccess ? DA_OK : DA_ERR_HIP;
+    }
+    a.k_cache_w = (uint8_t *)k_cache;
+    a.v_cache_w = (uint8_t *)v_cache;
+    a.k_new = (const uint8_t *)k_new;
+    a.v_new = (const uint8_t *)v_new;
+    int items = pl.items;
+    if (pl.fused_combine) {
+        a.seq_chunk_cap = pl.balanced ? kOneLaunchSeqChunks : 0;
+        a.counters = counters;
+        a.out = (uint16_t *)out;
+        items += p->batch;  // the items past the chunks flag contract-breaking sequences
+    }
+    (void)hipGetLastError();
+    hipError_t e = pl.variant == DA_VARIANT_MFMA ? launch_attn_mfma(a, items, fp16, s)
+                                                 : launch_attn_valu(a, items, fp16, s);
+    if (e == hipSuccess && !pl.fused_combine) e = launch_attn_combine(a, fp16, out, s);
+    return e == hipSuccess ? DA_OK : DA_ERR_HIP;
+}
+
+// ---- the allocation-free step's scratch ------------------------------------------
+// da_decode_step_static keeps its arrival counters (the first kScratchCounterBytes)
+// and its partials in this array, one copy per GPU the library runs on, held
+// until the process ends.  Host code never passes the array's name to a kernel
+// (on the host it is only a stand-in for the symbol): the device address comes
+// from hipGetSymbolAddress, once per device, with that device current, and the
+// counters are zeroed then, on the caller's stream, ahead of the step's kernels.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+constexpr size_t kScratchCounterBytes = (size_t)1 << 20;  // int32 counters of up to 262144 (sequence, KV head) pairs
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+struct ScratchOnDevice {
+    std::once_flag once;
+    uint8_t *ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+ScratchOnDevice g_scratch[kMaxDevices];
+
+hipError_t scratch_on_current_device(uint8_t **ptr, hipStream_t s) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    ScratchOnDevice &d = g_scratch[dev];
+    std::call_once(d.once, [&] {
+        void *addr = nullptr;
+        d.err = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+        if (d.err == hipSuccess) {
+            d.ptr = (uint8_t *)addr;
+            (void)hipGetLastError();
+            d.err = launch_fill_zero((int32_t *)d.ptr, (int)(kScratchCounterBytes / sizeof(int32_t)), s);
+        }
+    });
+    *ptr = d.ptr;
+    return d.err;
 }
 
 }  // namespace
@@ -351,54 +462,39 @@ da_status da_decode_step(const da_problem *p, const void *q, void *k_cache, void
                          void *out, void *stream) {
     const da_status st = check_problem(p);
     if (st != DA_OK) return st;
-    if (!q || !k_cache || !v_cache || !k_new || !v_new || !seq_pos || !workspace || !out)
-        return DA_ERR_INVALID_ARG;
-    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new) ||
-        !aligned16(workspace) || !aligned16(out) || ((uintptr_t)seq_pos & 3u))
-        return DA_ERR_INVALID_ARG;
+    if (!workspace || !aligned16(workspace)) return DA_ERR_INVALID_ARG;
+    if (!step_pointers_ok(q, k_cache, v_cache, k_new, v_new, seq_pos, out)) return DA_ERR_INVALID_ARG;
     da_plan pl;
     plan_of(p, &pl);
     if (workspace_bytes < pl.workspace_bytes) return DA_ERR_WORKSPACE;
-    const bool fp16 = p->dtype == DA_FP16;
+    const int32_t bh = p->batch * p->n_kv_heads;
+    float *acc = (float *)workspace;
+    float *ml = (float *)((uint8_t *)workspace + align256(ws_acc_floats(bh, pl.n_chunks, pl.rows, p->head_dim) * sizeof(float)));
+    return decode_step_on(p, pl, q, k_cache, v_cache, k_new, v_new, seq_pos, acc, ml, pl.n_chunks,
+                          counters_of(p, pl, workspace), out, (hipStream_t)stream);
+}
+
+da_status da_decode_step_static(const da_problem *p, const void *q, void *k_cache, void *v_cache,
+                                const void *k_new, const void *v_new, const int32_t *seq_pos, void *out,
+                                void *stream) {
+    const da_status st = check_problem(p);
+    if (st != DA_OK) return st;
+    if (!step_pointers_ok(q, k_cache, v_cache, k_new, v_new, seq_pos, out)) return DA_ERR_INVALID_ARG;
+    da_plan pl;
+    plan_of(p, &pl);
+    // partials: with the fused merge only the slots that step can fill
+    const int32_t bh = p->batch * p->n_kv_heads;
+    const int32_t slots = pl.fused_combine ? fused_slots(p, pl) : pl.n_chunks;
+    const size_t acc_bytes = align256(ws_acc_floats(bh, slots, pl.rows, p->head_dim) * sizeof(float));
+    const size_t ml_bytes = align256(ws_ml_floats(bh, slots, pl.rows) * sizeof(float));
+    if ((size_t)bh * sizeof(int32_t) > kScratchCounterBytes ||
+        kScratchCounterBytes + acc_bytes + ml_bytes > kScratchBytes)
+        return DA_ERR_SCRATCH_LIMIT;
     hipStream_t s = (hipStream_t)stream;
-    AttnParams a = attn_params(p, pl, q, k_cache, v_cache, seq_pos, workspace);
-    if (!one_launch_capable(pl.variant, pl.rows)) {  // append, attention, combine
-        AppendParams ap;
-        ap.k_cache = (uint8_t *)k_cache;
-        ap.v_cache = (uint8_t *)v_cache;
-        ap.k_new = (const uint8_t *)k_new;
-        ap.v_new = (const uint8_t *)v_new;
-        ap.seq_pos = seq_pos;
-        ap.rope_freqs = p->rope_freqs;
-        ap.layout = layout_of(p);
-        ap.head_dim = p->head_dim;
-        ap.rope_dim = p->rope_dim ? p->rope_dim : p->head_dim;
-        ap.batch = p->batch;
-        ap.q_len = p->q_len;
-        ap.n_kv_heads = p->n_kv_heads;
-        ap.max_seq = p->max_seq;
-        (void)hipGetLastError();
-        hipError_t e = launch_kv_append(ap, p->batch * p->q_len * p->n_kv_heads * (p->head_dim / 8), fp16, s);
-        if (e == hipSuccess) e = launch_attn_valu(a, pl.items, fp16, s);
-        if (e == hipSuccess) e = launch_attn_combine(a, fp16, out, s);
-        return e == hipSuccess ? DA_OK : DA_ERR_HIP;
-    }
-    a.k_cache_w = (uint8_t *)k_cache;
-    a.v_cache_w = (uint8_t *)v_cache;
-    a.k_new = (const uint8_t *)k_new;
-    a.v_new = (const uint8_t *)v_new;
-    int items = pl.items;
-    if (pl.fused_combine) {
-        a.seq_chunk_cap = pl.balanced ? kOneLaunchSeqChunks : 0;
-        a.counters = counters_of(p, pl, workspace);
-        a.out = (uint16_t *)out;
-        items += p->batch;  // the items past the chunks flag contract-breaking sequences
-    }
-    (void)hipGetLastError();
-    hipError_t e = pl.variant == DA_VARIANT_MFMA ? launch_attn_mfma(a, items, fp16, s)
-                                                 : launch_attn_valu(a, items, fp16, s);
-    if (e == hipSuccess && !pl.fused_combine) e = launch_attn_combine(a, fp16, out, s);
-    return e == hipSuccess ? DA_OK : DA_ERR_HIP;
+    uint8_t *base = nullptr;
+    if (scratch_on_current_device(&base, s) != hipSuccess) return DA_ERR_HIP;
+    return decode_step_on(p, pl, q, k_cache, v_cache, k_new, v_new, seq_pos, (float *)(base + kScratchCounterBytes),
+                          (float *)(base + kScratchCounterBytes + acc_bytes), slots, (int32_t *)base, out, s);
 }
 
 da_status da_chunk_layout(const da_problem *p, const int32_t *seq_pos_host, int32_t *n_chunks,
@@ -425,6 +521,7 @@ const char *da_status_str(da_status s) {
         case DA_ERR_UNSUPPORTED: return "unsupported problem";
         case DA_ERR_WORKSPACE: return "workspace too small";
         case DA_ERR_HIP: return "HIP launch failed";
+        case DA_ERR_SCRATCH_LIMIT: return "problem needs more scratch than the allocation-free step holds";
     }
     return "unknown status";
 }

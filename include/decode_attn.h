@@ -33,7 +33,8 @@
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
  *    work is enqueued asynchronously on it, in call order; nothing here
  *    synchronises, allocates, frees, or reads device memory on the host.
- *  - The caller owns every buffer.  The library keeps no state between calls.
+ *  - The caller owns every buffer.  The library keeps no state between calls,
+ *    except the scratch of da_decode_step_static (see there).
  *  - Layouts (row-major, contiguous, element = 2-byte bf16 or fp16):
  *        q, out          [B][q_len][Hq][D]
  *        k_new, v_new    [B][q_len][Hkv][D]
@@ -65,7 +66,8 @@ typedef enum {
     DA_ERR_INVALID_ARG = -1, /* null or misaligned pointer, non-positive size, Hq % Hkv != 0 */
     DA_ERR_UNSUPPORTED = -2, /* valid but not implemented: head_dim other than 128 / 256, q_len > 8, ... */
     DA_ERR_WORKSPACE = -3,   /* workspace smaller than da_workspace_bytes() */
-    DA_ERR_HIP = -4          /* the HIP runtime refused a launch */
+    DA_ERR_HIP = -4,         /* the HIP runtime refused a launch */
+    DA_ERR_SCRATCH_LIMIT = -5 /* da_decode_step_static: the problem needs more than its scratch */
 } da_status;
 
 typedef enum { DA_BF16 = 0, DA_FP16 = 1 } da_dtype;
@@ -245,6 +247,27 @@ da_status da_workspace_init(const da_problem *p, void *workspace, size_t workspa
 da_status da_decode_step(const da_problem *p, const void *q, void *k_cache, void *v_cache, const void *k_new,
                          const void *v_new, const int32_t *seq_pos, void *workspace, size_t workspace_bytes,
                          void *out, void *stream);
+
+/*
+ * da_decode_step without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, results and launches as da_decode_step
+ * minus `workspace`: the partials and the arrival counters live in a scratch
+ * array inside the library, 32 MiB on each GPU the library runs on, held until
+ * the process ends (its device address is looked up once per device, and its
+ * counters zeroed then, on `stream`).  Nothing here allocates.
+ *  - A problem whose partials and counters do not fit returns
+ *    DA_ERR_SCRATCH_LIMIT before anything is enqueued: with the fused merge
+ *    that takes B * Hkv * min(16, max_seq / 64) * rows * (head_dim + 2) * 4
+ *    bytes, plus 1 MiB for the counters (at most 262144 sequence x KV head
+ *    pairs); without it, the full da_workspace_bytes.
+ *  - Every call on one GPU shares that GPU's scratch, which keeps the last
+ *    call's partials: calls that overlap on one GPU (other streams, other
+ *    threads) race and give wrong results.  Order them on one stream.
+ */
+da_status da_decode_step_static(const da_problem *p, const void *q, void *k_cache, void *v_cache,
+                                const void *k_new, const void *v_new, const int32_t *seq_pos, void *out,
+                                void *stream);
 
 /*
  * The chunking da_gqa_decode_attn and the combine will use for these seq_pos

@@ -128,6 +128,27 @@ def test_decode_step_rejects_before_launch():
     assert da.lib.da_workspace_init(ctypes.byref(p), None, 1 << 30, None) == da.DA_ERR_INVALID_ARG
 
 
+def test_static_step_rejects_before_launch():
+    """da_decode_step_static: bad arguments, and problems whose partials do not fit
+    its scratch, return a status before any HIP call (no GPU is needed here)."""
+    buf = (ctypes.c_uint8 * 64)()
+    good = ctypes.addressof(buf) + (-ctypes.addressof(buf)) % 16
+    args = [good] * 6
+    p = P()
+    assert da.lib.da_decode_step_static(ctypes.byref(p), None, *args[1:], good, None) == da.DA_ERR_INVALID_ARG
+    assert da.lib.da_decode_step_static(ctypes.byref(p), *args, good + 4, None) == da.DA_ERR_INVALID_ARG
+    assert da.lib.da_decode_step_static(ctypes.byref(P(head_dim=64)), *args, good, None) == da.DA_ERR_UNSUPPORTED
+    # fused merge: 512 heads x 16 slots x 8 rows x 130 floats = 34 MB > 31 MiB of partials
+    big = P(batch=64, n_q_heads=64, n_kv_heads=8, max_seq=65536)
+    assert da.plan_attention(big)["fused_combine"]
+    assert da.lib.da_decode_step_static(ctypes.byref(big), *args, good, None) == da.DA_ERR_SCRATCH_LIMIT
+    # without the fused merge the whole separate-call workspace is needed
+    unfused = P(batch=8, q_len=4, n_q_heads=32, n_kv_heads=4, max_seq=8192)
+    assert not da.plan_attention(unfused)["fused_combine"]
+    assert da.lib.da_decode_step_static(ctypes.byref(unfused), *args, good, None) == da.DA_ERR_SCRATCH_LIMIT
+    assert "scratch" in da.status_str(da.DA_ERR_SCRATCH_LIMIT)
+
+
 @pytest.mark.parametrize("shape,fused", [
     (dict(batch=32, n_q_heads=16, n_kv_heads=8, max_seq=8192), True),    # vector ALU, 2 rows
     (dict(batch=1, n_q_heads=16, n_kv_heads=16, max_seq=4096, dtype="fp16"), True),  # MHA

@@ -1,0 +1,71 @@
+"""The allocation-free step, da_decode_step_static, called through the C ABI
+against da_decode_step on the same inputs: the caches bit for bit, the outputs
+bit for bit (same kernels, same chunking), and the outputs within the oracle's
+tolerance.  Two calls in a row on one GPU, the second with a smaller problem,
+so the second starts from the scratch the first left behind."""
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_append_amd as da
+import oracle
+from tests import gpu_util as gu
+from tests.oracle_pins import bits
+
+pytestmark = pytest.mark.gpu
+
+# (B, q_len, Hq, Hkv, max_seq, seq_pos, dtype): the matrix-core kernel with the
+# merge in the launch (several chunks per head), then a smaller vector-ALU case.
+CASES = [
+    (4, 1, 64, 8, 6000, [5999, 4100, 3000, 5500], torch.bfloat16),
+    (1, 2, 16, 8, 700, [640], torch.float16),
+]
+
+
+def _case(c, seed):
+    B, q_len, Hq, Hkv, S, sp, dt = c
+    return gu.make_case(B, q_len, Hq, Hkv, S, sp, dtype=dt, seed=seed)
+
+
+def _clone(inp):
+    return {k: v.clone() for k, v in inp.items()}
+
+
+def test_static_step_matches_workspace_step_twice():
+    for n, c in enumerate(CASES):
+        print(f"[no-alloc] call {n}: B, q_len, Hq, Hkv, max_seq, seq_pos = {c[:6]}", flush=True)
+        inp = _case(c, seed=900 + n)
+        ref_inp, st_inp = _clone(inp), _clone(inp)
+        p = da.problem_for(inp["q"], inp["k_cache"])
+        out_ws = gu.run_step(p, ref_inp)
+        out_st = torch.empty_like(out_ws)
+        da.decode_step_static(p, st_inp["q"], st_inp["k_cache"], st_inp["v_cache"], st_inp["k_new"],
+                              st_inp["v_new"], st_inp["seq_pos"], out_st)
+        torch.cuda.synchronize()
+        assert torch.equal(st_inp["k_cache"], ref_inp["k_cache"]) and torch.equal(st_inp["v_cache"], ref_inp["v_cache"])
+        assert torch.equal(out_st.view(torch.int16), out_ws.view(torch.int16)), f"call {n}: outputs differ"
+        # and the oracle: append bit for bit, attention within the tolerance
+        dt = gu.odt(inp["q"].dtype)
+        sp = inp["seq_pos"].cpu().numpy()
+        k_ref, v_ref = oracle.kv_append(bits(inp["k_cache"]), bits(inp["v_cache"]), bits(inp["k_new"]),
+                                        bits(inp["v_new"]), sp)
+        assert np.array_equal(bits(st_inp["k_cache"]), k_ref) and np.array_equal(bits(st_inp["v_cache"]), v_ref)
+        ref = oracle.gqa_decode(bits(inp["q"]), k_ref, v_ref, sp, dt)
+        gu.compare_out(out_st, ref, f"static step, call {n}")
+
+
+def test_static_step_repeats_bit_for_bit():
+    """The scratch's counters return to zero: the same step again gives the same bits."""
+    c = CASES[0]
+    print(f"[no-alloc] repeat: {c[:6]}", flush=True)
+    inp = _case(c, seed=77)
+    p = da.problem_for(inp["q"], inp["k_cache"])
+    outs = []
+    for _ in range(3):
+        out = torch.empty_like(inp["q"])
+        da.decode_step_static(p, inp["q"], inp["k_cache"], inp["v_cache"], inp["k_new"], inp["v_new"],
+                              inp["seq_pos"], out)
+        outs.append(out)
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
