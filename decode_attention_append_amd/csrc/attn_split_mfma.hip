@@ -30,14 +30,18 @@
 //  - P is rounded to the input's 16-bit type for P V, and the fp32 sum l adds
 //    those same rounded weights, so the result is a convex combination of the
 //    value rows up to fp32 rounding;
-//  - one MFMA applies a value row to 16 query rows at once, so a later draft
-//    token's value row meets earlier draft tokens' rows with weight exactly 0:
-//    finite values contribute nothing, as the mask requires, but an inf/NaN
-//    value there would reach them as 0 * inf.  Slots past the context are
+//  - one MFMA applies a value row to 16 query rows at once, so a key hidden
+//    from some of them would reach those rows as 0 * v, which is NaN for a
+//    non-finite v.  The only such keys are this step's later draft tokens
+//    (positions past seq_pos, at most q_len - 1 of them, in the chunk's last
+//    tiles): their value rows are zeroed in the MFMA operand and added on the
+//    vector ALU only to the rows that see them.  Slots past the context are
 //    never read into a product.
 #include "da_internal.h"
 
 #include <math.h>
+
+#include <type_traits>
 
 namespace da {
 
@@ -206,7 +210,10 @@ void attn_split_mfma_kernel(const int32_t *__restrict__ seq_pos, int32_t batch, 
     // tiles kw, kw + KS, ... of them.
     const int new_first = p.k_new ? sp - t0 : n_tok;
     const int n_all = (n_tok + 31) >> 5;
-    const int nt = min(n_tok >> 5, max(new_first, 0) >> 5);
+    // keys past draft_first (this step's later draft tokens) are hidden from some
+    // rows: they never sit in a whole tile (the per-row path handles them)
+    const int draft_first = sp - t0;
+    const int nt = min(n_tok >> 5, max(min(new_first, draft_first + 1), 0) >> 5);
     const int nj = kw < nt ? (nt - kw + KS - 1) / KS : 0;
 
     // B operand of S^T = K q^T for row block rb: q[rb*16 + l16][dims 32s + 8q .. +7],
@@ -288,10 +295,20 @@ void attn_split_mfma_kernel(const int32_t *__restrict__ seq_pos, int32_t batch, 
 
     // One 32-key tile: S^T and the online softmax of every row block, then
     // O^T += V^T P^T with each V operand serving every row block.
-    auto compute = [&](Tile &t, int tt) {
+    // On the tiles of the per-row path (kTail), this step's later draft keys
+    // (local keys past draft_first) are hidden from some rows, which meet them
+    // in the P V product with weight 0: exact for finite value rows.  If one of
+    // their value rows holds an inf or NaN, they are left out of the product
+    // and added on the vector ALU instead: for each such key k (wave-uniform) a
+    // lane takes its row's rounded weight of k from the lane that holds it and,
+    // if that weight is not 0, adds weight * v_k to its 32 dims, which it
+    // gathers from the tile's V operand of the four lanes that hold them.
+    auto compute = [&](Tile &t, int tt, auto tail) {
+        constexpr bool kTail = decltype(tail)::value;
         const int tb = tt * 32;
         if constexpr (RB > 1) asm volatile("" ::: "memory");  // keep the q reads inside the loop
         u32x4_t pop[RB];
+        float pvs[RB][8];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             // S^T for the two 16-key blocks: lane holds keys tb + 16*kblk + 4q + v of its row
@@ -332,6 +349,29 @@ void attn_split_mfma_kernel(const int32_t *__restrict__ seq_pos, int32_t batch, 
             // B operand of O^T: P^T, slot u <-> key pv_key(q, u) = s2 index u
 #pragma unroll
             for (int j = 0; j < 4; ++j) pop[rb][j] = pack16<F16>(pv[2 * j], pv[2 * j + 1]);
+            if constexpr (kTail) {
+#pragma unroll
+                for (int u = 0; u < 8; ++u) pvs[rb][u] = pv[u];
+            }
+        }
+        bool split = false;  // kTail: a later draft key's value row is not finite
+        if constexpr (kTail) {
+            bool bad = false;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (tb + pv_key(q, u) > draft_first) {
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) bad |= nonfinite2<F16>(t.v[u][w]);
+                }
+            split = __any(bad);
+        }
+        u32x4_t tv[8];  // the V operand, without the later draft keys when split
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            tv[u] = t.v[u];
+            if constexpr (kTail) {
+                if (split && tb + pv_key(q, u) > draft_first) tv[u] = u32x4_t{0u, 0u, 0u, 0u};
+            }
         }
 #pragma unroll
         for (int o = 0; o < 8; ++o) {
@@ -339,9 +379,49 @@ void attn_split_mfma_kernel(const int32_t *__restrict__ seq_pos, int32_t batch, 
             const uint32_t sel = (o & 1) ? 0x07060302u : 0x05040100u;
             u32x4_t vop;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) vop[j] = __builtin_amdgcn_perm(t.v[2 * j + 1][word], t.v[2 * j][word], sel);
+            for (int j = 0; j < 4; ++j) vop[j] = __builtin_amdgcn_perm(tv[2 * j + 1][word], tv[2 * j][word], sel);
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) oacc[rb][o] = mfma16<F16>(vop, pop[rb], oacc[rb][o]);
+        }
+        if constexpr (kTail) {
+            const int k_hi = split ? min(tb + 31, last) : -1;
+            for (int k = max(tb, draft_first + 1); k <= k_hi; ++k) {
+                const int kk = k - tb, qk = (kk & 15) >> 2;
+                const int uk = 4 * (kk >> 4) + (kk & 3);  // slot of key k in the lanes with q == qk
+                // v_k dims 8i .. 8i + 7 sit in slot uk of lane (i, qk); this lane
+                // wants dims 32q .. 32q + 31, from lanes (4q + v, qk), v = 0..3
+                u32x4_t vk;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    uint32_t x = 0;
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) x = u == uk ? t.v[u][w] : x;
+                    vk[w] = x;
+                }
+                u32x4_t vr[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) vr[v][w] = (uint32_t)__shfl((int)vk[w], 4 * q + v + 16 * qk);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    float pk = 0.f;
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) pk = u == uk ? pvs[rb][u] : pk;
+                    pk = __shfl(pk, l16 + 16 * qk);
+                    if (pk != 0.f) {
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+#pragma unroll
+                            for (int w = 0; w < 4; ++w) {
+                                float lo, hi;
+                                unpack2<F16>(vr[v][w], lo, hi);
+                                oacc[rb][2 * w][v] = fmaf(pk, lo, oacc[rb][2 * w][v]);
+                                oacc[rb][2 * w + 1][v] = fmaf(pk, hi, oacc[rb][2 * w + 1][v]);
+                            }
+                    }
+                }
+            }
         }
     };
 
@@ -355,16 +435,16 @@ void attn_split_mfma_kernel(const int32_t *__restrict__ seq_pos, int32_t batch, 
             int j = 0;
             for (; j + 2 <= nj; j += 2) {
                 load_full(tb_, cv, (kw + KS * (j + 1)) * 32, l16, q);
-                compute(ta, kw + KS * j);
+                compute(ta, kw + KS * j, std::false_type{});
                 if (j + 2 < nj) load_full(ta, cv, (kw + KS * (j + 2)) * 32, l16, q);
-                compute(tb_, kw + KS * (j + 1));
+                compute(tb_, kw + KS * (j + 1), std::false_type{});
             }
-            if (j < nj) compute(ta, kw + KS * j);
+            if (j < nj) compute(ta, kw + KS * j, std::false_type{});
         }
     } else {
         for (int j = 0; j < nj; ++j) {
             if (j > 0) load_full(ta, cv, (kw + KS * j) * 32, l16, q);
-            compute(ta, kw + KS * j);
+            compute(ta, kw + KS * j, std::false_type{});
         }
     }
 
@@ -388,7 +468,7 @@ void attn_split_mfma_kernel(const int32_t *__restrict__ seq_pos, int32_t batch, 
         if (i % KS != kw) continue;
         Tile tt_;
         load_rows<F16>(tt_, cv, i * 32, last, l16, q, rs);
-        compute(tt_, i);
+        compute(tt_, i, std::true_type{});
     }
 
     // ---- merge of the four waves, then one partial per chunk --------------------

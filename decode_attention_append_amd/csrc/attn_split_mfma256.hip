@@ -31,6 +31,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace da {
 namespace {
 
@@ -198,7 +200,10 @@ void attn_split_mfma256_kernel(const int32_t *__restrict__ seq_pos, int32_t batc
     // tiles kw, kw + KS, ... of them.
     const int new_first = p.k_new ? sp - t0 : n_tok;
     const int n_all = (n_tok + 15) >> 4;
-    const int nt = min(n_tok >> 4, max(new_first, 0) >> 4);
+    // keys past draft_first (this step's later draft tokens) are hidden from some
+    // rows: they never sit in a whole tile (the per-row path handles them)
+    const int draft_first = sp - t0;
+    const int nt = min(n_tok >> 4, max(min(new_first, draft_first + 1), 0) >> 4);
     const int nj = kw < nt ? (nt - kw + KS - 1) / KS : 0;
 
     // B operand of S^T = K q^T: q[row][32s + 8q .. +7] for s = 0..7.  The 16 rows
@@ -254,8 +259,17 @@ void attn_split_mfma256_kernel(const int32_t *__restrict__ seq_pos, int32_t batc
 #pragma unroll
         for (int o = 0; o < 8; ++o) oacc[hh][o] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // One 16-key tile: S^T, online softmax, O^T += V^T P^T.
-    auto compute = [&](Tile16 &t, int tt) {
+    // One 16-key tile: S^T, online softmax, O^T += V^T P^T.  On the tiles of
+    // the per-row path (kTail), this step's later draft keys (local keys past
+    // draft_first) are hidden from some rows, which meet them in the P V
+    // product with weight 0: exact for finite value rows.  If one of their value
+    // rows holds an inf or NaN, they are left out of the product and added on
+    // the vector ALU instead: for each such key k (wave-uniform) a lane takes its
+    // row's rounded weight of k from the lane that holds it and, if that weight
+    // is not 0, adds weight * v_k to its 64 dims, gathered from the tile's V
+    // operand of the four lanes that hold them.
+    auto compute = [&](Tile16 &t, int tt, auto tail) {
+        constexpr bool kTail = decltype(tail)::value;
         const int tb = tt * 16;
         asm volatile("" ::: "memory");  // keep the q reads inside the loop (no hoisting into registers)
         f32x4_t st = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -288,16 +302,78 @@ void attn_split_mfma256_kernel(const int32_t *__restrict__ seq_pos, int32_t batc
         m_run = m_new;
 
         const u32x2_t pop = {pack2<F16>(pw[0], pw[1]), pack2<F16>(pw[2], pw[3])};
+        bool split = false;  // kTail: a later draft key's value row is not finite
+        if constexpr (kTail) {
+            bool bad = false;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (tb + 4 * q + u > draft_first) {
+#pragma unroll
+                        for (int w = 0; w < 4; ++w) bad |= nonfinite2<F16>(t.v[hh][u][w]);
+                    }
+            split = __any(bad);
+        }
+        u32x4_t tv[2][4];  // the V operand, without the later draft keys when split
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                tv[hh][u] = t.v[hh][u];
+                if constexpr (kTail) {
+                    if (split && tb + 4 * q + u > draft_first) tv[hh][u] = u32x4_t{0u, 0u, 0u, 0u};
+                }
+            }
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
             for (int o = 0; o < 8; ++o) {
                 const int w = o >> 1;
                 const uint32_t sel = (o & 1) ? 0x07060302u : 0x05040100u;
-                const u32x2_t vop = {__builtin_amdgcn_perm(t.v[hh][1][w], t.v[hh][0][w], sel),
-                                     __builtin_amdgcn_perm(t.v[hh][3][w], t.v[hh][2][w], sel)};
+                const u32x2_t vop = {__builtin_amdgcn_perm(tv[hh][1][w], tv[hh][0][w], sel),
+                                     __builtin_amdgcn_perm(tv[hh][3][w], tv[hh][2][w], sel)};
                 oacc[hh][o] = mfma_k16<F16>(vop, pop, oacc[hh][o]);
             }
+        if constexpr (kTail) {
+            const int k_hi = split ? min(tb + 15, last) : -1;
+            for (int k = max(tb, draft_first + 1); k <= k_hi; ++k) {
+                const int qk = (k - tb) >> 2, uk = (k - tb) & 3;  // lanes with q == qk hold key k in slot uk
+                float pk = 0.f;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) pk = v == uk ? pw[v] : pk;
+                pk = __shfl(pk, l16 + 16 * qk);
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    // v_k dims 128 hh + 8i .. + 7 sit in slot uk of lane (i, qk);
+                    // this lane wants dims 128 hh + 32q .. + 31, from lanes (4q + v, qk)
+                    u32x4_t vk;
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        uint32_t x = 0;
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) x = u == uk ? t.v[hh][u][w] : x;
+                        vk[w] = x;
+                    }
+                    u32x4_t vr[4];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+#pragma unroll
+                        for (int w = 0; w < 4; ++w) vr[v][w] = (uint32_t)__shfl((int)vk[w], 4 * q + v + 16 * qk);
+                    if (pk != 0.f) {
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+#pragma unroll
+                            for (int w = 0; w < 4; ++w) {
+                                float lo, hi;
+                                unpack2<F16>(vr[v][w], lo, hi);
+                                oacc[hh][2 * w][v] = fmaf(pk, lo, oacc[hh][2 * w][v]);
+                                oacc[hh][2 * w + 1][v] = fmaf(pk, hi, oacc[hh][2 * w + 1][v]);
+                            }
+                    }
+                }
+            }
+        }
     };
 
     // full tiles through two buffers used in turn
@@ -305,11 +381,11 @@ void attn_split_mfma256_kernel(const int32_t *__restrict__ seq_pos, int32_t batc
         int j = 0;
         for (; j + 2 <= nj; j += 2) {
             load_full16(tb_, cv, (kw + KS * (j + 1)) * 16, l16, q);
-            compute(ta, kw + KS * j);
+            compute(ta, kw + KS * j, std::false_type{});
             if (j + 2 < nj) load_full16(ta, cv, (kw + KS * (j + 2)) * 16, l16, q);
-            compute(tb_, kw + KS * (j + 1));
+            compute(tb_, kw + KS * (j + 1), std::false_type{});
         }
-        if (j < nj) compute(ta, kw + KS * j);
+        if (j < nj) compute(ta, kw + KS * j, std::false_type{});
     }
 
     // the rest row by row (the chunk's last partial tile, this step's new rows),
@@ -332,7 +408,7 @@ void attn_split_mfma256_kernel(const int32_t *__restrict__ seq_pos, int32_t batc
         if (i % KS != kw) continue;
         Tile16 tt_;
         load_rows16<F16>(tt_, cv, i * 16, last, l16, q, rs);
-        compute(tt_, i);
+        compute(tt_, i, std::true_type{});
     }
 
     // ---- merge of the KS waves of a row group, then one partial per chunk ------

@@ -318,6 +318,14 @@ __device__ __forceinline__ void unpack2(uint32_t x, float &lo, float &hi) {
     }
 }
 
+// Whether either 16-bit element of a packed pair is inf or NaN (all exponent
+// bits set).
+template <bool F16>
+__device__ __forceinline__ bool nonfinite2(uint32_t x) {
+    constexpr uint32_t e = F16 ? 0x7c00u : 0x7f80u;
+    return (x & e) == e || ((x >> 16) & e) == e;
+}
+
 // fp32 -> 16-bit element, round to nearest even.
 template <bool F16>
 __device__ __forceinline__ uint16_t round16(float x) {

@@ -10,6 +10,7 @@ import pytest
 import torch
 
 import decode_attention_append_amd as da
+import oracle
 from decode_attention_append_amd.workloads import WORKLOADS, make_layer
 from tests import gpu_util as gu
 from tests.oracle_pins import bits
@@ -173,6 +174,39 @@ def test_later_draft_token_hidden_from_earlier_rows_valu(path):
     out = gu.run_step(p, inp, path=path)
     assert torch.isfinite(out[:, 0].float()).all()
     assert torch.isnan(out[:, 1].float()).all()
+
+
+@pytest.mark.parametrize("path", gu.PATHS)
+@pytest.mark.parametrize("bad", ["nan", "inf"])
+@pytest.mark.parametrize("hidden_from", [1, "last"])
+@pytest.mark.parametrize("B,q_len,Hq,Hkv,D,S,seq_pos", [
+    (2, 4, 32, 4, 128, 512, [30, 300]),   # 32 rows: two row blocks; new rows straddle a 32-key tile
+    (2, 4, 16, 4, 128, 512, [61, 200]),   # 16 rows: one row block
+    (1, 2, 32, 8, 128, 256, [100]),       # 8 rows
+    (2, 4, 16, 2, 256, 512, [14, 300]),   # head_dim 256, 32 rows (two row groups); straddles a 16-key tile
+    (2, 2, 16, 2, 256, 512, [14, 300]),   # head_dim 256, 16 rows
+])
+def test_later_draft_token_hidden_from_earlier_rows_mfma(B, q_len, Hq, Hkv, D, S, seq_pos, hidden_from, bad, path):
+    """A non-finite value row of a later draft token reaches only the rows that see
+    it: every earlier token's rows stay finite and equal the oracle's (which
+    excludes the hidden key), on the matrix-core kernels."""
+    i_bad = 1 if hidden_from == 1 else q_len - 1
+    _say("draft", B, q_len, Hq, Hkv, D, S, seq_pos, i_bad, bad, path)
+    inp = gu.make_case(B, q_len, Hq, Hkv, S, seq_pos, seed=31 + i_bad, head_dim=D)
+    p = da.problem_for(inp["q"], inp["k_cache"])
+    assert da.plan_attention(p)["variant"] == "mfma"
+    inp["v_new"][:, i_bad] = float(bad)
+    dt = gu.odt(inp["q"].dtype)
+    sp = inp["seq_pos"].cpu().numpy()
+    k_ref, v_ref = oracle.kv_append(bits(inp["k_cache"]), bits(inp["v_cache"]), bits(inp["k_new"]),
+                                    bits(inp["v_new"]), sp)
+    ref = oracle.gqa_decode(bits(inp["q"]), k_ref, v_ref, sp, dt)
+    out = gu.run_step(p, inp, path=path)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(inp["k_cache"]), k_ref) and np.array_equal(bits(inp["v_cache"]), v_ref)
+    assert torch.isfinite(out[:, :i_bad].float()).all()
+    gu.compare_out(out[:, :i_bad], ref[:, :i_bad], "tokens before the bad draft row")
+    assert not torch.isfinite(out[:, i_bad:].float()).any()
 
 
 def test_last_slot_and_exact_chunk_boundaries():
