@@ -14,17 +14,21 @@ One whole step (every layer) is captured into a HIP graph once, after the
 warm-up steps, and the timed steps are its replays: each replay runs every
 layer's kernels on the same inputs, exactly as an eager step does (the graph
 tests check replays against eager steps bit for bit), without the host launch
-gaps between layers.  --eager times eagerly launched steps instead.
+gaps between layers.  --eager times eagerly launched steps instead.  Steps that
+touch less than 1 GiB start cold: a 2 GiB buffer is read before each of them,
+outside the timing.
 
 Prints ONE JSON line: KV GB/s (algorithmic bytes per step / step time), ms per
-step, the attention kernel's roofline fraction against the 8 TB/s HBM peak
-(its average duration measured with HIP events on the launch stream around
-every attention launch of K eagerly launched steps, right after the timed
-replays; with --eager, of the timed steps themselves), and the fp64 CPU
-oracle's rate on a bounded sample of the same workload.
+step, the attention kernel's roofline fraction against the 8 TB/s HBM peak, the
+fp64 CPU oracle's rate on a bounded sample of the same workload, and under
+"configs" the same measurements for every other workload of the suite (the
+512-context layer, the MHA 4k layers, GQA-8 long context, the 4-token verify,
+the head_dim-256 gated layers).  Each record also carries the attention
+kernel's mean duration over cold launches, read from the GPU's own kernel
+timestamps (torch's profiler), and its fraction of the HBM peak.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--path step|separate]
-                    [--eager] [--no-cpu-baseline]
+                    [--eager] [--configs all|none] [--no-cpu-baseline] [--no-kernel-profiler]
 """
 import argparse
 import json
@@ -55,11 +59,17 @@ def parse():
     ap.add_argument("--eager", action="store_true",
                     help="time eagerly launched steps instead of replays of the step captured into a HIP "
                          "graph")
+    ap.add_argument("--configs", choices=["all", "none"], default=None,
+                    help="also measure every other workload of the suite (default: all for the default "
+                         "workload, none when --workload is given)")
+    ap.add_argument("--config-steps", type=int, default=20, help="timed steps per extra workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-profiler", action="store_true",
+                    help="skip the kernel durations from torch's profiler (e.g. under rocprofv3)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle sample")
     ap.add_argument("--flush", choices=["auto", "on", "off"], default="auto",
-                    help="read a 2 GiB buffer before every timed step (outside the timing) so the "
+                    help="read a 2 GiB buffer before every timed step (outside the timed span) so the "
                          "step starts with cold caches; auto = on when one step touches less than "
                          "1 GiB, which the 256 MB Infinity Cache could otherwise serve")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -99,14 +109,25 @@ def counters_for(kernel_tag, workload):
     return rec.get("hbm_bytes_per_launch")
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, layers_host_fn, n_layers, budget_s, freqs=None, block_table=None):
     """The oracle (append + attention, fp64, OpenMP; with the rotary embedding when a
     table is given, the output gate when the workload has one) on whole layers of the
     workload until about budget_s of CPU time is spent; returns the record for the JSON
     line."""
-    import numpy as np
     import oracle
     dt = oracle.FP16 if w.dtype == "fp16" else oracle.BF16
+    import numpy as np
     done_bytes, spent, n = 0, 0.0, 0
     for layer in range(n_layers):
         q, kc, vc, kn, vn, sp, gate = layers_host_fn(layer)
@@ -130,9 +151,203 @@ def cpu_baseline(w, layers_host_fn, n_layers, budget_s, freqs=None, block_table=
         if spent >= budget_s:
             break
     return {"value": done_bytes / spent / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{n} of {w.layers} layers of {w.name}, every sequence and head, "
                       f"append + attention in fp64 ({spent:.1f} s)"}
+
+
+class Bench:
+    """One workload on the GPU: its layers, problems, workspace and step functions."""
+
+    def __init__(self, w, args, dev, path, theta=0.0, paged=False, chunk=0, items=0):
+        import torch
+        import decode_attention_append_amd as da
+        from decode_attention_append_amd.workloads import make_layer, rope_freqs
+        self.w, self.dev, self.path, self.paged = w, dev, path, paged
+        self.layers = [make_layer(w, l, dev) for l in range(w.layers)]
+        self.seq_pos = self.layers[0]["seq_pos"].cpu().numpy()
+        self.theta = theta if theta > 0 else w.rope_theta
+        self.rope_dim = w.rope_dim or w.head_dim
+        self.freqs = rope_freqs(self.rope_dim, self.theta, dev) if self.theta > 0 else None
+        self.block_table, n_pages = None, 0
+        if paged:
+            # pages of every (sequence, KV head) cache, shuffled into one pool per layer and cache
+            pps = w.max_seq // 16
+            n_pages = w.batch * pps
+            perm = torch.randperm(n_pages, generator=torch.Generator().manual_seed(7))
+            self.block_table = perm.view(w.batch, pps).to(torch.int32).to(dev)
+            inv = torch.empty_like(perm)
+            inv[perm] = torch.arange(n_pages)
+            for L in self.layers:
+                for key in ("k_cache", "v_cache"):
+                    c = L[key].view(w.batch, w.n_kv_heads, pps, 16, w.head_dim).transpose(1, 2)
+                    pages = c.reshape(n_pages, w.n_kv_heads, 16, w.head_dim)  # page b * pps + i
+                    L[key] = pages[inv.to(dev)].contiguous()  # pool page perm[j] holds page j
+                    del c, pages
+            torch.cuda.synchronize()
+        # one problem per layer: a gated problem carries its layer's gate tensor
+        self.probs = [da.problem(w.batch, w.q_len, w.n_q_heads, w.n_kv_heads, w.head_dim, w.max_seq, w.dtype,
+                                 chunk_tokens=chunk, work_items=items, rope_freqs=self.freqs,
+                                 block_table=self.block_table, n_pages=n_pages,
+                                 rope_dim=self.rope_dim if self.freqs is not None else 0,
+                                 out_gate=L.get("out_gate"))
+                      for L in self.layers]
+        self.plan = da.plan_attention(self.probs[0])
+        self.ws = da.new_workspace(self.probs[0])
+        self.outs = [torch.empty_like(L["q"]) for L in self.layers]
+        self.stream = torch.cuda.current_stream()
+        self.launch_stream = [self.stream]  # None while capturing: the binding then uses torch's stream
+        self.da = da
+        torch.cuda.synchronize()
+
+    def step(self, events=None):
+        da, s = self.da, self.launch_stream[0]
+        for l, L in enumerate(self.layers):
+            p = self.probs[l]
+            if self.path == "separate":
+                da.kv_append(p, L["k_cache"], L["v_cache"], L["k_new"], L["v_new"], L["seq_pos"], s)
+                if events is not None:
+                    events[l][0].record(self.stream)
+                da.gqa_decode_attn(p, L["q"], L["k_cache"], L["v_cache"], L["seq_pos"], self.ws, s)
+                if events is not None:
+                    events[l][1].record(self.stream)
+                da.gqa_decode_attn_combine(p, self.ws, L["seq_pos"], self.outs[l], s)
+            else:
+                if events is not None:
+                    events[l][0].record(self.stream)
+                da.decode_step(p, L["q"], L["k_cache"], L["v_cache"], L["k_new"], L["v_new"], L["seq_pos"],
+                               self.ws, self.outs[l], s)
+                if events is not None:
+                    events[l][1].record(self.stream)
+
+    def kernel_name(self):
+        w = self.w
+        kernel = "attn_split_" + self.plan["variant"] + ("256" if w.head_dim == 256 else "")
+        if self.paged:
+            kernel += "_paged"
+        if self.freqs is not None:
+            kernel += "_rope"
+        if w.gated:
+            kernel += "_gate"
+        return kernel
+
+    def bytes(self):
+        """(algorithmic bytes per step, per attention launch)."""
+        w = self.w
+        kv_bytes, alg_bytes = algorithmic_bytes(w, self.seq_pos)
+        # The attention launch reads the K+V of the visible context (512 bytes per
+        # visible key per KV head at head_dim 128) and q; in the one-launch step it
+        # also writes the new rows into the cache and, with the merge fused, the
+        # output (reading the gate).  There the new rows are read once, from k_new,
+        # as part of the visible context.
+        q_bytes = w.batch * w.q_len * w.n_q_heads * w.head_dim * 2
+        attn_bytes = kv_bytes + q_bytes
+        if self.path == "step":
+            attn_bytes += 2 * w.batch * w.q_len * w.n_kv_heads * w.head_dim * 2
+            if self.plan["fused_combine"]:
+                attn_bytes += q_bytes * (2 if w.gated else 1)
+        return alg_bytes * w.layers, attn_bytes
+
+    def measure(self, steps, warmup, eager, flush_mode, kernel_profiler):
+        """Timed steps (graph replays unless eager), HIP events around every attention
+        launch of an eager pass, and optionally the attention kernels' durations from
+        the profiler over cold launches."""
+        import numpy as np
+        import torch
+        w = self.w
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        step_bytes, attn_bytes = self.bytes()
+        flush = flush_mode == "on" or (flush_mode == "auto" and step_bytes < (1 << 30))
+        flush_buf = torch.ones(1 << 30, dtype=torch.bfloat16, device=self.dev) if flush else None
+        ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+               for _ in range(w.layers)] for _ in range(steps)]
+        # one event pair per step (back to back when there is no flush), so the
+        # spread of the step time is reported beside its mean
+        marks = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+                 for _ in range(steps)]
+        torch.cuda.synchronize()
+        step_ms = []
+
+        def timed(run):
+            for k in range(steps):
+                if flush:
+                    flush_buf.sum(dtype=torch.float32)  # outside the timed span of the step
+                marks[k][0].record(self.stream)
+                run(k)
+                marks[k][1].record(self.stream)
+            torch.cuda.synchronize()
+            step_ms[:] = [a.elapsed_time(b) for a, b in marks]
+            return sum(step_ms)
+
+        if not eager:
+            graph = torch.cuda.CUDAGraph()
+            self.launch_stream[0] = None
+            with torch.cuda.graph(graph):
+                self.step()
+            self.launch_stream[0] = self.stream
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            ms_total = timed(lambda k: graph.replay())
+            replay_ms = list(step_ms)
+            timed(lambda k: self.step(ev[k]))  # eager pass for the kernel's own duration
+            step_ms[:] = replay_ms
+            del graph
+        else:
+            ms_total = timed(lambda k: self.step(ev[k]))
+        attn_ms = [e0.elapsed_time(e1) for evk in ev for (e0, e1) in evk]
+
+        kernel_us = None
+        if kernel_profiler:
+            from torch.profiler import ProfilerActivity, profile
+            n_prof = max(5, min(steps, 20))
+            with profile(activities=[ProfilerActivity.CUDA]) as prof:
+                for _ in range(n_prof):
+                    if flush:
+                        flush_buf.sum(dtype=torch.float32)
+                    self.step()
+                torch.cuda.synchronize()
+            kernel_us = {}
+            for e in prof.events():
+                for tag in ("attn_split", "attn_combine", "kv_append"):
+                    if tag in e.name:
+                        kernel_us.setdefault(tag, []).append(float(e.device_time))
+        del flush_buf
+        return {"ms_total": ms_total, "step_ms": step_ms, "attn_ms": attn_ms, "flush": flush,
+                "step_bytes": step_bytes, "attn_bytes": attn_bytes, "kernel_us": kernel_us}
+
+
+def config_record(b, m, steps, eager):
+    """The JSON record of one workload's measurements (see the module docstring)."""
+    import numpy as np
+    w, plan = b.w, b.plan
+    ms = m["ms_total"] / steps
+    rec = {
+        "us_per_step": round(ms * 1e3, 2),
+        "us_per_step_p10_p50_p90": [round(float(np.percentile(m["step_ms"], q)) * 1e3, 2) for q in (10, 50, 90)],
+        "gbs": round(m["step_bytes"] / (ms * 1e-3) / 1e9, 2),
+        "hbm_frac": round(m["step_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "bytes_per_step": m["step_bytes"],
+        "kernel": b.kernel_name(),
+        "kernel_bytes_per_launch": m["attn_bytes"],
+        "variant": plan["variant"], "path": b.path,
+        "fused_merge": bool(plan["fused_combine"]) and b.path == "step",
+        "launches_per_layer": (3 if b.path == "separate" else (1 if plan["fused_combine"] else 2)),
+        "layers": w.layers, "graph": not eager, "cold_cache_flush": m["flush"],
+        "context": int(b.seq_pos.max()) + w.q_len,
+    }
+    ku = m["kernel_us"]
+    if ku and ku.get("attn_split"):
+        us = float(np.mean(ku["attn_split"]))
+        rec["kernel_us_profiler"] = round(us, 2)
+        rec["kernel_gbs"] = round(m["attn_bytes"] / (us * 1e-6) / 1e9, 2)
+        rec["kernel_frac"] = round(m["attn_bytes"] / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+        rec["kernel_launches_profiled"] = len(ku["attn_split"])
+        if ku.get("attn_combine"):
+            rec["combine_us_profiler"] = round(float(np.mean(ku["attn_combine"])), 2)
+    return rec
 
 
 def main():
@@ -146,10 +361,10 @@ def main():
     import numpy as np
     import torch
 
-    import decode_attention_append_amd as da
-    from decode_attention_append_amd.workloads import BENCH_WORKLOAD, WORKLOADS, make_layer, rope_freqs
+    from decode_attention_append_amd.workloads import BENCH_WORKLOAD, WORKLOADS
 
     w = WORKLOADS[args.workload or BENCH_WORKLOAD]
+    configs = args.configs or ("none" if args.workload else "all")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.calibrate_copy:
@@ -162,134 +377,23 @@ def main():
     print(f"[bench] workload {w.name}: building {w.layers} layers on {torch.cuda.get_device_name(0)}",
           file=sys.stderr, flush=True)
 
-    layers = [make_layer(w, l, dev) for l in range(w.layers)]
-    seq_pos = layers[0]["seq_pos"].cpu().numpy()
-    theta = args.rope if args.rope > 0 else w.rope_theta
-    rope_dim = w.rope_dim or w.head_dim
-    freqs = rope_freqs(rope_dim, theta, dev) if theta > 0 else None
-    block_table, n_pages = None, 0
-    if args.paged:
-        # pages of every (sequence, KV head) cache, shuffled into one pool per layer and cache
-        pps = w.max_seq // 16
-        n_pages = w.batch * pps
-        perm = torch.randperm(n_pages, generator=torch.Generator().manual_seed(7))
-        block_table = perm.view(w.batch, pps).to(torch.int32).to(dev)
-        inv = torch.empty_like(perm)
-        inv[perm] = torch.arange(n_pages)
-        for L in layers:
-            for key in ("k_cache", "v_cache"):
-                c = L[key].view(w.batch, w.n_kv_heads, pps, 16, w.head_dim).transpose(1, 2)
-                pages = c.reshape(n_pages, w.n_kv_heads, 16, w.head_dim)  # page b * pps + i
-                L[key] = pages[inv.to(dev)].contiguous()  # pool page perm[j] holds page j
-                del c, pages
-        torch.cuda.synchronize()
-    # one problem per layer: a gated problem carries its layer's gate tensor
-    probs = [da.problem(w.batch, w.q_len, w.n_q_heads, w.n_kv_heads, w.head_dim, w.max_seq, w.dtype,
-                        chunk_tokens=args.chunk, work_items=args.items, rope_freqs=freqs, block_table=block_table, n_pages=n_pages,
-                        rope_dim=rope_dim if freqs is not None else 0, out_gate=L.get("out_gate"))
-             for L in layers]
-    p = probs[0]
-    plan = da.plan_attention(p)
-    ws = da.new_workspace(p)
-    outs = [torch.empty_like(L["q"]) for L in layers]
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream()
-    launch_stream = [stream]  # None while a graph is being captured: the binding then uses torch's stream
-
-    def step_separate(events=None):
-        for l, L in enumerate(layers):
-            p = probs[l]
-            da.kv_append(p, L["k_cache"], L["v_cache"], L["k_new"], L["v_new"], L["seq_pos"], launch_stream[0])
-            if events is not None:
-                events[l][0].record(stream)
-            da.gqa_decode_attn(p, L["q"], L["k_cache"], L["v_cache"], L["seq_pos"], ws, launch_stream[0])
-            if events is not None:
-                events[l][1].record(stream)
-            da.gqa_decode_attn_combine(p, ws, L["seq_pos"], outs[l], launch_stream[0])
-
-    def step_fused(events=None):
-        for l, L in enumerate(layers):
-            if events is not None:
-                events[l][0].record(stream)
-            da.decode_step(probs[l], L["q"], L["k_cache"], L["v_cache"], L["k_new"], L["v_new"], L["seq_pos"], ws,
-                           outs[l], launch_stream[0])
-            if events is not None:
-                events[l][1].record(stream)
-
-    step = step_fused if args.path == "step" else step_separate
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    kv_bytes, alg_bytes = algorithmic_bytes(w, seq_pos)
-    step_bytes = alg_bytes * w.layers
-    flush = args.flush == "on" or (args.flush == "auto" and step_bytes < (1 << 30))
-    flush_buf = torch.ones(1 << 30, dtype=torch.bfloat16, device=dev) if flush else None
-
-    # timed region: K steps, HIP events around every attention launch on the launch stream
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-           for _ in range(w.layers)] for _ in range(args.steps)]
-    # one event pair per step (back to back when there is no flush), so the
-    # spread of the step time is reported beside its mean
-    marks = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-             for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    step_ms = []
-
-    def timed(run):
-        for k in range(args.steps):
-            if flush:
-                flush_buf.sum(dtype=torch.float32)  # outside the timed span of the step
-            marks[k][0].record(stream)
-            run(k)
-            marks[k][1].record(stream)
-        torch.cuda.synchronize()
-        step_ms[:] = [a.elapsed_time(b) for a, b in marks]
-        return sum(step_ms)
-
-    if not args.eager:
-        graph = torch.cuda.CUDAGraph()
-        launch_stream[0] = None
-        with torch.cuda.graph(graph):
-            step()
-        launch_stream[0] = stream
-        torch.cuda.synchronize()
-        graph.replay()
-        torch.cuda.synchronize()
-        ms_total = timed(lambda k: graph.replay())
-        replay_ms = list(step_ms)
-        timed(lambda k: step(ev[k]))  # eager pass for the kernel's own duration
-        step_ms[:] = replay_ms
-    else:
-        ms_total = timed(lambda k: step(ev[k]))
-    attn_ms = [e0.elapsed_time(e1) for evk in ev for (e0, e1) in evk]
-
-    ms_per_step = ms_total / args.steps
+    b = Bench(w, args, dev, args.path, args.rope, args.paged, args.chunk, args.items)
+    m = b.measure(args.steps, args.warmup, args.eager, args.flush, not args.no_kernel_profiler)
+    ms_per_step = m["ms_total"] / args.steps
+    step_bytes, attn_bytes = m["step_bytes"], m["attn_bytes"]
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
 
-    # dominant kernel: the split-context attention.  Its algorithmic bytes per launch are the
-    # K+V of the visible context (512 bytes per visible key per KV head) plus q; in the
-    # one-launch step also the new rows' cache writes and, with the merge fused, the output
-    # (and the gate).  (There the new rows are read once, from k_new, as part of the visible
-    # context.)
+    # dominant kernel: the split-context attention.  Its duration from the HIP events
+    # around every launch, bounded (graph replay) by the replayed step time per layer,
+    # which the events can only exceed by their own overhead.
+    attn_ms = m["attn_ms"]
     attn_avg_ms = float(np.mean(attn_ms))
-    q_bytes = w.batch * w.q_len * w.n_q_heads * w.head_dim * 2
-    attn_bytes = kv_bytes + q_bytes
-    kernel = "attn_split_" + plan["variant"] + ("256" if w.head_dim == 256 else "")
-    if args.paged:
-        kernel += "_paged"
-    if freqs is not None:
-        kernel += "_rope"
-    if w.gated:
-        kernel += "_gate"
+    if not args.eager and args.path == "step" and b.plan["fused_combine"]:
+        attn_avg_ms = min(attn_avg_ms, ms_per_step / w.layers)
+    kernel = b.kernel_name()
     kernel_tag = kernel
     if args.path == "step":
-        attn_bytes += 2 * w.batch * w.q_len * w.n_kv_heads * w.head_dim * 2
-        if plan["fused_combine"]:
-            attn_bytes += q_bytes * (2 if w.gated else 1)
-        kernel_tag += "_step" if plan["fused_combine"] else "_step+attn_combine"
+        kernel_tag += "_step" if b.plan["fused_combine"] else "_step+attn_combine"
     attn_gbs = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
     traffic = counters_for(kernel_tag, w.name) if "+" not in kernel_tag else None
 
@@ -302,7 +406,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
         "us_per_step": round(ms_per_step * 1e3, 2),
-        "us_per_step_p10_p50_p90": [round(float(np.percentile(step_ms, q)) * 1e3, 2) for q in (10, 50, 90)],
+        "us_per_step_p10_p50_p90": [round(float(np.percentile(m["step_ms"], q)) * 1e3, 2) for q in (10, 50, 90)],
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -310,30 +414,35 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "q_len": w.q_len, "n_q_heads": w.n_q_heads,
-                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "context": int(seq_pos.max()) + w.q_len,
-                   "max_seq": w.max_seq, "layers": w.layers, "chunk_tokens": plan["chunk_tokens"],
-                   "target_items": plan["target_items"],
-                   "variant": plan["variant"], "path": args.path, "graph": not args.eager,
-                   "rope_theta": theta if freqs is not None else None,
-                   "rope_dim": rope_dim if freqs is not None else None, "output_gate": w.gated,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
+                   "context": int(b.seq_pos.max()) + w.q_len,
+                   "max_seq": w.max_seq, "layers": w.layers, "chunk_tokens": b.plan["chunk_tokens"],
+                   "target_items": b.plan["target_items"],
+                   "variant": b.plan["variant"], "path": args.path, "graph": not args.eager,
+                   "rope_theta": b.theta if b.freqs is not None else None,
+                   "rope_dim": b.rope_dim if b.freqs is not None else None, "output_gate": w.gated,
                    "paged": args.paged,
-                   "fused_merge": bool(plan["fused_combine"]) and args.path == "step",
+                   "fused_merge": bool(b.plan["fused_combine"]) and args.path == "step",
                    "bytes_per_step": step_bytes,
-                   "cold_cache_flush": flush},
+                   "cold_cache_flush": m["flush"]},
         "roofline": {"bound": "hbm", "kernel": kernel_tag, "achieved": round(attn_gbs, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
                      "avg_launch_us": round(attn_avg_ms * 1e3, 3),
+                     "avg_launch_us_events": round(float(np.mean(attn_ms)) * 1e3, 3),
                      "launch_us_p10_p50_p90": [round(float(np.percentile(attn_ms, q)) * 1e3, 2) for q in (10, 50, 90)],
                      "bytes_per_launch": attn_bytes,
                      "traffic": traffic},
         "cpu_baseline": None,
     }
+    ku = m["kernel_us"]
+    if ku and ku.get("attn_split"):
+        rec["roofline"]["kernel_us_profiler"] = round(float(np.mean(ku["attn_split"])), 3)
 
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on a sample", file=sys.stderr, flush=True)
 
         def host_layer_fn(l):
-            L = layers[l]
+            L = b.layers[l]
 
             def u16(t):
                 return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
@@ -341,8 +450,22 @@ def main():
                     u16(L["v_new"]), L["seq_pos"].cpu().numpy(),
                     u16(L["out_gate"]) if "out_gate" in L else None)
         rec["cpu_baseline"] = cpu_baseline(w, host_layer_fn, w.layers, args.cpu_seconds,
-                                           None if freqs is None else freqs.cpu().numpy(),
-                                           None if block_table is None else block_table.cpu().numpy())
+                                           None if b.freqs is None else b.freqs.cpu().numpy(),
+                                           None if b.block_table is None else b.block_table.cpu().numpy())
+
+    if configs == "all":
+        del b
+        torch.cuda.empty_cache()
+        rec["configs"] = {}
+        for name, wc in WORKLOADS.items():
+            if name == w.name:
+                continue
+            print(f"[bench] config {name}", file=sys.stderr, flush=True)
+            bc = Bench(wc, args, dev, "step")
+            mc = bc.measure(args.config_steps, args.warmup, False, "auto", not args.no_kernel_profiler)
+            rec["configs"][name] = config_record(bc, mc, args.config_steps, False)
+            del bc, mc
+            torch.cuda.empty_cache()
 
     print(json.dumps(rec), flush=True)
 

@@ -1,6 +1,6 @@
 """Summaries of rocprofv3 output for the committed profiles.
 
-    python -m decode_attention_append_amd.profiling trace  <kernel_stats.csv> <out.md> <title> <command>
+    python -m decode_attention_append_amd.profiling trace  <run_dir> <out.md> <title> <command> [<warm_launches>]
     python -m decode_attention_append_amd.profiling counters <fetch_dir> <write_dir> <kernel> <source> <workload>
                                                          <bytes_per_launch> <out.json> <fetch_cmd> <write_cmd>
 
@@ -11,6 +11,12 @@ bench runs first (the three largest copy-kernel dispatches), so the result is HB
 bytes per launch.  It records a hash of the kernel's sources (comments and
 whitespace aside), so a later change to the kernel makes the numbers stale
 (bench.py then reports traffic as null).
+
+`trace` reads the per-dispatch kernel trace of a `rocprofv3 --kernel-trace` run
+of bench.py and reports, per kernel, all launches and the cold ones only: when
+the run read the 2 GiB cache-flush buffer before its timed steps, the launches
+after the first flush; otherwise every launch after the first `warm_launches`
+(the warm-up steps), which then stream more than the caches hold anyway.
 """
 import csv
 import glob
@@ -92,24 +98,66 @@ def counters(fetch_dir, write_dir, kernel, source, workload, bytes_per_launch, o
     return rec
 
 
-def trace(stats_csv, out_md, title, command):
-    rows = list(csv.DictReader(open(stats_csv)))
+def _launches(run_dir):
+    rows = []
+    for path in glob.glob(os.path.join(run_dir, "**", "*kernel_trace.csv"), recursive=True):
+        rows += list(csv.DictReader(open(path)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    return [(r["Kernel_Name"], (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3) for r in rows]
+
+
+def _is_flush(name):
+    return "reduce_kernel" in name
+
+
+def _is_ours(name):
+    return re.match(r"(void )?da::", name) is not None
+
+
+def _stats(v):
+    v = sorted(v)
+    return len(v), sum(v) / len(v), v[len(v) // 2], v[0], v[-1]
+
+
+def trace(run_dir, out_md, title, command, warm_launches=0):
+    launches = _launches(run_dir)
+    ours = [n for n, _ in launches if _is_ours(n)]
+    flushed = any(_is_flush(n) for n, _ in launches)
+    cold, seen_flush, per_kernel_seen = {}, False, {}
+    for n, us in launches:
+        if _is_flush(n):
+            seen_flush = True
+            continue
+        if not _is_ours(n):
+            continue
+        per_kernel_seen[n] = per_kernel_seen.get(n, 0) + 1
+        if (flushed and seen_flush) or (not flushed and per_kernel_seen[n] > warm_launches):
+            cold.setdefault(n, []).append(us)
+    rule = ("launches after the first read of the 2 GiB cache-flush buffer (every timed step is preceded by one)"
+            if flushed else f"every launch after the first {warm_launches} of each kernel (the warm-up steps); "
+            "each step streams more than the caches hold")
     lines = [f"# Kernel trace: {title}", "", "Command (from the repository root on an MI355X, rocprofv3 of ROCm 7.2):",
              "", "```", command, "```", "",
-             "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
-    for r in rows:
-        n = r["Name"]
-        n = n if len(n) <= 70 else n[:67] + "..."
-        lines.append(f"| `{n}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
-                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
-                     f"{float(r['Percentage']):.2f} |")
+             f"Cold launches: {rule}.", "",
+             "| kernel | cold launches | cold mean us | cold median us | cold min us | cold max us | all launches | all mean us |",
+             "|---|---|---|---|---|---|---|---|"]
+    for n in sorted(set(ours), key=ours.index):
+        allv = [us for k, us in launches if k == n]
+        short = n if len(n) <= 70 else n[:67] + "..."
+        if n in cold:
+            c, mean, med, lo, hi = _stats(cold[n])
+            lines.append(f"| `{short}` | {c} | {mean:.2f} | {med:.2f} | {lo:.2f} | {hi:.2f} | {len(allv)} | "
+                         f"{sum(allv) / len(allv):.2f} |")
+        else:
+            lines.append(f"| `{short}` | 0 | - | - | - | - | {len(allv)} | {sum(allv) / len(allv):.2f} |")
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
+    return {n: _stats(v) for n, v in cold.items()}
 
 
 if __name__ == "__main__":
     if sys.argv[1] == "trace":
-        trace(*sys.argv[2:6])
+        trace(*sys.argv[2:6], *(int(x) for x in sys.argv[6:7]))
     elif sys.argv[1] == "counters":
         a = sys.argv[2:]
         print(json.dumps(counters(a[0], a[1], a[2], a[3], a[4], int(a[5]), a[6], a[7], a[8]), indent=1))
