@@ -107,13 +107,13 @@ __device__ __forceinline__ void load_full(Tile &t, const CacheView &cv, int tb, 
     for (int kblk = 0; kblk < 2; ++kblk) {
         const uint8_t *kr = cv.k + blk[kblk] + (size_t)l16 * kRowBytes + 16 * q;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) t.k[kblk][s] = ld16(kr + 64 * s);
+        for (int s = 0; s < 4; ++s) t.k[kblk][s] = ld16_stream(kr + 64 * s);
     }
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
         const uint8_t *v0 = cv.v + blk[half] + (size_t)(4 * q) * kRowBytes + 16 * l16;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) t.v[4 * half + u] = ld16(v0 + u * kRowBytes);
+        for (int u = 0; u < 4; ++u) t.v[4 * half + u] = ld16_stream(v0 + u * kRowBytes);
     }
 }
 

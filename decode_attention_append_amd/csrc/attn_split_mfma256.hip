@@ -101,12 +101,12 @@ __device__ __forceinline__ void load_full16(Tile16 &t, const CacheView &cv, int 
     const size_t blk = cv.block(tb / kPageTokens);
     const uint8_t *kr = cv.k + blk + (size_t)l16 * kRow + 16 * q;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) t.k[s] = ld16(kr + 64 * s);
+    for (int s = 0; s < 8; ++s) t.k[s] = ld16_stream(kr + 64 * s);
     const uint8_t *vr = cv.v + blk + (size_t)(4 * q) * kRow + 16 * l16;
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) t.v[hh][u] = ld16(vr + u * kRow + 256 * hh);
+        for (int u = 0; u < 4; ++u) t.v[hh][u] = ld16_stream(vr + u * kRow + 256 * hh);
 }
 
 // Where rows come from when a tile is not all plain cache rows: keys past

@@ -208,7 +208,7 @@ __global__ __launch_bounds__(64 * NW) void attn_split_valu_kernel(const int32_t 
     auto load_fast = [&](u32x4_t (&buf)[4], const uint8_t *base, int s_) {
         const uint8_t *r0 = slab_ptr(base, s_) + (size_t)gq * kRowBytes;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) buf[u] = ld16(r0 + u * 4 * kRowBytes);
+        for (int u = 0; u < 4; ++u) buf[u] = ld16_stream(r0 + u * 4 * kRowBytes);
     };
     auto load_rows = [&](u32x4_t (&buf)[4], const uint8_t *base, const uint8_t *nbase, uint8_t *wbase, bool rot,
                          int s_) {

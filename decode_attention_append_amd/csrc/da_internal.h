@@ -294,6 +294,19 @@ __device__ __forceinline__ u32x4_t ld16(const uint8_t *p) {
     return *reinterpret_cast<const u32x4_t *>(p);
 }
 
+// 16-byte load of the bulk K/V cache stream (whole tiles and slabs), which a
+// launch reads exactly once: a non-temporal load (`global_load_dwordx4 ... nt`),
+// so the stream neither allocates in nor evicts from the caches on its way.  On
+// gfx950 a plain 2 GiB read streams at 6.0-6.2 TB/s and a non-temporal one at
+// 6.9-7.2 TB/s (same lanes and depths); on the attention kernels it took the
+// headline one-launch layer from 179.8 to 161.8 us and GQA-8 long context's
+// attention launch from 43.8 to 41.1 us.  The per-row loads (partial tiles, new
+// rows) and the query rows keep plain loads: with every load non-temporal the
+// 512-context layer lost 0.6 us.
+__device__ __forceinline__ u32x4_t ld16_stream(const uint8_t *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+}
+
 // fp32 sum of a.lo*b.lo + a.hi*b.hi + c over packed 16-bit pairs.
 template <bool F16>
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
