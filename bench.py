@@ -304,16 +304,18 @@ class Bench:
             from torch.profiler import ProfilerActivity, profile
             n_prof = max(5, min(steps, 20))
             with profile(activities=[ProfilerActivity.CUDA]) as prof:
-                for _ in range(n_prof):
+                for _ in range(n_prof + 1):
                     if flush:
                         flush_buf.sum(dtype=torch.float32)
                     self.step()
                 torch.cuda.synchronize()
             kernel_us = {}
-            for e in prof.events():
+            for e in sorted(prof.events(), key=lambda e: e.time_range.start):
                 for tag in ("attn_split", "attn_combine", "kv_append"):
                     if tag in e.name:
                         kernel_us.setdefault(tag, []).append(float(e.device_time))
+            # the first profiled step's launches also pay the profiler's own start-up
+            kernel_us = {t: v[w.layers:] for t, v in kernel_us.items() if len(v) > w.layers}
         del flush_buf
         return {"ms_total": ms_total, "step_ms": step_ms, "attn_ms": attn_ms, "flush": flush,
                 "step_bytes": step_bytes, "attn_bytes": attn_bytes, "kernel_us": kernel_us}
