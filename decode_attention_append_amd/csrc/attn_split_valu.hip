@@ -13,7 +13,7 @@
 // chunks.  A key j is visible to query token i iff j <= seq_pos + i.
 //
 // Mapping on gfx950: one workgroup per (b, h, chunk), serving every query row
-// of KV head h, so each K/V byte is read once: 4 waves, or 16 (chunks of up to
+// of KV head h, so each K/V byte is read once: 4 waves, or 8 (chunks of up to
 // 8192 keys, one workgroup per compute unit) for up to 2 rows per KV head and
 // at least 128 (b, h) pairs.  Sixteen lanes hold
 // one 256-byte row (16 bytes each): a wave's 128-bit load covers four
@@ -22,7 +22,7 @@
 // The chunk's scores go to LDS; the chunk is two-pass (all scores, then the
 // maximum, then P.V), so no running rescale is needed inside a chunk.  Each
 // wave streams its 16-key slabs through two register buffers in turn, so the
-// next slab is in flight while the current one is computed; with 16 waves the
+// next slab is in flight while the current one is computed; with 8 waves the
 // K pass's slabs after each wave's first are claimed from an LDS counter.
 #include "da_internal.h"
 
@@ -95,7 +95,7 @@ constexpr int kValuOneLaunchRows = 8;
 
 // ROPE: the problem has a rotary table (a separate instantiation, so that the
 // rotation's registers never weigh on the kernel without one).
-// NW: waves per workgroup, 4 (chunks of up to 2048 keys) or 16 (up to 8192).
+// NW: waves per workgroup, 4 (chunks of up to 2048 keys) or 8 (up to 8192).
 template <bool F16, int RP, bool ROPE, int NW>
 __global__ __launch_bounds__(64 * NW) void attn_split_valu_kernel(const int32_t *__restrict__ seq_pos, int32_t batch, AttnParams p) {
     const int sp_first = first_seq_pos(seq_pos, batch, threadIdx.x & 63);
@@ -258,14 +258,14 @@ __global__ __launch_bounds__(64 * NW) void attn_split_valu_kernel(const int32_t 
         }
     };
 
-    // With 16 waves, the K pass's fast slabs after each wave's first are
+    // With 8 waves, the K pass's fast slabs after each wave's first are
     // claimed from a workgroup counter in LDS, so waves the memory system
     // serves faster take more slabs and none idles at the end of the pass
     // (every score still lands in its own slot: the result does not depend on
     // which wave took a slab).  The V pass keeps the fixed assignment, whose
     // per-wave sums are added in a fixed order.
     __shared__ int k_claim;
-    if constexpr (NW == 16) {
+    if constexpr (NW >= 8) {
         if (tid == 0) k_claim = 0;
         __syncthreads();
     }
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(64 * NW) void attn_split_valu_kernel(const int32_t 
             }
         }
     };
-    if constexpr (NW == 16)
+    if constexpr (NW >= 8)
         pass_claimed(p.k_cache, knb, kwb, fused_append, kb0, score_slab);
     else
         pass(p.k_cache, knb, kwb, fused_append, kb0, false, score_slab);
@@ -516,7 +516,7 @@ static hipError_t launch_nw(const AttnParams &p, int grid, hipStream_t s) {
 template <bool F16, int RP>
 static hipError_t launch_rp(const AttnParams &p, int grid, hipStream_t s) {
     if constexpr (RP <= 2) {
-        if (p.valu_waves == 16) return launch_nw<F16, RP, 16>(p, grid, s);
+        if (p.valu_waves == 8) return launch_nw<F16, RP, 8>(p, grid, s);
     }
     return launch_nw<F16, RP, 4>(p, grid, s);
 }

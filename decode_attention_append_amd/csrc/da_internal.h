@@ -133,7 +133,7 @@ struct AttnParams {
     const uint16_t *out_gate; // [B][q_len][Hq][D] sigmoid output gate, or null
     int32_t seq_chunk_cap; // balanced: at most this many chunks per sequence unless its
                            //   length needs more of max_chunk keys (0: no cap)
-    int32_t valu_waves;    // waves per workgroup of the vector-ALU kernel: 4 or 16
+    int32_t valu_waves;    // waves per workgroup of the vector-ALU kernel: 4 or 8
     int32_t chunk_align;   // balanced: a sequence whose chunks would be at least half
                            //   this long gets lengths rounded up to a multiple of it
                            //   (a multiple of 32; 32: no effect)

@@ -74,27 +74,29 @@ da_status check_problem(const da_problem *p) {
 // separate path): GQA-8 at 12k-16k context 50.0 / 49.7 / 52.1 us and the
 // 4-token verify 27.6 / 28.7 / 34.6 us at 256 / 512 / 1024 chunks; head_dim 256
 // on 16 x 2 KV heads at 8k context 52.8 / 55.3 / 56.2 us.
-// With 16-wave workgroups (below) the vector-ALU kernel also aims at one chunk
+// With 8-wave workgroups (below) the vector-ALU kernel also aims at one chunk
 // per compute unit.
 int default_target(int variant, int valu_waves) {
-    return variant == DA_VARIANT_MFMA || valu_waves == 16 ? 256 : 1024;
+    return variant == DA_VARIANT_MFMA || valu_waves >= 8 ? 256 : 1024;
 }
 
 // Waves per workgroup of the vector-ALU kernel.  Up to 2 rows, when there are
-// at least 128 (sequence, KV head) units, a 16-wave workgroup takes chunks of
-// up to 8192 keys: the same 16 waves per compute unit as four 4-wave
-// workgroups, but a (sequence, KV head) of up to 8192 keys is one chunk, whose
+// at least 128 (sequence, KV head) units, an 8-wave workgroup takes chunks of
+// up to 8192 keys: a (sequence, KV head) of up to 8192 keys is one chunk, whose
 // workgroup writes the output itself in the one-launch step: no partials, no
-// arrival and no merge.
+// arrival and no merge.  Eight waves per compute unit, each with two 16-key
+// slabs in flight, keep 64 KiB of non-temporal loads in flight per unit; with
+// 16 waves (128 KiB) the headline layer (batch 32, 8 KV heads, 8192 keys)
+// measured 161.5 us against 158.2 us (rocprofv3, cold, two interleaved runs).
 int valu_waves_of(int variant, int rows, int units) {
-    return variant == DA_VARIANT_VALU && rows <= 2 && units >= 128 ? 16 : 4;
+    return variant == DA_VARIANT_VALU && rows <= 2 && units >= 128 ? 8 : 4;
 }
 
 // Longest chunk a kernel accepts: the vector-ALU kernel keeps the chunk's
 // scores in LDS (rows x chunk floats, at most 64 KiB).
 int max_chunk_of(int variant, int rows, int valu_waves) {
     if (variant == DA_VARIANT_MFMA) return 4096;
-    if (valu_waves == 16) return 8192;
+    if (valu_waves >= 8) return 8192;
     const int rp = rows <= 1 ? 1 : rows <= 2 ? 2 : rows <= 4 ? 4 : rows <= 8 ? 8 : 16;
     return rp <= 8 ? 2048 : 1024;
 }

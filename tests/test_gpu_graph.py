@@ -21,7 +21,7 @@ def _say(*a):
 
 @pytest.mark.parametrize("B,q_len,Hq,Hkv,S,seq_pos,variant", [
     (2, 1, 16, 8, 700, [699, 345], None),                  # vector ALU, merge in the launch
-    # 16-wave vector-ALU workgroups (128 units, 2 rows): K slabs are claimed by
+    # 8-wave vector-ALU workgroups (128 units, 2 rows): K slabs are claimed by
     # whichever wave is free, and the results must still repeat bit for bit
     (16, 1, 16, 8, 3000, [2999 - 181 * i for i in range(16)], None),
     (2, 1, 64, 8, 3000, [2999, 1537], None),               # MFMA, merge in the launch

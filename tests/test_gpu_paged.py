@@ -117,7 +117,8 @@ def test_paged_pages_across_chunks(chunk, variant, path):
     (2, 64, 8, 128, 257, [4095, 2600], 4096, 256),     # MFMA: one page per thread
     (2, 16, 2, 256, 257, [4095, 2600], 4096, 256),     # head_dim 256
     (2, 16, 8, 128, 257, [4095, 2600], 2048, 128),     # vector ALU, 4 waves
-    (16, 16, 8, 128, 400, [6300] + [211 * i + 5 for i in range(15)], 6304, 394),  # 16 waves
+    (16, 16, 8, 128, 400, [6300] + [211 * i + 5 for i in range(15)], 6304, 394),  # 8 waves
+    (16, 16, 8, 128, 512, [8191] + [211 * i + 5 for i in range(15)], 8192, 512),  # 8 waves, one page per thread
 ])
 def test_paged_long_chunks(B, Hq, Hkv, D, pps, seq_pos, chunk, pages, path):
     """Chunks of up to one page per thread of the workgroup: each workgroup reads its
