@@ -739,21 +739,44 @@ __device__ inline void merge_row_wave(const AttnParams &p, uint16_t *out, int bh
     store_out<F16, NV>(p, out, out_row_off(p, b, h, r) + NV * lane, x);
 }
 
-// sigmoid(gate) of the NV output elements at `off` (1 without a gate).
+// The raw 16-bit gate values of the NV (2 or 4) output elements at `off`, one
+// 4- or 8-byte load (`off` is a multiple of NV and the gate is 16-byte aligned);
+// zeros without a gate.  Kept raw so that the load joins the merge's other loads
+// in flight: the sigmoid is taken after all of them are issued.
+template <int NV>
+__device__ __forceinline__ void gate_raw(const AttnParams &p, size_t off, uint32_t (&g)[NV / 2]) {
+    static_assert(NV == 2 || NV == 4, "two or four output elements per lane");
+#pragma unroll
+    for (int k = 0; k < NV / 2; ++k) g[k] = 0u;
+    if (p.out_gate) {
+        if constexpr (NV == 2) {
+            g[0] = *reinterpret_cast<const uint32_t *>(p.out_gate + off);
+        } else {
+            const u32x2_t x = *reinterpret_cast<const u32x2_t *>(p.out_gate + off);
+            g[0] = x[0];
+            g[1] = x[1];
+        }
+    }
+}
+
+// sigmoid(gate) of the NV output elements from their raw values (1 without a gate).
 template <bool F16, int NV>
-__device__ __forceinline__ void gate_factors(const AttnParams &p, size_t off, float (&g)[NV]) {
+__device__ __forceinline__ void gate_factors(const AttnParams &p, const uint32_t (&graw)[NV / 2], float (&g)[NV]) {
 #pragma unroll
     for (int k = 0; k < NV; ++k) g[k] = 1.f;
     if (p.out_gate) {
 #pragma unroll
-        for (int k = 0; k < NV; ++k) g[k] = sigmoid16<F16>(p.out_gate[off + k]);
+        for (int k = 0; k < NV; ++k) g[k] = sigmoid16<F16>((uint16_t)(graw[k / 2] >> (16 * (k & 1))));
     }
 }
 
 // Merge of query rows r0 and r0 + r_step (when below p.rows) of (b, h) over their
 // n <= 16 chunks by one wave, with every load of both rows in flight at once:
 // the (m, l) pairs, the partial sums and the gate.  Same arithmetic as
-// merge_row_wave.
+// merge_row_wave.  (With the gate's sigmoid taken as each row's loads were
+// issued, the wait for the first row's gate also waited for its partial sums
+// before the second row's loads went out: the head_dim-256 merge took two
+// round trips.)
 template <bool F16, int D>
 __device__ inline void merge_two_rows_wave(const AttnParams &p, int bh, int b, int h, int r0, int r_step, int n,
                                            int lane) {
@@ -762,7 +785,8 @@ __device__ inline void merge_two_rows_wave(const AttnParams &p, int bh, int b, i
     const uint32_t cs_ml = (uint32_t)p.rows * 2;
     const uint32_t cs_acc = (uint32_t)p.rows * D * 4;
     const int voff = lane * NV * 4;
-    float m[2], l[2], v[2][16][NV], g[2][NV];
+    float m[2], l[2], v[2][16][NV];
+    uint32_t graw[2][NV / 2];
     size_t off[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -786,8 +810,11 @@ __device__ inline void merge_two_rows_wave(const AttnParams &p, int bh, int b, i
             }
         }
         off[j] = out_row_off(p, b, h, r) + NV * lane;
-        gate_factors<F16, NV>(p, off[j], g[j]);
+        gate_raw<NV>(p, off[j], graw[j]);
     }
+    float g[2][NV];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) gate_factors<F16, NV>(p, graw[j], g[j]);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         if (j == 1 && r1 == r0) break;
