@@ -405,7 +405,8 @@ def main():
     if args.path == "step":
         kernel_tag += "_step" if b.plan["fused_combine"] else "_step+attn_combine"
     attn_gbs = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
-    traffic = counters_for(kernel_tag, w.name) if "+" not in kernel_tag else None
+    # counters of the attention launch (the dominant kernel, whose bytes `achieved` uses)
+    traffic = counters_for(kernel_tag.split("+")[0], w.name)
 
     rec = {
         "metric": "decode-attention KV GB/s (% of HBM peak) + us/step, Hq16/Hkv8/d128 ctx 8k",

@@ -59,6 +59,7 @@ class Problem(ctypes.Structure):
         ("block_table", ctypes.c_void_p),
         ("rope_dim", ctypes.c_int32),
         ("out_gate", ctypes.c_void_p),
+        ("merge", ctypes.c_int32),
     ]
 
     def __repr__(self):
@@ -141,7 +142,7 @@ def status_str(status: int) -> str:
 
 def problem(batch, q_len, n_q_heads, n_kv_heads, head_dim, max_seq, dtype, scale=0.0,
             chunk_tokens=0, variant=None, work_items=0, rope_freqs=None, block_table=None,
-            n_pages=0, page_size=16, rope_dim=0, out_gate=None) -> Problem:
+            n_pages=0, page_size=16, rope_dim=0, out_gate=None, merge=None) -> Problem:
     """variant: None (automatic), "valu" or "mfma"; chunk_tokens 0 = balanced chunks.
     rope_freqs: None, or a float32 GPU tensor of head_dim/2 rotary frequencies.
     block_table: None (contiguous caches), or an int32 GPU tensor [batch, pages_per_seq]
@@ -149,7 +150,9 @@ def problem(batch, q_len, n_q_heads, n_kv_heads, head_dim, max_seq, dtype, scale
     pages_per_seq * page_size).  rope_dim: rotate only the first rope_dim dims (0: all;
     rope_freqs then holds rope_dim/2 values).  out_gate: None, or a GPU tensor
     [batch, q_len, n_q_heads, head_dim] of the element type: the output is multiplied
-    by sigmoid(out_gate).  The problem keeps references to the tensors."""
+    by sigmoid(out_gate).  merge: None (automatic), "launch" (da_decode_step merges inside
+    the attention launch whenever the plan allows it) or "separate" (always the combine
+    launch).  The problem keeps references to the tensors."""
     if isinstance(dtype, torch.dtype):
         dtype = _DTYPE_CODE[dtype]
     elif isinstance(dtype, str):
@@ -169,26 +172,27 @@ def problem(batch, q_len, n_q_heads, n_kv_heads, head_dim, max_seq, dtype, scale
         pps = block_table.shape[1]
         bt = _dev(block_table, "block_table", None, torch.int32)
         ps = page_size
+    mg = {None: 0, "launch": 1, "separate": 2}[merge]
     pr = Problem(batch, q_len, n_q_heads, n_kv_heads, head_dim, max_seq, dtype, float(scale),
-                 chunk_tokens, v, work_items, rp, ps, pps, n_pages if ps else 0, bt, rope_dim, og)
+                 chunk_tokens, v, work_items, rp, ps, pps, n_pages if ps else 0, bt, rope_dim, og, mg)
     pr._refs = (rope_freqs, block_table, out_gate)  # keeps the tensors alive as long as the problem
     return pr
 
 
 def problem_for(q: torch.Tensor, k_cache: torch.Tensor, scale=0.0, chunk_tokens=0,
                 variant=None, work_items=0, rope_freqs=None, block_table=None, rope_dim=0,
-                out_gate=None) -> Problem:
+                out_gate=None, merge=None) -> Problem:
     """The problem described by q [B, q_len, Hq, D] and a cache [B, Hkv, S, D], or with a
     block table [B, pages_per_seq] a page pool [n_pages, Hkv, page_size, D]."""
     B, q_len, Hq, D = q.shape
     if block_table is None:
         _, Hkv, S, _ = k_cache.shape
         return problem(B, q_len, Hq, Hkv, D, S, q.dtype, scale, chunk_tokens, variant, work_items, rope_freqs,
-                       rope_dim=rope_dim, out_gate=out_gate)
+                       rope_dim=rope_dim, out_gate=out_gate, merge=merge)
     n_pages, Hkv, page_size, _ = k_cache.shape
     S = block_table.shape[1] * page_size
     return problem(B, q_len, Hq, Hkv, D, S, q.dtype, scale, chunk_tokens, variant, work_items, rope_freqs,
-                   block_table, n_pages, page_size, rope_dim, out_gate)
+                   block_table, n_pages, page_size, rope_dim, out_gate, merge)
 
 
 def plan_attention(p: Problem) -> dict:

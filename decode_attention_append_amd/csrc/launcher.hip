@@ -48,6 +48,7 @@ da_status check_problem(const da_problem *p) {
                              (p->rope_dim != 64 && p->rope_dim != 128 && p->rope_dim != 256)))
         return DA_ERR_UNSUPPORTED;
     if (p->out_gate && !aligned16(p->out_gate)) return DA_ERR_INVALID_ARG;
+    if (p->merge < 0 || p->merge > 2) return DA_ERR_INVALID_ARG;
     if (p->q_len > kMaxQLen) return DA_ERR_UNSUPPORTED;
     if ((int64_t)(p->n_q_heads / p->n_kv_heads) * p->q_len > kMaxRows) return DA_ERR_UNSUPPORTED;
     if (p->max_seq > kMaxSeq) return DA_ERR_UNSUPPORTED;
@@ -150,6 +151,28 @@ constexpr int kOneLaunchSeqChunks = 16;
 // rows; beyond (only when it is forced) da_decode_step makes three launches.
 bool one_launch_capable(int variant, int rows) { return variant == DA_VARIANT_MFMA || rows <= 8; }
 
+// Automatic choice of the in-launch merge.  After the last chunk of a (sequence,
+// KV head) ends, the merge inside the launch costs a chain of dependent memory
+// round trips (the partial's stores acknowledged, the arrival atomic, the other
+// partials' loads, the output store): about 5 us on the MFMA kernels, whose
+// partials are 8-32 rows wide; a separate combine launch costs less there.
+// Step times by graph replay, cold, in launch / separate combine: GQA 64:8 at
+// 12k-16k context (32 heads) 57.1 / 55.7 us; head_dim-256 gated 16:2 at 6k-8k
+// (32 heads) 50.7 / 48.0 us a layer; batch 1, 32:4, 32k context 40.1 / 21.9 us
+// a layer and head_dim 256 at 8k 27.2 / 17.2 us (the merge's cap of 16 chunks
+// a sequence also leaves most compute units idle there); batch 4, 32:4, 4k
+// context 17.4 / 16.1 us.  With at least 128 heads (at most two chunks each)
+// the merge is small and stays in the launch: batch 16, 64:8, 1k context 21.7 /
+// 22.4 us.  The vector-ALU kernel's partials are 1-8 rows wide and its merge
+// stays in the launch (batch-1 MHA at 4k: 14.9 / 15.1 us a layer; the
+// 512-context layer 20.2 / 21.5 us).
+constexpr int kMfmaMergeMinUnits = 128;
+
+bool merge_in_launch(const da_problem *p, int variant, int units) {
+    if (p->merge == 2) return false;
+    return p->merge == 1 || variant == DA_VARIANT_VALU || units >= kMfmaMergeMinUnits;
+}
+
 void plan_of(const da_problem *p, da_plan *pl) {
     const int rows = (p->n_q_heads / p->n_kv_heads) * p->q_len;
     const int variant = p->variant ? p->variant - 1
@@ -189,7 +212,7 @@ void plan_of(const da_problem *p, da_plan *pl) {
         const int64_t bound = need > kOneLaunchSeqChunks ? need : kOneLaunchSeqChunks;
         if (bound < nb_max) nb_max = bound;
     }
-    pl->fused_combine = one_launch_capable(variant, rows) &&
+    pl->fused_combine = merge_in_launch(p, variant, units) && one_launch_capable(variant, rows) &&
                         nb_max * rows <= fused_merge_rows(variant);
     const int32_t bh = units;
     pl->workspace_bytes = align256(ws_acc_floats(bh, pl->n_chunks, rows, p->head_dim) * sizeof(float)) +

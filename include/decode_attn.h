@@ -129,6 +129,14 @@ typedef struct {
                              by sigmoid(gate) in fp32 before rounding (the same
                              diagram's full-SDPA layers, whose Q projection also
                              yields a gate applied through a sigmoid)             */
+    int32_t merge;        /* how da_decode_step combines the chunks' partials:
+                             0 = automatic, 1 = inside the attention launch
+                             whenever the plan allows it, 2 = always the separate
+                             combine launch (a tuning and testing override).
+                             Automatic merges inside the launch on the vector-ALU
+                             kernel, and on the MFMA kernels only with at least
+                             128 (sequence, KV head) pairs, when each has at most
+                             two chunks.  Other values: DA_ERR_INVALID_ARG.       */
 } da_problem;
 
 /*
@@ -141,7 +149,7 @@ typedef struct {
  * maximum) and never shorter than 64 keys.  With an explicit chunk_tokens every
  * chunk has that length.  Either way the attention and the combine derive the
  * same chunks from the same seq_pos.  A chunk is the work of one workgroup:
- * 4 waves, or 16 on the vector-ALU kernel when there are at most 2 rows per KV
+ * 4 waves, or 8 on the vector-ALU kernel when there are at most 2 rows per KV
  * head and at least 128 (sequence, KV head) pairs (chunks of up to 8192 keys,
  * about 256 of them).
  */

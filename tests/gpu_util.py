@@ -1,5 +1,6 @@
 """Helpers for the GPU parity tests: run the library through its C ABI, compare with the oracle."""
 import numpy as np
+import pytest
 import torch
 
 import decode_attention_append_amd as da
@@ -14,12 +15,32 @@ def odt(dtype) -> int:
     return oracle.FP16 if dtype == torch.float16 else oracle.BF16
 
 
-PATHS = ("separate", "step")  # the three separate calls; the one-launch da_decode_step
+# the three separate calls; da_decode_step as planned; da_decode_step with the merge
+# forced into the attention launch (run only where that changes what is launched)
+PATHS = ("separate", "step", "step_launch")
+
+
+def with_merge(p, merge: str):
+    """A copy of problem ``p`` with its merge override set ("launch" or "separate")."""
+    q = type(p).from_buffer_copy(p)
+    q.merge = {"launch": 1, "separate": 2}[merge]
+    q._refs = getattr(p, "_refs", None)
+    return q
+
+
+def path_differs(p, path) -> bool:
+    """False for "step_launch" when forcing the merge into the launch changes nothing
+    (the plan already merges there, or cannot)."""
+    if path != "step_launch":
+        return True
+    return da.plan_attention(with_merge(p, "launch"))["fused_combine"] != da.plan_attention(p)["fused_combine"]
 
 
 def run_step(p, inp, stream=None, path="step", ws=None):
     """One decode step on the GPU through ``path``.  ``inp`` holds device tensors; the
     caches are updated in place.  Returns the output tensor (device)."""
+    if path == "step_launch":
+        p, path = with_merge(p, "launch"), "step"
     if ws is None:
         ws = da.new_workspace(p, stream=stream)
     out = torch.empty((p.batch, p.q_len, p.n_q_heads, p.head_dim), dtype=inp["q"].dtype,
@@ -70,6 +91,9 @@ def check_layer(p, inp, rows=None, stream=None, paths=PATHS):
         rows = np.asarray(rows, dtype=np.int32).reshape(-1, 3)
         ref = oracle.gqa_decode_rows(qb, k_ref, v_ref, sp, rows, dt, scale=scale)
     stats = {}
+    paths = [x for x in paths if path_differs(p, x)]
+    if not paths:
+        pytest.skip("forcing the merge into the attention launch changes nothing for this plan")
     for n, path in enumerate(paths):
         last = n == len(paths) - 1
         run = inp if last else dict(inp, k_cache=inp["k_cache"].clone(), v_cache=inp["v_cache"].clone())
@@ -153,6 +177,9 @@ def check_full(p, inp, freqs=None, rows=None, stream=None, paths=PATHS, ws=None)
         ref = oracle.output_gate(ref, gb, dt)
     new = appended_rows(k_ref.shape, sp, p.q_len, bt)
     stats = {}
+    paths = [x for x in paths if path_differs(p, x)]
+    if not paths:
+        pytest.skip("forcing the merge into the attention launch changes nothing for this plan")
     for n, path in enumerate(paths):
         last = n == len(paths) - 1
         run = inp if last else dict(inp, k_cache=inp["k_cache"].clone(), v_cache=inp["v_cache"].clone())

@@ -67,6 +67,13 @@ def test_plan_rejects(kw, status):
     assert da.workspace_bytes(p) == 0
 
 
+def test_plan_rejects_unknown_merge():
+    for bad in (-1, 3):
+        p = P()
+        p.merge = bad
+        assert da.lib.da_plan_attention(ctypes.byref(p), ctypes.byref(da.Plan())) == da.DA_ERR_INVALID_ARG
+
+
 def test_plan_is_pure_and_sized():
     p = P(batch=32, max_seq=8192)
     a, b = da.plan_attention(p), da.plan_attention(p)
@@ -139,7 +146,7 @@ def test_static_step_rejects_before_launch():
     assert da.lib.da_decode_step_static(ctypes.byref(p), *args, good + 4, None) == da.DA_ERR_INVALID_ARG
     assert da.lib.da_decode_step_static(ctypes.byref(P(head_dim=64)), *args, good, None) == da.DA_ERR_UNSUPPORTED
     # fused merge: 512 heads x 16 slots x 8 rows x 130 floats = 34 MB > 31 MiB of partials
-    big = P(batch=64, n_q_heads=64, n_kv_heads=8, max_seq=65536)
+    big = P(batch=64, n_q_heads=64, n_kv_heads=8, max_seq=65536, merge="launch")
     assert da.plan_attention(big)["fused_combine"]
     assert da.lib.da_decode_step_static(ctypes.byref(big), *args, good, None) == da.DA_ERR_SCRATCH_LIMIT
     # without the fused merge the whole separate-call workspace is needed
@@ -153,19 +160,29 @@ def test_static_step_rejects_before_launch():
     (dict(batch=32, n_q_heads=16, n_kv_heads=8, max_seq=8192), True),    # vector ALU, 2 rows
     (dict(batch=1, n_q_heads=16, n_kv_heads=16, max_seq=4096, dtype="fp16"), True),  # MHA
     (dict(batch=1, max_seq=512), True),
-    (dict(batch=4, n_q_heads=64, n_kv_heads=8, max_seq=16384), True),    # MFMA, 8 rows x 16 chunks
-    (dict(batch=8, q_len=4, n_q_heads=32, n_kv_heads=4, max_seq=8192), False),  # MFMA, 32 rows
-    (dict(batch=1, n_q_heads=64, n_kv_heads=8, max_seq=512), True),      # MFMA, 8 chunks at most
-    (dict(batch=1, n_q_heads=64, n_kv_heads=2, max_seq=65536), False),   # MFMA, 32 rows x 16 chunks
     (dict(batch=1, n_q_heads=16, n_kv_heads=1, max_seq=65536, variant="valu"), False),
-    # head_dim 256: the last workgroup merges, up to 256 chunk-rows
-    (dict(batch=16, n_q_heads=16, n_kv_heads=2, head_dim=256, max_seq=8192, dtype="fp16"), True),
-    (dict(batch=4, q_len=2, n_q_heads=16, n_kv_heads=2, head_dim=256, max_seq=8192), True),
-    (dict(batch=4, q_len=4, n_q_heads=16, n_kv_heads=2, head_dim=256, max_seq=8192), False),
+    # MFMA: automatic only with at least 128 (sequence, KV head) pairs
+    (dict(batch=4, n_q_heads=64, n_kv_heads=8, max_seq=16384), False),   # 32 heads
+    (dict(batch=16, n_q_heads=64, n_kv_heads=8, max_seq=1024), True),    # 128 heads
+    (dict(batch=16, n_q_heads=16, n_kv_heads=2, head_dim=256, max_seq=8192, dtype="fp16"), False),
+    (dict(batch=64, n_q_heads=16, n_kv_heads=2, head_dim=256, max_seq=8192, dtype="fp16"), True),
+    (dict(batch=32, q_len=4, n_q_heads=32, n_kv_heads=4, max_seq=8192), False),  # 32 rows x 16 chunks
+    # forced into the launch: up to 256 chunk-rows per (sequence, KV head)
+    (dict(batch=4, n_q_heads=64, n_kv_heads=8, max_seq=16384, merge="launch"), True),  # 8 rows x 16
+    (dict(batch=8, q_len=4, n_q_heads=32, n_kv_heads=4, max_seq=8192, merge="launch"), False),  # 32 rows
+    (dict(batch=1, n_q_heads=64, n_kv_heads=8, max_seq=512, merge="launch"), True),   # 8 chunks at most
+    (dict(batch=1, n_q_heads=64, n_kv_heads=2, max_seq=65536, merge="launch"), False),  # 32 rows x 16
+    (dict(batch=4, q_len=2, n_q_heads=16, n_kv_heads=2, head_dim=256, max_seq=8192, merge="launch"), True),
+    (dict(batch=4, q_len=4, n_q_heads=16, n_kv_heads=2, head_dim=256, max_seq=8192, merge="launch"), False),
+    # forced out of the launch
+    (dict(batch=32, n_q_heads=16, n_kv_heads=8, max_seq=8192, merge="separate"), False),
+    (dict(batch=16, n_q_heads=64, n_kv_heads=8, max_seq=1024, merge="separate"), False),
 ])
 def test_plan_fused_merge(shape, fused):
-    """The one-launch step merges inside the attention launch only when every
-    (sequence, KV head) has few chunk-rows, whatever the seq_pos values."""
+    """The one-launch step merges inside the attention launch when it is allowed to
+    (automatically: the vector-ALU kernel, or the MFMA kernels with at least 128
+    (sequence, KV head) pairs) and every (sequence, KV head) has few chunk-rows,
+    whatever the seq_pos values."""
     pl = da.plan_attention(P(**shape))
     assert pl["fused_combine"] == fused
     units = shape["batch"] * shape.get("n_kv_heads", 8)

@@ -128,15 +128,17 @@ def test_d256_contract_breaking_seq_pos(S, path):
     gu.compare_out(out[good], ref)
 
 
-@pytest.mark.parametrize("q_len,S,fused", [(1, 512, True), (1, 4096, True), (4, 4096, False)])
-def test_d256_decode_loop(q_len, S, fused):
+@pytest.mark.parametrize("q_len,S,merge,fused", [(1, 512, "launch", True), (1, 4096, "launch", True),
+                                                 (1, 4096, None, False), (4, 4096, "launch", False)])
+def test_d256_decode_loop(q_len, S, merge, fused):
     """Consecutive steps through one workspace with fresh q, gate and new rows; the
-    merge inside the attention launch, or (32 rows x 16 chunks) the separate one."""
+    merge inside the attention launch (forced), or the separate one (automatic for
+    4 heads, and the only one for 32 rows x 16 chunks)."""
     B, Hq, Hkv = 2, 16, 2
     sp = np.asarray([S - 4 * q_len - 2, S // 3], np.int32)
     inp = gu.make_case(B, q_len, Hq, Hkv, S, sp, torch.float16, seed=S, head_dim=256, gate=True)
     freqs = rope_freqs(64, 1.0e7, "cuda")
-    p = _problem(inp, freqs, 64)
+    p = _problem(inp, freqs, 64, merge=merge)
     assert da.plan_attention(p)["fused_combine"] == fused
     ws = da.new_workspace(p)
     gen = torch.Generator(device="cpu").manual_seed(S)

@@ -19,20 +19,21 @@ def _say(*a):
     print("[case]", *a, flush=True)
 
 
-@pytest.mark.parametrize("B,q_len,Hq,Hkv,S,seq_pos,variant", [
-    (2, 1, 16, 8, 700, [699, 345], None),                  # vector ALU, merge in the launch
+@pytest.mark.parametrize("B,q_len,Hq,Hkv,S,seq_pos,variant,merge", [
+    (2, 1, 16, 8, 700, [699, 345], None, None),            # vector ALU, merge in the launch
     # 8-wave vector-ALU workgroups (128 units, 2 rows): K slabs are claimed by
     # whichever wave is free, and the results must still repeat bit for bit
-    (16, 1, 16, 8, 3000, [2999 - 181 * i for i in range(16)], None),
-    (2, 1, 64, 8, 3000, [2999, 1537], None),               # MFMA, merge in the launch
-    (2, 4, 32, 4, 2100, [2096, 777], None),                # MFMA, 32 rows, causal, separate merge: two launches
-    (2, 2, 32, 4, 900, [898, 250], "valu"),                # forced 16-row VALU: three launches
+    (16, 1, 16, 8, 3000, [2999 - 181 * i for i in range(16)], None, None),
+    (2, 1, 64, 8, 3000, [2999, 1537], None, "launch"),     # MFMA, merge in the launch
+    (2, 1, 64, 8, 3000, [2999, 1537], None, None),         # MFMA, separate merge: two launches
+    (2, 4, 32, 4, 2100, [2096, 777], None, None),          # MFMA, 32 rows, causal, separate merge
+    (2, 2, 32, 4, 900, [898, 250], "valu", None),          # forced 16-row VALU: three launches
 ])
-def test_graph_replays_match_eager(B, q_len, Hq, Hkv, S, seq_pos, variant):
+def test_graph_replays_match_eager(B, q_len, Hq, Hkv, S, seq_pos, variant, merge):
     layers = 3
-    _say("graph", B, q_len, Hq, Hkv, S, seq_pos, variant)
+    _say("graph", B, q_len, Hq, Hkv, S, seq_pos, variant, merge)
     cases = [gu.make_case(B, q_len, Hq, Hkv, S, seq_pos, seed=100 + l) for l in range(layers)]
-    p = da.problem_for(cases[0]["q"], cases[0]["k_cache"], variant=variant)
+    p = da.problem_for(cases[0]["q"], cases[0]["k_cache"], variant=variant, merge=merge)
     ws = da.new_workspace(p)
 
     # eager reference on copies

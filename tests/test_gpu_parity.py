@@ -308,18 +308,20 @@ def test_kernel_reads_caller_data():
 
 # ------------------------------------------------------------------ the one-launch step
 
-@pytest.mark.parametrize("B,q_len,Hq,Hkv,S,sp0,fused", [
-    (3, 1, 16, 8, 3000, [2990, 100, 1500], True),      # vector ALU, merge in the launch
-    (1, 1, 64, 8, 512, [500], True),                   # MFMA, 8 rows, merge in the launch
-    (4, 1, 64, 8, 16384, [15000, 12288, 16380, 13000], True),   # MFMA, 8 rows x 16 chunks merged in the launch
-    (2, 4, 32, 4, 2100, [2000, 60], False),            # MFMA, 32 rows, separate merge
-    (2, 4, 8, 8, 700, [600, 61], True),                # vector ALU, 4 draft tokens
+@pytest.mark.parametrize("B,q_len,Hq,Hkv,S,sp0,merge,fused", [
+    (3, 1, 16, 8, 3000, [2990, 100, 1500], None, True),       # vector ALU, merge in the launch
+    (1, 1, 64, 8, 512, [500], "launch", True),                # MFMA, 8 rows, merge in the launch
+    (4, 1, 64, 8, 16384, [15000, 12288, 16380, 13000], "launch", True),  # MFMA, 8 rows x 16 chunks
+    (4, 1, 64, 8, 16384, [15000, 12288, 16380, 13000], None, False),     # the same, separate merge
+    (16, 1, 64, 8, 1024, [1000, 10, 600, 1023] * 4, None, True),         # MFMA, 128 heads: in the launch
+    (2, 4, 32, 4, 2100, [2000, 60], "launch", False),         # MFMA, 32 rows, separate merge
+    (2, 4, 8, 8, 700, [600, 61], None, True),                 # vector ALU, 4 draft tokens
 ])
-def test_decode_loop_reuses_workspace(B, q_len, Hq, Hkv, S, sp0, fused):
+def test_decode_loop_reuses_workspace(B, q_len, Hq, Hkv, S, sp0, merge, fused):
     """Consecutive steps through one workspace (its arrival counters must return to
     zero after every step), the cache growing by q_len per step and fresh q / new
     rows each step, checked against the oracle step by step."""
-    p = da.problem(B, q_len, Hq, Hkv, 128, S, "bf16")
+    p = da.problem(B, q_len, Hq, Hkv, 128, S, "bf16", merge=merge)
     assert da.plan_attention(p)["fused_combine"] == fused
     inp = gu.make_case(B, q_len, Hq, Hkv, S, sp0, seed=S + B)
     ws = da.new_workspace(p)

@@ -3,7 +3,9 @@
 the same launch.  A step captured into a HIP graph is replayed 1000 times; the
 merge order is fixed, so every replay must reproduce the first one bit for bit
 (outputs and whole caches), and the test stops at the first replay that does
-not.  A stale partial read by a merge would show up as a changed output."""
+not.  A stale partial read by a merge would show up as a changed output.  The two
+matrix-core workloads force the merge into the launch (with 32 heads their automatic
+plan merges in a separate combine launch)."""
 import pytest
 import torch
 
@@ -21,7 +23,7 @@ def _case(name):
         w = WORKLOADS[name]
         L = make_layer(w, 0, torch.device("cuda"))
         return L, da.problem(w.batch, w.q_len, w.n_q_heads, w.n_kv_heads, w.head_dim, w.max_seq, w.dtype,
-                             out_gate=L.get("out_gate"))
+                             out_gate=L.get("out_gate"), merge="launch")
     # a 4-wave vector-ALU shape merged in the launch: batch 1, 16 MHA heads, 4k context
     L = gu.make_case(1, 1, 16, 16, 4096, [4095], dtype=torch.float16, seed=5)
     return L, da.problem_for(L["q"], L["k_cache"])

@@ -1,8 +1,8 @@
 """The allocation-free step, da_decode_step_static, called through the C ABI
 against da_decode_step on the same inputs: the caches bit for bit, the outputs
 bit for bit (same kernels, same chunking), and the outputs within the oracle's
-tolerance.  Two calls in a row on one GPU, the second with a smaller problem,
-so the second starts from the scratch the first left behind."""
+tolerance.  Calls in a row on one GPU, each with a smaller problem than the one
+before, so each starts from the scratch the previous call left behind."""
 import numpy as np
 import pytest
 import torch
@@ -14,16 +14,18 @@ from tests.oracle_pins import bits
 
 pytestmark = pytest.mark.gpu
 
-# (B, q_len, Hq, Hkv, max_seq, seq_pos, dtype): the matrix-core kernel with the
-# merge in the launch (several chunks per head), then a smaller vector-ALU case.
+# (B, q_len, Hq, Hkv, max_seq, seq_pos, dtype, merge): the matrix-core kernel with
+# the merge forced into the launch (several chunks per head), the same kernel with
+# its automatic separate combine launch, then a smaller vector-ALU case.
 CASES = [
-    (4, 1, 64, 8, 6000, [5999, 4100, 3000, 5500], torch.bfloat16),
-    (1, 2, 16, 8, 700, [640], torch.float16),
+    (4, 1, 64, 8, 6000, [5999, 4100, 3000, 5500], torch.bfloat16, "launch"),
+    (2, 1, 64, 8, 3000, [2999, 1537], torch.bfloat16, None),
+    (1, 2, 16, 8, 700, [640], torch.float16, None),
 ]
 
 
 def _case(c, seed):
-    B, q_len, Hq, Hkv, S, sp, dt = c
+    B, q_len, Hq, Hkv, S, sp, dt, _ = c
     return gu.make_case(B, q_len, Hq, Hkv, S, sp, dtype=dt, seed=seed)
 
 
@@ -36,7 +38,7 @@ def test_static_step_matches_workspace_step_twice():
         print(f"[no-alloc] call {n}: B, q_len, Hq, Hkv, max_seq, seq_pos = {c[:6]}", flush=True)
         inp = _case(c, seed=900 + n)
         ref_inp, st_inp = _clone(inp), _clone(inp)
-        p = da.problem_for(inp["q"], inp["k_cache"])
+        p = da.problem_for(inp["q"], inp["k_cache"], merge=c[7])
         out_ws = gu.run_step(p, ref_inp)
         out_st = torch.empty_like(out_ws)
         da.decode_step_static(p, st_inp["q"], st_inp["k_cache"], st_inp["v_cache"], st_inp["k_new"],
@@ -59,7 +61,7 @@ def test_static_step_repeats_bit_for_bit():
     c = CASES[0]
     print(f"[no-alloc] repeat: {c[:6]}", flush=True)
     inp = _case(c, seed=77)
-    p = da.problem_for(inp["q"], inp["k_cache"])
+    p = da.problem_for(inp["q"], inp["k_cache"], merge=c[7])
     outs = []
     for _ in range(3):
         out = torch.empty_like(inp["q"])
