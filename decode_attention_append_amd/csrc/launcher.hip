@@ -190,11 +190,20 @@ void plan_of(const da_problem *p, da_plan *pl) {
         const int max_chunk = max_chunk_of(variant, rows, valu_waves_of(variant, rows, units));
         pl->balanced = 1;
         pl->chunk_tokens = max_chunk;
-        // slots for the most chunks a sequence can get; max_seq <= 2048 * max_chunk
-        // keeps ceil(ctx / max_chunk) within them, so no chunk exceeds max_chunk
-        const int slots = (p->max_seq + kMinChunk - 1) / kMinChunk;
-        pl->n_chunks = slots < kMaxChunks ? slots : kMaxChunks;
         pl->target_items = p->work_items > 0 ? p->work_items : default_target(variant, valu_waves_of(variant, rows, units));
+        // slots for the most chunks a sequence can get, whatever the seq_pos
+        // values: round(ctx / T) with T >= Hkv * (all visible keys) / target
+        // (a sequence holds at most all of them) is at most ceil(target / Hkv),
+        // unless T is clamped to max_chunk, where a sequence gets
+        // ceil(ctx / max_chunk); never more than one per 64 keys.  max_seq <=
+        // 2048 * max_chunk keeps ceil(ctx / max_chunk) within them, so no chunk
+        // exceeds max_chunk.
+        const int64_t per_seq_target = ((int64_t)pl->target_items + p->n_kv_heads - 1) / p->n_kv_heads;
+        const int64_t per_seq_long = (p->max_seq + max_chunk - 1) / max_chunk;
+        int64_t slots = per_seq_target > per_seq_long ? per_seq_target : per_seq_long;
+        const int64_t by_min = (p->max_seq + kMinChunk - 1) / kMinChunk;
+        if (slots > by_min) slots = by_min;
+        pl->n_chunks = (int32_t)(slots < kMaxChunks ? slots : kMaxChunks);
         // at most target + one rounding chunk per (sequence, head), or every
         // sequence in chunks of max_chunk keys when the target is too few
         const int64_t a = (int64_t)pl->target_items + units;

@@ -265,10 +265,13 @@ da_status da_decode_step(const da_problem *p, const void *q, void *k_cache, void
  * the process ends (its device address is looked up once per device, and its
  * counters zeroed then, on `stream`).  Nothing here allocates.
  *  - A problem whose partials and counters do not fit returns
- *    DA_ERR_SCRATCH_LIMIT before anything is enqueued: with the fused merge
- *    that takes B * Hkv * min(16, max_seq / 64) * rows * (head_dim + 2) * 4
- *    bytes, plus 1 MiB for the counters (at most 262144 sequence x KV head
- *    pairs); without it, the full da_workspace_bytes.
+ *    DA_ERR_SCRATCH_LIMIT before anything is enqueued: with the merge inside
+ *    the attention launch (plan.fused_combine) that takes
+ *    B * Hkv * min(16, max_seq / 64) * rows * (head_dim + 2) * 4 bytes, plus
+ *    1 MiB for the counters (at most 262144 sequence x KV head pairs); without
+ *    it, the full da_workspace_bytes.  A problem too large for the latter may
+ *    still fit with p->merge = 1 (the merge in the launch, where the plan
+ *    allows it).
  *  - Every call on one GPU shares that GPU's scratch, which keeps the last
  *    call's partials: calls that overlap on one GPU (other streams, other
  *    threads) race and give wrong results.  Order them on one stream.

@@ -32,7 +32,7 @@ def check_layout(p, seq_pos):
     return plan, lay, total
 
 
-@pytest.mark.parametrize("seed", range(40))
+@pytest.mark.parametrize("seed", range(300))
 def test_random_layouts(seed):
     rng = np.random.default_rng(seed)
     B = int(rng.integers(1, 40))
@@ -61,6 +61,29 @@ def test_random_layouts(seed):
     else:  # all full
         sp = np.full(B, S - q_len)
     check_layout(p, sp.astype(np.int32))
+
+
+@pytest.mark.parametrize("B,Hkv,S,work_items", [
+    (1, 1, 65536, 0), (1, 1, 65536, 5000), (1, 8, 16384, 0), (3, 2, 8192, 37), (1, 4, 100000, 0),
+    (2, 1, 1 << 21, 0),
+])
+def test_slots_bound_is_reached_not_exceeded(B, Hkv, S, work_items):
+    """The workspace's chunk slots per (sequence, KV head) are the most chunks one
+    sequence can get (ceil(target / Hkv), or ceil(S / longest chunk)): a single
+    sequence among empty ones, at the context where chunks are the shortest, comes
+    within a chunk of them, and no layout exceeds them."""
+    p = da.problem(B, 1, 2 * Hkv, Hkv, 128, S, "bf16", work_items=work_items)
+    plan = da.plan_attention(p)
+    best = 0
+    for ctx in (S, S - 1, S - 17, S // 2 + 31, 64 * plan["target_items"] // Hkv,
+                64 * plan["target_items"] // Hkv - 40):
+        if not 1 <= ctx <= S:
+            continue
+        sp = np.zeros(B, np.int32)
+        sp[0] = ctx - 1
+        _, lay, _ = check_layout(p, sp)
+        best = max(best, lay[0][0])
+    assert plan["n_chunks"] - 1 <= best <= plan["n_chunks"]
 
 
 def test_contract_breaking_positions_get_no_chunks():
