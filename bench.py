@@ -293,7 +293,10 @@ class Bench:
                 self.step()
             self.launch_stream[0] = self.stream
             torch.cuda.synchronize()
-            graph.replay()
+            # the first replays after the capture run a few percent slow (clocks and
+            # caches settling): W more untimed replays before the timed ones
+            for _ in range(max(1, warmup)):
+                graph.replay()
             torch.cuda.synchronize()
             ms_total = timed(lambda k: graph.replay())
             replay_ms = list(step_ms)

@@ -134,7 +134,7 @@ struct AttnParams {
     int32_t seq_chunk_cap; // balanced: at most this many chunks per sequence unless its
                            //   length needs more of max_chunk keys (0: no cap)
     int32_t valu_waves;    // waves per workgroup of the vector-ALU kernel: 4 or 8
-    int32_t chunk_align;   // balanced: a sequence whose chunks would be at least half
+    int32_t chunk_align;   // balanced: a sequence whose chunks would be at least 3/4
                            //   this long gets lengths rounded up to a multiple of it
                            //   (a multiple of 32; 32: no effect)
 
@@ -233,7 +233,7 @@ __host__ __device__ inline SeqChunks seq_chunks_at(const AttnParams &p, int sp, 
         n = min(max(n, 1), p.n_chunks);
         const int raw = round_up32(ceil_small(ctx, n));
         const int a = p.chunk_align;
-        len = a > 32 && 2 * raw >= a ? ceil_small(raw, a) * a : raw;
+        len = a > 32 && 4 * raw >= 3 * a ? ceil_small(raw, a) * a : raw;
         len = min(len, p.max_chunk);  // raw <= max_chunk: no chunk is shorter than raw
     }
     // rounding the length up may leave the last chunk empty: n from the length

@@ -106,8 +106,10 @@ constexpr int kMinChunk = 64;
 
 // Balanced chunk lengths on the head_dim-128 MFMA kernel are rounded up to whole
 // multiples of 512 KiB of K (and V) rows, 2048 keys, when a chunk would be at
-// least half that long, so chunks start on 512 KiB boundaries of a (sequence,
-// KV head) stream.  Measured with the attention launch alone on the GQA-8
+// least three quarters that long, so chunks start on 512 KiB boundaries of a
+// (sequence, KV head) stream.  (From half that long, chunks of 1024-1535 keys
+// grew by up to twice and halved the workgroups: batch-1 MHA at 16k, 1024-key
+// chunks, took 38.7 us a layer rounded against 27.7 us not.)  Measured with the attention launch alone on the GQA-8
 // long-context workload (contexts 12k-16k): 47.8-48.2 us against 50.1-50.6 us
 // with 32-key rounding (256 KiB: 47.5-48.2 us, but it lengthens the 4-token
 // verify's chunks and costs it 24%).  On the head_dim-256 kernel the same
@@ -121,12 +123,31 @@ int chunk_align_of(int variant, int head_dim) {
     return kMfma128ChunkAlignBytes / (head_dim * 2);
 }
 
-// Rows per KV head from which the matrix-core kernel is used.  Below 8 rows the
+// Rows per KV head from which the matrix-core kernel is used (and for fewer
+// rows, see auto_variant).  Below 8 rows the
 // vector-ALU kernel is memory-bound (its dot products cost about 4 wave
 // instructions per key and row); at 8 rows it needs some 34 wave instructions
 // per key and becomes ALU-bound near 40% of HBM bandwidth, while the MFMA
 // kernel streams at over 60%.
 constexpr int kMfmaRows = 8;
+
+// The automatic kernel.  The matrix-core kernel from kMfmaRows rows and for
+// head_dim 256.  Below that, with fewer than 128 (sequence, KV head) pairs and a
+// cache of at least 1024 slots, the matrix-core kernel as well: its 32-key
+// tiles carry K and V together and two of them stay in flight per wave (64 KiB
+// per wave against the vector-ALU kernel's 8 KiB, whose K and V passes each
+// wait for their own round trips), which is what a step with few heads is
+// short of.  Steps by graph replay, per layer, vector ALU / matrix cores:
+// batch-1 MHA 16 heads at 4k 14.9 / 13.9 us, at 1k 12.0 / 11.6 us, at 16k
+// 28.9 / 28.6 us; batch 1, 16:8, 32k 44.5 / 39.3 us; batch 8, 16:8, 2k 22.8 /
+// 20.2 us; batch 2, 32:8, 8k 24.6 / 20.8 us.  At 512 slots (batch 1, 16:8) the
+// vector-ALU kernel stays ahead (20.3 / 20.9 us), and from 128 pairs its 8-wave
+// workgroups with one chunk per head are (batch 4, MHA 32 heads, 4k: 46.2 /
+// 48.3 us).
+int auto_variant(const da_problem *p, int rows, int units) {
+    if (rows >= kMfmaRows || p->head_dim != kHeadDim) return DA_VARIANT_MFMA;
+    return units < 128 && p->max_seq >= 1024 ? DA_VARIANT_MFMA : DA_VARIANT_VALU;
+}
 
 // Most chunk-rows (chunks x query rows) one (sequence, KV head) may have for
 // the one-launch step to merge them inside the attention launch, where the
@@ -167,17 +188,21 @@ bool one_launch_capable(int variant, int rows) { return variant == DA_VARIANT_MF
 // stays in the launch (batch-1 MHA at 4k: 14.9 / 15.1 us a layer; the
 // 512-context layer 20.2 / 21.5 us).
 constexpr int kMfmaMergeMinUnits = 128;
+// ... or when the partials are at most 4 rows wide (the matrix-core kernel on
+// few-head steps, above): batch-1 MHA at 4k 13.9 against 15.0 us a layer,
+// batch 1, 16:8 at 32k 39.5 / 40.5 us, batch 8, 16:8 at 2k 20.25 / 20.9 us.
+constexpr int kMfmaMergeMaxRows = 4;
 
 bool merge_in_launch(const da_problem *p, int variant, int units) {
     if (p->merge == 2) return false;
-    return p->merge == 1 || variant == DA_VARIANT_VALU || units >= kMfmaMergeMinUnits;
+    const int rows = (p->n_q_heads / p->n_kv_heads) * p->q_len;
+    return p->merge == 1 || variant == DA_VARIANT_VALU || units >= kMfmaMergeMinUnits || rows <= kMfmaMergeMaxRows;
 }
 
 void plan_of(const da_problem *p, da_plan *pl) {
     const int rows = (p->n_q_heads / p->n_kv_heads) * p->q_len;
-    const int variant = p->variant ? p->variant - 1
-                                   : (rows >= kMfmaRows || p->head_dim != kHeadDim ? DA_VARIANT_MFMA : DA_VARIANT_VALU);
     const int units = p->batch * p->n_kv_heads;
+    const int variant = p->variant ? p->variant - 1 : auto_variant(p, rows, units);
     pl->rows = rows;
     pl->variant = variant;
     if (p->chunk_tokens) {  // fixed chunks

@@ -111,7 +111,7 @@ def test_fixed_chunks_match_override():
 
 
 def test_mfma128_chunks_start_on_512k_boundaries():
-    """On the head_dim-128 MFMA kernel a balanced chunk that would be at least 1024 keys
+    """On the head_dim-128 MFMA kernel a balanced chunk that would be at least 1536 keys
     long is rounded up to a multiple of 2048 keys (512 KiB of K or V rows), so every
     chunk of such a sequence starts on a 512 KiB boundary of its stream; shorter chunks
     keep 32-key rounding, and head_dim 256 is not rounded."""
@@ -131,8 +131,13 @@ def test_mfma128_chunks_start_on_512k_boundaries():
     sp = rng.integers(6143, 8192, 16).astype(np.int32)
     _, lay, _ = check_layout(p, sp)
     assert any(ln % 1024 for _, ln in lay)
+    # chunks of 1024-1535 keys are not rounded (it would halve the workgroups)
+    p = da.problem(1, 1, 16, 16, 128, 16384, "fp16")
+    assert da.plan_attention(p)["variant"] == "mfma"
+    _, lay, _ = check_layout(p, np.array([16383], np.int32))
+    assert lay == [(16, 1024)]
     # the vector-ALU kernel is unaffected
-    p = da.problem(4, 1, 16, 8, 128, 16384, "bf16")
+    p = da.problem(4, 1, 16, 8, 128, 16384, "bf16", variant="valu")
     sp = rng.integers(12287, 16384, 4).astype(np.int32)
     _, lay, _ = check_layout(p, sp)
     assert any(ln % 2048 for _, ln in lay)

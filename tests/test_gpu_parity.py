@@ -242,10 +242,14 @@ def test_custom_scale():
 def test_variant_choice():
     assert da.plan_attention(da.problem(8, 4, 32, 4, 128, 8192, "bf16"))["variant"] == "mfma"
     assert da.plan_attention(da.problem(4, 1, 64, 8, 128, 16384, "bf16"))["variant"] == "mfma"
-    assert da.plan_attention(da.problem(4, 1, 32, 8, 128, 16384, "bf16"))["variant"] == "valu"
     assert da.plan_attention(da.problem(1, 2, 8, 1, 128, 64, "bf16"))["variant"] == "mfma"
     assert da.plan_attention(da.problem(1, 1, 15, 1, 128, 64, "bf16"))["variant"] == "mfma"
     assert da.plan_attention(da.problem(1, 1, 7, 1, 128, 64, "bf16"))["variant"] == "valu"
+    # under 8 rows: matrix cores for fewer than 128 heads with at least 1024 slots
+    assert da.plan_attention(da.problem(4, 1, 32, 8, 128, 16384, "bf16"))["variant"] == "mfma"
+    assert da.plan_attention(da.problem(1, 1, 16, 16, 128, 4096, "fp16"))["variant"] == "mfma"
+    assert da.plan_attention(da.problem(1, 1, 16, 8, 128, 512, "bf16"))["variant"] == "valu"
+    assert da.plan_attention(da.problem(16, 1, 16, 8, 128, 4096, "bf16"))["variant"] == "valu"
 
 
 def test_errors_launch_nothing():
@@ -309,7 +313,8 @@ def test_kernel_reads_caller_data():
 # ------------------------------------------------------------------ the one-launch step
 
 @pytest.mark.parametrize("B,q_len,Hq,Hkv,S,sp0,merge,fused", [
-    (3, 1, 16, 8, 3000, [2990, 100, 1500], None, True),       # vector ALU, merge in the launch
+    (3, 1, 16, 8, 3000, [2990, 100, 1500], None, True),       # MFMA (few heads), 2 rows: merge in the launch
+    (3, 1, 16, 8, 1000, [990, 100, 500], None, True),         # vector ALU, merge in the launch
     (1, 1, 64, 8, 512, [500], "launch", True),                # MFMA, 8 rows, merge in the launch
     (4, 1, 64, 8, 16384, [15000, 12288, 16380, 13000], "launch", True),  # MFMA, 8 rows x 16 chunks
     (4, 1, 64, 8, 16384, [15000, 12288, 16380, 13000], None, False),     # the same, separate merge
