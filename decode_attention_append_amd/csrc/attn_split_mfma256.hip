@@ -491,7 +491,7 @@ void attn_split_mfma256_kernel(const int32_t *__restrict__ seq_pos, int32_t batc
         wait_mem();       // this wave's partial stores are complete
         __syncthreads();  // and so are the other waves'
         if (tid == 0)
-            s_last = __hip_atomic_fetch_add(&p.counters[bh], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            s_last = __hip_atomic_fetch_add(&p.counters[bh * kCounterStride], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                      sc.n - 1;
         __syncthreads();
         if (s_last) {
@@ -500,7 +500,7 @@ void attn_split_mfma256_kernel(const int32_t *__restrict__ seq_pos, int32_t batc
             } else {
                 for (int r = wave; r < p.rows; r += kWaves) merge_row_wave<F16, kD>(p, p.out, bh, b, h, r, sc.n, lane);
             }
-            if (tid == 0) p.counters[bh] = 0;
+            if (tid == 0) p.counters[bh * kCounterStride] = 0;
         }
     }
 }

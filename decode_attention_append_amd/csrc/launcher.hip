@@ -251,10 +251,11 @@ void plan_of(const da_problem *p, da_plan *pl) {
     const int32_t bh = units;
     pl->workspace_bytes = align256(ws_acc_floats(bh, pl->n_chunks, rows, p->head_dim) * sizeof(float)) +
                           align256(ws_ml_floats(bh, pl->n_chunks, rows) * sizeof(float)) +
-                          (size_t)bh * sizeof(int32_t);
+                          (size_t)bh * kCounterStride * sizeof(int32_t);
 }
 
-// Arrival counters of the one-launch step: int32 [B * Hkv] after the partials.
+// Arrival counters of the one-launch step: int32 [B * Hkv] at kCounterStride,
+// after the partials.
 int32_t *counters_of(const da_problem *p, const da_plan &pl, void *workspace) {
     const int32_t bh = p->batch * p->n_kv_heads;
     return (int32_t *)((uint8_t *)workspace +
@@ -390,7 +391,7 @@ da_status decode_step_on(const da_problem *p, const da_plan &pl, const void *q, 
 // from hipGetSymbolAddress, once per device, with that device current, and the
 // counters are zeroed then, on the caller's stream, ahead of the step's kernels.
 constexpr size_t kScratchBytes = (size_t)32 << 20;
-constexpr size_t kScratchCounterBytes = (size_t)1 << 20;  // int32 counters of up to 262144 (sequence, KV head) pairs
+constexpr size_t kScratchCounterBytes = (size_t)1 << 20;  // counters of up to 8192 (sequence, KV head) pairs
 static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 constexpr int kMaxDevices = 64;
@@ -510,7 +511,7 @@ da_status da_workspace_init(const da_problem *p, void *workspace, size_t workspa
     plan_of(p, &pl);
     if (workspace_bytes < pl.workspace_bytes) return DA_ERR_WORKSPACE;
     (void)hipGetLastError();
-    return launch_fill_zero(counters_of(p, pl, workspace), p->batch * p->n_kv_heads, (hipStream_t)stream) ==
+    return launch_fill_zero(counters_of(p, pl, workspace), p->batch * p->n_kv_heads * kCounterStride, (hipStream_t)stream) ==
                    hipSuccess
                ? DA_OK
                : DA_ERR_HIP;
@@ -546,7 +547,7 @@ da_status da_decode_step_static(const da_problem *p, const void *q, void *k_cach
     const int32_t slots = pl.fused_combine ? fused_slots(p, pl) : pl.n_chunks;
     const size_t acc_bytes = align256(ws_acc_floats(bh, slots, pl.rows, p->head_dim) * sizeof(float));
     const size_t ml_bytes = align256(ws_ml_floats(bh, slots, pl.rows) * sizeof(float));
-    if ((size_t)bh * sizeof(int32_t) > kScratchCounterBytes ||
+    if ((size_t)bh * kCounterStride * sizeof(int32_t) > kScratchCounterBytes ||
         kScratchCounterBytes + acc_bytes + ml_bytes > kScratchBytes)
         return DA_ERR_SCRATCH_LIMIT;
     hipStream_t s = (hipStream_t)stream;

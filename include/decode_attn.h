@@ -216,9 +216,10 @@ da_status da_gqa_decode_attn_combine(const da_problem *p, const void *workspace,
 
 /*
  * Prepares a workspace for da_decode_step: zeroes its arrival counters (one
- * int32 per sequence and KV head, after the partials), on `stream`, with a
- * kernel (no memset).  Call once after allocating the workspace, before its
- * first da_decode_step; every da_decode_step leaves the counters at zero again.
+ * int32 per sequence and KV head, 128 bytes apart, after the partials), on
+ * `stream`, with a kernel (no memset).  Call once after allocating the
+ * workspace, before its first da_decode_step; every da_decode_step leaves the
+ * counters at zero again.
  * The three separate entry points neither need nor touch them.
  */
 da_status da_workspace_init(const da_problem *p, void *workspace, size_t workspace_bytes, void *stream);
@@ -268,7 +269,8 @@ da_status da_decode_step(const da_problem *p, const void *q, void *k_cache, void
  *    DA_ERR_SCRATCH_LIMIT before anything is enqueued: with the merge inside
  *    the attention launch (plan.fused_combine) that takes
  *    B * Hkv * min(16, max_seq / 64) * rows * (head_dim + 2) * 4 bytes, plus
- *    1 MiB for the counters (at most 262144 sequence x KV head pairs); without
+ *    1 MiB for the counters (128 bytes each, so at most 8192 sequence x KV
+ *    head pairs); without
  *    it, the full da_workspace_bytes.  A problem too large for the latter may
  *    still fit with p->merge = 1 (the merge in the launch, where the plan
  *    allows it).

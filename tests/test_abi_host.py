@@ -154,6 +154,10 @@ def test_static_step_rejects_before_launch():
     unfused = P(batch=8, q_len=4, n_q_heads=32, n_kv_heads=4, max_seq=8192)
     assert not da.plan_attention(unfused)["fused_combine"]
     assert da.lib.da_decode_step_static(ctypes.byref(unfused), *args, good, None) == da.DA_ERR_SCRATCH_LIMIT
+    # partials that fit, but more than 8192 (sequence, KV head) arrival counters of 128 bytes
+    many = P(batch=1024, n_q_heads=16, n_kv_heads=16, max_seq=128)
+    assert da.plan_attention(many)["fused_combine"]
+    assert da.lib.da_decode_step_static(ctypes.byref(many), *args, good, None) == da.DA_ERR_SCRATCH_LIMIT
     assert "scratch" in da.status_str(da.DA_ERR_SCRATCH_LIMIT)
 
 
@@ -187,10 +191,10 @@ def test_plan_fused_merge(shape, fused):
     pl = da.plan_attention(P(**shape))
     assert pl["fused_combine"] == fused
     units = shape["batch"] * shape.get("n_kv_heads", 8)
-    # the counters sit after the partials
+    # the counters, one 128-byte line each, sit after the partials
     rows = pl["rows"]
     D = shape.get("head_dim", 128)
-    assert pl["workspace_bytes"] >= units * pl["n_chunks"] * rows * (D + 2) * 4 + units * 4
+    assert pl["workspace_bytes"] >= units * pl["n_chunks"] * rows * (D + 2) * 4 + units * 128
 
 
 def test_plan_head_dim_256():
