@@ -491,8 +491,8 @@ void attn_split_mfma256_kernel(const int32_t *__restrict__ seq_pos, int32_t batc
         wait_mem();       // this wave's partial stores are complete
         __syncthreads();  // and so are the other waves'
         if (tid == 0)
-            s_last = __hip_atomic_fetch_add(&p.counters[bh * kCounterStride], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                     sc.n - 1;
+            s_last = __hip_atomic_fetch_add(&p.counters[bh * kCounterStride], 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT) == sc.n - 1;
         __syncthreads();
         if (s_last) {
             if (sc.n <= 16) {

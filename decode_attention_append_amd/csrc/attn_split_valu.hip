@@ -479,8 +479,8 @@ __global__ __launch_bounds__(64 * NW) void attn_split_valu_kernel(const int32_t 
         wait_mem();       // this wave's partial stores are complete
         __syncthreads();  // and so are the other waves'
         if (tid == 0)
-            s_last = __hip_atomic_fetch_add(&p.counters[bh * kCounterStride], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                     sc.n - 1;
+            s_last = __hip_atomic_fetch_add(&p.counters[bh * kCounterStride], 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT) == sc.n - 1;
         __syncthreads();
         if (s_last) {
             merge_rows_block<F16, NW>(p, lds, bh, b, h, sc.n, tid);

@@ -147,7 +147,7 @@ struct AttnParams {
     uint8_t *v_cache_w;
     const uint8_t *k_new;      // [B][q_len][Hkv][D]: the chunk holding a sequence's new
     const uint8_t *v_new;      //   positions reads them from here and appends them
-    int32_t *counters;         // [B*Hkv] chunk arrivals for the fused combine (0 between calls)
+    int32_t *counters;         // [B*Hkv] chunk arrivals, kCounterStride apart, for the fused combine (0 between calls)
     uint16_t *out;             // output written by the fused combine
 };
 

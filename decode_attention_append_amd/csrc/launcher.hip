@@ -64,6 +64,8 @@ da_status check_problem(const da_problem *p) {
     if ((int64_t)p->batch * p->n_kv_heads * ((p->max_seq + kTokenTile - 1) / kTokenTile) > INT32_MAX / 2)
         return DA_ERR_UNSUPPORTED;
     if ((int64_t)p->batch * p->q_len * p->n_q_heads * 16 > INT32_MAX / 2) return DA_ERR_UNSUPPORTED;
+    // and so do the arrival counters' int32 offsets (B * Hkv <= 2^25)
+    if ((int64_t)p->batch * p->n_kv_heads * kCounterStride > INT32_MAX / 2) return DA_ERR_UNSUPPORTED;
     return DA_OK;
 }
 
@@ -511,7 +513,8 @@ da_status da_workspace_init(const da_problem *p, void *workspace, size_t workspa
     plan_of(p, &pl);
     if (workspace_bytes < pl.workspace_bytes) return DA_ERR_WORKSPACE;
     (void)hipGetLastError();
-    return launch_fill_zero(counters_of(p, pl, workspace), p->batch * p->n_kv_heads * kCounterStride, (hipStream_t)stream) ==
+    const int n_words = p->batch * p->n_kv_heads * kCounterStride;
+    return launch_fill_zero(counters_of(p, pl, workspace), n_words, (hipStream_t)stream) ==
                    hipSuccess
                ? DA_OK
                : DA_ERR_HIP;

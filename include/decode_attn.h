@@ -74,7 +74,7 @@ typedef enum { DA_BF16 = 0, DA_FP16 = 1 } da_dtype;
 
 /* Shape of one decode step.  Plain data, read only during the call. */
 typedef struct {
-    int32_t batch;        /* B >= 1                                               */
+    int32_t batch;        /* B >= 1, B * Hkv < 2^25                               */
     int32_t q_len;        /* new tokens per sequence this step, 1..8 (verify batches) */
     int32_t n_q_heads;    /* Hq >= 1                                              */
     int32_t n_kv_heads;   /* Hkv >= 1, Hq % Hkv == 0, (Hq / Hkv) * q_len <= 32    */

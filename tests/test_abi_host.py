@@ -56,6 +56,7 @@ def P(**kw):
     (dict(chunk_tokens=100), da.DA_ERR_INVALID_ARG),
     (dict(chunk_tokens=4096), da.DA_ERR_INVALID_ARG),
     (dict(q_len=8, max_seq=4), da.DA_ERR_INVALID_ARG),
+    (dict(batch=1 << 19, n_q_heads=64, n_kv_heads=64, max_seq=64), da.DA_ERR_UNSUPPORTED),  # B * Hkv = 2^25
 ])
 def test_plan_rejects(kw, status):
     p = P(**kw) if "dtype" not in kw or isinstance(kw["dtype"], str) else None
@@ -65,6 +66,14 @@ def test_plan_rejects(kw, status):
     pl = da.Plan()
     assert da.lib.da_plan_attention(ctypes.byref(p), ctypes.byref(pl)) == status
     assert da.workspace_bytes(p) == 0
+
+
+def test_plan_takes_the_largest_head_count():
+    """B * Hkv just below 2^25 plans (the arrival counters' int32 offsets still fit)."""
+    p = P(batch=(1 << 19) - 1, n_q_heads=64, n_kv_heads=64, max_seq=64)
+    pl = da.Plan()
+    assert da.lib.da_plan_attention(ctypes.byref(p), ctypes.byref(pl)) == da.DA_OK
+    assert pl.workspace_bytes >= ((1 << 19) - 1) * 64 * 128
 
 
 def test_plan_rejects_unknown_merge():
