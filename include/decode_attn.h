@@ -135,8 +135,11 @@ typedef struct {
                              combine launch (a tuning and testing override).
                              Automatic merges inside the launch on the vector-ALU
                              kernel, and on the MFMA kernels only with at least
-                             128 (sequence, KV head) pairs, when each has at most
-                             two chunks.  Other values: DA_ERR_INVALID_ARG.       */
+                             128 (sequence, KV head) pairs or at most 4 rows per
+                             KV head; in every case only when no (sequence, KV
+                             head) can have more than 256 chunk-rows (chunks x
+                             rows; 512 on the vector-ALU kernel).  Other values:
+                             DA_ERR_INVALID_ARG.                                  */
 } da_problem;
 
 /*
@@ -172,8 +175,10 @@ enum { DA_VARIANT_VALU = 0, DA_VARIANT_MFMA = 1 };
  * Plans the attention of *p: chunking, kernel variant, workspace size.  The
  * automatic variant is the MFMA kernel when rows >= 8 (Q K^T and P V are then
  * small matrix products, and on the vector ALU they would cost more issue
- * slots than streaming the keys from HBM) and always for head_dim 256, the
- * vector-ALU kernel otherwise.
+ * slots than streaming the keys from HBM), always for head_dim 256, and for
+ * fewer than 128 (sequence, KV head) pairs with max_seq >= 1024 (its single
+ * pass over a chunk has fewer dependent round trips than the vector-ALU
+ * kernel's two); the vector-ALU kernel otherwise.
  * Returns DA_OK, DA_ERR_INVALID_ARG or DA_ERR_UNSUPPORTED.  Host only.
  */
 da_status da_plan_attention(const da_problem *p, da_plan *plan);
