@@ -1,5 +1,5 @@
-// Split-context attention partials on the vector ALU, for problems whose
-// query rows per KV head (Hq/Hkv * q_len) are fewer than 16.
+// Split-context attention partials on the vector ALU, for problems with at
+// most 16 query rows per KV head (Hq/Hkv * q_len; chosen automatically below 8).
 //
 // What is computed ("Qwen MoE BringUp", Per-Layer IR Patterns, "Attention
 // Computation", split as in the split-KV phase of the 3-phase flash decode in

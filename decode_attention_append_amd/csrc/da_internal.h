@@ -15,7 +15,7 @@ constexpr int kMaxHeadDim = 256;  // the MFMA kernel also takes 256
 constexpr int kMaxRows = 32;      // (Hq/Hkv) * q_len limit
 constexpr int kMaxQLen = 8;
 constexpr int kTokenTile = 64;    // chunk sizes are multiples of this
-constexpr int kMaxChunk = 2048;
+constexpr int kMaxChunk = 2048;  // longest fixed chunk (chunk_tokens); balanced chunks go up to 4096 / 8192
 // int32s between two (sequence, KV head) arrival counters of the one-launch step:
 // one 128-byte line each, so the arrivals of different heads do not contend for
 // one line (batch-1 MHA at 4k, 16 chunks per head: 14.15 -> 13.6 us a layer).
