@@ -111,10 +111,10 @@ constexpr int kMinChunk = 64;
 // least three quarters that long, so chunks start on 512 KiB boundaries of a
 // (sequence, KV head) stream.  (From half that long, chunks of 1024-1535 keys
 // grew by up to twice and halved the workgroups: batch-1 MHA at 16k, 1024-key
-// chunks, took 38.7 us a layer rounded against 27.7 us not.)  Measured with the attention launch alone on the GQA-8
-// long-context workload (contexts 12k-16k): 47.8-48.2 us against 50.1-50.6 us
-// with 32-key rounding (256 KiB: 47.5-48.2 us, but it lengthens the 4-token
-// verify's chunks and costs it 24%).  On the head_dim-256 kernel the same
+// chunks, took 38.7 us a layer rounded against 27.7 us not.)  Measured with the
+// attention launch alone on the GQA-8 long-context workload (contexts 12k-16k):
+// 47.8-48.2 us against 50.1-50.6 us with 32-key rounding (256 KiB: 47.5-48.2
+// us, but it lengthens the 4-token verify's chunks and costs it 24%).  On the head_dim-256 kernel the same
 // rounding slows the one-launch step by 1.6%, so there chunks keep 32-key
 // rounding; the vector-ALU kernel's chunks are already whole 2048-key runs on
 // full-length batches.
@@ -136,7 +136,7 @@ constexpr int kMfmaRows = 8;
 // The automatic kernel.  The matrix-core kernel from kMfmaRows rows and for
 // head_dim 256.  Below that, with fewer than 128 (sequence, KV head) pairs and a
 // cache of at least 1024 slots, the matrix-core kernel as well: its 32-key
-// tiles carry K and V together and two of them stay in flight per wave (64 KiB
+// tiles carry K and V together and two of them stay in flight per wave (32 KiB
 // per wave against the vector-ALU kernel's 8 KiB, whose K and V passes each
 // wait for their own round trips), which is what a step with few heads is
 // short of.  Steps by graph replay, per layer, vector ALU / matrix cores:
