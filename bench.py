@@ -67,7 +67,7 @@ def parse():
     ap.add_argument("--configs", choices=["all", "none"], default=None,
                     help="also measure every other workload of the suite (default: all for the default "
                          "workload, none when --workload is given)")
-    ap.add_argument("--config-steps", type=int, default=20, help="timed steps per extra workload")
+    ap.add_argument("--config-steps", type=int, default=100, help="timed steps per extra workload")
     ap.add_argument("--config-record", action="store_true",
                     help="print only the per-workload record that the default run collects under "
                          "\"configs\" (what the default run starts once per workload, in a process of its own)")
