@@ -1,0 +1,111 @@
+"""Seeded random problems through every path of the step, against the oracle.
+
+Each case draws its shape and features together, so that combinations the
+fixed-shape tests do not list get run too: batch 1-5, 1-8 KV heads, 1-16 query
+heads per KV head, q_len 1-8 (at most 32 rows), head_dim 128 or 256, bf16 or
+fp16, contiguous caches or page pools of up to 3000 slots (a tenth of the cases
+8192-20000 slots over 4 or 8 KV heads, long enough for the longest chunks and
+their alignment), positions at the first slot, the last one or anywhere
+between, the rotary embedding over 64, 128 or 256 dims, the output gate, the
+kernel forced or automatic, fixed or balanced chunks and the merge in the
+launch, separate or automatic.  Every case runs the
+three separate calls, da_decode_step as planned, and da_decode_step with the
+merge forced into the launch where that changes the launches, and checks the
+caches bit for bit (rotated K rows within one ulp) and the output elementwise
+within 1e-2 + 1e-2 |oracle|.
+"""
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_append_amd as da
+from decode_attention_append_amd.workloads import rope_freqs
+from tests import gpu_util as gu
+from tests.test_gpu_paged import make_paged
+
+N_CASES = 128
+
+
+def spec(i: int) -> dict:
+    """The i-th case: a valid problem (the host planning test checks that it plans)."""
+    rng = np.random.default_rng(7000 + i)
+    while True:
+        D = int(rng.choice([128, 256], p=[0.7, 0.3]))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.choice([1, 2, 4, 8, 16]))
+        q_len = int(rng.choice([1, 1, 1, 2, 3, 4, 8]))
+        if G * q_len <= 32:
+            break
+    rows = G * q_len
+    B = int(rng.integers(1, 6))
+    long_ctx = bool(rng.random() < 0.1)  # chunks long enough for the 2048-key alignment
+    paged = bool(rng.random() < 0.3)
+    if long_ctx:
+        B, Hkv = int(rng.integers(1, 5)), int(rng.choice([4, 8]))
+        G = min(G, 32 // q_len, 8)
+        rows = G * q_len
+    if paged:
+        pps = int(rng.integers(512, 1251)) if long_ctx else int(rng.integers(1, 120))
+        S = 16 * pps
+    else:
+        pps = 0
+        S = int(rng.integers(8192, 20001)) if long_ctx else int(rng.integers(q_len, 3001))
+    if S < q_len:  # one page shorter than a verify batch
+        pps, S = 1, 16
+    sp = []
+    for _ in range(B):
+        u = rng.random()
+        sp.append(0 if u < 0.15 else S - q_len if u < 0.3 else int(rng.integers(0, S - q_len + 1)))
+    variant = None
+    u = rng.random()
+    if u < 0.15 and D == 128 and rows <= 16:
+        variant = "valu"
+    elif u < 0.3:
+        variant = "mfma"
+    rope_dim, theta = None, 0.0
+    if rng.random() < 0.3 and not (variant == "valu" and rows > 8):
+        rope_dim = int(rng.choice([w for w in (64, 128, 256) if w <= D]))
+        theta = float(rng.choice([1.0e4, 1.0e6, 1.0e7]))
+    gate = bool(rng.random() < 0.3)
+    chunk = 0 if rng.random() < 0.8 else 64 * int(rng.integers(1, 17))
+    merge = [None, None, None, "launch", "separate"][int(rng.integers(0, 5))]
+    dtype = "bf16" if rng.random() < 0.5 else "fp16"
+    return dict(B=B, q_len=q_len, Hq=G * Hkv, Hkv=Hkv, D=D, S=S, pps=pps, seq_pos=sp, dtype=dtype,
+                variant=variant, rope_dim=rope_dim, theta=theta, gate=gate, chunk=chunk, merge=merge,
+                seed=100 + i)
+
+
+def test_random_cases_plan():
+    """Host only: every case is a problem the library plans (no GPU needed)."""
+    for i in range(N_CASES):
+        s = spec(i)
+        p = da.problem(s["B"], s["q_len"], s["Hq"], s["Hkv"], s["D"], s["S"], s["dtype"],
+                       chunk_tokens=s["chunk"], variant=s["variant"], merge=s["merge"])
+        if s["rope_dim"]:
+            p.rope_freqs, p.rope_dim = 0x1000, s["rope_dim"]
+        if s["gate"]:
+            p.out_gate = 0x2000
+        if s["pps"]:
+            p.page_size, p.pages_per_seq, p.n_pages, p.block_table = 16, s["pps"], s["B"] * s["pps"] + 5, 0x3000
+        pl = da.plan_attention(p)
+        assert pl["rows"] == s["Hq"] // s["Hkv"] * s["q_len"], s
+        assert max(s["seq_pos"]) + s["q_len"] <= s["S"] and min(s["seq_pos"]) >= 0, s
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_problem(i):
+    s = spec(i)
+    print("[case] random", i, s, flush=True)
+    dt = torch.bfloat16 if s["dtype"] == "bf16" else torch.float16
+    if s["pps"]:
+        inp = make_paged(s["B"], s["q_len"], s["Hq"], s["Hkv"], s["pps"], s["seq_pos"], dt, seed=s["seed"],
+                         head_dim=s["D"], gate=s["gate"])
+    else:
+        inp = gu.make_case(s["B"], s["q_len"], s["Hq"], s["Hkv"], s["S"], s["seq_pos"], dt, seed=s["seed"],
+                           head_dim=s["D"], gate=s["gate"])
+    freqs = rope_freqs(s["rope_dim"], s["theta"], "cuda") if s["rope_dim"] else None
+    p = da.problem_for(inp["q"], inp["k_cache"], chunk_tokens=s["chunk"], variant=s["variant"],
+                       rope_freqs=freqs, block_table=inp.get("block_table"), rope_dim=s["rope_dim"] or 0,
+                       out_gate=inp.get("out_gate"), merge=s["merge"])
+    gu.check_full(p, inp, freqs=freqs)
