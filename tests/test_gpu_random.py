@@ -92,11 +92,8 @@ def test_random_cases_plan():
         assert max(s["seq_pos"]) + s["q_len"] <= s["S"] and min(s["seq_pos"]) >= 0, s
 
 
-@pytest.mark.gpu
-@pytest.mark.parametrize("i", range(N_CASES))
-def test_random_problem(i):
-    s = spec(i)
-    print("[case] random", i, s, flush=True)
+def case_inputs(s: dict):
+    """(device inputs, rotary table or None, problem) of case ``s``."""
     dt = torch.bfloat16 if s["dtype"] == "bf16" else torch.float16
     if s["pps"]:
         inp = make_paged(s["B"], s["q_len"], s["Hq"], s["Hkv"], s["pps"], s["seq_pos"], dt, seed=s["seed"],
@@ -108,4 +105,13 @@ def test_random_problem(i):
     p = da.problem_for(inp["q"], inp["k_cache"], chunk_tokens=s["chunk"], variant=s["variant"],
                        rope_freqs=freqs, block_table=inp.get("block_table"), rope_dim=s["rope_dim"] or 0,
                        out_gate=inp.get("out_gate"), merge=s["merge"])
+    return inp, freqs, p
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_problem(i):
+    s = spec(i)
+    print("[case] random", i, s, flush=True)
+    inp, freqs, p = case_inputs(s)
     gu.check_full(p, inp, freqs=freqs)

@@ -3,6 +3,8 @@ against da_decode_step on the same inputs: the caches bit for bit, the outputs
 bit for bit (same kernels, same chunking), and the outputs within the oracle's
 tolerance.  Calls in a row on one GPU, each with a smaller problem than the one
 before, so each starts from the scratch the previous call left behind."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -31,6 +33,11 @@ def _case(c, seed):
 
 def _clone(inp):
     return {k: v.clone() for k, v in inp.items()}
+
+
+def _same_bits(a, b):
+    """Equal bit patterns (page pools hold NaN in their unused pages)."""
+    return torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
 def test_static_step_matches_workspace_step_twice():
@@ -71,3 +78,37 @@ def test_static_step_repeats_bit_for_bit():
     torch.cuda.synchronize()
     for o in outs[1:]:
         assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+
+
+def test_static_step_random_problems_in_a_row():
+    """The random problems of the parity sweep, one after another through
+    da_decode_step_static (each call starting from the scratch the one before left
+    behind), against da_decode_step on the same inputs bit for bit; a problem whose
+    partials do not fit the scratch is refused before anything is enqueued, with the
+    caches untouched."""
+    from tests.test_gpu_random import N_CASES, case_inputs, spec
+    ran = 0
+    for i in range(N_CASES):
+        s = spec(i)
+        print(f"[no-alloc] random case {i}: {s}", flush=True)
+        inp, _, p = case_inputs(s)
+        ref_inp, st_inp = _clone(inp), _clone(inp)
+        out_st = torch.empty_like(inp["q"])
+        status = da.lib.da_decode_step_static(
+            ctypes.byref(p), st_inp["q"].data_ptr(), st_inp["k_cache"].data_ptr(), st_inp["v_cache"].data_ptr(),
+            st_inp["k_new"].data_ptr(), st_inp["v_new"].data_ptr(),
+            ctypes.cast(st_inp["seq_pos"].data_ptr(), ctypes.POINTER(ctypes.c_int32)), out_st.data_ptr(),
+            torch.cuda.current_stream().cuda_stream)
+        if status == da.DA_ERR_SCRATCH_LIMIT:
+            torch.cuda.synchronize()
+            assert _same_bits(st_inp["k_cache"], inp["k_cache"]) and _same_bits(st_inp["v_cache"], inp["v_cache"])
+            continue
+        assert status == da.DA_OK, da.status_str(status)
+        out_ws = gu.run_step(p, ref_inp)
+        torch.cuda.synchronize()
+        assert _same_bits(st_inp["k_cache"], ref_inp["k_cache"]), f"case {i}: k caches differ"
+        assert _same_bits(st_inp["v_cache"], ref_inp["v_cache"]), f"case {i}: v caches differ"
+        assert _same_bits(out_st, out_ws), f"case {i}: outputs differ"
+        ran += 1
+    print(f"[no-alloc] {ran} of {N_CASES} random cases fit the scratch", flush=True)
+    assert ran >= N_CASES // 2, f"only {ran} of {N_CASES} cases fit the scratch"
