@@ -115,3 +115,25 @@ def test_random_problem(i):
     print("[case] random", i, s, flush=True)
     inp, freqs, p = case_inputs(s)
     gu.check_full(p, inp, freqs=freqs)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(0, N_CASES, 4))
+def test_random_decode_loop(i):
+    """Every fourth case as a decode loop: four da_decode_step calls through one
+    workspace, positions advancing by q_len, fresh q, new rows and gate each step,
+    each step checked against the oracle from the caches the step before left."""
+    s = spec(i)
+    inp, freqs, p = case_inputs(s)
+    ws = da.new_workspace(p)
+    gen = torch.Generator(device="cpu").manual_seed(s["seed"])
+    sp = np.asarray(s["seq_pos"], dtype=np.int32)
+    for it in range(4):
+        if it:
+            sp = np.minimum(sp + s["q_len"], s["S"] - s["q_len"]).astype(np.int32)
+            for k in ("q", "k_new", "v_new", "out_gate"):
+                if k in inp:
+                    inp[k].copy_(torch.randn(inp[k].shape, generator=gen).to(inp[k].dtype))
+            inp["seq_pos"].copy_(torch.as_tensor(sp))
+        print("[case] random loop", i, "step", it, sp.tolist(), flush=True)
+        gu.check_full(p, inp, freqs=freqs, paths=("step",), ws=ws)
