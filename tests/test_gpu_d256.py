@@ -3,7 +3,8 @@ heads over 2 KV heads of 256 dims, rotary embedding on the first 64 dims, sigmoi
 output gate) and of the partial rotary width and the gate on head_dim 128.
 
 Every case runs through the three separate calls and the one-launch
-da_decode_step.  Caches bit for bit (rotated K rows within one ulp), outputs
+da_decode_step.  Caches bit for bit (rotated K rows within one ulp plus the fp32
+evaluation slack of gpu_util.check_rotated_k), outputs
 |gpu - oracle| <= 1e-2 + 1e-2 |oracle| elementwise.
 """
 import numpy as np

@@ -4,7 +4,8 @@ The pools follow the paged-attention layout [pages][KV heads][16 tokens][D];
 each sequence's pages are scattered over the pool by a random permutation, and
 the pool's unused pages hold NaN/inf so a read through a wrong page shows up.
 Whole pools must match the oracle's paged append bit for bit (rotated K rows
-within one ulp when a rotary table is given), outputs within
+within one ulp plus the fp32 evaluation slack when a rotary table is given),
+outputs within
 |d| <= 1e-2 + 1e-2 |ref| of the oracle's attention over the gathered caches.
 """
 import numpy as np
@@ -54,7 +55,7 @@ def check_paged(p, inp, path, freqs=None, rows=None):
     bt = inp["block_table"].cpu().numpy()
     sp = inp["seq_pos"].cpu().numpy()
     kp0, vp0 = bits(inp["k_cache"]), bits(inp["v_cache"])
-    kn = bits(inp["k_new"])
+    kn = kn_raw = bits(inp["k_new"])
     qb = bits(inp["q"])
     if freqs is not None:
         fr = freqs.cpu().numpy()
@@ -66,15 +67,11 @@ def check_paged(p, inp, path, freqs=None, rows=None):
     torch.cuda.synchronize()
     assert np.array_equal(bits(inp["v_cache"]), vp_ref), "v pool differs from the oracle's paged append"
     kg = bits(inp["k_cache"])
-    d = kg != kp_ref
     if freqs is None:
-        assert not d.any(), "k pool differs from the oracle's paged append"
-    elif d.any():
-        a, r = gu.oracle.decode(kg[d], dt), gu.oracle.decode(kp_ref[d], dt)
-        mbits = 10 if dt == gu.oracle.FP16 else 7
-        ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(r), 2.0 ** -14))) - mbits)
-        assert (np.abs(a - r) <= ulp).all(), "rotated K more than one ulp off"
-        assert d.mean() < 1e-3
+        assert np.array_equal(kg, kp_ref), "k pool differs from the oracle's paged append"
+    else:
+        new = gu.appended_rows(kp_ref.shape, sp, p.q_len, bt)
+        gu.check_rotated_k(kg, kp_ref, new, kn_raw, sp, p.q_len, 2 * freqs.numel(), dt, bt, "paged")
     kc, vc = gu.oracle.gather_paged(kp_ref, bt), gu.oracle.gather_paged(vp_ref, bt)
     if rows is None:
         ref = gu.oracle.gqa_decode(qb, kc, vc, sp, dt)
