@@ -2,7 +2,8 @@
 
 Each case draws its shape and features together, so that combinations the
 fixed-shape tests do not list get run too: batch 1-5, 1-8 KV heads, 1-16 query
-heads per KV head, q_len 1-8 (at most 32 rows), head_dim 128 or 256, bf16 or
+heads per KV head (a sixth of the cases 16-40 sequences over 4-16 KV heads, at
+least 128 (sequence, KV head) pairs, caches up to 1500 slots), q_len 1-8 (at most 32 rows), head_dim 128 or 256, bf16 or
 fp16, contiguous caches or page pools of up to 3000 slots (a tenth of the cases
 8192-20000 slots over 4 or 8 KV heads, long enough for the longest chunks and
 their alignment), positions at the first slot, the last one or anywhere
@@ -39,18 +40,26 @@ def spec(i: int) -> dict:
             break
     rows = G * q_len
     B = int(rng.integers(1, 6))
-    long_ctx = bool(rng.random() < 0.1)  # chunks long enough for the 2048-key alignment
+    mode = rng.random()
+    long_ctx = mode < 0.1  # chunks long enough for the 2048-key alignment
+    many = 0.1 <= mode < 0.25  # at least 128 (sequence, KV head) pairs: 8-wave VALU, merge rules
     paged = bool(rng.random() < 0.3)
     if long_ctx:
         B, Hkv = int(rng.integers(1, 5)), int(rng.choice([4, 8]))
         G = min(G, 32 // q_len, 8)
         rows = G * q_len
+    elif many:
+        B, Hkv = int(rng.integers(16, 41)), int(rng.choice([4, 8, 16]))
+        G = min(G, 4)
+        B = max(B, -(-128 // Hkv))
+        rows = G * q_len
+    hi = 1500 if many else 3000
     if paged:
-        pps = int(rng.integers(512, 1251)) if long_ctx else int(rng.integers(1, 120))
+        pps = int(rng.integers(512, 1251)) if long_ctx else int(rng.integers(1, hi // 16 + 1))
         S = 16 * pps
     else:
         pps = 0
-        S = int(rng.integers(8192, 20001)) if long_ctx else int(rng.integers(q_len, 3001))
+        S = int(rng.integers(8192, 20001)) if long_ctx else int(rng.integers(q_len, hi + 1))
     if S < q_len:  # one page shorter than a verify batch
         pps, S = 1, 16
     sp = []
