@@ -8,8 +8,9 @@ fp16, contiguous caches or page pools of up to 3000 slots (a tenth of the cases
 8192-20000 slots over 4 or 8 KV heads, long enough for the longest chunks and
 their alignment), positions at the first slot, the last one or anywhere
 between, the rotary embedding over 64, 128 or 256 dims, the output gate, the
-kernel forced or automatic, fixed or balanced chunks and the merge in the
-launch, separate or automatic.  Every case runs the
+kernel forced or automatic, fixed or balanced chunks, the merge in the launch,
+separate or automatic, inputs of spread 0.25, 1 or 4 (the last a sharp
+softmax, without a rotary table), and a custom softmax scale.  Every case runs the
 three separate calls, da_decode_step as planned, and da_decode_step with the
 merge forced into the launch where that changes the launches, and checks the
 caches bit for bit (rotated K rows within one ulp plus the fp32 evaluation
@@ -80,16 +81,26 @@ def spec(i: int) -> dict:
     chunk = 0 if rng.random() < 0.8 else 64 * int(rng.integers(1, 17))
     merge = [None, None, None, "launch", "separate"][int(rng.integers(0, 5))]
     dtype = "bf16" if rng.random() < 0.5 else "fp16"
+    # inputs N(0, 1) times this (4: scores of spread 16, a sharp softmax); a softmax
+    # scale other than 1/sqrt(head_dim) in a fifth of the cases.  A rotated q or K
+    # element may round either way at a 16-bit boundary (the rotation is an fp32
+    # evaluation); at spread 4 such a last-bit difference moves a score by up to
+    # about 0.2 and a sharp softmax's output past the tolerance, so the sharp cases
+    # run without a rotary table.
+    data = float(rng.choice([1.0, 1.0, 1.0, 4.0, 0.25]))
+    if rope_dim and data > 1.0:
+        data = 1.0
+    scale = float(rng.uniform(0.02, 0.3)) if rng.random() < 0.2 else 0.0
     return dict(B=B, q_len=q_len, Hq=G * Hkv, Hkv=Hkv, D=D, S=S, pps=pps, seq_pos=sp, dtype=dtype,
                 variant=variant, rope_dim=rope_dim, theta=theta, gate=gate, chunk=chunk, merge=merge,
-                seed=100 + i)
+                data=data, scale=scale, seed=100 + i)
 
 
 def test_random_cases_plan():
     """Host only: every case is a problem the library plans (no GPU needed)."""
     for i in range(N_CASES):
         s = spec(i)
-        p = da.problem(s["B"], s["q_len"], s["Hq"], s["Hkv"], s["D"], s["S"], s["dtype"],
+        p = da.problem(s["B"], s["q_len"], s["Hq"], s["Hkv"], s["D"], s["S"], s["dtype"], scale=s["scale"],
                        chunk_tokens=s["chunk"], variant=s["variant"], merge=s["merge"])
         if s["rope_dim"]:
             p.rope_freqs, p.rope_dim = 0x1000, s["rope_dim"]
@@ -107,12 +118,12 @@ def case_inputs(s: dict):
     dt = torch.bfloat16 if s["dtype"] == "bf16" else torch.float16
     if s["pps"]:
         inp = make_paged(s["B"], s["q_len"], s["Hq"], s["Hkv"], s["pps"], s["seq_pos"], dt, seed=s["seed"],
-                         head_dim=s["D"], gate=s["gate"])
+                         scale=s["data"], head_dim=s["D"], gate=s["gate"])
     else:
         inp = gu.make_case(s["B"], s["q_len"], s["Hq"], s["Hkv"], s["S"], s["seq_pos"], dt, seed=s["seed"],
-                           head_dim=s["D"], gate=s["gate"])
+                           scale=s["data"], head_dim=s["D"], gate=s["gate"])
     freqs = rope_freqs(s["rope_dim"], s["theta"], "cuda") if s["rope_dim"] else None
-    p = da.problem_for(inp["q"], inp["k_cache"], chunk_tokens=s["chunk"], variant=s["variant"],
+    p = da.problem_for(inp["q"], inp["k_cache"], scale=s["scale"], chunk_tokens=s["chunk"], variant=s["variant"],
                        rope_freqs=freqs, block_table=inp.get("block_table"), rope_dim=s["rope_dim"] or 0,
                        out_gate=inp.get("out_gate"), merge=s["merge"])
     return inp, freqs, p
