@@ -150,6 +150,8 @@ def rope_slack_rows(new, kn_raw, sp, q_len, R, dt, block_table=None):
     mag[..., half:R] = pm
     src = {}
     for b, s in enumerate(sp):
+        if s < 0 or (block_table is not None and (int(s) + q_len - 1) // 16 >= block_table.shape[1]):
+            continue  # a sequence whose position breaks the contract appends nothing
         for i in range(q_len):
             t = int(s) + i
             src[(b, t) if block_table is None else (int(block_table[b, t // 16]), t % 16)] = (b, i)
@@ -167,6 +169,8 @@ def check_rotated_k(kg, k_ref, new, kn_raw, sp, q_len, R, dt, block_table=None, 
     Returns that fraction."""
     d = kg != k_ref
     assert not d[~new].any(), f"{what}: k cache differs outside the appended rows"
+    if not new.any():  # every sequence broke the contract: nothing was appended
+        return 0.0
     a, r = oracle.decode(kg[new], dt), oracle.decode(k_ref[new], dt)
     slack = rope_slack_rows(new, kn_raw, sp, q_len, R, dt, block_table)
     assert (np.abs(a - r) <= _ulp(r, dt) + slack).all(), f"{what}: rotated K beyond one ulp and the fp32 slack"

@@ -24,6 +24,7 @@ import torch
 import decode_attention_append_amd as da
 from decode_attention_append_amd.workloads import rope_freqs
 from tests import gpu_util as gu
+from tests.oracle_pins import bits
 from tests.test_gpu_paged import make_paged
 
 N_CASES = 128
@@ -158,3 +159,70 @@ def test_random_decode_loop(i):
             inp["seq_pos"].copy_(torch.as_tensor(sp))
         print("[case] random loop", i, "step", it, sp.tolist(), flush=True)
         gu.check_full(p, inp, freqs=freqs, paths=("step",), ws=ws)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(2, N_CASES, 8))
+def test_random_contract_breaking(i):
+    """Every eighth case with about a third of its sequences (at least one) given a
+    position that breaks the contract (negative, or past max_seq - q_len): through the
+    separate calls and da_decode_step, those sequences' cache rows stay untouched and
+    their output rows are NaN, and the others match the oracle run on them alone."""
+    s = spec(i)
+    rng = np.random.default_rng(50000 + i)
+    B, q_len, S = s["B"], s["q_len"], s["S"]
+    bad = sorted(int(b) for b in rng.choice(B, max(1, B // 3), replace=False))
+    sp = list(s["seq_pos"])
+    for b in bad:
+        sp[b] = int(rng.choice([-1, -7, S - q_len + 1, S, S + 1000]))
+    s = dict(s, seq_pos=sp)
+    good = np.asarray([b for b in range(B) if b not in bad], dtype=np.int64)
+    print("[case] random contract", i, "bad", bad, s, flush=True)
+    inp, freqs, p = case_inputs(s)
+    dt = gu.odt(inp["q"].dtype)
+    spa = np.asarray(sp, dtype=np.int32)
+    bt = inp.get("block_table")
+    bt = None if bt is None else bt.cpu().numpy()
+    kc0, vc0 = bits(inp["k_cache"]), bits(inp["v_cache"])
+    kn_all = bits(inp["k_new"])
+    k_ref, v_ref = kc0.copy(), vc0.copy()
+    new = np.zeros(kc0.shape[:3], bool)
+    ref = None
+    if good.size:
+        spg = spa[good]
+        kn, vn, qb = kn_all[good], bits(inp["v_new"])[good], bits(inp["q"])[good]
+        if freqs is not None:
+            fr = freqs.cpu().numpy()
+            pos = spg[:, None, None] + np.arange(q_len, dtype=np.int32)[None, :, None]
+            kn = gu.oracle.rope_rows(kn, np.broadcast_to(pos, kn.shape[:3]), fr, dt)
+            qb = gu.oracle.rope_q(qb, spg, fr, dt)
+        if bt is None:
+            k_ref[good], v_ref[good] = gu.oracle.kv_append(kc0[good], vc0[good], kn, vn, spg)
+            kc, vc = k_ref[good], v_ref[good]
+        else:
+            k_ref, v_ref = gu.oracle.kv_append_paged(kc0, vc0, kn, vn, spg, np.ascontiguousarray(bt[good]))
+            kc = gu.oracle.gather_paged(k_ref, np.ascontiguousarray(bt[good]))
+            vc = gu.oracle.gather_paged(v_ref, np.ascontiguousarray(bt[good]))
+        ref = gu.oracle.gqa_decode(qb, kc, vc, spg, dt, scale=p.scale if p.scale > 0 else None)
+        if "out_gate" in inp:
+            ref = gu.oracle.output_gate(ref, np.ascontiguousarray(bits(inp["out_gate"])[good]), dt)
+        for b in good:
+            for t in range(spa[b], spa[b] + q_len):
+                if bt is None:
+                    new[b, :, t] = True
+                else:
+                    new[bt[b, t // 16], :, t % 16] = True
+    for path in ("separate", "step"):
+        run = dict(inp, k_cache=inp["k_cache"].clone(), v_cache=inp["v_cache"].clone())
+        out = gu.run_step(p, run, path=path)
+        torch.cuda.synchronize()
+        kg = bits(run["k_cache"])
+        assert np.array_equal(bits(run["v_cache"]), v_ref), f"{path}: v cache"
+        if freqs is None:
+            assert np.array_equal(kg, k_ref), f"{path}: k cache"
+        else:
+            gu.check_rotated_k(kg, k_ref, new, kn_all, spa, q_len, 2 * freqs.numel(), dt, bt, path)
+        o = out.float().cpu()
+        assert torch.isnan(o[bad]).all(), f"{path}: rows of contract-breaking sequences are not NaN"
+        if ref is not None:
+            gu.compare_out(out[good.tolist()], ref, f"{path}: the other sequences")
