@@ -226,3 +226,49 @@ def test_random_contract_breaking(i):
         assert torch.isnan(o[bad]).all(), f"{path}: rows of contract-breaking sequences are not NaN"
         if ref is not None:
             gu.compare_out(out[good.tolist()], ref, f"{path}: the other sequences")
+
+
+def _same_bits(a, b):
+    return torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(1, N_CASES, 8))
+def test_random_graph_replays(i):
+    """Every eighth case captured into a HIP graph (one da_decode_step): three
+    replays, with unrelated eager work and synchronisations between them, each
+    reproduce the eager step bit for bit, output and whole caches (a replay appends
+    the same rows at the same positions again)."""
+    s = spec(i)
+    print("[case] random graph", i, s, flush=True)
+    inp, _, p = case_inputs(s)
+    ws = da.new_workspace(p)
+    e = dict(inp, k_cache=inp["k_cache"].clone(), v_cache=inp["v_cache"].clone())
+    ref_out = gu.run_step(p, e, ws=ws)
+    torch.cuda.synchronize()
+    out = torch.empty_like(inp["q"])
+
+    def step():
+        da.decode_step(p, inp["q"], inp["k_cache"], inp["v_cache"], inp["k_new"], inp["v_new"], inp["seq_pos"],
+                       ws, out)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # the first run outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    junk = torch.randn(512, 512, device="cuda")
+    for rep in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert _same_bits(out, ref_out), f"replay {rep}: output differs from the eager step"
+        assert _same_bits(inp["k_cache"], e["k_cache"]) and _same_bits(inp["v_cache"], e["v_cache"]), \
+            f"replay {rep}: caches differ from the eager step"
+        junk = junk @ junk.t() / 512.0
+        torch.cuda.synchronize()
