@@ -392,7 +392,9 @@ da_status decode_step_on(const da_problem *p, const da_plan &pl, const void *q, 
 // (on the host it is only a stand-in for the symbol): the device address comes
 // from hipGetSymbolAddress, once per device, with that device current, and the
 // counters are zeroed then, on the caller's stream, ahead of the step's kernels.
-constexpr size_t kScratchBytes = (size_t)32 << 20;
+// 64 MiB holds every workload of the suite as planned (the largest, a 4-token
+// verify with its separate combine, needs 32.5 MiB).
+constexpr size_t kScratchBytes = (size_t)64 << 20;
 constexpr size_t kScratchCounterBytes = (size_t)1 << 20;  // counters of up to 8192 (sequence, KV head) pairs
 static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 

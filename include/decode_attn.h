@@ -267,7 +267,7 @@ da_status da_decode_step(const da_problem *p, const void *q, void *k_cache, void
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc).  Same arguments, results and launches as da_decode_step
  * minus `workspace`: the partials and the arrival counters live in a scratch
- * array inside the library, 32 MiB on each GPU the library runs on, held until
+ * array inside the library, 64 MiB on each GPU the library runs on, held until
  * the process ends (its device address is looked up once per device, and its
  * counters zeroed then, on `stream`).  Nothing here allocates.
  *  - A problem whose partials and counters do not fit returns
@@ -275,10 +275,9 @@ da_status da_decode_step(const da_problem *p, const void *q, void *k_cache, void
  *    the attention launch (plan.fused_combine) that takes
  *    B * Hkv * min(16, max_seq / 64) * rows * (head_dim + 2) * 4 bytes, plus
  *    1 MiB for the counters (128 bytes each, so at most 8192 sequence x KV
- *    head pairs); without
- *    it, the full da_workspace_bytes.  A problem too large for the latter may
- *    still fit with p->merge = 1 (the merge in the launch, where the plan
- *    allows it).
+ *    head pairs); without it, the full da_workspace_bytes.  A problem too
+ *    large for the latter may still fit with p->merge = 1 (the merge in the
+ *    launch, where the plan allows it).
  *  - Every call on one GPU shares that GPU's scratch, which keeps the last
  *    call's partials: calls that overlap on one GPU (other streams, other
  *    threads) race and give wrong results.  Order them on one stream.

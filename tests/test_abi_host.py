@@ -155,12 +155,12 @@ def test_static_step_rejects_before_launch():
     assert da.lib.da_decode_step_static(ctypes.byref(p), None, *args[1:], good, None) == da.DA_ERR_INVALID_ARG
     assert da.lib.da_decode_step_static(ctypes.byref(p), *args, good + 4, None) == da.DA_ERR_INVALID_ARG
     assert da.lib.da_decode_step_static(ctypes.byref(P(head_dim=64)), *args, good, None) == da.DA_ERR_UNSUPPORTED
-    # fused merge: 512 heads x 16 slots x 8 rows x 130 floats = 34 MB > 31 MiB of partials
-    big = P(batch=64, n_q_heads=64, n_kv_heads=8, max_seq=65536, merge="launch")
+    # fused merge: 1024 heads x 16 slots x 8 rows x 130 floats = 65 MiB > 63 MiB of partials
+    big = P(batch=128, n_q_heads=64, n_kv_heads=8, max_seq=65536, merge="launch")
     assert da.plan_attention(big)["fused_combine"]
     assert da.lib.da_decode_step_static(ctypes.byref(big), *args, good, None) == da.DA_ERR_SCRATCH_LIMIT
     # without the fused merge the whole separate-call workspace is needed
-    unfused = P(batch=8, q_len=4, n_q_heads=32, n_kv_heads=4, max_seq=8192)
+    unfused = P(batch=16, q_len=4, n_q_heads=32, n_kv_heads=4, max_seq=8192)  # 65 MiB
     assert not da.plan_attention(unfused)["fused_combine"]
     assert da.lib.da_decode_step_static(ctypes.byref(unfused), *args, good, None) == da.DA_ERR_SCRATCH_LIMIT
     # partials that fit, but more than 8192 (sequence, KV head) arrival counters of 128 bytes

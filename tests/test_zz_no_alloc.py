@@ -112,3 +112,25 @@ def test_static_step_random_problems_in_a_row():
         ran += 1
     print(f"[no-alloc] {ran} of {N_CASES} random cases fit the scratch", flush=True)
     assert ran >= N_CASES // 2, f"only {ran} of {N_CASES} cases fit the scratch"
+
+
+@pytest.mark.parametrize("name", ["verify4_gqa32x4_b8_pos2048_8188", "qwen35_gqa16x2_d256_gated_b16_ctx8192_10l"])
+def test_static_step_full_size_workloads(name):
+    """The two workloads whose partials take the most scratch (their separate-call
+    workspaces, 32.5 and 32.3 MiB), one full-size layer each (the head_dim-256 one
+    with its rotary table and gate), against da_decode_step bit for bit."""
+    from decode_attention_append_amd.workloads import WORKLOADS, make_layer, rope_freqs
+    w = WORKLOADS[name]
+    print(f"[no-alloc] full size: {name}", flush=True)
+    inp = make_layer(w, 0, "cuda")
+    freqs = rope_freqs(w.rope_dim or w.head_dim, w.rope_theta, "cuda") if w.rope_theta > 0 else None
+    p = da.problem(w.batch, w.q_len, w.n_q_heads, w.n_kv_heads, w.head_dim, w.max_seq, w.dtype,
+                   rope_freqs=freqs, rope_dim=w.rope_dim, out_gate=inp.get("out_gate"))
+    ref_inp, st_inp = _clone(inp), _clone(inp)
+    out_ws = gu.run_step(p, ref_inp)
+    out_st = torch.empty_like(out_ws)
+    da.decode_step_static(p, st_inp["q"], st_inp["k_cache"], st_inp["v_cache"], st_inp["k_new"], st_inp["v_new"],
+                          st_inp["seq_pos"], out_st)
+    torch.cuda.synchronize()
+    assert _same_bits(st_inp["k_cache"], ref_inp["k_cache"]) and _same_bits(st_inp["v_cache"], ref_inp["v_cache"])
+    assert _same_bits(out_st, out_ws), f"{name}: outputs differ"
