@@ -131,11 +131,6 @@ def _integer_draws(w: Workload):
     return seq_pos, km, nm
 
 
-def draw_seq_pos(w: Workload) -> torch.Tensor:
-    """Per-sequence slot of the first new token, int32 [B] on the CPU."""
-    return _integer_draws(w)[0]
-
-
 def make_tensors(batch, q_len, n_q_heads, n_kv_heads, head_dim, max_seq, dtype, seed,
                  device="cpu", value_scale=1.0, gate=False):
     """q, k_cache, v_cache, k_new, v_new drawn N(0,1)*value_scale in ``dtype``; with
