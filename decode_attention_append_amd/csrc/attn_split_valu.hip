@@ -338,18 +338,50 @@ __global__ __launch_bounds__(64 * NW) void attn_split_valu_kernel(const int32_t 
 
     // ---- chunk maximum and weights p = 2^(s - m), sum l ------------------------
     const int n_pad = n_slab * 16;
+    // Both loops over a row's scores take them eight at a time while eight remain,
+    // every LDS read of the eight issued before any is used, so a lane waits for
+    // one LDS round trip per eight scores instead of one per score (the headline
+    // layer's 8192 scores per row: 16 per lane, whose serial reads took about 3 us
+    // between the passes); the rest go one at a time, as a short chunk's single
+    // score does.  The max and the sum keep the order t = t0, t0 + stride, ... of
+    // every lane.
+    constexpr int kBatch = 8;
+    auto row_max = [&](int r, int t0, int stride) {
+        float m = -INFINITY;
+        int tb = t0;
+        for (; tb + (kBatch - 1) * stride < n_pad; tb += kBatch * stride) {
+            float x[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) x[j] = lds[(tb + j * stride) * RP + r];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) m = fmaxf(m, x[j]);
+        }
+        for (; tb < n_pad; tb += stride) m = fmaxf(m, lds[tb * RP + r]);
+        return m;
+    };
+    // p = 2^(s - m) written over the scores, and their sum
+    auto row_exp = [&](int r, int t0, int stride, float m) {
+        float l = 0.f;
+        auto weigh = [&](int t, float x) {
+            const float e = (m == -INFINITY) ? 0.f : exp2_fast(x - m);
+            lds[t * RP + r] = e;
+            l += e;
+        };
+        int tb = t0;
+        for (; tb + (kBatch - 1) * stride < n_pad; tb += kBatch * stride) {
+            float x[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) x[j] = lds[(tb + j * stride) * RP + r];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) weigh(tb + j * stride, x[j]);
+        }
+        for (; tb < n_pad; tb += stride) weigh(tb, lds[tb * RP + r]);
+        return l;
+    };
     if constexpr (NW == 4) {  // a wave per row
         for (int r = wave; r < RP; r += 4) {
-            float m = -INFINITY;
-            for (int t = lane; t < n_pad; t += 64) m = fmaxf(m, lds[t * RP + r]);
-            m = wave_max(m);
-            float l = 0.f;
-            for (int t = lane; t < n_pad; t += 64) {
-                const float e = (m == -INFINITY) ? 0.f : exp2_fast(lds[t * RP + r] - m);
-                lds[t * RP + r] = e;
-                l += e;
-            }
-            l = wave_sum(l);
+            const float m = wave_max(row_max(r, lane, 64));
+            const float l = wave_sum(row_exp(r, lane, 64, m));
             if (lane == 0) {
                 row_m[r] = m;
                 row_l[r] = l;
@@ -359,9 +391,7 @@ __global__ __launch_bounds__(64 * NW) void attn_split_valu_kernel(const int32_t 
         float mr[RP];
 #pragma unroll
         for (int r = 0; r < RP; ++r) {
-            float m = -INFINITY;
-            for (int t = wave * 64 + lane; t < n_pad; t += NW * 64) m = fmaxf(m, lds[t * RP + r]);
-            m = wave_max(m);
+            const float m = wave_max(row_max(r, wave * 64 + lane, NW * 64));
             if (lane == 0) wpart[wave][r] = m;
         }
         __syncthreads();
@@ -375,13 +405,7 @@ __global__ __launch_bounds__(64 * NW) void attn_split_valu_kernel(const int32_t 
         __syncthreads();  // every wave has read the maxima
 #pragma unroll
         for (int r = 0; r < RP; ++r) {
-            float l = 0.f;
-            for (int t = wave * 64 + lane; t < n_pad; t += NW * 64) {
-                const float e = (mr[r] == -INFINITY) ? 0.f : exp2_fast(lds[t * RP + r] - mr[r]);
-                lds[t * RP + r] = e;
-                l += e;
-            }
-            l = wave_sum(l);
+            const float l = wave_sum(row_exp(r, wave * 64 + lane, NW * 64, mr[r]));
             if (lane == 0) wpart[wave][r] = l;
         }
         __syncthreads();
