@@ -12,18 +12,17 @@
 // and (m, l, acc) is written to the workspace.  The combine kernel merges the
 // chunks.  A key j is visible to query token i iff j <= seq_pos + i.
 //
-// Mapping on gfx950: one workgroup per (b, h, chunk), serving every query row
-// of KV head h, so each K/V byte is read once: 4 waves, or 8 (chunks of up to
-// 8192 keys, one workgroup per compute unit) for up to 2 rows per KV head and
-// at least 128 (b, h) pairs.  Sixteen lanes hold
+// Mapping on gfx950: one workgroup of 4 waves per (b, h, chunk), serving every
+// query row of KV head h, so each K/V byte is read once; chunks of up to 2048
+// keys (1024 at 16 rows), or of up to 8192 (one workgroup per compute unit)
+// for up to 2 rows per KV head and at least 128 (b, h) pairs.  Sixteen lanes hold
 // one 256-byte row (16 bytes each): a wave's 128-bit load covers four
 // consecutive keys, 1 KiB contiguous.  Q.K partial dots use the packed
 // dot2 (bf16/fp16 pair -> fp32) instruction, then a 16-lane DPP butterfly.
 // The chunk's scores go to LDS; the chunk is two-pass (all scores, then the
 // maximum, then P.V), so no running rescale is needed inside a chunk.  Each
 // wave streams its 16-key slabs through two register buffers in turn, so the
-// next slab is in flight while the current one is computed; with 8 waves the
-// K pass's slabs after each wave's first are claimed from an LDS counter.
+// next slab is in flight while the current one is computed.
 #include "da_internal.h"
 
 #include <math.h>
@@ -93,17 +92,19 @@ __device__ void merge_rows_block(const AttnParams &p, float *red, int bh, int b,
 // step as three launches and refuses it a rotary table.
 constexpr int kValuOneLaunchRows = 8;
 
+// Waves per workgroup.
+constexpr int kValuWaves = 4;
+
 // ROPE: the problem has a rotary table (a separate instantiation, so that the
 // rotation's registers never weigh on the kernel without one).
-// NW: waves per workgroup, 4 (chunks of up to 2048 keys) or 8 (up to 8192).
-template <bool F16, int RP, bool ROPE, int NW>
-__global__ __launch_bounds__(64 * NW) void attn_split_valu_kernel(const int32_t *__restrict__ seq_pos, int32_t batch, AttnParams p) {
+template <bool F16, int RP, bool ROPE>
+__global__ __launch_bounds__(64 * kValuWaves) void attn_split_valu_kernel(const int32_t *__restrict__ seq_pos, int32_t batch, AttnParams p) {
+    constexpr int NW = kValuWaves;
     const int sp_first = first_seq_pos(seq_pos, batch, threadIdx.x & 63);
     constexpr bool kOneLaunch = RP <= kValuOneLaunchRows;
     static_assert(!ROPE || kOneLaunch, "the rotary embedding is compiled up to 8 rows");
     extern __shared__ float lds[];  // scores [chunk][RP], later the wave sums [NW][RP][128]
     __shared__ float row_m[RP], row_l[RP];
-    __shared__ float wpart[NW > 4 ? NW : 1][RP];  // per-wave maxima, then sums (NW > 4)
 
     const int n_chunks = p.n_chunks;
     int b, h, c;
@@ -127,14 +128,19 @@ __global__ __launch_bounds__(64 * NW) void attn_split_valu_kernel(const int32_t 
     const int cq = lane & 15;  // 16-byte column: dims 8*cq .. 8*cq+7
 
     // Paged caches: the pool page of every 16-token block of the chunk is read
-    // once, one entry per thread (a chunk has at most 64 * NW blocks), issued
-    // before the query loads and kept in LDS.  A block-table load per slab
-    // would be a vector load whose wait also waits for the slabs in flight.
+    // once, at most two entries per thread (a chunk has at most 512 blocks),
+    // issued before the query loads and kept in LDS.  A block-table load per
+    // slab would be a vector load whose wait also waits for the slabs in flight.
     const int lp0 = t0 / kPageTokens;
     const bool paged = p.layout.block_table != nullptr;
-    __shared__ int pg_tab[64 * NW];
-    int pg_mine = 0;  // checked against the pool when stored, after the query loads are issued
-    if (paged && tid < n_slab) pg_mine = p.layout.block_table[(size_t)b * p.layout.pages_per_seq + lp0 + tid];
+    constexpr int kTabPerThread = kValuLongChunk / kPageTokens / (64 * NW);
+    __shared__ int pg_tab[kValuLongChunk / kPageTokens];
+    int pg_mine[kTabPerThread];  // checked against the pool when stored, after the query loads are issued
+#pragma unroll
+    for (int j = 0; j < kTabPerThread; ++j) {
+        const int s_ = tid + j * 64 * NW;
+        pg_mine[j] = paged && s_ < n_slab ? p.layout.block_table[(size_t)b * p.layout.pages_per_seq + lp0 + s_] : 0;
+    }
 
     // Query rows: r = i * group + g is query token i of query head h*group + g.
     uint32_t qr[RP][4];
@@ -169,7 +175,11 @@ __global__ __launch_bounds__(64 * NW) void attn_split_valu_kernel(const int32_t 
     }
 
     if (paged) {
-        if (tid < n_slab) pg_tab[tid] = (unsigned)pg_mine < (unsigned)p.layout.n_pages ? pg_mine : -1;
+#pragma unroll
+        for (int j = 0; j < kTabPerThread; ++j) {
+            const int s_ = tid + j * 64 * NW;
+            if (s_ < n_slab) pg_tab[s_] = (unsigned)pg_mine[j] < (unsigned)p.layout.n_pages ? pg_mine[j] : -1;
+        }
         __syncthreads();
     }
 
@@ -258,49 +268,6 @@ __global__ __launch_bounds__(64 * NW) void attn_split_valu_kernel(const int32_t 
         }
     };
 
-    // With 8 waves, the K pass's fast slabs after each wave's first are
-    // claimed from a workgroup counter in LDS, so waves the memory system
-    // serves faster take more slabs and none idles at the end of the pass
-    // (every score still lands in its own slot: the result does not depend on
-    // which wave took a slab).  The V pass keeps the fixed assignment, whose
-    // per-wave sums are added in a fixed order.
-    __shared__ int k_claim;
-    if constexpr (NW >= 8) {
-        if (tid == 0) k_claim = 0;
-        __syncthreads();
-    }
-    auto claim = [&]() {
-        int r = 0;
-        if (lane == 0) r = atomicAdd(&k_claim, 1);
-        return NW + __builtin_amdgcn_readfirstlane(r);
-    };
-    auto pass_claimed = [&](const uint8_t *base, const uint8_t *nbase, uint8_t *wbase, bool rot, u32x4_t (&b0)[4],
-                            auto &&body) {
-        int i0 = wave < n_fast ? wave : n_fast;
-        if (i0 < n_fast) {
-            u32x4_t b1[4];
-            load_fast(b0, base, i0);
-            int i1 = claim();
-            while (true) {
-                if (i1 < n_fast) load_fast(b1, base, i1);
-                const int i2 = i1 < n_fast ? claim() : n_fast;
-                body(b0, i0);
-                if (i1 >= n_fast) break;
-                if (i2 < n_fast) load_fast(b0, base, i2);
-                const int i3 = i2 < n_fast ? claim() : n_fast;
-                body(b1, i1);
-                if (i2 >= n_fast) break;
-                i0 = i2;
-                i1 = i3;
-            }
-        }
-        for (int s_ = first_slow; s_ < n_slab; s_ += NW) {
-            u32x4_t c0[4];
-            load_rows(c0, base, nbase, wbase, rot, s_);
-            body(c0, s_);
-        }
-    };
-
     // ---- pass 1: scores of the chunk into LDS ----------------------------------
     const uint8_t *knb = fused_append ? p.k_new + new_off : nullptr;
     const uint8_t *vnb = fused_append ? p.v_new + new_off : nullptr;
@@ -327,10 +294,7 @@ __global__ __launch_bounds__(64 * NW) void attn_split_valu_kernel(const int32_t 
             }
         }
     };
-    if constexpr (NW >= 8)
-        pass_claimed(p.k_cache, knb, kwb, fused_append, kb0, score_slab);
-    else
-        pass(p.k_cache, knb, kwb, fused_append, kb0, false, score_slab);
+    pass(p.k_cache, knb, kwb, fused_append, kb0, false, score_slab);
     // The V pass's first slab does not depend on the weights: issue it now, so
     // its latency overlaps the other waves' last K slabs and the softmax.
     if (nf > 0) load_fast(vb0, p.v_cache, wave);
@@ -340,10 +304,10 @@ __global__ __launch_bounds__(64 * NW) void attn_split_valu_kernel(const int32_t 
     const int n_pad = n_slab * 16;
     // Both loops over a row's scores take them eight at a time while eight remain,
     // every LDS read of the eight issued before any is used, so a lane waits for
-    // one LDS round trip per eight scores instead of one per score (the headline
-    // layer's 8192 scores per row: 16 per lane, whose serial reads took about 3 us
-    // between the passes); the rest go one at a time, as a short chunk's single
-    // score does.  The max and the sum keep the order t = t0, t0 + stride, ... of
+    // one LDS round trip per eight scores instead of one per score (a long chunk's
+    // 8192 scores per row are 128 per lane of the row's wave; read one at a time,
+    // 16 per lane over 8 waves took about 3 us between the passes); the rest go
+    // one at a time, as a short chunk's single score does.  The max and the sum keep the order t = t0, t0 + stride, ... of
     // every lane.
     constexpr int kBatch = 8;
     auto row_max = [&](int r, int t0, int stride) {
@@ -378,40 +342,12 @@ __global__ __launch_bounds__(64 * NW) void attn_split_valu_kernel(const int32_t 
         for (; tb < n_pad; tb += stride) weigh(tb, lds[tb * RP + r]);
         return l;
     };
-    if constexpr (NW == 4) {  // a wave per row
-        for (int r = wave; r < RP; r += 4) {
-            const float m = wave_max(row_max(r, lane, 64));
-            const float l = wave_sum(row_exp(r, lane, 64, m));
-            if (lane == 0) {
-                row_m[r] = m;
-                row_l[r] = l;
-            }
-        }
-    } else {  // every wave takes keys wave*64 + lane, + NW*64, ... of every row
-        float mr[RP];
-#pragma unroll
-        for (int r = 0; r < RP; ++r) {
-            const float m = wave_max(row_max(r, wave * 64 + lane, NW * 64));
-            if (lane == 0) wpart[wave][r] = m;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int r = 0; r < RP; ++r) {
-            float m = -INFINITY;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) m = fmaxf(m, wpart[w][r]);
-            mr[r] = m;
-        }
-        __syncthreads();  // every wave has read the maxima
-#pragma unroll
-        for (int r = 0; r < RP; ++r) {
-            const float l = wave_sum(row_exp(r, wave * 64 + lane, NW * 64, mr[r]));
-            if (lane == 0) wpart[wave][r] = l;
-        }
-        __syncthreads();
-        if (tid < RP) {
-            row_m[tid] = mr[tid];
-            row_l[tid] = tree_sum<NW>([&](int w) { return wpart[w][tid]; });
+    for (int r = wave; r < RP; r += NW) {  // a wave per row
+        const float m = wave_max(row_max(r, lane, 64));
+        const float l = wave_sum(row_exp(r, lane, 64, m));
+        if (lane == 0) {
+            row_m[r] = m;
+            row_l[r] = l;
         }
     }
     __syncthreads();
@@ -524,25 +460,18 @@ static size_t lds_bytes_of(const AttnParams &p) {
     return f * sizeof(float);
 }
 
-template <bool F16, int RP, int NW>
-static hipError_t launch_nw(const AttnParams &p, int grid, hipStream_t s) {
-    const size_t lds = lds_bytes_of<RP, NW>(p);
+template <bool F16, int RP>
+static hipError_t launch_rp(const AttnParams &p, int grid, hipStream_t s) {
+    const size_t lds = lds_bytes_of<RP, kValuWaves>(p);
+    const dim3 block(64 * kValuWaves);
     if constexpr (RP <= kValuOneLaunchRows) {
         if (p.rope_freqs) {
-            hipLaunchKernelGGL((attn_split_valu_kernel<F16, RP, true, NW>), dim3(grid), dim3(64 * NW), lds, s, p.seq_pos, p.batch, p);
+            hipLaunchKernelGGL((attn_split_valu_kernel<F16, RP, true>), dim3(grid), block, lds, s, p.seq_pos, p.batch, p);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((attn_split_valu_kernel<F16, RP, false, NW>), dim3(grid), dim3(64 * NW), lds, s, p.seq_pos, p.batch, p);
+    hipLaunchKernelGGL((attn_split_valu_kernel<F16, RP, false>), dim3(grid), block, lds, s, p.seq_pos, p.batch, p);
     return hipGetLastError();
-}
-
-template <bool F16, int RP>
-static hipError_t launch_rp(const AttnParams &p, int grid, hipStream_t s) {
-    if constexpr (RP <= 2) {
-        if (p.valu_waves == 8) return launch_nw<F16, RP, 8>(p, grid, s);
-    }
-    return launch_nw<F16, RP, 4>(p, grid, s);
 }
 
 template <bool F16>

@@ -16,6 +16,7 @@ constexpr int kMaxRows = 32;      // (Hq/Hkv) * q_len limit
 constexpr int kMaxQLen = 8;
 constexpr int kTokenTile = 64;    // chunk sizes are multiples of this
 constexpr int kMaxChunk = 2048;  // longest fixed chunk (chunk_tokens); balanced chunks go up to 4096 / 8192
+constexpr int kValuLongChunk = 8192;  // the vector-ALU kernel's long chunks (at most 2 rows)
 // int32s between two (sequence, KV head) arrival counters of the one-launch step:
 // one 128-byte line each, so the arrivals of different heads do not contend for
 // one line (batch-1 MHA at 4k, 16 chunks per head: 14.15 -> 13.6 us a layer).
@@ -137,7 +138,6 @@ struct AttnParams {
     const uint16_t *out_gate; // [B][q_len][Hq][D] sigmoid output gate, or null
     int32_t seq_chunk_cap; // balanced: at most this many chunks per sequence unless its
                            //   length needs more of max_chunk keys (0: no cap)
-    int32_t valu_waves;    // waves per workgroup of the vector-ALU kernel: 4 or 8
     int32_t chunk_align;   // balanced: a sequence whose chunks would be at least 3/4
                            //   this long gets lengths rounded up to a multiple of it
                            //   (a multiple of 32; 32: no effect)

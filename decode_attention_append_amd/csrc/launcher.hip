@@ -77,29 +77,34 @@ da_status check_problem(const da_problem *p) {
 // separate path): GQA-8 at 12k-16k context 50.0 / 49.7 / 52.1 us and the
 // 4-token verify 27.6 / 28.7 / 34.6 us at 256 / 512 / 1024 chunks; head_dim 256
 // on 16 x 2 KV heads at 8k context 52.8 / 55.3 / 56.2 us.
-// With 8-wave workgroups (below) the vector-ALU kernel also aims at one chunk
-// per compute unit.
-int default_target(int variant, int valu_waves) {
-    return variant == DA_VARIANT_MFMA || valu_waves >= 8 ? 256 : 1024;
+// With long chunks (below) the vector-ALU kernel also aims at one chunk per
+// compute unit.
+int default_target(int variant, bool long_chunks) {
+    return variant == DA_VARIANT_MFMA || long_chunks ? 256 : 1024;
 }
 
-// Waves per workgroup of the vector-ALU kernel.  Up to 2 rows, when there are
-// at least 128 (sequence, KV head) units, an 8-wave workgroup takes chunks of
-// up to 8192 keys: a (sequence, KV head) of up to 8192 keys is one chunk, whose
-// workgroup writes the output itself in the one-launch step: no partials, no
-// arrival and no merge.  Eight waves per compute unit, each with two 16-key
-// slabs in flight, keep 64 KiB of non-temporal loads in flight per unit; with
-// 16 waves (128 KiB) the headline layer (batch 32, 8 KV heads, 8192 keys)
-// measured 161.5 us against 158.2 us (rocprofv3, cold, two interleaved runs).
-int valu_waves_of(int variant, int rows, int units) {
-    return variant == DA_VARIANT_VALU && rows <= 2 && units >= 128 ? 8 : 4;
+// Long chunks on the vector-ALU kernel.  Up to 2 rows, when there are at least
+// 128 (sequence, KV head) units, a workgroup takes chunks of up to
+// kValuLongChunk (8192) keys: a (sequence, KV head) of up to 8192 keys is one
+// chunk, whose workgroup writes the output itself in the one-launch step: no
+// partials, no arrival and no merge.  Its four waves, each with two 16-key
+// slabs in flight, keep 32 KiB of non-temporal loads in flight per compute
+// unit, where a loads-only probe streams best.  Measured against 8-wave
+// workgroups on the same chunks (64 KiB in flight), steps by eager launches:
+// the headline layer (batch 32, 8 KV heads, 8192 keys, 28 layers) 4.28 against
+// 4.40 ms; batch 64 at 4k 1258 / 1268 us for 8 layers, batch 32 MHA at 2k 641
+// / 653 us, batch 16 at 16k 622 / 635 us for 4 layers, batch 4 MHA 32 heads at
+// 4k and batch 32 at ragged 1k-8k contexts equal (two runs each); 16 waves
+// were slower still (161.5 against 158.2 us a headline layer).
+bool valu_long_chunks(int variant, int rows, int units) {
+    return variant == DA_VARIANT_VALU && rows <= 2 && units >= 128;
 }
 
 // Longest chunk a kernel accepts: the vector-ALU kernel keeps the chunk's
 // scores in LDS (rows x chunk floats, at most 64 KiB).
-int max_chunk_of(int variant, int rows, int valu_waves) {
+int max_chunk_of(int variant, int rows, bool long_chunks) {
     if (variant == DA_VARIANT_MFMA) return 4096;
-    if (valu_waves >= 8) return 8192;
+    if (long_chunks) return kValuLongChunk;
     const int rp = rows <= 1 ? 1 : rows <= 2 ? 2 : rows <= 4 ? 4 : rows <= 8 ? 8 : 16;
     return rp <= 8 ? 2048 : 1024;
 }
@@ -143,8 +148,8 @@ constexpr int kMfmaRows = 8;
 // batch-1 MHA 16 heads at 4k 14.9 / 13.9 us, at 1k 12.0 / 11.6 us, at 16k
 // 28.9 / 28.6 us; batch 1, 16:8, 32k 44.5 / 39.3 us; batch 8, 16:8, 2k 22.8 /
 // 20.2 us; batch 2, 32:8, 8k 24.6 / 20.8 us.  At 512 slots (batch 1, 16:8) the
-// vector-ALU kernel stays ahead (20.3 / 20.9 us), and from 128 pairs its 8-wave
-// workgroups with one chunk per head are (batch 4, MHA 32 heads, 4k: 46.2 /
+// vector-ALU kernel stays ahead (20.3 / 20.9 us), and from 128 pairs its long
+// chunks, one per head, are (batch 4, MHA 32 heads, 4k: 46.2 /
 // 48.3 us).
 int auto_variant(const da_problem *p, int rows, int units) {
     if (rows >= kMfmaRows || p->head_dim != kHeadDim) return DA_VARIANT_MFMA;
@@ -214,10 +219,11 @@ void plan_of(const da_problem *p, da_plan *pl) {
         pl->target_items = units * pl->n_chunks;
         pl->items = units * pl->n_chunks;
     } else {
-        const int max_chunk = max_chunk_of(variant, rows, valu_waves_of(variant, rows, units));
+        const bool long_chunks = valu_long_chunks(variant, rows, units);
+        const int max_chunk = max_chunk_of(variant, rows, long_chunks);
         pl->balanced = 1;
         pl->chunk_tokens = max_chunk;
-        pl->target_items = p->work_items > 0 ? p->work_items : default_target(variant, valu_waves_of(variant, rows, units));
+        pl->target_items = p->work_items > 0 ? p->work_items : default_target(variant, long_chunks);
         // slots for the most chunks a sequence can get, whatever the seq_pos
         // values: round(ctx / T) with T >= Hkv * (all visible keys) / target
         // (a sequence holds at most all of them) is at most ceil(target / Hkv),
@@ -315,7 +321,6 @@ AttnParams attn_params(const da_problem *p, const da_plan &pl, const void *q, co
     a.scale_log2 = (float)(scale * 1.4426950408889634);  // log2(e)
     a.seq_chunk_cap = 0;
     a.chunk_align = chunk_align_of(pl.variant, p->head_dim);
-    a.valu_waves = valu_waves_of(pl.variant, pl.rows, p->batch * p->n_kv_heads);
     a.rope_freqs = p->rope_freqs;
     a.rope_dim = p->rope_dim ? p->rope_dim : p->head_dim;
     a.layout = layout_of(p);

@@ -151,10 +151,10 @@ typedef struct {
  * `target_items` chunks in all), never longer than `chunk_tokens` (the plan's
  * maximum) and never shorter than 64 keys.  With an explicit chunk_tokens every
  * chunk has that length.  Either way the attention and the combine derive the
- * same chunks from the same seq_pos.  A chunk is the work of one workgroup:
- * 4 waves, or 8 on the vector-ALU kernel when there are at most 2 rows per KV
- * head and at least 128 (sequence, KV head) pairs (chunks of up to 8192 keys,
- * about 256 of them).
+ * same chunks from the same seq_pos.  A chunk is the work of one workgroup of
+ * 4 waves.  On the vector-ALU kernel, with at most 2 rows per KV head and at
+ * least 128 (sequence, KV head) pairs, chunks go up to 8192 keys (about 256 of
+ * them).
  */
 typedef struct {
     int32_t chunk_tokens;    /* longest chunk (fixed mode: every chunk)          */

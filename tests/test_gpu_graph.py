@@ -21,8 +21,8 @@ def _say(*a):
 
 @pytest.mark.parametrize("B,q_len,Hq,Hkv,S,seq_pos,variant,merge", [
     (2, 1, 16, 8, 700, [699, 345], None, None),            # vector ALU, merge in the launch
-    # 8-wave vector-ALU workgroups (128 units, 2 rows): K slabs are claimed by
-    # whichever wave is free, and the results must still repeat bit for bit
+    # vector-ALU long chunks (128 units, 2 rows): one chunk per sequence or
+    # several, merged in the launch
     (16, 1, 16, 8, 3000, [2999 - 181 * i for i in range(16)], None, None),
     (2, 1, 64, 8, 3000, [2999, 1537], None, "launch"),     # MFMA, merge in the launch
     (2, 1, 64, 8, 3000, [2999, 1537], None, None),         # MFMA, separate merge: two launches

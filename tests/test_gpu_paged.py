@@ -115,13 +115,14 @@ def test_paged_pages_across_chunks(chunk, variant, path):
     (2, 16, 2, 256, 257, [4095, 2600], 4096, 256, None),     # head_dim 256
     (2, 16, 8, 128, 257, [4095, 2600], 4096, 256, None),     # MFMA, 2 rows
     (2, 16, 8, 128, 257, [4095, 2600], 2048, 128, "valu"),   # vector ALU, 4 waves
-    (16, 16, 8, 128, 400, [6300] + [211 * i + 5 for i in range(15)], 6304, 394, None),  # 8 waves
-    (16, 16, 8, 128, 512, [8191] + [211 * i + 5 for i in range(15)], 8192, 512, None),  # 8 waves, one page per thread
+    (16, 16, 8, 128, 400, [6300] + [211 * i + 5 for i in range(15)], 6304, 394, None),  # vector ALU, long chunks
+    (16, 16, 8, 128, 512, [8191] + [211 * i + 5 for i in range(15)], 8192, 512, None),  # vector ALU, two pages per thread
 ])
 def test_paged_long_chunks(B, Hq, Hkv, D, pps, seq_pos, chunk, pages, variant, path):
-    """Chunks of up to one page per thread of the workgroup: each workgroup reads its
-    chunk's page list into LDS once and takes every tile's or slab's page from there.
-    One requested work item gives every sequence its fewest, longest chunks."""
+    """Chunks of up to one page per thread of the workgroup (two on the vector-ALU
+    kernel's long chunks): each workgroup reads its chunk's page list into LDS once and
+    takes every tile's or slab's page from there.  One requested work item gives every
+    sequence its fewest, longest chunks."""
     _say("paged long chunks", B, Hq, Hkv, D, pps, chunk, path)
     inp = make_paged(B, 1, Hq, Hkv, pps, seq_pos, head_dim=D, seed=pps + D)
     p = da.problem_for(inp["q"], inp["k_cache"], block_table=inp["block_table"], work_items=1, variant=variant)

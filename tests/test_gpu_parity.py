@@ -434,21 +434,21 @@ def test_decode_step_errors_launch_nothing():
     assert torch.equal(inp["k_cache"], before_k) and not out.any()
 
 
-# ------------------------------------------------------------------ 8-wave vector-ALU workgroups
+# ------------------------------------------------------------------ vector-ALU long chunks
 
 @pytest.mark.parametrize("B,Hq,Hkv,S,dtype,seed", [
     (16, 16, 8, 3000, torch.bfloat16, 1),     # 2 rows, 128 units, ragged: one chunk or several
     (128, 1, 1, 9000, torch.float16, 2),      # 1 row, 128 units, chunks up to 8192 keys
     (32, 8, 4, 1500, torch.bfloat16, 3),      # 2 rows, 128 units, short contexts
 ])
-def test_valu_8_wave_workgroups(B, Hq, Hkv, S, dtype, seed):
-    """At least 128 (sequence, KV head) units with up to 2 rows take 8-wave workgroups and
-    chunks of up to 8192 keys; in the one-launch step a sequence that is one chunk writes its
+def test_valu_long_chunks(B, Hq, Hkv, S, dtype, seed):
+    """At least 128 (sequence, KV head) units with up to 2 rows take chunks of up to 8192
+    keys (two pages' worth of block-table entries per thread when paged); in the one-launch step a sequence that is one chunk writes its
     output directly, the others merge in the launch."""
     rng = np.random.default_rng(seed)
     sp = rng.integers(0, S, B).astype(np.int32)
     sp[0], sp[-1] = S - 1, 0
-    _say("valu8", B, Hq, Hkv, S, dtype)
+    _say("valu long chunks", B, Hq, Hkv, S, dtype)
     inp = gu.make_case(B, 1, Hq, Hkv, S, sp, dtype, seed=seed)
     p = da.problem_for(inp["q"], inp["k_cache"])
     pl = da.plan_attention(p)
@@ -458,9 +458,9 @@ def test_valu_8_wave_workgroups(B, Hq, Hkv, S, dtype, seed):
     gu.check_layer(p, inp)
 
 
-def test_valu_8_wave_merge_split_over_waves():
+def test_valu_merge_split_over_waves():
     """More than 16 chunks and fewer than 4 rows: the merge splits each row's chunks over the
-    8 waves (fixed 64-key chunks)."""
+    4 waves (fixed 64-key chunks)."""
     sp = [2047, 1500, 900, 64] * 16
     inp = gu.make_case(64, 1, 4, 2, 2048, sp, seed=4)
     p = da.problem_for(inp["q"], inp["k_cache"], chunk_tokens=64)
@@ -469,7 +469,7 @@ def test_valu_8_wave_merge_split_over_waves():
 
 
 @pytest.mark.parametrize("path", gu.PATHS)
-def test_valu_8_wave_rope_and_paged(path):
+def test_valu_long_chunks_rope_and_paged(path):
     from tests.test_gpu_paged import make_paged, check_paged
     from decode_attention_append_amd.workloads import rope_freqs
     freqs = rope_freqs(128, 1.0e6, "cuda")
@@ -479,7 +479,7 @@ def test_valu_8_wave_rope_and_paged(path):
     check_paged(p, inp, path, freqs=freqs)
 
 
-def test_valu_8_wave_decode_loop():
+def test_valu_long_chunks_decode_loop():
     B, S = 32, 2000
     p = da.problem(B, 1, 8, 4, 128, S, "bf16")  # 2 rows, 128 units
     assert da.plan_attention(p)["chunk_tokens"] == 8192
@@ -489,7 +489,7 @@ def test_valu_8_wave_decode_loop():
     k_ref, v_ref = bits(inp["k_cache"]), bits(inp["v_cache"])
     gen = torch.Generator(device="cpu").manual_seed(6)
     for it in range(4):
-        _say("valu8 loop", it)
+        _say("valu long chunks loop", it)
         if it:
             for k in ("q", "k_new", "v_new"):
                 inp[k] = torch.randn(inp[k].shape, generator=gen).to(torch.bfloat16).cuda()

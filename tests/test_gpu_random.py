@@ -44,7 +44,7 @@ def spec(i: int) -> dict:
     B = int(rng.integers(1, 6))
     mode = rng.random()
     long_ctx = mode < 0.1  # chunks long enough for the 2048-key alignment
-    many = 0.1 <= mode < 0.25  # at least 128 (sequence, KV head) pairs: 8-wave VALU, merge rules
+    many = 0.1 <= mode < 0.25  # at least 128 (sequence, KV head) pairs: long VALU chunks, merge rules
     paged = bool(rng.random() < 0.3)
     if long_ctx:
         B, Hkv = int(rng.integers(1, 5)), int(rng.choice([4, 8]))
