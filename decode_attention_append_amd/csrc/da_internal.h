@@ -128,6 +128,8 @@ struct AttnParams {
     int32_t n_chunks;      // chunk slots per (sequence, KV head) in the workspace
     int32_t fixed_chunk;   // > 0: every chunk has this many keys; 0: balanced chunks
     int32_t target_wg;     // balanced: chunks to aim for over the whole launch
+    int32_t alt_target_wg; // balanced: the target for contexts too uneven for target_wg's
+                           //   long chunks (0: none; see balanced_chunk)
     int32_t min_chunk;     // balanced: smallest chunk (multiple of 32)
     int32_t max_chunk;     // largest chunk the kernel accepts (multiple of 32)
     float scale_log2;      // softmax scale * log2(e): scores are kept in log2 units
@@ -157,7 +159,12 @@ struct AttnParams {
 // per chunk, T = ceil32(Hkv * sum_b ctx_b / target_wg) clamped to
 // [min_chunk, max_chunk]; sequence b gets n_b = max(round(ctx_b / T),
 // ceil(ctx_b / max_chunk)) chunks of ceil32(ctx_b / n_b) keys, so chunks of
-// one sequence are equal and all chunks are close to T.  With seq_chunk_cap,
+// one sequence are equal and all chunks are close to T.  With alt_target_wg
+// (the vector-ALU kernel's long chunks, about one per compute unit), when the
+// longest chunk of that plan is more than 5/4 of the equal share the contexts
+// are too uneven for one chunk per compute unit, whose longest chunk then sets
+// the launch's time, and T comes from alt_target_wg instead (more, shorter
+// chunks, which the dispatcher balances over the compute units).  With seq_chunk_cap,
 // round(ctx_b / T) is first capped at it (fewer, longer chunks).  Fixed mode: chunks of
 // fixed_chunk keys.  A sequence whose seq_pos breaks the contract has no
 // chunks.  Work items (chunks) are laid out sequence-major: for b, for h, for c.
@@ -193,32 +200,24 @@ __host__ __device__ inline bool seq_pos_ok(const AttnParams &p, int sp) {
     return sp >= 0 && sp <= p.max_seq - p.q_len;
 }
 
-// Balanced chunk length for `total` visible keys over all sequences.
-__host__ __device__ inline int balanced_len(const AttnParams &p, int64_t total) {
-    // ceil(total * Hkv / target_wg) clamped to max_chunk, with a 32-bit division
+// Balanced chunk length for `total` visible keys over all sequences and
+// `target` chunks.
+__host__ __device__ inline int balanced_len(const AttnParams &p, int64_t total, int target) {
+    // ceil(total * Hkv / target) clamped to max_chunk, with a 32-bit division
     // whenever the clamp does not decide it (a 64-bit division is a long
     // instruction sequence on this GPU)
     const int64_t x = total * p.n_kv_heads;
     int t;
-    if (x >= (int64_t)p.target_wg * p.max_chunk)
+    if (x >= (int64_t)target * p.max_chunk)
         t = p.max_chunk;
-    else if (__builtin_expect(pow2(p.target_wg), 1))  // the automatic targets: a shift
-        t = (int)((x + p.target_wg - 1) >> __builtin_ctz((unsigned)p.target_wg));
-    else if (x + p.target_wg <= (int64_t)0xffffffffu)
-        t = (int)(((uint32_t)x + (uint32_t)p.target_wg - 1u) / (uint32_t)p.target_wg);
+    else if (__builtin_expect(pow2(target), 1))  // the automatic targets: a shift
+        t = (int)((x + target - 1) >> __builtin_ctz((unsigned)target));
+    else if (x + target <= (int64_t)0xffffffffu)
+        t = (int)(((uint32_t)x + (uint32_t)target - 1u) / (uint32_t)target);
     else
-        t = (int)((x + p.target_wg - 1) / p.target_wg);
+        t = (int)((x + target - 1) / target);
     t = round_up32(t);
     return t < p.min_chunk ? p.min_chunk : (t > p.max_chunk ? p.max_chunk : t);
-}
-
-__host__ __device__ inline int balanced_chunk(const AttnParams &p) {
-    int64_t total = 0;
-    for (int b = 0; b < p.batch; ++b) {
-        const int sp = p.seq_pos[b];
-        if (seq_pos_ok(p, sp)) total += sp + p.q_len;
-    }
-    return balanced_len(p, total);
 }
 
 // Chunks of a sequence whose first new token sits at `sp`, for chunk length T
@@ -246,6 +245,32 @@ __host__ __device__ inline SeqChunks seq_chunks_at(const AttnParams &p, int sp, 
 
 __host__ __device__ inline SeqChunks seq_chunks(const AttnParams &p, int b, int T) {
     return seq_chunks_at(p, p.seq_pos[b], T);
+}
+
+// True when the longest chunk of target_wg's plan (`longest` keys) exceeds 5/4
+// of the equal share ceil(Hkv * total / target_wg): then alt_target_wg's plan
+// is used.  Measured on the vector-ALU kernel's long chunks (batch 32, 8 KV
+// heads, 8 layers, steps by eager launches, target_wg / alt_target_wg):
+// contexts 7k-8k 1209 / 1222 us and 6k-8k 1159 / 1299 us (longest at most
+// 1.14 share), 4k-8k 1084 / 966 us, 2k-8k 1053 / 977 us and 1k-8k 1014 / 824
+// us (1.33 share and more); batch 16 MHA 16 heads at 4k-8k 1028 / 979 us;
+// with two (sequence, KV head) pairs per compute unit, batch 64 at 2k-4k
+// (longest 0.67 share), 1024 / 1064 us.
+__host__ __device__ inline bool long_plan_uneven(const AttnParams &p, int64_t total, int longest) {
+    return (int64_t)4 * longest * p.target_wg > (int64_t)5 * p.n_kv_heads * total;
+}
+
+__host__ __device__ inline int balanced_chunk(const AttnParams &p) {
+    int64_t total = 0;
+    for (int b = 0; b < p.batch; ++b) {
+        const int sp = p.seq_pos[b];
+        if (seq_pos_ok(p, sp)) total += sp + p.q_len;
+    }
+    const int T = balanced_len(p, total, p.target_wg);
+    if (p.alt_target_wg <= 0) return T;
+    int longest = 0;
+    for (int b = 0; b < p.batch; ++b) longest = max(longest, seq_chunks(p, b, T).len);
+    return long_plan_uneven(p, total, longest) ? balanced_len(p, total, p.alt_target_wg) : T;
 }
 
 // Which (b, h, c) work item `w` is; false if w is past the last chunk, and then
@@ -512,14 +537,24 @@ __device__ __forceinline__ int first_seq_pos(const int32_t *__restrict__ seq_pos
 // first_seq_pos()'s value for this lane (the first 64 sequences).
 __device__ inline int balanced_chunk_wave(const AttnParams &p, const int32_t *__restrict__ seq_pos, int batch,
                                           int sp_first, int lane) {
-    int64_t total = wave_sum_i(lane < batch && seq_pos_ok(p, sp_first) ? sp_first + p.q_len : 0);
+    const int sp0 = lane < batch ? sp_first : -1;  // the first 64 sequences
+    int64_t total = wave_sum_i(seq_pos_ok(p, sp0) ? sp0 + p.q_len : 0);
 #pragma unroll 1
     for (int b0 = 64; __builtin_expect(b0 < batch, 0); b0 += 64) {
         const int b = b0 + lane;
         const int sp = b < batch ? seq_pos[b] : -1;
         total += wave_sum_i(seq_pos_ok(p, sp) ? sp + p.q_len : 0);
     }
-    return balanced_len(p, total);
+    const int T = balanced_len(p, total, p.target_wg);
+    if (p.alt_target_wg <= 0) return T;
+    // the longest chunk of that plan (lengths are at most 2^14: exact as floats)
+    float longest = wave_max((float)seq_chunks_at(p, sp0, T).len);
+#pragma unroll 1
+    for (int b0 = 64; __builtin_expect(b0 < batch, 0); b0 += 64) {
+        const int b = b0 + lane;
+        longest = fmaxf(longest, wave_max((float)seq_chunks_at(p, b < batch ? seq_pos[b] : -1, T).len));
+    }
+    return long_plan_uneven(p, total, (int)longest) ? balanced_len(p, total, p.alt_target_wg) : T;
 }
 
 // locate() by a whole wave; also returns the sequence's seq_pos.  Every lane
@@ -531,17 +566,7 @@ __device__ inline int balanced_chunk_wave(const AttnParams &p, const int32_t *__
 __device__ inline bool locate_wave(const AttnParams &p, const int32_t *__restrict__ seq_pos, int batch,
                                    int sp_first, int &w, int &b, int &h, int &c, SeqChunks &sc, int &sp, int lane) {
     const int sp0 = lane < batch ? sp_first : -1;  // the first 64 sequences
-    int T = p.fixed_chunk;
-    if (T <= 0) {
-        int64_t total = wave_sum_i(seq_pos_ok(p, sp0) ? sp0 + p.q_len : 0);
-#pragma unroll 1
-        for (int b0 = 64; __builtin_expect(b0 < batch, 0); b0 += 64) {
-            const int bb = b0 + lane;
-            const int s1 = bb < batch ? seq_pos[bb] : -1;
-            total += wave_sum_i(seq_pos_ok(p, s1) ? s1 + p.q_len : 0);
-        }
-        T = balanced_len(p, total);
-    }
+    const int T = p.fixed_chunk > 0 ? p.fixed_chunk : balanced_chunk_wave(p, seq_pos, batch, sp_first, lane);
     // lane j holds sequence b0 + j, which has `here` items; the item is in the
     // sequence where the inclusive count first passes w
 #pragma unroll 1

@@ -100,6 +100,13 @@ bool valu_long_chunks(int variant, int rows, int units) {
     return variant == DA_VARIANT_VALU && rows <= 2 && units >= 128;
 }
 
+// The alternate target of the long chunks: the chunk plan switches to it
+// when the contexts are too uneven for one chunk per compute unit (see
+// long_plan_uneven).  None with an explicit work_items.
+int alt_target_of(const da_problem *p, int variant, int rows, int units) {
+    return p->work_items == 0 && valu_long_chunks(variant, rows, units) ? default_target(variant, false) : 0;
+}
+
 // Longest chunk a kernel accepts: the vector-ALU kernel keeps the chunk's
 // scores in LDS (rows x chunk floats, at most 64 KiB).
 int max_chunk_of(int variant, int rows, bool long_chunks) {
@@ -224,6 +231,9 @@ void plan_of(const da_problem *p, da_plan *pl) {
         pl->balanced = 1;
         pl->chunk_tokens = max_chunk;
         pl->target_items = p->work_items > 0 ? p->work_items : default_target(variant, long_chunks);
+        // the larger of the two targets the device may plan for
+        const int32_t alt = alt_target_of(p, variant, rows, units);
+        const int32_t target = pl->target_items > alt ? pl->target_items : alt;
         // slots for the most chunks a sequence can get, whatever the seq_pos
         // values: round(ctx / T) with T >= Hkv * (all visible keys) / target
         // (a sequence holds at most all of them) is at most ceil(target / Hkv),
@@ -231,7 +241,7 @@ void plan_of(const da_problem *p, da_plan *pl) {
         // ceil(ctx / max_chunk); never more than one per 64 keys.  max_seq <=
         // 2048 * max_chunk keeps ceil(ctx / max_chunk) within them, so no chunk
         // exceeds max_chunk.
-        const int64_t per_seq_target = ((int64_t)pl->target_items + p->n_kv_heads - 1) / p->n_kv_heads;
+        const int64_t per_seq_target = ((int64_t)target + p->n_kv_heads - 1) / p->n_kv_heads;
         const int64_t per_seq_long = (p->max_seq + max_chunk - 1) / max_chunk;
         int64_t slots = per_seq_target > per_seq_long ? per_seq_target : per_seq_long;
         const int64_t by_min = (p->max_seq + kMinChunk - 1) / kMinChunk;
@@ -239,7 +249,7 @@ void plan_of(const da_problem *p, da_plan *pl) {
         pl->n_chunks = (int32_t)(slots < kMaxChunks ? slots : kMaxChunks);
         // at most target + one rounding chunk per (sequence, head), or every
         // sequence in chunks of max_chunk keys when the target is too few
-        const int64_t a = (int64_t)pl->target_items + units;
+        const int64_t a = (int64_t)target + units;
         const int64_t b = (int64_t)units * ((p->max_seq + max_chunk - 1) / max_chunk);
         pl->items = (int32_t)(a > b ? a : b);
     }
@@ -315,6 +325,7 @@ AttnParams attn_params(const da_problem *p, const da_plan &pl, const void *q, co
     a.n_chunks = pl.n_chunks;
     a.fixed_chunk = pl.balanced ? 0 : pl.chunk_tokens;
     a.target_wg = pl.target_items;
+    a.alt_target_wg = pl.balanced ? alt_target_of(p, pl.variant, pl.rows, p->batch * p->n_kv_heads) : 0;
     a.min_chunk = kMinChunk;
     a.max_chunk = pl.chunk_tokens;
     const double scale = p->scale > 0.f ? (double)p->scale : 1.0 / sqrt((double)p->head_dim);

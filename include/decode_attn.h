@@ -154,7 +154,9 @@ typedef struct {
  * same chunks from the same seq_pos.  A chunk is the work of one workgroup of
  * 4 waves.  On the vector-ALU kernel, with at most 2 rows per KV head and at
  * least 128 (sequence, KV head) pairs, chunks go up to 8192 keys (about 256 of
- * them).
+ * them), unless the contexts are so uneven that the longest of those chunks
+ * would exceed 5/4 of an equal share: then about 1024 shorter chunks (automatic
+ * targets only; the plan's workspace and grid hold either).
  */
 typedef struct {
     int32_t chunk_tokens;    /* longest chunk (fixed mode: every chunk)          */

@@ -89,10 +89,12 @@ def test_plan_is_pure_and_sized():
     assert a == b
     rows = 2
     assert a["balanced"] and a["variant"] == "valu"
-    # slots for the most chunks one sequence can get: the 256 aimed at over 8 KV heads
-    assert a["n_chunks"] == 256 // 8
+    # long chunks aim at 256; slots and grid hold the most chunks of the plan for
+    # uneven contexts, which aims at 1024 (over 8 KV heads: 128 per sequence)
+    assert a["target_items"] == 256 and a["chunk_tokens"] == 8192
+    assert a["n_chunks"] == 1024 // 8
     assert a["workspace_bytes"] >= 32 * 8 * a["n_chunks"] * rows * (128 + 2) * 4
-    assert a["items"] >= a["target_items"] + 32 * 8
+    assert a["items"] >= 1024 + 32 * 8
     assert da.plan_attention(P(q_len=4, n_q_heads=32, n_kv_heads=4))["variant"] == "mfma"
     fixed = da.plan_attention(P(chunk_tokens=128))
     assert not fixed["balanced"] and fixed["chunk_tokens"] == 128 and fixed["n_chunks"] == 8

@@ -141,3 +141,33 @@ def test_mfma128_chunks_start_on_512k_boundaries():
     sp = rng.integers(12287, 16384, 4).astype(np.int32)
     _, lay, _ = check_layout(p, sp)
     assert any(ln % 2048 for _, ln in lay)
+
+
+def test_long_chunks_fall_back_on_uneven_contexts():
+    """The vector-ALU kernel's long chunks (up to 2 rows, at least 128 (sequence, KV
+    head) pairs) aim at one chunk per compute unit, unless the contexts are so uneven
+    that the longest chunk of that plan exceeds 5/4 of an equal share: then the plan
+    aims at 1024 shorter chunks."""
+    p = da.problem(32, 1, 16, 8, 128, 8192, "bf16")
+    rng = np.random.default_rng(5)
+
+    def lengths(sp):
+        _, lay, total = check_layout(p, sp)
+        return [ln for _, ln in lay], total
+
+    full = np.full(32, 8191, np.int32)
+    lens, total = lengths(full)
+    assert set(lens) == {8192} and total == 32 * 8
+    near = rng.integers(6143, 8192, 32).astype(np.int32)  # longest chunk under 5/4 of the share
+    near[0] = 8191
+    lens, total = lengths(near)
+    assert total == 32 * 8 and max(lens) == 8192
+    wide = rng.integers(1023, 8192, 32).astype(np.int32)
+    wide[0] = 8191
+    lens, total = lengths(wide)
+    share = -(-8 * int((wide + 1).sum()) // 1024)  # keys per chunk for 1024 chunks
+    # round(ctx / T) chunks of ceil32(ctx / n) keys: at most 1.5 T, rounded up
+    assert total > 512 and max(lens) <= 1.5 * (share + 31) + 32
+    # an explicit target keeps its own plan
+    q = da.problem(32, 1, 16, 8, 128, 8192, "bf16", work_items=256)
+    assert max(ln for _, ln in da.chunk_layout(q, wide)) > 2 * share
