@@ -267,7 +267,8 @@ __host__ __device__ inline int balanced_chunk(const AttnParams &p) {
         if (seq_pos_ok(p, sp)) total += sp + p.q_len;
     }
     const int T = balanced_len(p, total, p.target_wg);
-    if (p.alt_target_wg <= 0) return T;
+    // no chunk exceeds max_chunk: when that is even, the plan stands unchecked
+    if (p.alt_target_wg <= 0 || !long_plan_uneven(p, total, p.max_chunk)) return T;
     int longest = 0;
     for (int b = 0; b < p.batch; ++b) longest = max(longest, seq_chunks(p, b, T).len);
     return long_plan_uneven(p, total, longest) ? balanced_len(p, total, p.alt_target_wg) : T;
@@ -546,7 +547,9 @@ __device__ inline int balanced_chunk_wave(const AttnParams &p, const int32_t *__
         total += wave_sum_i(seq_pos_ok(p, sp) ? sp + p.q_len : 0);
     }
     const int T = balanced_len(p, total, p.target_wg);
-    if (p.alt_target_wg <= 0) return T;
+    // no chunk exceeds max_chunk: when that is even, the plan stands unchecked
+    // (8192-key contexts on 8 KV heads of 32 sequences: no pass over the sequences)
+    if (p.alt_target_wg <= 0 || !long_plan_uneven(p, total, p.max_chunk)) return T;
     // the longest chunk of that plan (lengths are at most 2^14: exact as floats)
     float longest = wave_max((float)seq_chunks_at(p, sp0, T).len);
 #pragma unroll 1
