@@ -458,6 +458,25 @@ def test_valu_long_chunks(B, Hq, Hkv, S, dtype, seed):
     gu.check_layer(p, inp)
 
 
+
+def test_valu_long_chunks_uneven_many_sequences():
+    """130 sequences (three groups of 64 positions for every workgroup's chunk plan) whose
+    contexts are so uneven that the long plan's longest chunk exceeds 5/4 of an equal
+    share: every kernel switches to the plan for 1024 chunks, on every path."""
+    B, S = 130, 400
+    rng = np.random.default_rng(31)
+    sp = rng.integers(0, 60, B).astype(np.int32)
+    sp[[5, 70, 129]] = S - 1
+    _say("valu long chunks, uneven, many sequences", B, S)
+    inp = gu.make_case(B, 1, 16, 8, S, sp, seed=31)
+    p = da.problem_for(inp["q"], inp["k_cache"])
+    pl = da.plan_attention(p)
+    assert pl["variant"] == "valu" and pl["target_items"] == 256 and pl["chunk_tokens"] == 8192
+    lay = da.chunk_layout(p, sp)
+    assert max(n for n, _ in lay) > 1  # the long sequences are split: the shorter plan
+    gu.check_layer(p, inp)
+
+
 def test_valu_merge_split_over_waves():
     """More than 16 chunks and fewer than 4 rows: the merge splits each row's chunks over the
     4 waves (fixed 64-key chunks)."""
