@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     # the first tenth of a second or so of sustained load runs up to 5% slow (the
-    # headline step's first 5-20 replays in a process take 4.6 ms, the rest 4.4 ms):
+    # default workload's first 5-20 steps in a process take 4.6 ms, the rest 4.4 ms):
     # the default warm-up covers it
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default=None)
@@ -504,7 +504,7 @@ def main():
 
     if configs == "all":
         # Every other workload runs in a child process of its own, as it would run
-        # alone: measured after the headline's 30 GB in this process, the same kernels
+        # alone: measured after the default workload's 30 GB in this process, the same kernels
         # took 4-5% longer (where the caching allocator then places a workload's
         # caches changes its streaming rate).
         del b

@@ -344,9 +344,9 @@ __global__ __launch_bounds__(64 * kValuWaves) void attn_split_valu_kernel(const 
     };
     // A wave per row; with fewer rows than waves and at least 1024 keys, every
     // wave takes keys wave*64 + lane, + NW*64, ... of every row instead, and the
-    // waves' maxima and sums meet in LDS (a fixed-order sum): on the headline
-    // layer's 8192-key chunks (2 rows) 152.9 against 153.7 us, where a wave per
-    // row left two waves idle.
+    // waves' maxima and sums meet in LDS (a fixed-order sum): on 8192-key chunks
+    // of 2 rows (batch 32, 8 KV heads) 152.9 against 153.7 us a launch, where a
+    // wave per row left two waves idle.
     if (RP >= NW || n_pad < 1024) {
         for (int r = wave; r < RP; r += NW) {
             const float m = wave_max(row_max(r, lane, 64));

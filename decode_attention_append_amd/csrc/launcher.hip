@@ -91,11 +91,11 @@ int default_target(int variant, bool long_chunks) {
 // slabs in flight, keep 32 KiB of non-temporal loads in flight per compute
 // unit, where a loads-only probe streams best.  Measured against 8-wave
 // workgroups on the same chunks (64 KiB in flight), steps by eager launches:
-// the headline layer (batch 32, 8 KV heads, 8192 keys, 28 layers) 4.28 against
+// batch 32, 8 KV heads, 8192 keys, 2 rows, 28 layers 4.28 against
 // 4.40 ms; batch 64 at 4k 1258 / 1268 us for 8 layers, batch 32 MHA at 2k 641
 // / 653 us, batch 16 at 16k 622 / 635 us for 4 layers, batch 4 MHA 32 heads at
 // 4k and batch 32 at ragged 1k-8k contexts equal (two runs each); 16 waves
-// were slower still (161.5 against 158.2 us a headline layer).
+// were slower still (161.5 against 158.2 us a layer of that step).
 bool valu_long_chunks(int variant, int rows, int units) {
     return variant == DA_VARIANT_VALU && rows <= 2 && units >= 128;
 }
